@@ -1,0 +1,233 @@
+"""Benchmark of the paged-attention step on one MI355X.
+
+One step = the cache write of the batch's new K/V rows followed by paged
+attention of its query rows, both through the C ABI on torch's current
+stream.  Default workload: the Llama-3-70B-shaped GQA decode layer (256
+requests, 64 query / 8 KV heads, D=128, bf16, log-normal contexts with median
+1024 clipped to [16, 8192], shuffled 16-token blocks).
+
+Prints one JSON line.  ``value`` is KV GB/s: the attention's algorithmic
+K/V bytes per step divided by the step time (inputs resident in HBM).
+``roofline`` reports the attention launch alone (split-K decode + merge),
+timed with HIP events on the launch stream.  ``cpu_baseline`` times the fp64
+CPU oracle on a bounded sample of the same requests.  Parity of this exact
+launch configuration against the oracle is the job of the GPU tests; the
+oracle is used here only for the CPU baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def algorithmic_bytes(c) -> dict:
+    """Bytes the attention must move for this batch (no re-reads, no partial-block over-read)."""
+    s = 2 if c.dtype == "bf16" else 4
+    L = c.seq_lens.astype(np.int64)
+    n = c.q_lens.astype(np.int64)
+    kv = int((L * c.num_kv_heads * c.head_dim * 2 * s).sum())
+    q = int(n.sum() * c.num_q_heads * c.head_dim * s)
+    o = q
+    tables = int(4 * (-(-L // 16)).sum())
+    meta = 4 * (2 * c.num_seqs + 1)
+    cw = int(2 * 2 * (c.slot_mapping >= 0).sum() * c.num_kv_heads * c.head_dim * s + 8 * c.total_q)
+    return dict(kv=kv, q=q, o=o, tables=tables, meta=meta, attention=kv + q + o + tables + meta, cache_write=cw)
+
+
+def attention_flops(c) -> float:
+    """4 * D * Hq per (row, visible key)."""
+    L = c.seq_lens.astype(np.int64)
+    n = c.q_lens.astype(np.int64)
+    keys = 0
+    for Lb, nb in zip(L, n):
+        keys += int(nb * (Lb - nb) + nb * (nb + 1) // 2)
+    return 4.0 * c.head_dim * c.num_q_heads * keys
+
+
+def cpu_baseline(c, budget_s: float = 12.0) -> dict:
+    """Time the fp64 oracle on whole requests until the budget is spent (one BLAS thread)."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limit = None
+    kp, vp = oracle.oracle_cache_write(c.k_cache, c.v_cache, c.k_new, c.v_new, c.slot_mapping)
+    order = np.random.default_rng(1).permutation(c.num_seqs)
+    s = 2 if c.dtype == "bf16" else 4
+    done_rows = done_kv = 0
+    t0 = time.perf_counter()
+    reqs = 0
+    for b in order:
+        rows = list(range(int(c.cu_seqlens[b]), int(c.cu_seqlens[b + 1])))
+        if not rows:
+            continue
+        oracle.oracle_attention_varlen(c.q, kp, vp, c.cu_seqlens, c.seq_lens, c.block_tables, c.scale,
+                                       c.num_kv_heads, c.dtype, rows=rows, validate=False)
+        done_rows += len(rows)
+        done_kv += int(c.seq_lens[b]) * c.num_kv_heads * c.head_dim * 2 * s
+        reqs += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    if limit is not None:
+        limit.unregister() if hasattr(limit, "unregister") else None
+    return {"value": done_kv / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reqs} of {c.num_seqs} requests ({done_rows} query rows, "
+                      f"{done_kv / 1e9:.3f} GB of KV) in {dt:.1f} s, fp64 NumPy, one BLAS thread",
+            "query_tokens_per_s": done_rows / dt}
+
+
+class _DeviceBatch:
+    """The workload's arrays in HBM, and the two ABI calls of one step."""
+
+    def __init__(self, c, torch, pa):
+        self.c, self.torch, self.pa = c, torch, pa
+
+        def dev(a):
+            if c.dtype == "bf16":
+                return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+            return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+        self.q, self.k_cache, self.v_cache = dev(c.q), dev(c.k_cache), dev(c.v_cache)
+        self.k_new, self.v_new = dev(c.k_new), dev(c.v_new)
+        self.slots = torch.from_numpy(c.slot_mapping).to("cuda:0")
+        self.cu = torch.from_numpy(c.cu_seqlens).to("cuda:0")
+        self.seq_lens = torch.from_numpy(c.seq_lens).to("cuda:0")
+        self.tables = torch.from_numpy(c.block_tables).to("cuda:0")
+        self.out = torch.empty_like(self.q)
+        self.ws = None
+
+    def cache_write(self):
+        self.pa.cache_write(self.k_new, self.v_new, self.k_cache, self.v_cache, self.slots)
+
+    def attention(self, partition_size):
+        c = self.c
+        if self.ws is None:
+            p = self.pa.make_params(self.q, self.k_cache, self.cu, self.tables, c.num_kv_heads, float(c.scale),
+                                    c.max_query_len, c.max_seq_len, out=self.out, partition_size=partition_size)
+            self.ws = self.torch.empty(max(16, self.pa.workspace_size(p)), dtype=self.torch.uint8, device="cuda:0")
+        self.pa.attention_varlen(self.out, self.q, self.k_cache, self.v_cache, self.cu, self.seq_lens, self.tables,
+                                 float(c.scale), c.max_query_len, c.max_seq_len, workspace=self.ws,
+                                 partition_size=partition_size)
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gqa_decode_bf16")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_371_amd as pa
+    from workloads import make_config
+
+    c = make_config(args.workload, args.seed, poison=False)
+    dc = _DeviceBatch(c, torch, pa)
+    ab = algorithmic_bytes(c)
+    flops = attention_flops(c)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        dc.cache_write()
+        dc.attention(partition_size=args.partition_size)
+
+    step()
+    torch.cuda.synchronize()
+    if not bool(torch.isfinite(dc.out.float()).all()):
+        raise SystemExit("non-finite attention output")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        dc.cache_write()
+        ev[i][0].record(stream)
+        dc.attention(partition_size=args.partition_size)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms_per_step = wall * 1e3 / args.steps
+
+    value = ab["kv"] / (ms_per_step * 1e-3) / 1e9
+    achieved = ab["attention"] / (attn_ms * 1e-3) / 1e9
+    result = {
+        "metric": "paged-attn decode KV GB/s (% of HBM peak) and query tokens/s at 1 MI355X",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": c.name,
+            "seed": args.seed,
+            "num_seqs": c.num_seqs,
+            "total_q": c.total_q,
+            "num_q_heads": c.num_q_heads,
+            "num_kv_heads": c.num_kv_heads,
+            "head_dim": c.head_dim,
+            "block_size": c.block_size,
+            "num_blocks": c.num_blocks,
+            "mean_context": float(c.seq_lens.mean()),
+            "partition_size": args.partition_size or 512,
+            "step": "cache_write + attention_varlen",
+        },
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "query_tokens_per_s": round(c.total_q / (ms_per_step * 1e-3), 1),
+        "attention_ms": round(attn_ms, 5),
+        "kv_bytes_per_step": ab["kv"],
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "attention launch (decode_kernel + merge_kernel)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": ab["attention"],
+            "attention_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(c, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+/*
+ * pa.h -- C ABI of the paged-attention library for MI355X (gfx950).
+ *
+ * Two device operations make up one step of attention over a paged KV cache:
+ *
+ *   pa_cache_write       scatter this step's new K/V rows into the block pool
+ *                        through slot_mapping;
+ *   pa_attention_varlen  causal softmax attention of packed query rows over
+ *                        the pool, reached through per-request block tables.
+ *
+ * Sources, cited by page title and section:
+ *   [Q67]  quant67, "【大模型基础设施工程】12：PagedAttention 与 Continuous
+ *          Batching": §3.2 (KV cut into fixed-size blocks, logical->physical
+ *          mapping through a block table), §3.3 (data structures, the worked
+ *          address example, and the per-step order: compute the new token's
+ *          K/V, append it to its block, then attend through the block table),
+ *          §3.6 (the kernel walks block_table[seq][i] and accumulates an
+ *          online softmax), §3.7 (16 tokens per block), §4.2 (chunked prefill
+ *          mixes prompt chunks with decode rows), §8.3 (bytes per block count
+ *          every KV head).
+ *   [ICE]  ice-wocker, "推理优化与服务：从 PagedAttention 到分离式部署", latest
+ *          developments: scheduled query tokens packed as [total_q, H, D]
+ *          with cu_seqlens request boundaries, so one forward runs mixed
+ *          prefill and decode.
+ *
+ * Conventions shared by every call (this library's reading of the pages):
+ *   - Pools: K and V are separate device arrays [num_blocks, Hkv, 16, D],
+ *     row-major.  One block id covers every KV head ([Q67] §8.3); each
+ *     (block, head) tile of 16 x D elements is contiguous.
+ *   - slot = physical_block * 16 + offset ([Q67] §3.3: token 18 of table
+ *     [17, 42] lives in block 42 at offset 2, slot 674).
+ *   - Request b owns packed query rows cu_seqlens[b] .. cu_seqlens[b+1]-1
+ *     ([ICE]).  Its context length seq_lens[b] = L_b already counts those
+ *     rows (new K/V are written before attention reads them, [Q67] §3.3).
+ *     Row j (0-based within the request, n_b rows) is the token at position
+ *     L_b - n_b + j and attends to keys 0 .. L_b - n_b + j (bottom-right
+ *     causal alignment; a decode row sees all L_b keys).
+ *   - GQA: query head h reads KV head h / G, G = num_q_heads / num_kv_heads.
+ *   - q, out, the pools and the new rows share one element type (pa_dtype).
+ *     Accumulation is fp32; bf16 results are rounded to nearest even.
+ *
+ * Pointers are DEVICE pointers unless marked host.  The library allocates
+ * nothing and keeps no state between calls; the caller owns every buffer.
+ * Both hot calls only enqueue work on `stream` (a hipStream_t passed as
+ * void*, NULL = the null stream) and return; they never synchronise, read
+ * device memory from the host, or allocate, so they can be captured in a HIP
+ * graph.  Buffers must stay alive until the stream's work completes.
+ * Host-checkable preconditions are checked first; on failure a negative
+ * status is returned and nothing is enqueued.  Device metadata (slots, block
+ * ids, lengths) is trusted on the hot path; pa_validate_metadata checks it.
+ * No C++ exception crosses this interface.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_BLOCK_SIZE 16
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,         /* a required pointer is NULL */
+  PA_ERR_SHAPE = -2,        /* a size is out of range or inconsistent */
+  PA_ERR_UNSUPPORTED = -3,  /* dtype / head_dim / group size / block size not built */
+  PA_ERR_ALIGN = -4,        /* pointer or row stride not 16-byte aligned */
+  PA_ERR_WORKSPACE = -5,    /* workspace missing or smaller than required */
+  PA_ERR_LAUNCH = -6,       /* the HIP runtime rejected a kernel launch */
+  PA_ERR_METADATA = -7      /* pa_validate_metadata found a bad entry */
+} pa_status;
+
+typedef enum {
+  PA_F32 = 0,   /* IEEE fp32 */
+  PA_BF16 = 1   /* bfloat16 */
+} pa_dtype;
+
+/* Host struct describing one pa_attention_varlen call. */
+typedef struct {
+  int32_t num_seqs;            /* B >= 0 */
+  int64_t total_q;             /* packed query rows, = cu_seqlens_q[B] */
+  int32_t num_q_heads;         /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;        /* Hkv */
+  int32_t head_dim;            /* D: 64 or 128 */
+  int32_t block_size;          /* must be 16 */
+  int64_t num_blocks;          /* physical blocks in each pool */
+  int32_t max_blocks_per_seq;  /* row length of block_tables */
+  int32_t max_query_len;       /* host bound: >= every n_b */
+  int32_t max_seq_len;         /* host bound: >= every L_b */
+  int64_t q_row_stride;        /* elements between consecutive packed rows of q  (>= Hq*D) */
+  int64_t o_row_stride;        /* elements between consecutive packed rows of out (>= Hq*D) */
+  float scale;                 /* softmax scale, usually 1/sqrt(D) */
+  pa_dtype dtype;
+  int32_t partition_size;      /* tokens per split-K context partition; 0 = library
+                                  default (512); else a multiple of 64 in [64, 8192] */
+} pa_attn_params;
+
+/*
+ * pa_cache_write -- [Q67] §3.3: each new token's K and V are appended to the
+ * block that holds its position.
+ *
+ * For every row i < num_tokens with slot_mapping[i] >= 0 and every KV head h:
+ *   k_cache[s/16][h][s%16][:] = k_new[i*kv_row_stride + h*D + :]
+ *   v_cache[s/16][h][s%16][:] = v_new[i*kv_row_stride + h*D + :]
+ * with s = slot_mapping[i].  Rows with a negative slot are skipped.  The
+ * copy is bit-exact.  Slots must be unique and < num_blocks*16 (not checked
+ * here).  k_new/v_new: [num_tokens, Hkv, D] rows kv_row_stride elements
+ * apart (>= Hkv*D).  k_cache, v_cache: [num_blocks, Hkv, 16, D] in place.
+ * num_tokens == 0 is a no-op.  Errors: NULL pointers (when num_tokens > 0),
+ * non-positive sizes, block_size != 16, D not in {64, 128}, unaligned
+ * pointers or stride.
+ */
+pa_status pa_cache_write(const void* k_new, const void* v_new, int64_t kv_row_stride,
+                         void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                         int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int64_t num_blocks, pa_dtype dtype,
+                         void* stream);
+
+/*
+ * Bytes of device workspace pa_attention_varlen needs for these parameters
+ * (0 when no request can span more than one context partition).  Returns
+ * 0 as well for invalid parameters; pa_attention_varlen reports those.
+ */
+size_t pa_attention_workspace_size(const pa_attn_params* p);
+
+/*
+ * pa_attention_varlen -- [Q67] §3.6 and [ICE]: for every request b, row j,
+ * query head h:
+ *   s_t = scale * <q[row, h, :], K_b[t, h/G, :]>       for t <= L_b - n_b + j
+ *   out[row, h, :] = sum_t softmax(s)_t * V_b[t, h/G, :]
+ * where K_b[t] = k_cache[block_tables[b][t/16]][h/G][t%16] (same for V) and
+ * row = cu_seqlens_q[b] + j.
+ *
+ *   out           [total_q, Hq, D] rows o_row_stride elements apart (written)
+ *   q             [total_q, Hq, D] rows q_row_stride elements apart
+ *   k_cache/v_cache  pools as above (read only)
+ *   cu_seqlens_q  int32 [B+1], [0] = 0, nondecreasing, [B] = total_q
+ *   seq_lens      int32 [B], L_b >= n_b = cu[b+1]-cu[b]; n_b == 0 is allowed
+ *   block_tables  int32 [B, max_blocks_per_seq]; entries at or past
+ *                 ceil(L_b/16) are never read
+ *   workspace     device scratch of >= pa_attention_workspace_size(p) bytes
+ *                 (may be NULL when that size is 0); contents need no init
+ *
+ * Requests with one row run on the split-K decode kernels; in bf16, requests
+ * with more rows run on the MFMA prefill kernel.  Results do not depend on
+ * the other requests in the batch or on block placement.  `out` must not
+ * alias q or the pools.
+ */
+pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                              const int32_t* block_tables, const pa_attn_params* p,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bits of the result word written by pa_validate_metadata. */
+#define PA_BAD_CU_SEQLENS   1   /* cu[0] != 0, cu decreasing, or cu[B] != total_q */
+#define PA_BAD_LENGTHS      2   /* n_b > L_b, L_b < 0, n_b > max_query_len or L_b > max_seq_len */
+#define PA_BAD_TABLE_WIDTH  4   /* ceil(L_b/16) > max_blocks_per_seq */
+#define PA_BAD_BLOCK_ID     8   /* a used block-table entry outside [0, num_blocks) */
+#define PA_BAD_SLOT_RANGE  16   /* a slot >= num_blocks*16 */
+#define PA_BAD_SLOT_DUP    32   /* two rows share a non-negative slot */
+
+/*
+ * pa_validate_metadata -- debugging aid for the device-resident metadata
+ * the hot calls trust.  Enqueues checks on `stream` and returns; when the
+ * stream's work is done, *result (DEVICE, one int32 owned by the caller)
+ * holds the OR of the PA_BAD_* bits of every failed check, 0 if all pass.
+ * slot_mapping may be NULL (num_slots ignored); the duplicate-slot check is
+ * quadratic in num_slots.  Host-side errors as for pa_attention_varlen.
+ */
+pa_status pa_validate_metadata(const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                               const int32_t* block_tables, const int64_t* slot_mapping,
+                               int64_t num_slots, const pa_attn_params* p,
+                               int32_t* result, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* pa_status_string(pa_status s);
+
+/* ABI version of this header: major*100 + minor. */
+int32_t pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

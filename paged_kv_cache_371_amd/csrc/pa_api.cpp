@@ -1,0 +1,196 @@
+// C ABI of the paged-attention library: argument checks, kernel choice,
+// grid and workspace sizing, launch on the caller's stream.  See include/pa.h
+// for the contract of each entry point.
+#include "../../include/pa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "pa_internal.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int elem_bytes(pa_dtype d) { return d == PA_BF16 ? 2 : 4; }
+
+inline bool dtype_ok(pa_dtype d) { return d == PA_F32 || d == PA_BF16; }
+
+inline int effective_partition(const pa_attn_params* p) {
+  return p->partition_size > 0 ? p->partition_size : pa::kDefaultPartition;
+}
+
+// Requests with more than one row take the MFMA prefill kernel in bf16 when
+// it is built for this (D, G); the decode kernel serves every other request.
+inline bool use_prefill(const pa_attn_params* p) {
+  return p->dtype == PA_BF16 && p->max_query_len > 1 &&
+         pa::prefill_supported(p->head_dim, p->num_q_heads / p->num_kv_heads);
+}
+
+inline int64_t partial_rows(const pa_attn_params* p) {
+  return use_prefill(p) ? int64_t(p->num_seqs) : p->total_q;
+}
+
+inline int64_t max_parts(const pa_attn_params* p) {
+  const int ps = effective_partition(p);
+  return p->max_seq_len > 0 ? (int64_t(p->max_seq_len) + ps - 1) / ps : 1;
+}
+
+pa_status check_params(const pa_attn_params* p) {
+  if (!p) return PA_ERR_NULL;
+  if (!dtype_ok(p->dtype)) return PA_ERR_UNSUPPORTED;
+  if (p->block_size != PA_BLOCK_SIZE) return PA_ERR_UNSUPPORTED;
+  if (p->num_seqs < 0 || p->total_q < 0 || p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->head_dim <= 0 ||
+      p->num_blocks <= 0 || p->max_blocks_per_seq <= 0 || p->max_query_len < 0 || p->max_seq_len < 0)
+    return PA_ERR_SHAPE;
+  if (p->num_q_heads % p->num_kv_heads) return PA_ERR_SHAPE;
+  if (p->num_seqs > 65535) return PA_ERR_SHAPE;
+  if (p->max_query_len > p->max_seq_len) return PA_ERR_SHAPE;
+  if (int64_t(p->max_blocks_per_seq) * PA_BLOCK_SIZE < p->max_seq_len) return PA_ERR_SHAPE;
+  if (p->total_q > 0 && p->num_seqs == 0) return PA_ERR_SHAPE;
+  const int64_t hd = int64_t(p->num_q_heads) * p->head_dim;
+  if (p->q_row_stride < hd || p->o_row_stride < hd) return PA_ERR_SHAPE;
+  if (!std::isfinite(p->scale)) return PA_ERR_SHAPE;
+  const int g = p->num_q_heads / p->num_kv_heads;
+  const int ps = effective_partition(p);
+  if (p->partition_size != 0 && (p->partition_size < 16 || p->partition_size % 16)) return PA_ERR_SHAPE;
+  if (!pa::decode_supported(p->dtype == PA_BF16 ? 1 : 0, p->head_dim, g, ps)) return PA_ERR_UNSUPPORTED;
+  const int eb = elem_bytes(p->dtype);
+  if ((p->q_row_stride * eb) % 16 || (p->o_row_stride * eb) % 16) return PA_ERR_ALIGN;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_abi_version(void) { return 100; }
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK: success";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: a size is out of range or inconsistent";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: dtype, head_dim, group size or block size not built";
+    case PA_ERR_ALIGN: return "PA_ERR_ALIGN: pointer or row stride not 16-byte aligned";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: kernel launch failed";
+    case PA_ERR_METADATA: return "PA_ERR_METADATA: device metadata failed validation";
+  }
+  return "unknown pa_status";
+}
+
+pa_status pa_cache_write(const void* k_new, const void* v_new, int64_t kv_row_stride, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int64_t num_blocks, pa_dtype dtype, void* stream) {
+  if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
+  if (block_size != PA_BLOCK_SIZE) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+  if (kv_row_stride < int64_t(num_kv_heads) * head_dim) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+  const int eb = elem_bytes(dtype);
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (kv_row_stride * eb) % 16)
+    return PA_ERR_ALIGN;
+  hipError_t e = pa::launch_cache_write(k_new, v_new, kv_row_stride * eb, k_cache, v_cache, slot_mapping, num_tokens,
+                                        num_kv_heads, head_dim * eb, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+size_t pa_attention_workspace_size(const pa_attn_params* p) {
+  if (check_params(p) != PA_OK) return 0;
+  const int64_t parts = max_parts(p);
+  if (parts <= 1) return 0;
+  const int64_t rows = partial_rows(p);
+  return size_t(rows) * p->num_q_heads * parts * (p->head_dim + 2) * sizeof(float);
+}
+
+pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* cu_seqlens_q, const int32_t* seq_lens, const int32_t* block_tables,
+                              const pa_attn_params* p, void* workspace, size_t workspace_bytes, void* stream) {
+  pa_status st = check_params(p);
+  if (st != PA_OK) return st;
+  if (p->num_seqs == 0 || p->total_q == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !cu_seqlens_q || !seq_lens || !block_tables) return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
+  const size_t need = pa_attention_workspace_size(p);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return PA_ERR_ALIGN;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int g = p->num_q_heads / p->num_kv_heads;
+  const int ps = effective_partition(p);
+  const int64_t parts = max_parts(p);
+  const int64_t prows = partial_rows(p);
+  const bool prefill = use_prefill(p);
+  const float scale_log2 = p->scale * kLog2e;
+
+  pa::DecodeArgs d{};
+  d.out = out;
+  d.q = q;
+  d.k_cache = k_cache;
+  d.v_cache = v_cache;
+  d.cu_seqlens = cu_seqlens_q;
+  d.seq_lens = seq_lens;
+  d.block_tables = block_tables;
+  d.ws_o = static_cast<float*>(workspace);
+  d.ws_ml = parts > 1 ? static_cast<float*>(workspace) + prows * p->num_q_heads * parts * p->head_dim : nullptr;
+  d.q_row_stride = p->q_row_stride;
+  d.o_row_stride = p->o_row_stride;
+  d.num_seqs = p->num_seqs;
+  d.num_q_heads = p->num_q_heads;
+  d.num_kv_heads = p->num_kv_heads;
+  d.max_blocks_per_seq = p->max_blocks_per_seq;
+  d.part_size = ps;
+  d.max_parts = int32_t(parts);
+  d.scale_log2 = scale_log2;
+  d.single_row_only = prefill ? 1 : 0;
+  d.partial_by_seq = prefill ? 1 : 0;
+  if (parts > 65535) return PA_ERR_SHAPE;
+
+  hipError_t e = pa::launch_decode(p->dtype == PA_BF16 ? 1 : 0, p->head_dim, g, d, parts > 1 ? prows : 0, s);
+  if (e != hipSuccess) return PA_ERR_LAUNCH;
+  if (prefill) {
+    pa::PrefillArgs f{};
+    f.out = out;
+    f.q = q;
+    f.k_cache = k_cache;
+    f.v_cache = v_cache;
+    f.cu_seqlens = cu_seqlens_q;
+    f.seq_lens = seq_lens;
+    f.block_tables = block_tables;
+    f.q_row_stride = p->q_row_stride;
+    f.o_row_stride = p->o_row_stride;
+    f.num_seqs = p->num_seqs;
+    f.num_q_heads = p->num_q_heads;
+    f.num_kv_heads = p->num_kv_heads;
+    f.max_blocks_per_seq = p->max_blocks_per_seq;
+    const int rpt = pa::prefill_rows_per_tile(p->head_dim, g);
+    f.m_tiles = (p->max_query_len + rpt - 1) / rpt;
+    f.scale_log2 = scale_log2;
+    e = pa::launch_prefill(p->head_dim, g, f, s);
+    if (e != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  return PA_OK;
+}
+
+pa_status pa_validate_metadata(const int32_t* cu_seqlens_q, const int32_t* seq_lens, const int32_t* block_tables,
+                               const int64_t* slot_mapping, int64_t num_slots, const pa_attn_params* p,
+                               int32_t* result, void* stream) {
+  if (!p || !result) return PA_ERR_NULL;
+  if (p->num_seqs < 0 || p->total_q < 0 || p->num_blocks <= 0 || p->max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  if (p->num_seqs > 0 && (!cu_seqlens_q || !seq_lens || !block_tables)) return PA_ERR_NULL;
+  if (!slot_mapping) num_slots = 0;
+  if (num_slots < 0) return PA_ERR_SHAPE;
+  hipError_t e = pa::launch_validate(cu_seqlens_q, seq_lens, block_tables, slot_mapping, num_slots, p->num_seqs,
+                                     p->total_q, p->max_query_len, p->max_seq_len, p->max_blocks_per_seq,
+                                     p->num_blocks, result, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,123 @@
+"""The C-ABI library loads, exports what include/pa.h declares, and rejects
+bad arguments on the host before touching the GPU (CPU only)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_kv_cache_371_amd as pa
+
+pytestmark = pytest.mark.cpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(pa.lib_path()):
+        pytest.skip("libpa.so not built")
+    return pa.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    declared = _declared_functions()
+    assert declared, "no declarations parsed"
+    assert sorted(pa.exported_symbols()) == declared
+    for name in declared:
+        assert hasattr(L, name)
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.lib_path()], capture_output=True, text=True).stdout
+    for name in declared:
+        assert re.search(rf"\bT {name}$", out, re.M), name
+
+
+def test_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "pa.h"\n'
+        "int main(void){printf(\"%zu\", sizeof(pa_attn_params));\n"
+        + "".join(f'printf(" %zu", offsetof(pa_attn_params, {f}));\n' for f, _ in pa.AttnParams._fields_)
+        + "return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", f"-I{os.path.dirname(HEADER)}", str(src), "-o", str(exe)], check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(pa.AttnParams)
+    assert vals[1:] == [getattr(pa.AttnParams, f).offset for f, _ in pa.AttnParams._fields_]
+
+
+def test_status_strings_and_version(L):
+    assert L.pa_abi_version() == 100
+    for code in range(0, -8, -1):
+        s = L.pa_status_string(code).decode()
+        assert s.startswith("PA_")
+    assert L.pa_status_string(-99).decode() == "unknown pa_status"
+
+
+def _params(**over):
+    p = pa.AttnParams()
+    vals = dict(num_seqs=2, total_q=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, num_blocks=10,
+                max_blocks_per_seq=4, max_query_len=1, max_seq_len=64, q_row_stride=1024, o_row_stride=1024,
+                scale=0.088, dtype=pa.PA_BF16, partition_size=0)
+    vals.update(over)
+    for k, v in vals.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(block_size=8), -3),
+    (dict(head_dim=96), -3),
+    (dict(dtype=7), -3),
+    (dict(num_q_heads=6, num_kv_heads=4), -2),
+    (dict(num_q_heads=48, num_kv_heads=2, q_row_stride=6144, o_row_stride=6144), -3),  # G=24 not built
+    (dict(max_blocks_per_seq=3), -2),               # 3 * 16 < max_seq_len
+    (dict(q_row_stride=100), -2),
+    (dict(q_row_stride=1028), -4),                  # 2056 bytes: not 16-byte aligned
+    (dict(partition_size=24), -2),
+    (dict(scale=float("nan")), -2),
+    (dict(max_query_len=65), -2),
+])
+def test_host_rejects_bad_params_before_any_launch(L, over, code):
+    p = _params(**over)
+    st = L.pa_attention_varlen(16, 16, 16, 16, 16, 16, 16, ctypes.byref(p), None, 0, None)
+    assert st == code
+    assert L.pa_attention_workspace_size(ctypes.byref(p)) == 0
+
+
+def test_host_null_and_workspace_errors(L):
+    p = _params(max_seq_len=2048, max_blocks_per_seq=128)
+    need = L.pa_attention_workspace_size(ctypes.byref(p))
+    assert need == 2 * 8 * 4 * (128 + 2) * 4      # rows * Hq * parts * (D + 2) * fp32
+    assert L.pa_attention_varlen(None, 16, 16, 16, 16, 16, 16, ctypes.byref(p), None, 0, None) == -1
+    assert L.pa_attention_varlen(16, 16, 16, 16, 16, 16, 16, ctypes.byref(p), 16, need - 1, None) == -5
+    assert L.pa_attention_varlen(16, 16, 16, 16, 16, 16, 16, None, None, 0, None) == -1
+    assert L.pa_attention_varlen(24, 16, 16, 16, 16, 16, 16, ctypes.byref(p), 16, need, None) == -4
+    # an empty batch is a no-op
+    assert L.pa_attention_varlen(None, None, None, None, None, None, None,
+                                 ctypes.byref(_params(num_seqs=0, total_q=0)), None, 0, None) == 0
+
+
+def test_cache_write_host_errors(L):
+    f = L.pa_cache_write
+    assert f(16, 16, 1024, 16, 16, 16, 0, 8, 128, 16, 10, pa.PA_BF16, None) == 0       # no rows: no-op
+    assert f(16, 16, 1024, 16, 16, 16, 4, 8, 128, 8, 10, pa.PA_BF16, None) == -3       # block size
+    assert f(16, 16, 1024, 16, 16, 16, 4, 8, 96, 16, 10, pa.PA_BF16, None) == -3       # head dim
+    assert f(16, 16, 1000, 16, 16, 16, 4, 8, 128, 16, 10, pa.PA_BF16, None) == -2      # stride < Hkv*D
+    assert f(None, 16, 1024, 16, 16, 16, 4, 8, 128, 16, 10, pa.PA_BF16, None) == -1
+    assert f(16, 16, 1028, 16, 16, 16, 4, 1, 128, 16, 10, pa.PA_BF16, None) == -4      # unaligned stride
+    assert f(8, 16, 1024, 16, 16, 16, 4, 8, 128, 16, 10, pa.PA_BF16, None) == -4       # unaligned pointer
+
+
+def test_validate_host_errors(L):
+    p = _params()
+    assert L.pa_validate_metadata(16, 16, 16, None, 0, ctypes.byref(p), None, None) == -1
+    assert L.pa_validate_metadata(None, 16, 16, None, 0, ctypes.byref(p), 16, None) == -1
