@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int b = blockIdx.z;
   const int q0 = a.cu_seqlens[b];
   const int n = a.cu_seqlens[b + 1] - q0;
-  if (n == 0 || (a.single_row_only && n > 1)) return;
+  if (n == 0 || (a.row_mode == kSingleRowOnly && n > 1) || (a.row_mode == kMultiRowOnly && n == 1)) return;
   const int L = a.seq_lens[b];
   const int tok0 = part * a.part_size;
   if (tok0 >= L) return;
@@ -321,6 +321,7 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a) {
     const int b = lo;
     const int q0 = a.cu_seqlens[b];
     const int n = a.cu_seqlens[b + 1] - q0;
+    if ((a.row_mode == kSingleRowOnly && n > 1) || (a.row_mode == kMultiRowOnly && n == 1)) return;
     ctx = a.seq_lens[b] - n + (row - q0) + 1;
   }
   const int nparts = (ctx + a.part_size - 1) / a.part_size;
@@ -353,15 +354,21 @@ static size_t lds_bytes(int part_size) {
   return (size_t(a > b ? a : b) + 2 * G) * sizeof(float);
 }
 
+template <typename E, int D>
+static hipError_t launch_merge_t(const DecodeArgs& a, int64_t partial_rows, hipStream_t stream) {
+  if (a.max_parts <= 1 || partial_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL((merge_kernel<E, D>), dim3(partial_rows, a.num_q_heads), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <typename E, int D, int G>
 static hipError_t launch_one(const DecodeArgs& a, int64_t partial_rows, hipStream_t stream) {
   const size_t lds = lds_bytes<E, D, G>(a.part_size);
   dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
   hipLaunchKernelGGL((decode_kernel<E, D, G>), grid, dim3(256), lds, stream, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.max_parts <= 1 || partial_rows == 0) return e;
-  hipLaunchKernelGGL((merge_kernel<E, D>), dim3(partial_rows, a.num_q_heads), dim3(64), 0, stream, a);
-  return hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_merge_t<E, D>(a, partial_rows, stream);
 }
 
 template <typename E, int D>
@@ -387,6 +394,17 @@ bool decode_supported(int dtype, int head_dim, int group, int part_size) {
 size_t decode_lds_bytes(int dtype, int head_dim, int group, int part_size) {
   const size_t a = size_t(part_size) * group, b = size_t(4) * group * head_dim;
   return ((a > b ? a : b) + 2 * group) * sizeof(float);
+}
+
+hipError_t launch_merge(int dtype, int head_dim, const DecodeArgs& a, int64_t partial_rows, hipStream_t stream) {
+  if (dtype == 1) {
+    if (head_dim == 128) return launch_merge_t<BF16, 128>(a, partial_rows, stream);
+    if (head_dim == 64) return launch_merge_t<BF16, 64>(a, partial_rows, stream);
+  } else if (dtype == 0) {
+    if (head_dim == 128) return launch_merge_t<F32, 128>(a, partial_rows, stream);
+    if (head_dim == 64) return launch_merge_t<F32, 64>(a, partial_rows, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(int dtype, int head_dim, int group, const DecodeArgs& a, int64_t partial_rows,

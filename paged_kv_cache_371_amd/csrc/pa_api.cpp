@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 
 #include "pa_internal.h"
@@ -23,20 +24,65 @@ inline int effective_partition(const pa_attn_params* p) {
   return p->partition_size > 0 ? p->partition_size : pa::kDefaultPartition;
 }
 
-// Requests with more than one row take the MFMA prefill kernel in bf16 when
-// it is built for this (D, G); the decode kernel serves every other request.
-inline bool use_prefill(const pa_attn_params* p) {
-  return p->dtype == PA_BF16 && p->max_query_len > 1 &&
-         pa::prefill_supported(p->head_dim, p->num_q_heads / p->num_kv_heads);
-}
-
-inline int64_t partial_rows(const pa_attn_params* p) {
-  return use_prefill(p) ? int64_t(p->num_seqs) : p->total_q;
-}
+// How one call is split between the kernels.  Single-row (decode) requests
+// take the fast bf16 kernel when it is built for (D, G); in bf16, requests
+// with more rows take the MFMA prefill kernel when it is built for (D, G).
+// The generic decode kernel serves whatever is left.  Split-K partials live
+// in two workspace regions: A, indexed by request (single-row requests), and
+// B, indexed by packed row (requests the generic kernel serves row by row).
+struct Plan {
+  bool ok;            // every kernel the call needs is built for these parameters
+  bool fast;          // fast single-row kernel
+  bool prefill;       // MFMA prefill kernel for multi-row requests
+  int generic_mode;   // -1: generic kernel not launched, else its pa::RowMode
+  bool generic_by_seq;
+  int64_t parts;      // partitions per request, upper bound
+  int64_t rows_a;     // partial rows in region A
+  int64_t rows_b;     // partial rows in region B
+};
 
 inline int64_t max_parts(const pa_attn_params* p) {
   const int ps = effective_partition(p);
   return p->max_seq_len > 0 ? (int64_t(p->max_seq_len) + ps - 1) / ps : 1;
+}
+
+inline Plan make_plan(const pa_attn_params* p) {
+  Plan pl{};
+  const int dt = p->dtype == PA_BF16 ? 1 : 0;
+  const int g = p->num_q_heads / p->num_kv_heads;
+  const bool multi = p->max_query_len > 1;
+  const int ps = effective_partition(p);
+  pl.fast = pa::decode_gqa_supported(dt, p->head_dim, g, ps);
+  pl.prefill = dt == 1 && multi && pa::prefill_supported(p->head_dim, g);
+  pl.parts = max_parts(p);
+  if (pl.fast) {
+    pl.generic_mode = (multi && !pl.prefill) ? pa::kMultiRowOnly : -1;
+    pl.generic_by_seq = false;
+  } else if (pl.prefill) {
+    pl.generic_mode = pa::kSingleRowOnly;
+    pl.generic_by_seq = true;
+  } else {
+    pl.generic_mode = pa::kAllRows;
+    pl.generic_by_seq = false;
+  }
+  pl.ok = pl.generic_mode < 0 || pa::decode_supported(dt, p->head_dim, g, ps);
+  if (pl.parts > 1) {
+    const bool a_used = pl.fast || (pl.generic_mode >= 0 && pl.generic_by_seq);
+    const bool b_used = pl.generic_mode >= 0 && !pl.generic_by_seq;
+    pl.rows_a = a_used ? p->num_seqs : 0;
+    pl.rows_b = b_used ? p->total_q : 0;
+  }
+  return pl;
+}
+
+inline size_t region_floats(const pa_attn_params* p, int64_t rows, int64_t parts) {
+  return size_t(rows) * p->num_q_heads * parts * (p->head_dim + 2);
+}
+
+// Workspace: [fast kernel's work list, padded to 256 B][region A][region B].
+inline size_t plan_bytes(const pa_attn_params* p, const Plan& pl) {
+  if (!pl.fast) return 0;
+  return (pa::decode_gqa_plan_bytes(p->num_seqs, pl.parts) + 255) / 256 * 256;
 }
 
 pa_status check_params(const pa_attn_params* p) {
@@ -54,10 +100,7 @@ pa_status check_params(const pa_attn_params* p) {
   const int64_t hd = int64_t(p->num_q_heads) * p->head_dim;
   if (p->q_row_stride < hd || p->o_row_stride < hd) return PA_ERR_SHAPE;
   if (!std::isfinite(p->scale)) return PA_ERR_SHAPE;
-  const int g = p->num_q_heads / p->num_kv_heads;
-  const int ps = effective_partition(p);
   if (p->partition_size != 0 && (p->partition_size < 16 || p->partition_size % 16)) return PA_ERR_SHAPE;
-  if (!pa::decode_supported(p->dtype == PA_BF16 ? 1 : 0, p->head_dim, g, ps)) return PA_ERR_UNSUPPORTED;
   const int eb = elem_bytes(p->dtype);
   if ((p->q_row_stride * eb) % 16 || (p->o_row_stride * eb) % 16) return PA_ERR_ALIGN;
   return PA_OK;
@@ -104,10 +147,10 @@ pa_status pa_cache_write(const void* k_new, const void* v_new, int64_t kv_row_st
 
 size_t pa_attention_workspace_size(const pa_attn_params* p) {
   if (check_params(p) != PA_OK) return 0;
-  const int64_t parts = max_parts(p);
-  if (parts <= 1) return 0;
-  const int64_t rows = partial_rows(p);
-  return size_t(rows) * p->num_q_heads * parts * (p->head_dim + 2) * sizeof(float);
+  const Plan pl = make_plan(p);
+  if (!pl.ok) return 0;
+  return plan_bytes(p, pl) +
+         (region_floats(p, pl.rows_a, pl.parts) + region_floats(p, pl.rows_b, pl.parts)) * sizeof(float);
 }
 
 pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -123,12 +166,16 @@ pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, con
   if (workspace && !aligned16(workspace)) return PA_ERR_ALIGN;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const int dt = p->dtype == PA_BF16 ? 1 : 0;
   const int g = p->num_q_heads / p->num_kv_heads;
-  const int ps = effective_partition(p);
-  const int64_t parts = max_parts(p);
-  const int64_t prows = partial_rows(p);
-  const bool prefill = use_prefill(p);
+  const Plan pl = make_plan(p);
+  if (!pl.ok) return PA_ERR_UNSUPPORTED;
+  if (pl.parts > 65535 || int64_t(p->num_seqs) * pl.parts * p->num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
   const float scale_log2 = p->scale * kLog2e;
+  const size_t pbytes = plan_bytes(p, pl);
+  float* ws = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pbytes) : nullptr;
+  float* region_a = ws;
+  float* region_b = ws ? ws + region_floats(p, pl.rows_a, pl.parts) : nullptr;
 
   pa::DecodeArgs d{};
   d.out = out;
@@ -138,24 +185,40 @@ pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, con
   d.cu_seqlens = cu_seqlens_q;
   d.seq_lens = seq_lens;
   d.block_tables = block_tables;
-  d.ws_o = static_cast<float*>(workspace);
-  d.ws_ml = parts > 1 ? static_cast<float*>(workspace) + prows * p->num_q_heads * parts * p->head_dim : nullptr;
   d.q_row_stride = p->q_row_stride;
   d.o_row_stride = p->o_row_stride;
   d.num_seqs = p->num_seqs;
   d.num_q_heads = p->num_q_heads;
   d.num_kv_heads = p->num_kv_heads;
   d.max_blocks_per_seq = p->max_blocks_per_seq;
-  d.part_size = ps;
-  d.max_parts = int32_t(parts);
+  d.part_size = effective_partition(p);
+  d.max_parts = int32_t(pl.parts);
   d.scale_log2 = scale_log2;
-  d.single_row_only = prefill ? 1 : 0;
-  d.partial_by_seq = prefill ? 1 : 0;
-  if (parts > 65535) return PA_ERR_SHAPE;
+  d.plan = pl.fast ? static_cast<int32_t*>(workspace) : nullptr;
 
-  hipError_t e = pa::launch_decode(p->dtype == PA_BF16 ? 1 : 0, p->head_dim, g, d, parts > 1 ? prows : 0, s);
-  if (e != hipSuccess) return PA_ERR_LAUNCH;
-  if (prefill) {
+  // Partials of a region: o [rows, Hq, parts, D] followed by (m, l) [rows, Hq, parts, 2].
+  auto point_at = [&](float* region, int64_t rows) {
+    d.ws_o = region;
+    d.ws_ml = region ? region + int64_t(rows) * p->num_q_heads * pl.parts * p->head_dim : nullptr;
+  };
+
+  hipError_t e = hipSuccess;
+  if (pl.fast) {
+    point_at(region_a, pl.rows_a);
+    d.row_mode = pa::kSingleRowOnly;
+    d.partial_by_seq = 1;
+    e = pa::launch_decode_gqa(g, d, s);
+    if (e == hipSuccess) e = pa::launch_merge(dt, p->head_dim, d, pl.rows_a, s);
+    if (e != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  if (pl.generic_mode >= 0) {
+    point_at(pl.generic_by_seq ? region_a : region_b, pl.generic_by_seq ? pl.rows_a : pl.rows_b);
+    d.row_mode = pl.generic_mode;
+    d.partial_by_seq = pl.generic_by_seq ? 1 : 0;
+    e = pa::launch_decode(dt, p->head_dim, g, d, pl.generic_by_seq ? pl.rows_a : pl.rows_b, s);
+    if (e != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  if (pl.prefill) {
     pa::PrefillArgs f{};
     f.out = out;
     f.q = q;

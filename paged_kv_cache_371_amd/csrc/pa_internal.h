@@ -28,9 +28,14 @@ struct DecodeArgs {
   int32_t part_size;      // tokens per partition, multiple of 16
   int32_t max_parts;      // ceil(max_seq_len / part_size)
   float scale_log2;       // softmax scale * log2(e)
-  int32_t single_row_only;  // 1: skip requests with more than one row
+  int32_t* plan;            // fast kernel's work list (header + items), in the workspace
+  int32_t row_mode;         // which requests this launch serves (RowMode)
   int32_t partial_by_seq;   // 1: partials indexed by request, else by packed row
 };
+
+// Requests a decode launch serves: all of them, only those with exactly one
+// query row, or only those with more than one row.  Empty requests never.
+enum RowMode : int32_t { kAllRows = 0, kSingleRowOnly = 1, kMultiRowOnly = 2 };
 
 // Arguments of the MFMA prefill kernel (bf16, requests with n_b > 1).
 struct PrefillArgs {
@@ -59,6 +64,16 @@ hipError_t launch_cache_write(const void* k_new, const void* v_new, int64_t kv_r
 hipError_t launch_decode(int dtype, int head_dim, int group, const DecodeArgs& a, int64_t partial_rows,
                          hipStream_t stream);
 bool decode_supported(int dtype, int head_dim, int group, int part_size);
+
+// Fast single-row decode (bf16, D = 128, G in {1, 2, 4, 8}); partials by request.
+// It needs decode_gqa_plan_bytes() of workspace for its work list (a.plan).
+constexpr int kPlanHeaderInts = 64;      // counter, entry count, padding to 256 B
+constexpr int kMaxPartBuckets = 512;     // partition_size / 16 of the fast kernel, at most
+bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size);
+size_t decode_gqa_plan_bytes(int64_t num_seqs, int64_t max_parts);
+hipError_t launch_decode_gqa(int group, const DecodeArgs& a, hipStream_t stream);
+// Partition merge alone (for a DecodeArgs whose partials are already written).
+hipError_t launch_merge(int dtype, int head_dim, const DecodeArgs& a, int64_t partial_rows, hipStream_t stream);
 size_t decode_lds_bytes(int dtype, int head_dim, int group, int part_size);
 
 hipError_t launch_prefill(int head_dim, int group, const PrefillArgs& a, hipStream_t stream);

@@ -96,7 +96,10 @@ def test_host_rejects_bad_params_before_any_launch(L, over, code):
 def test_host_null_and_workspace_errors(L):
     p = _params(max_seq_len=2048, max_blocks_per_seq=128)
     need = L.pa_attention_workspace_size(ctypes.byref(p))
-    assert need == 2 * 8 * 4 * (128 + 2) * 4      # rows * Hq * parts * (D + 2) * fp32
+    # the fast kernel's work list (64-int header + a (request, partition) pair per
+    # possible partition, padded to 256 B), then rows * Hq * parts * (D + 2) fp32 partials
+    plan = -(-(64 + 2 * 2 * 4) * 4 // 256) * 256
+    assert need == plan + 2 * 8 * 4 * (128 + 2) * 4
     assert L.pa_attention_varlen(None, 16, 16, 16, 16, 16, 16, ctypes.byref(p), None, 0, None) == -1
     assert L.pa_attention_varlen(16, 16, 16, 16, 16, 16, 16, ctypes.byref(p), 16, need - 1, None) == -5
     assert L.pa_attention_varlen(16, 16, 16, 16, 16, 16, 16, None, None, 0, None) == -1
