@@ -94,8 +94,12 @@ typedef struct {
   int64_t o_row_stride;        /* elements between consecutive packed rows of out (>= Hq*D) */
   float scale;                 /* softmax scale, usually 1/sqrt(D) */
   pa_dtype dtype;
-  int32_t partition_size;      /* tokens per split-K context partition; 0 = library
-                                  default (512); else a multiple of 64 in [64, 8192] */
+  int32_t partition_size;      /* tokens per split-K context partition, a multiple of 16
+                                  in [16, 8192].  Given explicitly, a request's result
+                                  depends only on the request (bitwise the same in any
+                                  batch).  0 = library default: 512, 1024 or 2048 chosen
+                                  from num_seqs, num_kv_heads and max_seq_len (results may
+                                  then differ in the last bits between batch shapes). */
 } pa_attn_params;
 
 /*

@@ -51,6 +51,10 @@
 #include "pa_common.h"
 #include "pa_internal.h"
 
+#ifndef PA_DECODE_RING
+#define PA_DECODE_RING 3
+#endif
+
 namespace pa {
 namespace {
 
@@ -62,6 +66,11 @@ constexpr float kRescaleThreshold = 8.f;      // log2 units
 constexpr float kMinusBig = -1e30f;           // finite "no token yet" max
 constexpr uint32_t kBf16OnePair = 0x3F803F80u;
 constexpr int kMaxDevices = 64;
+// Tiles in flight per wave.  One workgroup per CU (one wave per SIMD): a
+// second workgroup only competes for issue slots (its waves starve while the
+// first one runs), so its registers are better spent on a deeper ring.
+constexpr int kRing = PA_DECODE_RING;
+constexpr int kItemSlots = 64;   // list entries a wave stages in LDS
 
 // Pairing masks of the 16-lane reduction steps and their DPP controls.
 constexpr int kStepMask[4] = {8, 7, 2, 1};
@@ -90,6 +99,19 @@ __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int
 template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Read-only metadata is read through the constant address space: the loads
+// are then scalar (s_load) even though the kernel also stores to memory the
+// compiler cannot prove disjoint from it.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+
+__device__ __forceinline__ int32_t load_const(const int32_t* p, int64_t i) {
+  return ((const_i32*)(p))[i];
+}
+// Same, but the load may not be moved (sunk towards its use): for prefetches.
+__device__ __forceinline__ int32_t load_const_early(const int32_t* p, int64_t i) {
+  return ((volatile const_i32*)(p))[i];
 }
 
 template <int Ctrl>
@@ -153,68 +175,184 @@ __device__ __forceinline__ float rows_sum(float v) {
   return a + b;
 }
 
-template <int G>
-struct GqaSmem {
-  float m[kWavesPerGroup][G];
-  float l[kWavesPerGroup][G];
-  float M[G];
-  float L[G];
-  float o[kWavesPerGroup][G * kD];
+// Geometry of one work item: (request b, KV head kvh, partition part) of a
+// single-row request, served by one wave.  All fields are wave-uniform.
+struct Item {
+  int valid;
+  int b, kvh, part, q0;
+  int tok1;      // end of the partition's tokens
+  int lb0;       // first logical block of the partition
+  int nb;        // blocks (tiles) in the partition; >= 1 for a valid item
+  int nbr;       // nb rounded up to a multiple of kRing (the item's stream length)
+  int nparts;    // partitions of the request
+  const int32_t* table;
+  const char* kbase;
+  const char* vbase;
 };
 
-// One work item: (request b, KV head kvh, partition part) of a single-row
-// request whose partition holds at least one token.  Ends with a barrier, so
-// the caller may reuse the shared memory right after.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <typename T>
+__device__ __forceinline__ T* uni_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = uint32_t(uni(int(uint32_t(v)))), hi = uint32_t(uni(int(uint32_t(v >> 32))));
+  return reinterpret_cast<T*>(lo | (hi << 32));
+}
+
+// Item t of the list plan_kernel built: entry t / Hkv (passed in), KV head
+// t % Hkv.  An index past the list gives a placeholder with in-range
+// addresses and no tiles.  Every field goes through readfirstlane, so the descriptors and
+// table loads built from it stay scalar.
+__device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t, int4 ent) {
+  Item it;
+  it.valid = t < total;
+  int b = 0, part = 0, q0 = 0, L = 1, kvh = 0;
+  if (it.valid) {
+    kvh = t % a.num_kv_heads;
+    b = ent.x;
+    part = ent.y;
+    q0 = ent.z;
+    L = ent.w;
+  }
+  const int P = a.part_size;
+  const int tok0 = part * P;
+  const int tok1 = min(tok0 + P, L);
+  const int lb0 = tok0 / kBlock;
+  const int nb = it.valid ? (tok1 + kBlock - 1) / kBlock - lb0 : 0;
+  it.b = uni(b);
+  it.kvh = uni(kvh);
+  it.part = uni(part);
+  it.q0 = uni(q0);
+  it.tok1 = uni(tok1);
+  it.lb0 = uni(lb0);
+  it.nb = uni(nb);
+  it.nbr = uni(kRing * ((nb + kRing - 1) / kRing));
+  it.nparts = uni((L + P - 1) / P);
+  it.valid = uni(it.valid);
+  it.table = uni_ptr(a.block_tables + int64_t(b) * a.max_blocks_per_seq);
+  it.kbase = uni_ptr(static_cast<const char*>(a.k_cache) + int64_t(kvh) * kTileBytes);
+  it.vbase = uni_ptr(static_cast<const char*>(a.v_cache) + int64_t(kvh) * kTileBytes);
+  return it;
+}
+
+// Persistent kernel; every wave is an independent worker (no barriers).
+// Worker w of NW takes item i*NW + w in even rounds i and i*NW + NW-1-w in
+// odd ones; with the list sorted by decreasing size this zig-zag keeps every
+// worker's share within a few percent of the mean.  (Claiming items through
+// memory atomics balances better in principle, but under a saturated HBM
+// queue each atomic round trip costs tens of microseconds.)
+//
+// A wave sees its items as one stream of tiles: an item contributes nbr
+// stream slots (its nb tiles padded with empty ones to a multiple of 3), so
+// the last load group of an item already fetches the next item's first three
+// tiles and the HBM queue of the wave never drains at item boundaries.  The
+// physical block id of the slot issued next is fetched one issue ahead.
 template <int G>
-__device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int kvh, int part, GqaSmem<G>& sm) {
+__global__ __launch_bounds__(256, 1) void decode_gqa_kernel(DecodeArgs a) {
   constexpr int K = log2_of<G>();
   constexpr int kRot = 16 / G;          // lanes between consecutive heads in a row
   constexpr int kNV = G * 8;            // accumulators per lane
   constexpr int kNZ = kNV / 4;          // accumulators per lane after the row reduce-scatter
-  auto& s_m = sm.m;
-  auto& s_l = sm.l;
-  auto& s_M = sm.M;
-  auto& s_L = sm.L;
-  auto& s_o = sm.o;
+  constexpr int kRun = kNZ < 8 ? kNZ : 8;   // consecutive d values per output run
 
-  const int q0 = a.cu_seqlens[b];
-  const int L = a.seq_lens[b];
-  const int tok0 = part * a.part_size;
-  const int tok1 = min(tok0 + a.part_size, L);
-  const int nparts = (L + a.part_size - 1) / a.part_size;
-  const int lb0 = tok0 / kBlock;
-  const int nblk = (tok1 + kBlock - 1) / kBlock - lb0;
-  const int lb_last = lb0 + nblk - 1;
-
+  const int total = load_const(a.plan, kPlanCountInt) * a.num_kv_heads;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int NW = gridDim.x * kWavesPerGroup;
+  const int wid = int(blockIdx.x) * kWavesPerGroup + wave;
+  auto item_of_round = [&](int i) {   // item index of round i, or total if none
+    const int64_t base = int64_t(i) * NW;
+    const int64_t t = base + ((i & 1) ? NW - 1 - wid : wid);
+    return t < total ? int(t) : total;
+  };
+
   const int r = lane & 15;
   const int tg = lane >> 4;
   const int hr = r >> (4 - K);
+  const int voff = tg * (kD * 2) + r * 16;
+  const int64_t bstride = int64_t(a.num_kv_heads) * kTileBytes;
+  const float scale_log2 = a.scale_log2;
+  // direction of row_ror within a row: the head of accumulator slot j is (hr + dir*j) mod G
+  int dir = 1;
+  if constexpr (G > 1) {
+    const int src = int(dpp_u32<0x120 + kRot>(uint32_t(r)));
+    dir = ((src >> (4 - K)) == ((hr + 1) & (G - 1))) ? 1 : -1;
+  }
 
-  // q slices of the G heads, in lane-relative order h(r ^ M_j).
-  u32x4_t qreg[G];
+  // Each wave stages the next item's q rows in its own LDS slot: fetched into a
+  // few VGPRs when the item starts (not used by the tile loop, so the loop
+  // never waits for them) and moved to qreg through LDS after the item.
+  constexpr int kQDw = G;   // q dwords per lane: G rows x 256 B over 64 lanes
+  __shared__ uint32_t sq[kWavesPerGroup][64 * kQDw];
+  auto fetch_q = [&](const Item& it, uint32_t(&qt)[kQDw]) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(
+        static_cast<const char*>(a.q) + (int64_t(it.q0) * a.q_row_stride + int64_t(it.kvh) * G * kD) * 2);
+    if constexpr (kQDw >= 4) {
+#pragma unroll
+      for (int c = 0; c < kQDw / 4; ++c) {
+        const u32x4_t v = reinterpret_cast<const u32x4_t*>(src)[lane * (kQDw / 4) + c];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) qt[4 * c + w] = v[w];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < kQDw; ++c) qt[c] = src[lane * kQDw + c];
+    }
+  };
+  auto park_q = [&](const uint32_t(&qt)[kQDw]) {
+#pragma unroll
+    for (int c = 0; c < kQDw; ++c) sq[wave][lane * kQDw + c] = qt[c];
+  };
+  auto read_q = [&](u32x4_t(&qreg)[G]) {   // q slices, lane-relative order h(r ^ M_j)
+    const char* base = reinterpret_cast<const char*>(&sq[wave][0]);
+    static_for<G>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      const int hh = (r ^ q_mask<K>(j)) >> (4 - K);
+      qreg[j] = *reinterpret_cast<const u32x4_t*>(base + hh * (kD * 2) + r * 16);
+    });
+  };
+
+  // The list entries of this wave's first kItemSlots items are staged in its
+  // LDS slot once, so setting up an item costs an LDS read, not a scalar
+  // memory round trip on the critical path (later items, if any, load directly).
+  __shared__ int4 sitems[kWavesPerGroup][kItemSlots];
   {
-    const char* qrow = static_cast<const char*>(a.q) + (int64_t(q0) * a.q_row_stride + int64_t(kvh) * G * kD) * 2;
+    const int4* entries = reinterpret_cast<const int4*>(a.plan + kPlanHeaderInts);
+    const int t = item_of_round(lane);
+    if (lane < kItemSlots && t < total) sitems[wave][lane] = entries[t / a.num_kv_heads];
+  }
+  auto entry_of_round = [&](int i) -> int4 {
+    const int t = item_of_round(i);
+    int4 e = {0, 0, 0, 1};
+    if (t < total) {
+      if (i < kItemSlots) {
+        e = sitems[wave][i];
+      } else {
+        const int32_t* p = a.plan + kPlanHeaderInts + 4 * int64_t(t / a.num_kv_heads);
+        e = make_int4(load_const(p, 0), load_const(p, 1), load_const(p, 2), load_const(p, 3));
+      }
+    }
+    return e;
+  };
+  auto item_for_round = [&](int i) { return make_item(a, total, item_of_round(i), entry_of_round(i)); };
+
+  Item cur = item_for_round(0);
+  if (!cur.valid) return;
+
+  auto load_q = [&](u32x4_t(&qreg)[G], const Item& it) {   // q slices, lane-relative order h(r ^ M_j)
+    const char* qrow =
+        static_cast<const char*>(a.q) + (int64_t(it.q0) * a.q_row_stride + int64_t(it.kvh) * G * kD) * 2;
     static_for<G>([&](auto J) {
       constexpr int j = decltype(J)::value;
       const int hh = (r ^ q_mask<K>(j)) >> (4 - K);
       qreg[j] = *reinterpret_cast<const u32x4_t*>(qrow + hh * (kD * 2) + r * 16);
     });
-  }
-
-  const int nb = nblk > wave ? (nblk - wave + kWavesPerGroup - 1) / kWavesPerGroup : 0;
-  const int32_t* __restrict__ table = a.block_tables + int64_t(b) * a.max_blocks_per_seq;
-  const char* kbase = static_cast<const char*>(a.k_cache) + int64_t(kvh) * kTileBytes;
-  const char* vbase = static_cast<const char*>(a.v_cache) + int64_t(kvh) * kTileBytes;
-  const int64_t bstride = int64_t(a.num_kv_heads) * kTileBytes;
-  const int voff = tg * (kD * 2) + r * 16;
-  const float scale_log2 = a.scale_log2;
-
-  auto issue = [&](u32x4_t(&kb)[4], u32x4_t(&vb)[4], int k) {
-    const int lb = lb0 + wave + kWavesPerGroup * k;
-    const int nrec = k < nb ? kTileBytes : 0;
-    const int64_t phys = table[min(lb, lb_last)];
+  };
+  auto tile_phys = [&](const Item& it, int j) -> int64_t {
+    return load_const(it.table, it.lb0 + min(j, it.nb - 1));
+  };
+  auto load_tile = [&](u32x4_t(&kb)[4], u32x4_t(&vb)[4], const char* kbase, const char* vbase, bool live,
+                       int64_t phys) {
+    const int nrec = live ? kTileBytes : 0;
     const __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + phys * bstride), 0, nrec, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rv =
@@ -225,256 +363,247 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int kvh,
     for (int i = 0; i < 4; ++i) vb[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + i * 1024, 0, 0);
   };
 
-  float acc[G][8];
-#pragma unroll
-  for (int j = 0; j < G; ++j)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
-  float m = kMinusBig;   // reference max of this lane's (row, head), log2 units
-  float l = 0.f;         // sum of rounded p relative to m
+  u32x4_t qreg[G];
+  u32x4_t kr[kRing][4], vr[kRing][4];   // the ring: K and V of kRing tiles
+  load_q(qreg, cur);
+  __builtin_amdgcn_sched_barrier(0);
+  static_for<kRing>([&](auto S) {
+    constexpr int st = decltype(S)::value;
+    load_tile(kr[st], vr[st], cur.kbase, cur.vbase, st < cur.nb, tile_phys(cur, st));
+    __builtin_amdgcn_sched_barrier(0);
+  });
 
-  auto process = [&](u32x4_t(&kb)[4], u32x4_t(&vb)[4], int k) {
-    const int tb = (lb0 + wave + kWavesPerGroup * k) * kBlock;   // first token of the block
-    float sc[4];
+  for (int i = 0;; ++i) {
+    const Item nxt = item_for_round(i + 1);
+    uint32_t qt[kQDw];
+    if (nxt.valid) fetch_q(nxt, qt);
+    __builtin_amdgcn_sched_barrier(0);
+
+    float acc[G][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float s[G];
+    for (int j = 0; j < G; ++j)
 #pragma unroll
-      for (int j = 0; j < G; ++j) s[j] = dot16_bf16(qreg[j], kb[i]);
-      sc[i] = row_reduce<G, 0>(s) * scale_log2;
-    }
-    if (tb + kBlock > tok1) {   // the context ends inside this block
+      for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+    float m = kMinusBig;   // reference max of this lane's (row, head), log2 units
+    float l = 0.f;         // sum of rounded p relative to m
+
+    // Stream slot j of this item: its own tile j, or tile j - nbr of the next
+    // item.  Every field is a scalar select, so a slot costs one scalar load.
+    auto slot_phys = [&](int j) -> int64_t {
+      const bool own = j < cur.nbr;
+      const int jj = own ? j : j - cur.nbr;
+      const int32_t* tb = own ? cur.table : nxt.table;
+      const int lb0 = own ? cur.lb0 : nxt.lb0;
+      const int nbl = own ? cur.nb : nxt.nb;
+      return load_const_early(tb, lb0 + max(min(jj, nbl - 1), 0));
+    };
+    int64_t pf = slot_phys(kRing);   // block id of the next slot to issue
+    auto issue = [&](u32x4_t(&kb)[4], u32x4_t(&vb)[4], int j) {
+      const int64_t phys = pf;
+      pf = slot_phys(j + 1);
+      const bool own = j < cur.nbr;
+      const int jj = own ? j : j - cur.nbr;
+      const int nbl = own ? cur.nb : nxt.nb;
+      load_tile(kb, vb, own ? cur.kbase : nxt.kbase, own ? cur.vbase : nxt.vbase, jj < nbl, phys);
+    };
+
+    auto process = [&](u32x4_t(&kb)[4], u32x4_t(&vb)[4], int k) {
+      const int tb = (cur.lb0 + k) * kBlock;   // first token of the block
+      float sc[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool dead = tb + 4 * i + tg >= tok1;
-        sc[i] = dead ? -__builtin_inff() : sc[i];
+        float s[G];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) vb[i][w] = dead ? 0u : vb[i][w];
+        for (int j = 0; j < G; ++j) s[j] = dot16_bf16(qreg[j], kb[i]);
+        sc[i] = row_reduce<G, 0>(s) * scale_log2;
       }
-    }
-    const float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    if (__builtin_amdgcn_ballot_w64(bm > m + kRescaleThreshold)) {
-      const float mn = fmaxf(m, bm);
-      const float alpha = fast_exp2(m - mn);
-      m = mn;
-      l *= alpha;
-      static_for<G>([&](auto J) {
-        constexpr int j = decltype(J)::value;
-        float c = alpha;
-        if constexpr (j > 0) c = dpp_f32<0x120 + j * kRot>(alpha);
+      if (tb + kBlock > cur.tok1) {   // the context ends inside this block
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[j][e] *= c;
+        for (int i = 0; i < 4; ++i) {
+          const bool dead = tb + 4 * i + tg >= cur.tok1;
+          sc[i] = dead ? -__builtin_inff() : sc[i];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) vb[i][w] = dead ? 0u : vb[i][w];
+        }
+      }
+      const float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      if (__builtin_amdgcn_ballot_w64(bm > m + kRescaleThreshold)) {
+        const float mn = fmaxf(m, bm);
+        const float alpha = fast_exp2(m - mn);
+        m = mn;
+        l *= alpha;
+        static_for<G>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          float c = alpha;
+          if constexpr (j > 0) c = dpp_f32<0x120 + j * kRot>(alpha);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[j][e] *= c;
+        });
+      }
+      uint32_t p2[2];
+      p2[0] = pack_bf16x2(fast_exp2(sc[0] - m), fast_exp2(sc[1] - m));
+      p2[1] = pack_bf16x2(fast_exp2(sc[2] - m), fast_exp2(sc[3] - m));
+      l = dot2_bf16(p2[0], kBf16OnePair, l);
+      l = dot2_bf16(p2[1], kBf16OnePair, l);
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp) {
+        uint32_t pg[G];
+        static_for<G>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          if constexpr (j == 0) pg[j] = p2[kp];
+          else pg[j] = dpp_u32<0x120 + j * kRot>(p2[kp]);
+        });
+        uint32_t vp[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          vp[2 * w] = __builtin_amdgcn_perm(vb[2 * kp + 1][w], vb[2 * kp][w], 0x05040100u);
+          vp[2 * w + 1] = __builtin_amdgcn_perm(vb[2 * kp + 1][w], vb[2 * kp][w], 0x07060302u);
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[j][e] = dot2_bf16(pg[j], vp[e], acc[j][e]);
+      }
+    };
+
+    // ---- this item's tiles; the last group issues the next item's first tiles ----
+    // The scheduling barriers keep the loads of every stage in issue order, so
+    // each stage waits only for its own tile (vmcnt = the 16 loads after it).
+    for (int k = 0; k < cur.nb; k += kRing) {
+      static_for<kRing>([&](auto S) {
+        constexpr int st = decltype(S)::value;
+        if (st == 0 || k + st < cur.nb) process(kr[st], vr[st], k + st);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(kr[st], vr[st], k + kRing + st);
+        __builtin_amdgcn_sched_barrier(0);
       });
+      // Last group: park the next item's q in LDS.  Here, in the loop body, the
+      // compiler sees the 8*kRing loads of this group issued after the q fetch
+      // and waits for vmcnt(8*kRing), leaving the next item's first tiles in
+      // flight (after the loop it could only wait for vmcnt(0) and drain them).
+      if (k + kRing >= cur.nb && nxt.valid) park_q(qt);
     }
-    uint32_t p2[2];
-    p2[0] = pack_bf16x2(fast_exp2(sc[0] - m), fast_exp2(sc[1] - m));
-    p2[1] = pack_bf16x2(fast_exp2(sc[2] - m), fast_exp2(sc[3] - m));
-    l = dot2_bf16(p2[0], kBf16OnePair, l);
-    l = dot2_bf16(p2[1], kBf16OnePair, l);
+
+    // ---- combine the 4 token rows: common max, rescale, reduce-scatter -----------
+    const float mw = rows_max(m);
+    const float c = fast_exp2(m - mw);
+    const float lw = rows_sum(l * c);   // every lane: (max, sum) of head hr over the partition
+    static_for<G>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      float cj = c;
+      if constexpr (j > 0) cj = dpp_f32<0x120 + j * kRot>(c);
 #pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
-      uint32_t pg[G];
-      static_for<G>([&](auto J) {
-        constexpr int j = decltype(J)::value;
-        if constexpr (j == 0) pg[j] = p2[kp];
-        else pg[j] = dpp_u32<0x120 + j * kRot>(p2[kp]);
-      });
-      uint32_t vp[8];
+      for (int e = 0; e < 8; ++e) acc[j][e] *= cj;
+    });
+    // after the reduce-scatter, row rho holds accumulator x + rho*kNZ of d-slice r
+    float* flat = &acc[0][0];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        vp[2 * w] = __builtin_amdgcn_perm(vb[2 * kp + 1][w], vb[2 * kp][w], 0x05040100u);
-        vp[2 * w + 1] = __builtin_amdgcn_perm(vb[2 * kp + 1][w], vb[2 * kp][w], 0x07060302u);
-      }
-#pragma unroll
-      for (int j = 0; j < G; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[j][e] = dot2_bf16(pg[j], vp[e], acc[j][e]);
+    for (int x = 0; x < kNV / 2; ++x) {
+      float p = flat[x], q = flat[x + kNV / 2];
+      swap32(p, q);
+      flat[x] = p + q;
     }
-  };
-
-  // ---- main loop: three tiles in flight per wave ---------------------------------
-  // The scheduling barriers keep the loads of every stage in issue order, the
-  // same before the loop as inside it, so each stage waits only for its own
-  // tile (vmcnt = the 16 loads issued after it), never for the whole ring.
-  {
-    u32x4_t k0[4], v0[4], k1[4], v1[4], k2[4], v2[4];
-    __builtin_amdgcn_sched_barrier(0);
-    issue(k0, v0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(k1, v1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(k2, v2, 2);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int k = 0; k < nb; k += 3) {
-      process(k0, v0, k);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(k0, v0, k + 3);
-      __builtin_amdgcn_sched_barrier(0);
-      if (k + 1 < nb) process(k1, v1, k + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(k1, v1, k + 4);
-      __builtin_amdgcn_sched_barrier(0);
-      if (k + 2 < nb) process(k2, v2, k + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(k2, v2, k + 5);
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int x = 0; x < kNZ; ++x) {
+      float p = flat[x], q = flat[x + kNZ];
+      swap16(p, q);
+      flat[x] = p + q;
     }
-  }
+    if (nxt.valid) read_q(qreg);   // the next item's q, parked in the last group
+    __builtin_amdgcn_sched_barrier(0);
 
-  // ---- combine the 4 token rows of the wave, then the 4 waves -----------------------
-  const float mw = rows_max(m);
-  const float lw = rows_sum(l * fast_exp2(m - mw));
-  if (tg == 0 && (r & (kRot - 1)) == 0) {
-    s_m[wave][hr] = mw;
-    s_l[wave][hr] = lw;
-  }
-  __syncthreads();
-  float M = s_m[0][hr];
 #pragma unroll
-  for (int w = 1; w < kWavesPerGroup; ++w) M = fmaxf(M, s_m[w][hr]);
-  if (threadIdx.x < G * kRot && (r & (kRot - 1)) == 0) {   // one lane per head (wave 0, row 0)
-    float Lt = 0.f;
+    for (int x0 = 0; x0 < kNZ; x0 += kRun) {
+      const int v = x0 + tg * kNZ;
+      const int j = v >> 3;
+      const int e0 = v & 7;
+      const int head = (hr + dir * j) & (G - 1);
+      const int src = head * kRot;   // a lane of row 0 whose head is `head`
+      const float Lh = __shfl(lw, src);
+      const int hq = cur.kvh * G + head;
+      if (cur.nparts == 1) {
+        const float inv = 1.f / Lh;
+        if constexpr (kRun == 8) {
+          u32x4_t o;
 #pragma unroll
-    for (int w = 0; w < kWavesPerGroup; ++w) Lt += s_l[w][hr] * fast_exp2(s_m[w][hr] - M);
-    s_M[hr] = M;
-    s_L[hr] = Lt;
-  }
-  // scale this lane's row to the common max and rotate the factor to each slot
-  const float c = fast_exp2(m - M);
-  static_for<G>([&](auto J) {
-    constexpr int j = decltype(J)::value;
-    float cj = c;
-    if constexpr (j > 0) cj = dpp_f32<0x120 + j * kRot>(c);
+          for (int w = 0; w < 4; ++w) o[w] = pack_bf16x2(flat[x0 + 2 * w] * inv, flat[x0 + 2 * w + 1] * inv);
+          *reinterpret_cast<u32x4_t*>(static_cast<__bf16*>(a.out) + int64_t(cur.q0) * a.o_row_stride +
+                                      int64_t(hq) * kD + r * 8 + e0) = o;
+        } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[j][e] *= cj;
-  });
-  // direction of row_ror within the row: head of slot j is (hr + dir*j) mod G
-  int dir = 1;
-  if constexpr (G > 1) {
-    const int src = int(dpp_u32<0x120 + kRot>(uint32_t(r)));
-    dir = ((src >> (4 - K)) == ((hr + 1) & (G - 1))) ? 1 : -1;
-  }
-  // reduce-scatter over the rows: after it, row rho holds accumulator x + rho*kNZ
-  float* flat = &acc[0][0];
+          for (int x = 0; x < kRun; ++x)
+            static_cast<__bf16*>(a.out)[int64_t(cur.q0) * a.o_row_stride + int64_t(hq) * kD + r * 8 + e0 + x] =
+                (__bf16)(flat[x0 + x] * inv);
+        }
+      } else {
+        const int64_t slot = (int64_t(cur.b) * a.num_q_heads + hq) * a.max_parts + cur.part;
+        float* dst = a.ws_o + slot * kD + r * 8 + e0;
 #pragma unroll
-  for (int x = 0; x < kNV / 2; ++x) {
-    float p = flat[x], q = flat[x + kNV / 2];
-    swap32(p, q);
-    flat[x] = p + q;
-  }
-#pragma unroll
-  for (int x = 0; x < kNZ; ++x) {
-    float p = flat[x], q = flat[x + kNZ];
-    swap16(p, q);
-    flat[x] = p + q;
-  }
-#pragma unroll
-  for (int x = 0; x < kNZ; ++x) {
-    const int v = x + tg * kNZ;
-    const int j = v >> 3;
-    const int e = v & 7;
-    const int head = (hr + dir * j) & (G - 1);
-    s_o[wave][head * kD + r * 8 + e] = flat[x];
-  }
-  __syncthreads();
-
-  const int64_t row = q0;
-  for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
-    float o = s_o[0][idx];
-#pragma unroll
-    for (int w = 1; w < kWavesPerGroup; ++w) o += s_o[w][idx];
-    const int h = idx >> 7;
-    const int d = idx & (kD - 1);
-    const int hq = kvh * G + h;
-    if (nparts == 1) {
-      static_cast<__bf16*>(a.out)[row * a.o_row_stride + int64_t(hq) * kD + d] = (__bf16)(o / s_L[h]);
-    } else {
-      const int64_t slot = (int64_t(b) * a.num_q_heads + hq) * a.max_parts + part;
-      a.ws_o[slot * kD + d] = o;
-      if (d == 0) {
-        a.ws_ml[2 * slot] = s_M[h];
-        a.ws_ml[2 * slot + 1] = s_L[h];
+        for (int x = 0; x < kRun; ++x) dst[x] = flat[x0 + x];
       }
     }
-  }
-  __syncthreads();
-}
-
-// Persistent kernel.  Item t is entry t / Hkv of the list plan_kernel built,
-// KV head t % Hkv (the KV heads of one partition run side by side).  Round i
-// hands items [i*W, (i+1)*W) to the W workgroups, in reverse order on odd
-// rounds; with the list sorted by decreasing size this zig-zag keeps every
-// workgroup's total within a few percent of the mean, with no atomics.
-template <int G>
-__global__ __launch_bounds__(256, 2) void decode_gqa_kernel(DecodeArgs a) {
-  __shared__ GqaSmem<G> sm;
-  const int32_t* items = a.plan + kPlanHeaderInts;
-  const int hkv = a.num_kv_heads;
-  const int total = __builtin_amdgcn_readfirstlane(a.plan[1]) * hkv;
-  const int W = gridDim.x;
-  for (int i = 0, base = 0; base < total; ++i, base += W) {
-    const int t = base + ((i & 1) ? W - 1 - int(blockIdx.x) : int(blockIdx.x));
-    if (t >= total) continue;
-    const int e = t / hkv;
-    const int kvh = t - e * hkv;
-    const int b = __builtin_amdgcn_readfirstlane(items[2 * e]);
-    const int part = __builtin_amdgcn_readfirstlane(items[2 * e + 1]);
-    decode_item<G>(a, b, kvh, part, sm);
+    if (cur.nparts > 1 && tg == 0 && (r & (kRot - 1)) == 0) {   // one lane per head
+      const int64_t slot = (int64_t(cur.b) * a.num_q_heads + cur.kvh * G + hr) * a.max_parts + cur.part;
+      a.ws_ml[2 * slot] = mw;
+      a.ws_ml[2 * slot + 1] = lw;
+    }
+    if (!nxt.valid) break;
+    cur = nxt;
   }
 }
 
-// Builds the item list of the persistent kernel for the single-row requests:
-// plan[1] = number of list entries (plan[0] and the rest of the 256-byte
-// header are unused), then
-// (request, partition) pairs -- every full partition first, then the partial
-// last partitions by decreasing length, so the small items run at the end.
+// Builds the work list of the persistent kernel for the single-row requests:
+// plan[8] = number of entries (the rest of the 256-byte header is unused),
+// then one int4 (request, partition, query row, context length) per
+// non-empty partition -- every full partition first, then the partial last
+// partitions by decreasing number of blocks, so the small items run last.
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_lens,
                                                     int32_t num_seqs, int32_t part_size, int32_t* __restrict__ plan) {
   __shared__ int s_hist[kMaxPartBuckets];
-  __shared__ int s_cursor[kMaxPartBuckets];
+  __shared__ int s_scan[kMaxPartBuckets];
   __shared__ int s_full;
   __shared__ int s_fullcur;
   const int nbk = part_size / kBlock;
-  for (int i = threadIdx.x; i < nbk; i += blockDim.x) s_hist[i] = 0;
-  if (threadIdx.x == 0) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < nbk; i += blockDim.x) s_hist[i] = 0;
+  if (tid == 0) {
     s_full = 0;
     s_fullcur = 0;
   }
   __syncthreads();
-  for (int b = threadIdx.x; b < num_seqs; b += blockDim.x) {
-    if (cu[b + 1] - cu[b] != 1) continue;
+  for (int b = tid; b < num_seqs; b += blockDim.x) {
+    const int q0 = cu[b];
+    if (cu[b + 1] - q0 != 1) continue;
     const int L = seq_lens[b];
     const int nf = L / part_size;
     const int rem = L - nf * part_size;
-    atomicAdd(&s_full, nf);
+    if (nf) atomicAdd(&s_full, nf);
     if (rem > 0) atomicAdd(&s_hist[(rem - 1) / kBlock], 1);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = s_full;
-    for (int k = nbk - 1; k >= 0; --k) {
-      s_cursor[k] = run;
-      run += s_hist[k];
-    }
-    plan[1] = run;
+  // inclusive scan of the bucket counts from the largest bucket down
+  // (Hillis-Steele over nbk <= 512 entries, index i <-> bucket nbk-1-i)
+  int x = tid < nbk ? s_hist[nbk - 1 - tid] : 0;
+  for (int off = 1; off < nbk; off <<= 1) {
+    if (tid < nbk) s_scan[tid] = x;
+    __syncthreads();
+    if (tid < nbk && tid >= off) x += s_scan[tid - off];
+    __syncthreads();
   }
+  // s_hist[k] becomes the first list position of bucket k
+  if (tid < nbk) s_hist[nbk - 1 - tid] = s_full + x - s_hist[nbk - 1 - tid];
+  if (tid == nbk - 1 || (nbk == 0 && tid == 0)) plan[kPlanCountInt] = s_full + x;
   __syncthreads();
-  int32_t* items = plan + kPlanHeaderInts;
-  for (int b = threadIdx.x; b < num_seqs; b += blockDim.x) {
-    if (cu[b + 1] - cu[b] != 1) continue;
+  int4* entries = reinterpret_cast<int4*>(plan + kPlanHeaderInts);
+  for (int b = tid; b < num_seqs; b += blockDim.x) {
+    const int q0 = cu[b];
+    if (cu[b + 1] - q0 != 1) continue;
     const int L = seq_lens[b];
     const int nf = L / part_size;
     const int rem = L - nf * part_size;
-    int pos = atomicAdd(&s_fullcur, nf);
-    for (int p = 0; p < nf; ++p, ++pos) {
-      items[2 * pos] = b;
-      items[2 * pos + 1] = p;
-    }
-    if (rem > 0) {
-      pos = atomicAdd(&s_cursor[(rem - 1) / kBlock], 1);
-      items[2 * pos] = b;
-      items[2 * pos + 1] = nf;
-    }
+    int pos = nf ? atomicAdd(&s_fullcur, nf) : 0;
+    for (int p = 0; p < nf; ++p, ++pos) entries[pos] = make_int4(b, p, q0, L);
+    if (rem > 0) entries[atomicAdd(&s_hist[(rem - 1) / kBlock], 1)] = make_int4(b, nf, q0, L);
   }
 }
 
@@ -486,7 +615,7 @@ bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size) {
 }
 
 size_t decode_gqa_plan_bytes(int64_t num_seqs, int64_t max_parts) {
-  return (size_t(kPlanHeaderInts) + 2 * size_t(num_seqs) * size_t(max_parts)) * sizeof(int32_t);
+  return (size_t(kPlanHeaderInts) + 4 * size_t(num_seqs) * size_t(max_parts)) * sizeof(int32_t);
 }
 
 namespace {
@@ -503,7 +632,7 @@ int persistent_groups() {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_gqa_kernel<G>, 256, 0) != hipSuccess || occ <= 0)
     occ = 1;
-  v = cus * occ;
+  v = cus * std::min(occ, 1);
   cache[dev].store(v, std::memory_order_relaxed);
   return v;
 }
@@ -522,6 +651,18 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+int decode_gqa_workers(int group) {
+  int g = 0;
+  switch (group) {
+    case 1: g = persistent_groups<1>(); break;
+    case 2: g = persistent_groups<2>(); break;
+    case 4: g = persistent_groups<4>(); break;
+    case 8: g = persistent_groups<8>(); break;
+    default: g = 256;
+  }
+  return g * kWavesPerGroup;
+}
 
 hipError_t launch_decode_gqa(int group, const DecodeArgs& a, hipStream_t stream) {
   switch (group) {

@@ -20,8 +20,24 @@ inline int elem_bytes(pa_dtype d) { return d == PA_BF16 ? 2 : 4; }
 
 inline bool dtype_ok(pa_dtype d) { return d == PA_F32 || d == PA_BF16; }
 
+// Tokens per split-K partition.  An explicit partition_size is used as given;
+// then a request's result depends only on the request itself (bitwise the
+// same in any batch).  The default (0) picks, for the fast decode kernel, the
+// largest of 2048 / 1024 / 512 tokens that still gives every wave of the
+// persistent grid about 8 work items by the host's upper bound
+// B * Hkv * ceil(max_seq_len / P): long partitions cost less per token (one
+// merge per partition), but too few of them leave waves idle.
 inline int effective_partition(const pa_attn_params* p) {
-  return p->partition_size > 0 ? p->partition_size : pa::kDefaultPartition;
+  if (p->partition_size > 0) return p->partition_size;
+  const int g = p->num_kv_heads > 0 ? p->num_q_heads / p->num_kv_heads : 0;
+  const int dt = p->dtype == PA_BF16 ? 1 : 0;
+  if (!pa::decode_gqa_supported(dt, p->head_dim, g, pa::kDefaultPartition)) return pa::kDefaultPartition;
+  const int64_t want = int64_t(8) * pa::decode_gqa_workers(g);
+  for (int ps : {2048, 1024}) {
+    const int64_t items = int64_t(p->num_seqs) * p->num_kv_heads * ((int64_t(p->max_seq_len) + ps - 1) / ps);
+    if (items >= want) return ps;
+  }
+  return pa::kDefaultPartition;
 }
 
 // How one call is split between the kernels.  Single-row (decode) requests

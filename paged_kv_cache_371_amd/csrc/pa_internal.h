@@ -67,10 +67,13 @@ bool decode_supported(int dtype, int head_dim, int group, int part_size);
 
 // Fast single-row decode (bf16, D = 128, G in {1, 2, 4, 8}); partials by request.
 // It needs decode_gqa_plan_bytes() of workspace for its work list (a.plan).
-constexpr int kPlanHeaderInts = 64;      // counter, entry count, padding to 256 B
+constexpr int kPlanHeaderInts = 64;      // claim counters, entry count, padding to 256 B
+constexpr int kPlanCountInt = 8;         // header slot holding the number of list entries
 constexpr int kMaxPartBuckets = 512;     // partition_size / 16 of the fast kernel, at most
 bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size);
 size_t decode_gqa_plan_bytes(int64_t num_seqs, int64_t max_parts);
+// Waves of the persistent fast decode kernel on the current device.
+int decode_gqa_workers(int group);
 hipError_t launch_decode_gqa(int group, const DecodeArgs& a, hipStream_t stream);
 // Partition merge alone (for a DecodeArgs whose partials are already written).
 hipError_t launch_merge(int dtype, int head_dim, const DecodeArgs& a, int64_t partial_rows, hipStream_t stream);
