@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 
-SOURCES = ["pa_api.cpp", "cache_write.hip", "decode.hip", "decode_gqa.hip", "prefill.hip", "validate.hip"]
+SOURCES = ["pa_api.cpp", "cache_write.hip", "plan.hip", "decode.hip", "decode_gqa.hip", "prefill.hip", "validate.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

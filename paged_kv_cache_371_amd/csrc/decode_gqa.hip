@@ -101,18 +101,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Read-only metadata is read through the constant address space: the loads
-// are then scalar (s_load) even though the kernel also stores to memory the
-// compiler cannot prove disjoint from it.
-typedef __attribute__((address_space(4))) const int32_t const_i32;
-
-__device__ __forceinline__ int32_t load_const(const int32_t* p, int64_t i) {
-  return ((const_i32*)(p))[i];
-}
-// Same, but the load may not be moved (sunk towards its use): for prefetches.
-__device__ __forceinline__ int32_t load_const_early(const int32_t* p, int64_t i) {
-  return ((volatile const_i32*)(p))[i];
-}
 
 template <int Ctrl>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
@@ -144,36 +132,6 @@ __device__ __forceinline__ float dot16_bf16(const u32x4_t& q, const u32x4_t& k) 
   return s;
 }
 
-__device__ __forceinline__ void swap32(float& a, float& b) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  a = __uint_as_float(r[0]);
-  b = __uint_as_float(r[1]);
-}
-__device__ __forceinline__ void swap16(float& a, float& b) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  a = __uint_as_float(r[0]);
-  b = __uint_as_float(r[1]);
-}
-
-// max / sum over the 4 token rows (lanes r, r+16, r+32, r+48); every lane gets the result.
-__device__ __forceinline__ float rows_max(float v) {
-  float a = v, b = v;
-  swap32(a, b);
-  v = fmaxf(a, b);
-  a = v;
-  b = v;
-  swap16(a, b);
-  return fmaxf(a, b);
-}
-__device__ __forceinline__ float rows_sum(float v) {
-  float a = v, b = v;
-  swap32(a, b);
-  v = a + b;
-  a = v;
-  b = v;
-  swap16(a, b);
-  return a + b;
-}
 
 // Geometry of one work item: (request b, KV head kvh, partition part) of a
 // single-row request, served by one wave.  All fields are wave-uniform.
@@ -190,13 +148,6 @@ struct Item {
   const char* vbase;
 };
 
-__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-template <typename T>
-__device__ __forceinline__ T* uni_ptr(T* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint64_t lo = uint32_t(uni(int(uint32_t(v)))), hi = uint32_t(uni(int(uint32_t(v >> 32))));
-  return reinterpret_cast<T*>(lo | (hi << 32));
-}
 
 // Item t of the list plan_kernel built: entry t / Hkv (passed in), KV head
 // t % Hkv.  An index past the list gives a placeholder with in-range
@@ -552,70 +503,11 @@ __global__ __launch_bounds__(256, 1) void decode_gqa_kernel(DecodeArgs a) {
   }
 }
 
-// Builds the work list of the persistent kernel for the single-row requests:
-// plan[8] = number of entries (the rest of the 256-byte header is unused),
-// then one int4 (request, partition, query row, context length) per
-// non-empty partition -- every full partition first, then the partial last
-// partitions by decreasing number of blocks, so the small items run last.
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_lens,
-                                                    int32_t num_seqs, int32_t part_size, int32_t* __restrict__ plan) {
-  __shared__ int s_hist[kMaxPartBuckets];
-  __shared__ int s_scan[kMaxPartBuckets];
-  __shared__ int s_full;
-  __shared__ int s_fullcur;
-  const int nbk = part_size / kBlock;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < nbk; i += blockDim.x) s_hist[i] = 0;
-  if (tid == 0) {
-    s_full = 0;
-    s_fullcur = 0;
-  }
-  __syncthreads();
-  for (int b = tid; b < num_seqs; b += blockDim.x) {
-    const int q0 = cu[b];
-    if (cu[b + 1] - q0 != 1) continue;
-    const int L = seq_lens[b];
-    const int nf = L / part_size;
-    const int rem = L - nf * part_size;
-    if (nf) atomicAdd(&s_full, nf);
-    if (rem > 0) atomicAdd(&s_hist[(rem - 1) / kBlock], 1);
-  }
-  __syncthreads();
-  // inclusive scan of the bucket counts from the largest bucket down
-  // (Hillis-Steele over nbk <= 512 entries, index i <-> bucket nbk-1-i)
-  int x = tid < nbk ? s_hist[nbk - 1 - tid] : 0;
-  for (int off = 1; off < nbk; off <<= 1) {
-    if (tid < nbk) s_scan[tid] = x;
-    __syncthreads();
-    if (tid < nbk && tid >= off) x += s_scan[tid - off];
-    __syncthreads();
-  }
-  // s_hist[k] becomes the first list position of bucket k
-  if (tid < nbk) s_hist[nbk - 1 - tid] = s_full + x - s_hist[nbk - 1 - tid];
-  if (tid == nbk - 1 || (nbk == 0 && tid == 0)) plan[kPlanCountInt] = s_full + x;
-  __syncthreads();
-  int4* entries = reinterpret_cast<int4*>(plan + kPlanHeaderInts);
-  for (int b = tid; b < num_seqs; b += blockDim.x) {
-    const int q0 = cu[b];
-    if (cu[b + 1] - q0 != 1) continue;
-    const int L = seq_lens[b];
-    const int nf = L / part_size;
-    const int rem = L - nf * part_size;
-    int pos = nf ? atomicAdd(&s_fullcur, nf) : 0;
-    for (int p = 0; p < nf; ++p, ++pos) entries[pos] = make_int4(b, p, q0, L);
-    if (rem > 0) entries[atomicAdd(&s_hist[(rem - 1) / kBlock], 1)] = make_int4(b, nf, q0, L);
-  }
-}
-
 }  // namespace
 
 bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size) {
   return dtype == 1 && head_dim == kD && (group == 1 || group == 2 || group == 4 || group == 8) &&
          part_size % kBlock == 0 && part_size / kBlock <= kMaxPartBuckets;
-}
-
-size_t decode_gqa_plan_bytes(int64_t num_seqs, int64_t max_parts) {
-  return (size_t(kPlanHeaderInts) + 4 * size_t(num_seqs) * size_t(max_parts)) * sizeof(int32_t);
 }
 
 namespace {
@@ -642,10 +534,6 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   const int64_t upper = int64_t(a.num_seqs) * a.max_parts * a.num_kv_heads;
   const int64_t grid = std::min<int64_t>(upper, persistent_groups<G>());
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, a.seq_lens, a.num_seqs, a.part_size,
-                     a.plan);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_gqa_kernel<G>, dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

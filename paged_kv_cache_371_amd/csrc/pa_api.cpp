@@ -95,10 +95,18 @@ inline size_t region_floats(const pa_attn_params* p, int64_t rows, int64_t parts
   return size_t(rows) * p->num_q_heads * parts * (p->head_dim + 2);
 }
 
-// Workspace: [fast kernel's work list, padded to 256 B][region A][region B].
+// Entries the prefill work list can hold: tiles of kPrefillPairs (row, head) pairs.
+inline int64_t prefill_capacity(const pa_attn_params* p) {
+  const int g = p->num_q_heads / p->num_kv_heads;
+  const int64_t rows = pa::kPrefillPairs / g;
+  return int64_t(p->num_seqs) * ((int64_t(p->max_query_len) + rows - 1) / rows);
+}
+inline int64_t decode_capacity(const pa_attn_params* p, const Plan& pl) { return int64_t(p->num_seqs) * pl.parts; }
+
+// Workspace: [work lists of the persistent kernels][region A][region B].
 inline size_t plan_bytes(const pa_attn_params* p, const Plan& pl) {
-  if (!pl.fast) return 0;
-  return (pa::decode_gqa_plan_bytes(p->num_seqs, pl.parts) + 255) / 256 * 256;
+  if (!pl.fast && !pl.prefill) return 0;
+  return pa::plan_bytes(pl.fast ? decode_capacity(p, pl) : 0, pl.prefill ? prefill_capacity(p) : 0);
 }
 
 pa_status check_params(const pa_attn_params* p) {
@@ -210,7 +218,7 @@ pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, con
   d.part_size = effective_partition(p);
   d.max_parts = int32_t(pl.parts);
   d.scale_log2 = scale_log2;
-  d.plan = pl.fast ? static_cast<int32_t*>(workspace) : nullptr;
+  d.plan = (pl.fast || pl.prefill) ? static_cast<int32_t*>(workspace) : nullptr;
 
   // Partials of a region: o [rows, Hq, parts, D] followed by (m, l) [rows, Hq, parts, 2].
   auto point_at = [&](float* region, int64_t rows) {
@@ -219,6 +227,21 @@ pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, con
   };
 
   hipError_t e = hipSuccess;
+  if (pl.fast || pl.prefill) {
+    pa::PlanArgs pa_{};
+    pa_.cu_seqlens = cu_seqlens_q;
+    pa_.seq_lens = seq_lens;
+    pa_.plan = static_cast<int32_t*>(workspace);
+    pa_.pref_off_ints = pl.fast ? 4 * decode_capacity(p, pl) : 0;
+    pa_.num_seqs = p->num_seqs;
+    pa_.part_size = d.part_size;
+    pa_.group = g;
+    pa_.decode = pl.fast ? 1 : 0;
+    pa_.prefill = pl.prefill ? 1 : 0;
+    pa_.max_query_len = p->max_query_len;
+    pa_.max_seq_len = p->max_seq_len;
+    if (pa::launch_plan(pa_, s) != hipSuccess) return PA_ERR_LAUNCH;
+  }
   if (pl.fast) {
     point_at(region_a, pl.rows_a);
     d.row_mode = pa::kSingleRowOnly;
@@ -249,8 +272,8 @@ pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, con
     f.num_q_heads = p->num_q_heads;
     f.num_kv_heads = p->num_kv_heads;
     f.max_blocks_per_seq = p->max_blocks_per_seq;
-    const int rpt = pa::prefill_rows_per_tile(p->head_dim, g);
-    f.m_tiles = (p->max_query_len + rpt - 1) / rpt;
+    f.plan = static_cast<const int32_t*>(workspace);
+    f.pref_off_ints = pl.fast ? 4 * decode_capacity(p, pl) : 0;
     f.scale_log2 = scale_log2;
     e = pa::launch_prefill(p->head_dim, g, f, s);
     if (e != hipSuccess) return PA_ERR_LAUNCH;

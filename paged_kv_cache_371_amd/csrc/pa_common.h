@@ -80,6 +80,61 @@ __device__ __forceinline__ float group_max(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---- lanes 16 / 32 apart ---------------------------------------------------------
+// v_permlane32_swap: lanes 32..63 of a <-> lanes 0..31 of b; v_permlane16_swap:
+// odd 16-lane rows of a <-> even rows of b.  Summing or maxing the two results
+// combines values 32 (resp. 16) lanes apart.
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+// max / sum over lanes l, l^16, l^32, l^48 (the four 16-lane rows); every lane gets the result.
+__device__ __forceinline__ float rows_max(float v) {
+  float a = v, b = v;
+  swap32(a, b);
+  v = fmaxf(a, b);
+  a = v;
+  b = v;
+  swap16(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  float a = v, b = v;
+  swap32(a, b);
+  v = a + b;
+  a = v;
+  b = v;
+  swap16(a, b);
+  return a + b;
+}
+
+// ---- wave-uniform values ----------------------------------------------------------
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <typename T>
+__device__ __forceinline__ T* uni_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = uint32_t(uni(int(uint32_t(v)))), hi = uint32_t(uni(int(uint32_t(v >> 32))));
+  return reinterpret_cast<T*>(lo | (hi << 32));
+}
+
+// Read-only metadata is read through the constant address space: the loads
+// are then scalar (s_load) even when the kernel also stores to memory the
+// compiler cannot prove disjoint from it.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+
+__device__ __forceinline__ int32_t load_const(const int32_t* p, int64_t i) { return ((const_i32*)(p))[i]; }
+// Same, but the load may not be moved (sunk towards its use): for prefetches.
+__device__ __forceinline__ int32_t load_const_early(const int32_t* p, int64_t i) {
+  return ((volatile const_i32*)(p))[i];
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 }  // namespace pa

@@ -52,7 +52,8 @@ struct PrefillArgs {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t max_blocks_per_seq;
-  int32_t m_tiles;        // query-row tiles per request = ceil(max_query_len / rows per tile)
+  const int32_t* plan;    // work list (prefill entries at plan + kPlanHeaderInts + pref_off_ints)
+  int64_t pref_off_ints;
   float scale_log2;
 };
 
@@ -65,13 +66,34 @@ hipError_t launch_decode(int dtype, int head_dim, int group, const DecodeArgs& a
                          hipStream_t stream);
 bool decode_supported(int dtype, int head_dim, int group, int part_size);
 
-// Fast single-row decode (bf16, D = 128, G in {1, 2, 4, 8}); partials by request.
-// It needs decode_gqa_plan_bytes() of workspace for its work list (a.plan).
-constexpr int kPlanHeaderInts = 64;      // claim counters, entry count, padding to 256 B
-constexpr int kPlanCountInt = 8;         // header slot holding the number of list entries
+// Work lists of the persistent kernels (plan.hip), in the workspace.
+constexpr int kPlanHeaderInts = 64;      // header words (256 bytes)
+constexpr int kPlanCountInt = 8;         // header slot: number of decode entries
+constexpr int kPlanPrefCountInt = 9;     // header slot: number of prefill entries
 constexpr int kMaxPartBuckets = 512;     // partition_size / 16 of the fast kernel, at most
+constexpr int kPrefillPairs = 128;       // (query row, head) pairs per prefill work item
+constexpr int kPrefillKeys = 64;         // keys per prefill K/V tile
+
+struct PlanArgs {
+  const int32_t* cu_seqlens;
+  const int32_t* seq_lens;
+  int32_t* plan;
+  int64_t pref_off_ints;   // prefill entries start at plan + kPlanHeaderInts + pref_off_ints
+  int32_t num_seqs;
+  int32_t part_size;       // decode partition size
+  int32_t group;           // query heads per KV head
+  int32_t decode;          // build the decode list
+  int32_t prefill;         // build the prefill list
+  int32_t max_query_len;   // requests beyond these bounds get no entries, so the
+  int32_t max_seq_len;     // lists never outgrow the capacity the host sized
+};
+hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
+// Bytes of a plan buffer for these capacities (entries), rounded to 256.
+size_t plan_bytes(int64_t decode_capacity, int64_t prefill_capacity);
+
+// Fast single-row decode (bf16, D = 128, G in {1, 2, 4, 8}); partials by request.
+// Reads its work list from a.plan (built by launch_plan first).
 bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size);
-size_t decode_gqa_plan_bytes(int64_t num_seqs, int64_t max_parts);
 // Waves of the persistent fast decode kernel on the current device.
 int decode_gqa_workers(int group);
 hipError_t launch_decode_gqa(int group, const DecodeArgs& a, hipStream_t stream);
@@ -79,9 +101,9 @@ hipError_t launch_decode_gqa(int group, const DecodeArgs& a, hipStream_t stream)
 hipError_t launch_merge(int dtype, int head_dim, const DecodeArgs& a, int64_t partial_rows, hipStream_t stream);
 size_t decode_lds_bytes(int dtype, int head_dim, int group, int part_size);
 
+// MFMA kernel for multi-row requests (bf16, D = 128, G in {1, 2, 4, 8}).
 hipError_t launch_prefill(int head_dim, int group, const PrefillArgs& a, hipStream_t stream);
 bool prefill_supported(int head_dim, int group);
-int prefill_rows_per_tile(int head_dim, int group);
 
 hipError_t launch_validate(const int32_t* cu, const int32_t* seq_lens, const int32_t* bt, const int64_t* slots,
                            int64_t num_slots, int32_t num_seqs, int64_t total_q, int32_t max_query_len,

@@ -1,0 +1,132 @@
+// Work lists of the persistent attention kernels, built on the device from
+// cu_seqlens and seq_lens so the host never reads request lengths.
+//
+// Layout of the plan buffer (int32 words):
+//   [kPlanCountInt]      number of decode entries
+//   [kPlanPrefCountInt]  number of prefill entries
+//   [kPlanHeaderInts ..)                   decode entries, int4 (request, partition, query row, context length)
+//   [kPlanHeaderInts + pref_off ..)        prefill entries, int4 (request, row tile, query row, query rows)
+//
+// Decode list: one entry per non-empty context partition of every single-row
+// request -- all full partitions first, then the partial last partitions by
+// decreasing number of blocks.  Prefill list: one entry per tile of
+// kPrefillPairs (query row, head) pairs of every multi-row request, by
+// decreasing number of 64-key tiles the tile has to visit.  Both orders put
+// the largest items first, which the consumers' zig-zag assignment relies on.
+// Requests whose lengths break the bounds the host sized the buffer for get no
+// entries (their output rows are left untouched).
+#include "pa_common.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kPrefBuckets = 512;   // key-tile counts are clamped into this many buckets
+
+// Exclusive positions of the buckets in decreasing bucket order, written over
+// hist[0..n); returns the total.  Hillis-Steele scan, n <= blockDim.x.
+__device__ int scan_desc(int* hist, int* tmp, int n, int base) {
+  const int tid = threadIdx.x;
+  int x = tid < n ? hist[n - 1 - tid] : 0;
+  for (int off = 1; off < n; off <<= 1) {
+    if (tid < n) tmp[tid] = x;
+    __syncthreads();
+    if (tid < n && tid >= off) x += tmp[tid - off];
+    __syncthreads();
+  }
+  if (tid == n - 1) tmp[0] = base + x;   // total
+  __syncthreads();
+  const int total = tmp[0];
+  if (tid < n) hist[n - 1 - tid] = base + x - hist[n - 1 - tid];
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
+  __shared__ int s_hist[kPrefBuckets > kMaxPartBuckets ? kPrefBuckets : kMaxPartBuckets];
+  __shared__ int s_tmp[kPrefBuckets > kMaxPartBuckets ? kPrefBuckets : kMaxPartBuckets];
+  __shared__ int s_full;
+  __shared__ int s_cursor;
+  const int tid = threadIdx.x;
+  const int32_t* __restrict__ cu = a.cu_seqlens;
+  const int32_t* __restrict__ seq_lens = a.seq_lens;
+
+  if (a.decode) {
+    const int P = a.part_size;
+    const int nbk = P / kBlock;
+    for (int i = tid; i < nbk; i += blockDim.x) s_hist[i] = 0;
+    if (tid == 0) {
+      s_full = 0;
+      s_cursor = 0;
+    }
+    __syncthreads();
+    for (int b = tid; b < a.num_seqs; b += blockDim.x) {
+      if (cu[b + 1] - cu[b] != 1) continue;
+      const int L = seq_lens[b];
+      if (L > a.max_seq_len) continue;
+      const int nf = L / P;
+      const int rem = L - nf * P;
+      if (nf) atomicAdd(&s_full, nf);
+      if (rem > 0) atomicAdd(&s_hist[(rem - 1) / kBlock], 1);
+    }
+    __syncthreads();
+    const int total = scan_desc(s_hist, s_tmp, nbk, s_full);
+    if (tid == 0) a.plan[kPlanCountInt] = total;
+    int4* entries = reinterpret_cast<int4*>(a.plan + kPlanHeaderInts);
+    for (int b = tid; b < a.num_seqs; b += blockDim.x) {
+      const int q0 = cu[b];
+      if (cu[b + 1] - q0 != 1) continue;
+      const int L = seq_lens[b];
+      if (L > a.max_seq_len) continue;
+      const int nf = L / P;
+      const int rem = L - nf * P;
+      int pos = nf ? atomicAdd(&s_cursor, nf) : 0;
+      for (int p = 0; p < nf; ++p, ++pos) entries[pos] = make_int4(b, p, q0, L);
+      if (rem > 0) entries[atomicAdd(&s_hist[(rem - 1) / kBlock], 1)] = make_int4(b, nf, q0, L);
+    }
+    __syncthreads();
+  }
+
+  if (a.prefill) {
+    const int rows = kPrefillPairs / a.group;   // query rows per tile
+    for (int i = tid; i < kPrefBuckets; i += blockDim.x) s_hist[i] = 0;
+    __syncthreads();
+    // bucket of a tile = number of 64-key tiles its last row visits, clamped
+    auto bucket = [&](int L, int n, int mt) {
+      const int last = min(n, (mt + 1) * rows);   // rows [mt*rows, last)
+      const int keys = L - n + last;
+      return min((keys + kPrefillKeys - 1) / kPrefillKeys, kPrefBuckets - 1);
+    };
+    for (int b = tid; b < a.num_seqs; b += blockDim.x) {
+      const int n = cu[b + 1] - cu[b];
+      const int L = seq_lens[b];
+      if (n < 2 || n > a.max_query_len || L < n || L > a.max_seq_len) continue;
+      for (int mt = 0; mt * rows < n; ++mt) atomicAdd(&s_hist[bucket(L, n, mt)], 1);
+    }
+    __syncthreads();
+    const int total = scan_desc(s_hist, s_tmp, kPrefBuckets, 0);
+    if (tid == 0) a.plan[kPlanPrefCountInt] = total;
+    int4* entries = reinterpret_cast<int4*>(a.plan + kPlanHeaderInts + a.pref_off_ints);
+    for (int b = tid; b < a.num_seqs; b += blockDim.x) {
+      const int q0 = cu[b];
+      const int n = cu[b + 1] - q0;
+      const int L = seq_lens[b];
+      if (n < 2 || n > a.max_query_len || L < n || L > a.max_seq_len) continue;
+      for (int mt = 0; mt * rows < n; ++mt) entries[atomicAdd(&s_hist[bucket(L, n, mt)], 1)] = make_int4(b, mt, q0, n);
+    }
+  }
+}
+
+}  // namespace
+
+size_t plan_bytes(int64_t decode_capacity, int64_t prefill_capacity) {
+  const size_t ints = size_t(kPlanHeaderInts) + 4 * size_t(decode_capacity) + 4 * size_t(prefill_capacity);
+  return (ints * sizeof(int32_t) + 255) / 256 * 256;
+}
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

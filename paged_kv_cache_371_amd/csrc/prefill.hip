@@ -1,11 +1,338 @@
-// MFMA prefill kernel for multi-row requests (placeholder until built).
+// MFMA attention for multi-row (chunked-prefill) requests, bf16, D = 128.
+//
+// quant67, "PagedAttention 与 Continuous Batching" §4.2: a long prompt is
+// processed in chunks batched with decode rows; a chunk's rows attend to the
+// cached prefix plus the causal part of their own chunk (bottom-right
+// alignment: row j of a request with n rows and context L sees keys
+// 0 .. L-n+j).  Every K/V byte serves many query rows here, so Q.K^T and P.V
+// are dense contractions and run on the matrix cores
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
+//
+// Work item: (request, KV head, tile of 128 (query row, head) pairs), the
+// pairs packed as m = row * G + head over the G query heads of the KV head.
+// Four waves own 32 pairs each (two 16-column MFMA blocks).  Keys are visited
+// in tiles of 64 (four paged blocks; wave w fetches block w of the tile, so
+// every load has a wave-uniform base).  Tiles are fetched into registers two
+// ahead and written to one of two LDS stages: K as 16-byte d-chunks, chunk
+// major (a 16-lane MFMA read is 256 contiguous bytes), V transposed (V^T,
+// d-major, rows padded to 136 bytes) by a 4 x 8 register transpose.  Both
+// layouts make the staging writes and the MFMA operand reads bank-conflict
+// free.
+//
+// Per tile and wave: S^T = K Q^T (keys x pairs, d contracted in 4 steps of
+// 32), so a lane holds one pair's column and the online softmax over keys is
+// in-lane plus two permlane swaps.  P^T then feeds O^T = V^T P^T as the B
+// operand without moving data: inside each 32-key step the keys are taken in
+// the order the S^T accumulators hold them (lane row h owns keys 4h..4h+3 and
+// 16+4h..16+4h+3), and V^T is read from LDS in that same order.  P is rounded
+// to bf16 for the MFMA, and the softmax sum uses the rounded values.
+//
+// Positions past the context (the partial last block, clamped block ids)
+// are zeroed when staged and masked as keys, so NaN in unused slots cannot
+// reach the output.
+#include <atomic>
+
 #include "pa_common.h"
 #include "pa_internal.h"
 
 namespace pa {
+namespace {
 
-bool prefill_supported(int, int) { return false; }
-int prefill_rows_per_tile(int, int) { return 1; }
-hipError_t launch_prefill(int, int, const PrefillArgs&, hipStream_t) { return hipErrorInvalidValue; }
+constexpr int kD = 128;
+constexpr int kPairs = kPrefillPairs;        // (row, head) pairs per work item
+constexpr int kKeys = kPrefillKeys;          // keys per tile = kBlock * waves
+constexpr int kTileBytes = kBlock * kD * 2;  // one (block, KV head) tile of bf16
+constexpr int kKChunk = kKeys * 16 + 16;     // LDS bytes per 8-wide d-chunk of K (64 keys + pad)
+constexpr int kVRow = kKeys * 2 + 8;         // LDS bytes per d row of V^T (64 keys + pad)
+constexpr int kKBytes = (kD / 8) * kKChunk;
+constexpr int kVBytes = kD * kVRow;
+constexpr int kStageBytes = kKBytes + kVBytes;
+constexpr int kLdsBytes = 2 * kStageBytes;
+constexpr unsigned kRsrcWord3 = 0x00020000u;
+constexpr float kMinusBig = -1e30f;
+
+static_assert(kKeys == 4 * kBlock, "a key tile is one paged block per wave");
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+__device__ __forceinline__ f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
+                                                  0);
+}
+
+// One thread's share of a 64-key tile, both from block `wave` of the tile:
+//   k[kk]: key 4*(lane/16) + kk of the block, d-chunk lane%16
+//   v[kk]: key 4*(lane%4)  + kk of the block, d-chunk lane/4
+struct TileRegs {
+  u32x4_t k[4];
+  u32x4_t v[4];
+};
+
+template <int G>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
+  constexpr int kRows = kPairs / G;   // query rows per work item
+  extern __shared__ __align__(16) char smem[];
+
+  const int hkv = a.num_kv_heads;
+  const int total = load_const(a.plan, kPlanPrefCountInt) * hkv;
+  const int W = gridDim.x;
+  const int wg = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uni(tid >> 6);
+  const int h = lane >> 4;    // 16-lane row of the wave
+  const int lc = lane & 15;   // MFMA column of the lane
+  // staging coordinates (see TileRegs)
+  const int kkey = 4 * (lane >> 4), kchunk = lane & 15;
+  const int vkey = 4 * (lane & 3), vchunk = lane >> 2;
+  const int64_t bstride = int64_t(hkv) * kTileBytes;
+  const float scale_log2 = a.scale_log2;
+  const int32_t* entries = a.plan + kPlanHeaderInts + a.pref_off_ints;
+
+  for (int i = 0, base = 0; base < total; ++i, base += W) {
+    const int t = base + ((i & 1) ? W - 1 - wg : wg);
+    if (t >= total) continue;
+    const int e = t / hkv;
+    const int kvh = t - e * hkv;
+    const int b = load_const(entries, 4 * int64_t(e));
+    const int mt = load_const(entries, 4 * int64_t(e) + 1);
+    const int q0 = load_const(entries, 4 * int64_t(e) + 2);
+    const int n = load_const(entries, 4 * int64_t(e) + 3);
+    const int L = load_const(a.seq_lens, b);
+    const int P = L - n;                  // cached tokens before this request's rows
+    const int j0 = mt * kRows;            // rows [j0, j1) of the request
+    const int j1 = min(n, j0 + kRows);
+    const int kmax = P + j1;              // keys visible to the last row
+    const int KT = (kmax + kKeys - 1) / kKeys;
+    const int nblk = max(1, min((L + kBlock - 1) / kBlock, a.max_blocks_per_seq));
+    const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks_per_seq;
+    const char* kbase = static_cast<const char*>(a.k_cache) + int64_t(kvh) * kTileBytes;
+    const char* vbase = static_cast<const char*>(a.v_cache) + int64_t(kvh) * kTileBytes;
+
+    // ---- this lane's two pairs: m = wave*32 + mb*16 + lc ----------------------
+    int jrow[2], hq[2], limit[2];
+    bool mvalid[2];
+    u32x4_t qb[2][4];   // B operand Q^T: pair lc, d = 32s + 8h .. +7
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int m = wave * 32 + mb * 16 + lc;
+      jrow[mb] = j0 + m / G;
+      hq[mb] = kvh * G + m % G;
+      mvalid[mb] = jrow[mb] < j1;
+      limit[mb] = mvalid[mb] ? P + jrow[mb] : 0;
+      const char* qrow = static_cast<const char*>(a.q) +
+                         (int64_t(q0 + (mvalid[mb] ? jrow[mb] : 0)) * a.q_row_stride + int64_t(hq[mb]) * kD) * 2;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qrow + (32 * s + 8 * h) * 2);
+        qb[mb][s] = mvalid[mb] ? v : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+
+    f32x4_t acc[2][8];   // O^T blocks: d = 16*db + 4h + r, pair lc
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int db = 0; db < 8; ++db) acc[mb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float mrun[2] = {kMinusBig, kMinusBig};
+    float lrun[2] = {0.f, 0.f};
+
+    // ---- K/V tile staging -----------------------------------------------------
+    // Physical block of this wave's part of tile kt (clamped into the table;
+    // positions past the context are zeroed when staged).
+    auto phys_of = [&](int kt) -> int { return load_const_early(table, min(kt * 4 + wave, nblk - 1)); };
+    auto fetch = [&](TileRegs& rg, int kt, int phys) {
+      const int nrec = kt < KT ? kTileBytes : 0;
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + int64_t(phys) * bstride), 0, nrec, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + int64_t(phys) * bstride), 0, nrec, kRsrcWord3);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        rg.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, (kkey + kk) * (kD * 2) + kchunk * 16, 0, 0);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        rg.v[kk] = __builtin_amdgcn_raw_buffer_load_b128(rv, (vkey + kk) * (kD * 2) + vchunk * 16, 0, 0);
+    };
+    auto stage_write = [&](TileRegs& rg, int kt, int st) {
+      char* ks = smem + st * kStageBytes;
+      char* vs = ks + kKBytes;
+      const int key0 = kt * kKeys + wave * kBlock;   // first position of this wave's block
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const u32x4_t kv = key0 + kkey + kk < L ? rg.k[kk] : z;
+        *reinterpret_cast<u32x4_t*>(ks + kchunk * kKChunk + (wave * kBlock + kkey + kk) * 16) = kv;
+      }
+      u32x4_t vv[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) vv[kk] = key0 + vkey + kk < L ? rg.v[kk] : z;
+      // V^T: d rows 8*vchunk + 2w (+1) get this thread's 4 keys (8 bytes each)
+      char* vcol = vs + (wave * kBlock + vkey) * 2;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t lo01 = __builtin_amdgcn_perm(vv[1][w], vv[0][w], 0x05040100u);
+        const uint32_t lo23 = __builtin_amdgcn_perm(vv[3][w], vv[2][w], 0x05040100u);
+        const uint32_t hi01 = __builtin_amdgcn_perm(vv[1][w], vv[0][w], 0x07060302u);
+        const uint32_t hi23 = __builtin_amdgcn_perm(vv[3][w], vv[2][w], 0x07060302u);
+        *reinterpret_cast<u32x2_t*>(vcol + (8 * vchunk + 2 * w) * kVRow) = u32x2_t{lo01, lo23};
+        *reinterpret_cast<u32x2_t*>(vcol + (8 * vchunk + 2 * w + 1) * kVRow) = u32x2_t{hi01, hi23};
+      }
+    };
+
+    // ---- one tile from LDS stage st -----------------------------------------------
+    auto compute = [&](int kt, int st) {
+      const char* ks = smem + st * kStageBytes;
+      const char* vs = ks + kKBytes;
+      f32x4_t sacc[4][2];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) sacc[c][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(ks + (4 * s + h) * kKChunk + (16 * c + lc) * 16);
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) sacc[c][mb] = mfma16(ka, qb[mb][s], sacc[c][mb]);
+        }
+      const bool diag = kt * kKeys + kKeys - 1 > P + j0;   // some key of the tile is past some row's limit
+      u32x4_t pb[2][2];   // B operand P^T per (pair block, 32-key step)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        float sc[4][4];
+        float tmax = -__builtin_inff();
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float v = sacc[c][mb][r] * scale_log2;
+            if (diag && kt * kKeys + 16 * c + 4 * h + r > limit[mb]) v = -__builtin_inff();
+            sc[c][r] = v;
+            tmax = fmaxf(tmax, v);
+          }
+        tmax = rows_max(tmax);
+        const float mnew = fmaxf(mrun[mb], tmax);
+        const float alpha = fast_exp2(mrun[mb] - mnew);
+        mrun[mb] = mnew;
+        float lsum = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          uint32_t w[4];
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int c = 2 * u + half;
+            w[2 * half] = pack_bf16x2(fast_exp2(sc[c][0] - mnew), fast_exp2(sc[c][1] - mnew));
+            w[2 * half + 1] = pack_bf16x2(fast_exp2(sc[c][2] - mnew), fast_exp2(sc[c][3] - mnew));
+          }
+#pragma unroll
+          for (int x = 0; x < 4; ++x) lsum += bf16_lo(w[x]) + bf16_hi(w[x]);
+          pb[mb][u] = u32x4_t{w[0], w[1], w[2], w[3]};
+        }
+        lrun[mb] = lrun[mb] * alpha + lsum;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) acc[mb][db] *= alpha;
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const char* vrow = vs + (16 * db + lc) * kVRow;
+          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow + (32 * u + 4 * h) * 2);
+          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + (32 * u + 16 + 4 * h) * 2);
+          const u32x4_t va = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) acc[mb][db] = mfma16(va, pb[mb][u], acc[mb][db]);
+        }
+    };
+
+    // ---- tile pipeline: registers two tiles ahead, two LDS stages -------------------
+    // Each barrier separates the staging write of a stage from the computes
+    // that read it, before and after.
+    __syncthreads();   // the previous item is done with both stages
+    TileRegs ra, rb;
+    int pha = phys_of(0);
+    const int phb = phys_of(1);
+    int phc = phys_of(2);
+    fetch(ra, 0, pha);
+    fetch(rb, 1, phb);
+    stage_write(ra, 0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; kt += 2) {
+      // tile kt (stage 0) computed; tile kt+2 fetched into ra; tile kt+1 staged
+      fetch(ra, kt + 2, phc);
+      pha = phys_of(kt + 3);
+      compute(kt, 0);
+      if (kt + 1 < KT) stage_write(rb, kt + 1, 1);
+      __syncthreads();
+      if (kt + 1 >= KT) break;
+      // tile kt+1 (stage 1) computed; tile kt+3 fetched into rb; tile kt+2 staged
+      fetch(rb, kt + 3, pha);
+      phc = phys_of(kt + 4);
+      compute(kt + 1, 1);
+      if (kt + 2 < KT) stage_write(ra, kt + 2, 0);
+      __syncthreads();
+    }
+
+    // ---- normalise and store ----------------------------------------------------
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const float inv = 1.f / rows_sum(lrun[mb]);
+      if (mvalid[mb]) {
+        __bf16* orow = static_cast<__bf16*>(a.out) + int64_t(q0 + jrow[mb]) * a.o_row_stride + int64_t(hq[mb]) * kD;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const u32x2_t o = {pack_bf16x2(acc[mb][db][0] * inv, acc[mb][db][1] * inv),
+                             pack_bf16x2(acc[mb][db][2] * inv, acc[mb][db][3] * inv)};
+          *reinterpret_cast<u32x2_t*>(orow + 16 * db + 4 * h) = o;
+        }
+      }
+    }
+  }
+}
+
+template <int G>
+int prefill_groups() {
+  static std::atomic<int> cache{0};
+  int v = cache.load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int dev = 0, cus = 0, occ = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, prefill_kernel<G>, 256, kLdsBytes) != hipSuccess || occ <= 0)
+    occ = 1;
+  v = cus * occ;
+  cache.store(v, std::memory_order_relaxed);
+  return v;
+}
+
+template <int G>
+hipError_t launch_g(const PrefillArgs& a, hipStream_t stream) {
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<G>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(prefill_kernel<G>, dim3(prefill_groups<G>()), dim3(256), kLdsBytes, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_supported(int head_dim, int group) {
+  return head_dim == kD && (group == 1 || group == 2 || group == 4 || group == 8);
+}
+
+hipError_t launch_prefill(int head_dim, int group, const PrefillArgs& a, hipStream_t stream) {
+  if (head_dim != kD) return hipErrorInvalidValue;
+  switch (group) {
+    case 1: return launch_g<1>(a, stream);
+    case 2: return launch_g<2>(a, stream);
+    case 4: return launch_g<4>(a, stream);
+    case 8: return launch_g<8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 }  // namespace pa

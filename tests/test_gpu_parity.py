@@ -95,6 +95,22 @@ def test_multirow_and_empty_requests(dtype, D, Hq, Hkv):
         assert ok, (ps, mx, mean)
 
 
+PREFILL_N = [2, 7, 16, 17, 64, 65, 129, 300, 1, 1]
+PREFILL_L = [2, 40, 16, 200, 64, 1000, 129, 700, 33, 1]
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 4), (16, 4), (16, 2)])
+def test_prefill_chunk_edges(Hq, Hkv):
+    """Multi-row requests on the MFMA path: chunk lengths around the 16-row
+    MFMA blocks and the 128-pair row tiles, with and without a cached prefix
+    (L == n is a whole prompt in one chunk), mixed with decode rows."""
+    c = build_case(f"prefill_{Hq}_{Hkv}", 8, "bf16", Hq, Hkv, 128, PREFILL_N, PREFILL_L)
+    say("case", c.name)
+    mx, mean, ok, _ = run_and_compare(c)
+    say(f"  max {mx:.3g} mean {mean:.3g}")
+    assert ok, (mx, mean)
+
+
 def test_context_length_one_is_v_bitwise():
     c = build_case("len1", 7, "bf16", 8, 2, 128, [1, 1, 1], [1, 1, 1])
     dc = DeviceCase(c)
