@@ -8,9 +8,18 @@ requests, 64 query / 8 KV heads, D=128, bf16, log-normal contexts with median
 
 Prints one JSON line.  ``value`` is KV GB/s: the attention's algorithmic
 K/V bytes per step divided by the step time (inputs resident in HBM).
-``roofline`` reports the attention launch alone (split-K decode + merge),
-timed with HIP events on the launch stream.  ``cpu_baseline`` times the fp64
-CPU oracle on a bounded sample of the same requests.  Parity of this exact
+``roofline`` reports one pa_attention_varlen call (the work-list kernel, the
+split-K decode kernel and the partition merge; the prefill kernel too when the
+batch has multi-row requests), timed with HIP events on the launch stream.
+Its ``traffic`` is the HBM bytes per call that rocprofv3's FETCH_SIZE and
+WRITE_SIZE counters measured, scaled by the same counters' reading for a
+plain copy of known size; it is read from the committed counter summary
+under profiles/ and reported only while the kernel sources still hash to
+the digest recorded there (null otherwise).  ``cpu_baseline`` times the fp64
+CPU oracle on a bounded sample of the same requests.
+
+``--calibrate-copy`` runs only a 1 GiB device-to-device copy (the counters'
+calibration run).  Parity of this exact
 launch configuration against the oracle is the job of the GPU tests; the
 oracle is used here only for the CPU baseline.
 """
@@ -32,6 +41,38 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+CSRC = os.path.join(ROOT, "paged_kv_cache_371_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 1 << 30
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the HIP/C++ sources of the library (file names and bytes, sorted by name)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".cpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention call from the committed counter summary, or None
+    when there is none or the kernels changed since it was taken."""
+    import re
+
+    path = os.path.join(PROFILES, f"attention_call_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    dig = re.search(r"^source_sha256:\s*([0-9a-f]{64})", text, re.M)
+    val = re.search(r"^traffic_bytes_per_call:\s*(\d+)", text, re.M)
+    if not dig or not val or dig.group(1) != kernel_source_digest():
+        return None
+    return int(val.group(1))
 
 
 def algorithmic_bytes(c) -> dict:
@@ -59,7 +100,8 @@ def attention_flops(c) -> float:
 
 
 def cpu_baseline(c, budget_s: float = 12.0) -> dict:
-    """Time the fp64 oracle on whole requests until the budget is spent (one BLAS thread)."""
+    """Time the fp64 oracle on whole requests, in passes over the batch in a
+    fixed shuffled order, until the budget is spent (one BLAS thread)."""
     import oracle
 
     try:
@@ -70,27 +112,40 @@ def cpu_baseline(c, budget_s: float = 12.0) -> dict:
     kp, vp = oracle.oracle_cache_write(c.k_cache, c.v_cache, c.k_new, c.v_new, c.slot_mapping)
     order = np.random.default_rng(1).permutation(c.num_seqs)
     s = 2 if c.dtype == "bf16" else 4
-    done_rows = done_kv = 0
+    done_rows = done_kv = reqs = 0
     t0 = time.perf_counter()
-    reqs = 0
-    for b in order:
-        rows = list(range(int(c.cu_seqlens[b]), int(c.cu_seqlens[b + 1])))
-        if not rows:
-            continue
-        oracle.oracle_attention_varlen(c.q, kp, vp, c.cu_seqlens, c.seq_lens, c.block_tables, c.scale,
-                                       c.num_kv_heads, c.dtype, rows=rows, validate=False)
-        done_rows += len(rows)
-        done_kv += int(c.seq_lens[b]) * c.num_kv_heads * c.head_dim * 2 * s
-        reqs += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
+    while time.perf_counter() - t0 < budget_s:
+        for b in order:
+            rows = list(range(int(c.cu_seqlens[b]), int(c.cu_seqlens[b + 1])))
+            if not rows:
+                continue
+            oracle.oracle_attention_varlen(c.q, kp, vp, c.cu_seqlens, c.seq_lens, c.block_tables, c.scale,
+                                           c.num_kv_heads, c.dtype, rows=rows, validate=False)
+            done_rows += len(rows)
+            done_kv += int(c.seq_lens[b]) * c.num_kv_heads * c.head_dim * 2 * s
+            reqs += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
     dt = time.perf_counter() - t0
-    if limit is not None:
-        limit.unregister() if hasattr(limit, "unregister") else None
+    if limit is not None and hasattr(limit, "unregister"):
+        limit.unregister()
     return {"value": done_kv / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reqs} of {c.num_seqs} requests ({done_rows} query rows, "
-                      f"{done_kv / 1e9:.3f} GB of KV) in {dt:.1f} s, fp64 NumPy, one BLAS thread",
+            "sample": f"{reqs} requests of the {c.num_seqs}-request batch in passes over it "
+                      f"({done_rows} query rows, {done_kv / 1e9:.3f} GB of KV) in {dt:.1f} s, "
+                      f"fp64 NumPy, one BLAS thread",
             "query_tokens_per_s": done_rows / dt}
+
+
+def calibrate_copy() -> None:
+    """One device-to-device copy of COPY_BYTES (the counter calibration run)."""
+    import torch
+
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": COPY_BYTES}), flush=True)
 
 
 class _DeviceBatch:
@@ -112,6 +167,7 @@ class _DeviceBatch:
         self.tables = torch.from_numpy(c.block_tables).to("cuda:0")
         self.out = torch.empty_like(self.q)
         self.ws = None
+        self.partition_size = None
 
     def cache_write(self):
         self.pa.cache_write(self.k_new, self.v_new, self.k_cache, self.v_cache, self.slots)
@@ -122,6 +178,7 @@ class _DeviceBatch:
             p = self.pa.make_params(self.q, self.k_cache, self.cu, self.tables, c.num_kv_heads, float(c.scale),
                                     c.max_query_len, c.max_seq_len, out=self.out, partition_size=partition_size)
             self.ws = self.torch.empty(max(16, self.pa.workspace_size(p)), dtype=self.torch.uint8, device="cuda:0")
+            self.partition_size = self.pa.partition_size(p)
         self.pa.attention_varlen(self.out, self.q, self.k_cache, self.v_cache, self.cu, self.seq_lens, self.tables,
                                  float(c.scale), c.max_query_len, c.max_seq_len, workspace=self.ws,
                                  partition_size=partition_size)
@@ -137,10 +194,15 @@ def main() -> None:
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this framework runs the path on one GPU; --gpus must be 1 "
+                                   "(sharding across GPUs is designed, not built)"}))
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     import torch
 
@@ -166,17 +228,19 @@ def main() -> None:
         step()
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        dc.cache_write()
         ev[i][0].record(stream)
-        dc.attention(partition_size=args.partition_size)
+        dc.cache_write()
         ev[i][1].record(stream)
+        dc.attention(partition_size=args.partition_size)
+        ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    cw_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     ms_per_step = wall * 1e3 / args.steps
 
     value = ab["kv"] / (ms_per_step * 1e-3) / 1e9
@@ -205,21 +269,23 @@ def main() -> None:
             "block_size": c.block_size,
             "num_blocks": c.num_blocks,
             "mean_context": float(c.seq_lens.mean()),
-            "partition_size": args.partition_size or 512,
+            "partition_size": dc.partition_size,
             "step": "cache_write + attention_varlen",
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "query_tokens_per_s": round(c.total_q / (ms_per_step * 1e-3), 1),
         "attention_ms": round(attn_ms, 5),
+        "cache_write_ms": round(cw_ms, 5),
         "kv_bytes_per_step": ab["kv"],
         "roofline": {
             "bound": "hbm",
-            "kernel": "attention launch (decode_kernel + merge_kernel)",
+            "kernel": "pa_attention_varlen call: plan_kernel + decode_gqa_kernel + merge_kernel"
+                      + (" + prefill_kernel" if c.max_query_len > 1 else ""),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(c.name),
             "algorithmic_bytes_per_launch": ab["attention"],
             "attention_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 3),
         },

@@ -131,6 +131,15 @@ pa_status pa_cache_write(const void* k_new, const void* v_new, int64_t kv_row_st
 size_t pa_attention_workspace_size(const pa_attn_params* p);
 
 /*
+ * Context-partition length (tokens) pa_attention_varlen uses for these
+ * parameters: p->partition_size when it is non-zero, else the library
+ * default.  Returns 0 for invalid parameters.  A caller that needs results
+ * independent of the batch shape can read the default here once and pass it
+ * explicitly from then on.
+ */
+int32_t pa_attention_partition_size(const pa_attn_params* p);
+
+/*
  * pa_attention_varlen -- [Q67] §3.6 and [ICE]: for every request b, row j,
  * query head h:
  *   s_t = scale * <q[row, h, :], K_b[t, h/G, :]>       for t <= L_b - n_b + j

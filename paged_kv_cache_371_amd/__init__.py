@@ -48,6 +48,7 @@ _SIGNATURES = {
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]),
     "pa_attention_workspace_size": (ctypes.c_size_t, [ctypes.c_void_p]),
+    "pa_attention_partition_size": (ctypes.c_int32, [ctypes.c_void_p]),
     "pa_attention_varlen": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_void_p,
                                                                  ctypes.c_size_t, ctypes.c_void_p]),
     "pa_validate_metadata": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -196,6 +197,11 @@ def make_params(q, k_cache, cu_seqlens, block_tables, num_kv_heads: int, scale: 
 
 def workspace_size(params: AttnParams) -> int:
     return int(lib().pa_attention_workspace_size(ctypes.byref(params)))
+
+
+def partition_size(params: AttnParams) -> int:
+    """Context-partition length the attention call uses for ``params`` (0 if they are invalid)."""
+    return int(lib().pa_attention_partition_size(ctypes.byref(params)))
 
 
 def attention_varlen(out, q, k_cache, v_cache, cu_seqlens, seq_lens, block_tables, scale: float,

@@ -6,10 +6,11 @@
 // half of the path (every decode step reads the whole context once), so the
 // design goal is bytes in flight and few VALU instructions per byte.
 //
-// Work split: one workgroup of 4 waves per (request, KV head, context
-// partition).  Wave w owns logical blocks w, w+4, w+8, ... of the partition
-// and serves ALL G query heads of the KV head, so each K/V byte enters the
-// chip once and is used G times from registers.
+// Work split: one wave per work item (request, KV head, context partition);
+// the wave streams the partition's 16-token tiles and serves ALL G query
+// heads of the KV head, so each K/V byte enters the chip once and is used G
+// times from registers.  Items come from a device-built list (largest first)
+// and are dealt to the persistent waves in a zig-zag order (see below).
 //
 // Lane layout for one 16-token tile of one KV head (16 x 256 B, contiguous):
 // lane l = 16*tg + r loads 16 B at token 4*i + tg, d-slice [8r, 8r+8), for
@@ -38,9 +39,9 @@
 // v_perm_b32; each v_dot2_f32_bf16 then adds two tokens' contributions to one
 // fp32 accumulator.  Lane r's accumulator slot j holds head (h(r) +- j) mod G.
 //
-// End of the partition: the 4 token rows of a wave are combined with
-// v_permlane32_swap / v_permlane16_swap (reduce-scatter), the 4 waves through
-// LDS in a fixed order (deterministic).  A request whose context fits in one
+// End of the partition: the 4 token rows of the wave are combined with
+// v_permlane32_swap / v_permlane16_swap (a reduce-scatter, fixed order, so
+// the result is deterministic).  A request whose context fits in one
 // partition is normalised and stored as bf16 (round to nearest even); else
 // the partition's (max, sum, unnormalised output) go to the workspace and the
 // merge kernel combines them.
@@ -193,7 +194,7 @@ __device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t,
 // queue each atomic round trip costs tens of microseconds.)
 //
 // A wave sees its items as one stream of tiles: an item contributes nbr
-// stream slots (its nb tiles padded with empty ones to a multiple of 3), so
+// stream slots (its nb tiles padded with empty ones to a multiple of kRing), so
 // the last load group of an item already fetches the next item's first three
 // tiles and the HBM queue of the wave never drains at item boundaries.  The
 // physical block id of the slot issued next is fetched one issue ahead.

@@ -124,7 +124,8 @@ pa_status check_params(const pa_attn_params* p) {
   const int64_t hd = int64_t(p->num_q_heads) * p->head_dim;
   if (p->q_row_stride < hd || p->o_row_stride < hd) return PA_ERR_SHAPE;
   if (!std::isfinite(p->scale)) return PA_ERR_SHAPE;
-  if (p->partition_size != 0 && (p->partition_size < 16 || p->partition_size % 16)) return PA_ERR_SHAPE;
+  if (p->partition_size != 0 && (p->partition_size < 16 || p->partition_size > 8192 || p->partition_size % 16))
+    return PA_ERR_SHAPE;
   const int eb = elem_bytes(p->dtype);
   if ((p->q_row_stride * eb) % 16 || (p->o_row_stride * eb) % 16) return PA_ERR_ALIGN;
   return PA_OK;
@@ -175,6 +176,11 @@ size_t pa_attention_workspace_size(const pa_attn_params* p) {
   if (!pl.ok) return 0;
   return plan_bytes(p, pl) +
          (region_floats(p, pl.rows_a, pl.parts) + region_floats(p, pl.rows_b, pl.parts)) * sizeof(float);
+}
+
+int32_t pa_attention_partition_size(const pa_attn_params* p) {
+  if (check_params(p) != PA_OK) return 0;
+  return effective_partition(p);
 }
 
 pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, const void* v_cache,

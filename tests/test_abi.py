@@ -83,6 +83,7 @@ def _params(**over):
     (dict(q_row_stride=100), -2),
     (dict(q_row_stride=1028), -4),                  # 2056 bytes: not 16-byte aligned
     (dict(partition_size=24), -2),
+    (dict(partition_size=8208), -2),                # above the 8192-token maximum
     (dict(scale=float("nan")), -2),
     (dict(max_query_len=65), -2),
 ])
@@ -96,10 +97,13 @@ def test_host_rejects_bad_params_before_any_launch(L, over, code):
 def test_host_null_and_workspace_errors(L):
     p = _params(max_seq_len=2048, max_blocks_per_seq=128)
     need = L.pa_attention_workspace_size(ctypes.byref(p))
-    # the fast kernel's work list (64-int header + a (request, partition) pair per
-    # possible partition, padded to 256 B), then rows * Hq * parts * (D + 2) fp32 partials
-    plan = -(-(64 + 2 * 2 * 4) * 4 // 256) * 256
-    assert need == plan + 2 * 8 * 4 * (128 + 2) * 4
+    ps = L.pa_attention_partition_size(ctypes.byref(p))
+    assert ps in (512, 1024, 2048)
+    parts = -(-2048 // ps)
+    # the work list (64-int header + one int4 entry per possible (request,
+    # partition), padded to 256 B), then rows * Hq * parts * (D + 2) fp32 partials
+    plan = -(-(64 + 4 * 2 * parts) * 4 // 256) * 256
+    assert need == plan + 2 * 8 * parts * (128 + 2) * 4
     assert L.pa_attention_varlen(None, 16, 16, 16, 16, 16, 16, ctypes.byref(p), None, 0, None) == -1
     assert L.pa_attention_varlen(16, 16, 16, 16, 16, 16, 16, ctypes.byref(p), 16, need - 1, None) == -5
     assert L.pa_attention_varlen(16, 16, 16, 16, 16, 16, 16, None, None, 0, None) == -1
@@ -107,6 +111,17 @@ def test_host_null_and_workspace_errors(L):
     # an empty batch is a no-op
     assert L.pa_attention_varlen(None, None, None, None, None, None, None,
                                  ctypes.byref(_params(num_seqs=0, total_q=0)), None, 0, None) == 0
+
+
+def test_partition_size_query(L):
+    assert L.pa_attention_partition_size(ctypes.byref(_params(partition_size=256))) == 256
+    assert L.pa_attention_partition_size(ctypes.byref(_params(partition_size=24))) == 0    # not a multiple of 16
+    assert L.pa_attention_partition_size(None) == 0
+    # the default never makes partitions shorter than 512 tokens
+    assert L.pa_attention_partition_size(ctypes.byref(_params())) in (512, 1024, 2048)
+    big = _params(num_seqs=1, total_q=1, max_seq_len=65536, max_blocks_per_seq=4096)
+    assert L.pa_attention_partition_size(ctypes.byref(big)) in (512, 1024, 2048)
+    assert pa.partition_size(_params(partition_size=64)) == 64
 
 
 def test_cache_write_host_errors(L):
