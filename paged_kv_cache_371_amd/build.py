@@ -32,6 +32,12 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
+# Per-source extras.  The decode kernel claims work with a single-lane atomic
+# whose result it reads much later; the atomic optimizer would rewrite it into
+# a wave-wide broadcast read right after the atomic, stalling on its round trip.
+EXTRA_FLAGS = {
+    "decode_gqa.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+}
 
 
 def _hipcc() -> str:
@@ -43,7 +49,7 @@ def _hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + FLAGS
+    cmd = [_hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + FLAGS + EXTRA_FLAGS.get(src, [])
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")

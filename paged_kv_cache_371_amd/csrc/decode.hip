@@ -30,6 +30,8 @@
 //      kernel combines them with log-sum-exp weights.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "pa_common.h"
 #include "pa_internal.h"
 
@@ -344,6 +346,59 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a) {
 #pragma unroll
   for (int e = 0; e < kPer; ++e)
     store_out<E>(a.out, int64_t(row) * a.o_row_stride + int64_t(h) * D + e * 64 + threadIdx.x, o[e] * inv);
+}
+
+// Merge for the fast decode kernel's partials (bf16, D = 128): only the
+// requests on the work list's merge list, one wave per (request, query head).
+// Lanes read the partitions' (max, sum) in parallel and reduce them in a fixed
+// tree; then every lane combines its two d values over the partitions in
+// order, so the result is deterministic.
+__global__ __launch_bounds__(256) void merge_list_kernel(DecodeArgs a) {
+  constexpr int D = 128;
+  const int count = load_const(a.plan, kPlanMergeCountInt);
+  const int32_t* list = a.plan + kPlanHeaderInts + a.merge_off_ints;
+  const int lane = threadIdx.x & 63;
+  const int64_t NW = int64_t(gridDim.x) * 4;
+  const int64_t total = int64_t(count) * a.num_q_heads;
+  for (int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6); t < total; t += NW) {
+    const int e = int(t / a.num_q_heads);
+    const int h = int(t - int64_t(e) * a.num_q_heads);
+    const int b = load_const(list, e);
+    const int L = load_const(a.seq_lens, b);
+    const int q0 = load_const(a.cu_seqlens, b);
+    const int nparts = (L + a.part_size - 1) / a.part_size;
+    const int64_t base = (int64_t(b) * a.num_q_heads + h) * a.max_parts;
+    const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + base;
+    float M = -__builtin_inff();
+    for (int p = lane; p < nparts; p += 64) M = fmaxf(M, ml[p].x);
+    M = group_max<64>(M);
+    float denom = 0.f;
+    for (int p = lane; p < nparts; p += 64) {
+      const float2 v = ml[p];
+      denom = fmaf(fast_exp2(v.x - M), v.y, denom);
+    }
+    denom = group_sum<64>(denom);
+    const float2* po = reinterpret_cast<const float2*>(a.ws_o + base * D) + lane;
+    float ox = 0.f, oy = 0.f;
+#pragma unroll 4
+    for (int p = 0; p < nparts; ++p) {
+      const float w = fast_exp2(ml[p].x - M);
+      const float2 v = po[int64_t(p) * (D / 2)];
+      ox = fmaf(w, v.x, ox);
+      oy = fmaf(w, v.y, oy);
+    }
+    const float inv = 1.f / denom;
+    reinterpret_cast<uint32_t*>(static_cast<__bf16*>(a.out) + int64_t(q0) * a.o_row_stride + int64_t(h) * D)[lane] =
+        pack_bf16x2(ox * inv, oy * inv);
+  }
+}
+
+hipError_t launch_merge_list(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t waves = int64_t(a.num_seqs) * a.num_q_heads;
+  const int64_t grid = std::min<int64_t>((waves + 3) / 4, 1024);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(merge_list_kernel, dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -71,7 +71,21 @@ constexpr int kMaxDevices = 64;
 // second workgroup only competes for issue slots (its waves starve while the
 // first one runs), so its registers are better spent on a deeper ring.
 constexpr int kRing = PA_DECODE_RING;
-constexpr int kItemSlots = 64;   // list entries a wave stages in LDS
+#ifndef PA_DECODE_STATIC_ROUNDS
+#define PA_DECODE_STATIC_ROUNDS 1
+#endif
+constexpr int kStaticRounds = PA_DECODE_STATIC_ROUNDS;   // rounds dealt without claims
+static_assert(kStaticRounds >= 1, "round 0 is static");
+#ifndef PA_DECODE_CLAIM_BATCH
+#define PA_DECODE_CLAIM_BATCH 2
+#endif
+constexpr int kQueue = 16;                         // LDS queue slots of claimed items per workgroup
+constexpr int kClaimBatch = PA_DECODE_CLAIM_BATCH; // items per claim
+#ifndef PA_DECODE_REQUEST_TILES
+#define PA_DECODE_REQUEST_TILES 12
+#endif
+constexpr int kRequestTiles = PA_DECODE_REQUEST_TILES;   // tiles before an item's end its worker asks for the next
+static_assert(kClaimBatch <= kWavesPerGroup && kWavesPerGroup <= kQueue, "one queued item per worker at most");
 
 // Pairing masks of the 16-lane reduction steps and their DPP controls.
 constexpr int kStepMask[4] = {8, 7, 2, 1};
@@ -186,12 +200,18 @@ __device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t,
   return it;
 }
 
-// Persistent kernel; every wave is an independent worker (no barriers).
-// Worker w of NW takes item i*NW + w in even rounds i and i*NW + NW-1-w in
-// odd ones; with the list sorted by decreasing size this zig-zag keeps every
-// worker's share within a few percent of the mean.  (Claiming items through
-// memory atomics balances better in principle, but under a saturated HBM
-// queue each atomic round trip costs tens of microseconds.)
+// Persistent kernel.  Each workgroup has kWavesPerGroup worker waves, which
+// never synchronise with each other, plus one scheduler wave.  The list is
+// sorted by decreasing size.  Rounds 0 .. kStaticRounds-1 are dealt
+// statically: worker w of NW takes item i*NW + w in even rounds i and
+// i*NW + NW-1-w in odd ones.  Later items are claimed from a counter in the
+// list header, in list order, so faster workers take more of the small items
+// at the end (the 8 XCDs stream at rates up to ~20% apart, which a static
+// split cannot absorb).  The scheduler wave makes the claims and hands the
+// items to its workgroup's workers through a small LDS queue: under a
+// saturated HBM queue a device-scope atomic takes microseconds to return,
+// and a worker that issued one would stall its tile stream on it (vector
+// memory counters complete in order).
 //
 // A wave sees its items as one stream of tiles: an item contributes nbr
 // stream slots (its nb tiles padded with empty ones to a multiple of kRing), so
@@ -199,7 +219,7 @@ __device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t,
 // tiles and the HBM queue of the wave never drains at item boundaries.  The
 // physical block id of the slot issued next is fetched one issue ahead.
 template <int G>
-__global__ __launch_bounds__(256, 1) void decode_gqa_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kernel(DecodeArgs a) {
   constexpr int K = log2_of<G>();
   constexpr int kRot = 16 / G;          // lanes between consecutive heads in a row
   constexpr int kNV = G * 8;            // accumulators per lane
@@ -211,10 +231,88 @@ __global__ __launch_bounds__(256, 1) void decode_gqa_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int NW = gridDim.x * kWavesPerGroup;
   const int wid = int(blockIdx.x) * kWavesPerGroup + wave;
-  auto item_of_round = [&](int i) {   // item index of round i, or total if none
+  auto item_of_round = [&](int i) {   // item index of static round i, or total if none
     const int64_t base = int64_t(i) * NW;
     const int64_t t = base + ((i & 1) ? NW - 1 - wid : wid);
     return t < total ? int(t) : total;
+  };
+  const int64_t dyn0 = int64_t(kStaticRounds) * NW;   // first item handed out by claims
+  int* claim_counter = a.plan + kPlanClaimInt;
+
+  // Queue of claimed items with their list entries.  Slot s receives queue
+  // index p = s, s + kQueue, ...; s_qfree[s] is the index it may receive next
+  // (the consumer of index p sets it to p + kQueue once it has read the
+  // item), so the scheduler never overwrites an item that has not been taken.
+  __shared__ int s_qitem[kQueue];
+  __shared__ int4 s_qent[kQueue];
+  __shared__ int s_qfree[kQueue];
+  __shared__ int s_qhead;   // queue indices handed to workers
+  __shared__ int s_qtail;   // queue indices filled
+  __shared__ int s_qend;    // final number of filled indices, once known
+  __shared__ int s_qreq;    // requests made by the workers
+  if (threadIdx.x < kQueue) s_qfree[threadIdx.x] = threadIdx.x;
+  if (threadIdx.x == 0) {
+    s_qreq = 0;
+    s_qhead = 0;
+    s_qtail = 0;
+    s_qend = 0x7fffffff;
+  }
+  __syncthreads();
+  auto lds_load = [](int* p) { return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP); };
+  auto lds_store = [](int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP); };
+  const int4* entries = reinterpret_cast<const int4*>(a.plan + kPlanHeaderInts);
+
+  if (wave == kWavesPerGroup) {   // the scheduler: one claim per batch of requests
+    if (lane == 0) {
+      const int64_t ndyn = int64_t(total) - dyn0;
+      int pushed = 0, served = 0;
+      for (bool more = ndyn > 0; more;) {
+        int req;
+        while ((req = lds_load(&s_qreq)) <= served) __builtin_amdgcn_s_sleep(1);
+        const int want = min(req - served, kClaimBatch);
+        const int c = __hip_atomic_fetch_add(claim_counter, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int n = int(max<int64_t>(0, min<int64_t>(want, ndyn - c)));
+        for (int j = 0; j < n; ++j) {
+          const int q = pushed + j;
+          const int t = int(dyn0 + c + j);
+          const int4 e = entries[t / a.num_kv_heads];
+          while (lds_load(&s_qfree[q % kQueue]) != q) __builtin_amdgcn_s_sleep(1);
+          s_qitem[q % kQueue] = t;
+          s_qent[q % kQueue] = e;
+        }
+        pushed += n;
+        served += want;
+        lds_store(&s_qtail, pushed);
+        more = n == want;
+      }
+      lds_store(&s_qend, pushed);
+    }
+    return;
+  }
+  // A worker asks for its next claimed item (once per item, before taking it).
+  auto request = [&]() {
+    if (lane == 0) __hip_atomic_fetch_add(&s_qreq, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+  // Next claimed item for this worker (index and list entry); index total
+  // when there is none left.
+  auto take = [&](int& t, int4& e) {
+    int q = 0;
+    if (lane == 0) q = __hip_atomic_fetch_add(&s_qhead, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    q = uni(q);
+    for (;;) {
+      if (q < uni(lds_load(&s_qtail))) {
+        t = uni(s_qitem[q % kQueue]);
+        const int4 v = s_qent[q % kQueue];
+        e = make_int4(uni(v.x), uni(v.y), uni(v.z), uni(v.w));
+        if (lane == 0) lds_store(&s_qfree[q % kQueue], q + kQueue);
+        return;
+      }
+      if (q >= uni(lds_load(&s_qend))) {
+        t = total;
+        return;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
   };
 
   const int r = lane & 15;
@@ -263,29 +361,19 @@ __global__ __launch_bounds__(256, 1) void decode_gqa_kernel(DecodeArgs a) {
     });
   };
 
-  // The list entries of this wave's first kItemSlots items are staged in its
-  // LDS slot once, so setting up an item costs an LDS read, not a scalar
-  // memory round trip on the critical path (later items, if any, load directly).
-  __shared__ int4 sitems[kWavesPerGroup][kItemSlots];
+  // The list entries of this wave's static items are staged in its LDS slot
+  // once, so setting up an item costs an LDS read, not a scalar memory round
+  // trip on the critical path.
+  __shared__ int4 sitems[kWavesPerGroup][kStaticRounds];
   {
-    const int4* entries = reinterpret_cast<const int4*>(a.plan + kPlanHeaderInts);
     const int t = item_of_round(lane);
-    if (lane < kItemSlots && t < total) sitems[wave][lane] = entries[t / a.num_kv_heads];
+    if (lane < kStaticRounds && t < total) sitems[wave][lane] = entries[t / a.num_kv_heads];
   }
-  auto entry_of_round = [&](int i) -> int4 {
+  auto static_entry = [&](int i) -> int4 {
     const int t = item_of_round(i);
-    int4 e = {0, 0, 0, 1};
-    if (t < total) {
-      if (i < kItemSlots) {
-        e = sitems[wave][i];
-      } else {
-        const int32_t* p = a.plan + kPlanHeaderInts + 4 * int64_t(t / a.num_kv_heads);
-        e = make_int4(load_const(p, 0), load_const(p, 1), load_const(p, 2), load_const(p, 3));
-      }
-    }
-    return e;
+    return t < total ? sitems[wave][i] : make_int4(0, 0, 0, 1);
   };
-  auto item_for_round = [&](int i) { return make_item(a, total, item_of_round(i), entry_of_round(i)); };
+  auto item_for_round = [&](int i) { return make_item(a, total, item_of_round(i), static_entry(i)); };
 
   Item cur = item_for_round(0);
   if (!cur.valid) return;
@@ -326,9 +414,29 @@ __global__ __launch_bounds__(256, 1) void decode_gqa_kernel(DecodeArgs a) {
   });
 
   for (int i = 0;; ++i) {
-    const Item nxt = item_for_round(i + 1);
+    // The next item.  A static one is known now.  A claimed one is requested
+    // kRequestTiles tiles before this item ends and taken at the start of its
+    // second-to-last load group, just before its first block ids are needed,
+    // so it is handed out as late as the tile stream allows.
+    const bool dyn = i + 1 >= kStaticRounds;
+    Item nxt = make_item(a, total, total, make_int4(0, 0, 0, 1));
     uint32_t qt[kQDw];
-    if (nxt.valid) fetch_q(nxt, qt);
+    bool requested = false;
+    auto get_next = [&]() {
+      if (!requested) request();
+      requested = true;
+      int t;
+      int4 e;
+      take(t, e);
+      nxt = make_item(a, total, t, e);
+      if (nxt.valid) fetch_q(nxt, qt);
+    };
+    if (!dyn) {
+      nxt = make_item(a, total, item_of_round(i + 1), static_entry(i + 1));
+      if (nxt.valid) fetch_q(nxt, qt);
+    } else if (cur.nb <= 2 * kRing) {
+      get_next();
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     float acc[G][8];
@@ -422,6 +530,16 @@ __global__ __launch_bounds__(256, 1) void decode_gqa_kernel(DecodeArgs a) {
     // The scheduling barriers keep the loads of every stage in issue order, so
     // each stage waits only for its own tile (vmcnt = the 16 loads after it).
     for (int k = 0; k < cur.nb; k += kRing) {
+      if (dyn && cur.nb > 2 * kRing) {
+        if (!requested && cur.nb - k <= kRequestTiles) {
+          request();
+          requested = true;
+        }
+        if (k + 2 * kRing >= cur.nb && k + kRing < cur.nb) {
+          get_next();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       static_for<kRing>([&](auto S) {
         constexpr int st = decltype(S)::value;
         if (st == 0 || k + st < cur.nb) process(kr[st], vr[st], k + st);
@@ -523,7 +641,9 @@ int persistent_groups() {
   if (v > 0) return v;
   int cus = 0, occ = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_gqa_kernel<G>, 256, 0) != hipSuccess || occ <= 0)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_gqa_kernel<G>, 64 * (kWavesPerGroup + 1), 0) !=
+          hipSuccess ||
+      occ <= 0)
     occ = 1;
   v = cus * std::min(occ, 1);
   cache[dev].store(v, std::memory_order_relaxed);
@@ -535,7 +655,7 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   const int64_t upper = int64_t(a.num_seqs) * a.max_parts * a.num_kv_heads;
   const int64_t grid = std::min<int64_t>(upper, persistent_groups<G>());
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_gqa_kernel<G>, dim3(grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(decode_gqa_kernel<G>, dim3(grid), dim3(64 * (kWavesPerGroup + 1)), 0, stream, a);
   return hipGetLastError();
 }
 

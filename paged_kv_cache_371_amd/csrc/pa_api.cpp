@@ -106,7 +106,13 @@ inline int64_t decode_capacity(const pa_attn_params* p, const Plan& pl) { return
 // Workspace: [work lists of the persistent kernels][region A][region B].
 inline size_t plan_bytes(const pa_attn_params* p, const Plan& pl) {
   if (!pl.fast && !pl.prefill) return 0;
-  return pa::plan_bytes(pl.fast ? decode_capacity(p, pl) : 0, pl.prefill ? prefill_capacity(p) : 0);
+  return pa::plan_bytes(pl.fast ? decode_capacity(p, pl) : 0, pl.prefill ? prefill_capacity(p) : 0,
+                        pl.fast ? p->num_seqs : 0);
+}
+// Offsets (ints after the header) of the prefill entries and the merge list.
+inline int64_t pref_off(const pa_attn_params* p, const Plan& pl) { return pl.fast ? 4 * decode_capacity(p, pl) : 0; }
+inline int64_t merge_off(const pa_attn_params* p, const Plan& pl) {
+  return pref_off(p, pl) + (pl.prefill ? 4 * prefill_capacity(p) : 0);
 }
 
 pa_status check_params(const pa_attn_params* p) {
@@ -225,6 +231,7 @@ pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, con
   d.max_parts = int32_t(pl.parts);
   d.scale_log2 = scale_log2;
   d.plan = (pl.fast || pl.prefill) ? static_cast<int32_t*>(workspace) : nullptr;
+  d.merge_off_ints = merge_off(p, pl);
 
   // Partials of a region: o [rows, Hq, parts, D] followed by (m, l) [rows, Hq, parts, 2].
   auto point_at = [&](float* region, int64_t rows) {
@@ -238,7 +245,8 @@ pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, con
     pa_.cu_seqlens = cu_seqlens_q;
     pa_.seq_lens = seq_lens;
     pa_.plan = static_cast<int32_t*>(workspace);
-    pa_.pref_off_ints = pl.fast ? 4 * decode_capacity(p, pl) : 0;
+    pa_.pref_off_ints = pref_off(p, pl);
+    pa_.merge_off_ints = merge_off(p, pl);
     pa_.num_seqs = p->num_seqs;
     pa_.part_size = d.part_size;
     pa_.group = g;
@@ -253,7 +261,7 @@ pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, con
     d.row_mode = pa::kSingleRowOnly;
     d.partial_by_seq = 1;
     e = pa::launch_decode_gqa(g, d, s);
-    if (e == hipSuccess) e = pa::launch_merge(dt, p->head_dim, d, pl.rows_a, s);
+    if (e == hipSuccess && pl.parts > 1) e = pa::launch_merge_list(d, s);
     if (e != hipSuccess) return PA_ERR_LAUNCH;
   }
   if (pl.generic_mode >= 0) {
@@ -279,7 +287,7 @@ pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, con
     f.num_kv_heads = p->num_kv_heads;
     f.max_blocks_per_seq = p->max_blocks_per_seq;
     f.plan = static_cast<const int32_t*>(workspace);
-    f.pref_off_ints = pl.fast ? 4 * decode_capacity(p, pl) : 0;
+    f.pref_off_ints = pref_off(p, pl);
     f.scale_log2 = scale_log2;
     e = pa::launch_prefill(p->head_dim, g, f, s);
     if (e != hipSuccess) return PA_ERR_LAUNCH;

@@ -29,6 +29,7 @@ struct DecodeArgs {
   int32_t max_parts;      // ceil(max_seq_len / part_size)
   float scale_log2;       // softmax scale * log2(e)
   int32_t* plan;            // fast kernel's work list (header + items), in the workspace
+  int64_t merge_off_ints;   // list of requests with more than one partition: plan + kPlanHeaderInts + this
   int32_t row_mode;         // which requests this launch serves (RowMode)
   int32_t partial_by_seq;   // 1: partials indexed by request, else by packed row
 };
@@ -70,6 +71,8 @@ bool decode_supported(int dtype, int head_dim, int group, int part_size);
 constexpr int kPlanHeaderInts = 64;      // header words (256 bytes)
 constexpr int kPlanCountInt = 8;         // header slot: number of decode entries
 constexpr int kPlanPrefCountInt = 9;     // header slot: number of prefill entries
+constexpr int kPlanMergeCountInt = 10;   // header slot: number of decode requests with > 1 partition
+constexpr int kPlanClaimInt = 11;        // header slot: claim counter of the fast decode kernel (zeroed by the plan)
 constexpr int kMaxPartBuckets = 512;     // partition_size / 16 of the fast kernel, at most
 constexpr int kPrefillPairs = 128;       // (query row, head) pairs per prefill work item
 constexpr int kPrefillKeys = 64;         // keys per prefill K/V tile
@@ -79,6 +82,7 @@ struct PlanArgs {
   const int32_t* seq_lens;
   int32_t* plan;
   int64_t pref_off_ints;   // prefill entries start at plan + kPlanHeaderInts + pref_off_ints
+  int64_t merge_off_ints;  // merge list (request ids) starts at plan + kPlanHeaderInts + merge_off_ints
   int32_t num_seqs;
   int32_t part_size;       // decode partition size
   int32_t group;           // query heads per KV head
@@ -89,7 +93,7 @@ struct PlanArgs {
 };
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
 // Bytes of a plan buffer for these capacities (entries), rounded to 256.
-size_t plan_bytes(int64_t decode_capacity, int64_t prefill_capacity);
+size_t plan_bytes(int64_t decode_capacity, int64_t prefill_capacity, int64_t merge_capacity);
 
 // Fast single-row decode (bf16, D = 128, G in {1, 2, 4, 8}); partials by request.
 // Reads its work list from a.plan (built by launch_plan first).
@@ -99,6 +103,9 @@ int decode_gqa_workers(int group);
 hipError_t launch_decode_gqa(int group, const DecodeArgs& a, hipStream_t stream);
 // Partition merge alone (for a DecodeArgs whose partials are already written).
 hipError_t launch_merge(int dtype, int head_dim, const DecodeArgs& a, int64_t partial_rows, hipStream_t stream);
+// Merge for the fast decode kernel's partials (bf16, D = 128): only the
+// requests on the plan's merge list, one wave per (request, query head).
+hipError_t launch_merge_list(const DecodeArgs& a, hipStream_t stream);
 size_t decode_lds_bytes(int dtype, int head_dim, int group, int part_size);
 
 // MFMA kernel for multi-row requests (bf16, D = 128, G in {1, 2, 4, 8}).

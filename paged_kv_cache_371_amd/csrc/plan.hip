@@ -4,8 +4,11 @@
 // Layout of the plan buffer (int32 words):
 //   [kPlanCountInt]      number of decode entries
 //   [kPlanPrefCountInt]  number of prefill entries
+//   [kPlanMergeCountInt] number of single-row requests with more than one partition
+//   [kPlanClaimInt]      claim counter of the decode kernel's dynamic rounds, zeroed here
 //   [kPlanHeaderInts ..)                   decode entries, int4 (request, partition, query row, context length)
 //   [kPlanHeaderInts + pref_off ..)        prefill entries, int4 (request, row tile, query row, query rows)
+//   [kPlanHeaderInts + merge_off ..)       merge list: request ids (any order)
 //
 // Decode list: one entry per non-empty context partition of every single-row
 // request -- all full partitions first, then the partial last partitions by
@@ -47,6 +50,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
   __shared__ int s_tmp[kPrefBuckets > kMaxPartBuckets ? kPrefBuckets : kMaxPartBuckets];
   __shared__ int s_full;
   __shared__ int s_cursor;
+  __shared__ int s_merge;
   const int tid = threadIdx.x;
   const int32_t* __restrict__ cu = a.cu_seqlens;
   const int32_t* __restrict__ seq_lens = a.seq_lens;
@@ -58,6 +62,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
     if (tid == 0) {
       s_full = 0;
       s_cursor = 0;
+      s_merge = 0;
     }
     __syncthreads();
     for (int b = tid; b < a.num_seqs; b += blockDim.x) {
@@ -73,6 +78,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
     const int total = scan_desc(s_hist, s_tmp, nbk, s_full);
     if (tid == 0) a.plan[kPlanCountInt] = total;
     int4* entries = reinterpret_cast<int4*>(a.plan + kPlanHeaderInts);
+    int32_t* merge = a.plan + kPlanHeaderInts + a.merge_off_ints;
     for (int b = tid; b < a.num_seqs; b += blockDim.x) {
       const int q0 = cu[b];
       if (cu[b + 1] - q0 != 1) continue;
@@ -83,8 +89,13 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
       int pos = nf ? atomicAdd(&s_cursor, nf) : 0;
       for (int p = 0; p < nf; ++p, ++pos) entries[pos] = make_int4(b, p, q0, L);
       if (rem > 0) entries[atomicAdd(&s_hist[(rem - 1) / kBlock], 1)] = make_int4(b, nf, q0, L);
+      if (nf + (rem > 0) > 1) merge[atomicAdd(&s_merge, 1)] = b;
     }
     __syncthreads();
+    if (tid == 0) {
+      a.plan[kPlanMergeCountInt] = s_merge;
+      a.plan[kPlanClaimInt] = 0;
+    }
   }
 
   if (a.prefill) {
@@ -119,8 +130,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
 
 }  // namespace
 
-size_t plan_bytes(int64_t decode_capacity, int64_t prefill_capacity) {
-  const size_t ints = size_t(kPlanHeaderInts) + 4 * size_t(decode_capacity) + 4 * size_t(prefill_capacity);
+size_t plan_bytes(int64_t decode_capacity, int64_t prefill_capacity, int64_t merge_capacity) {
+  const size_t ints =
+      size_t(kPlanHeaderInts) + 4 * size_t(decode_capacity) + 4 * size_t(prefill_capacity) + size_t(merge_capacity);
   return (ints * sizeof(int32_t) + 255) / 256 * 256;
 }
 

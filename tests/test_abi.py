@@ -100,9 +100,10 @@ def test_host_null_and_workspace_errors(L):
     ps = L.pa_attention_partition_size(ctypes.byref(p))
     assert ps in (512, 1024, 2048)
     parts = -(-2048 // ps)
-    # the work list (64-int header + one int4 entry per possible (request,
-    # partition), padded to 256 B), then rows * Hq * parts * (D + 2) fp32 partials
-    plan = -(-(64 + 4 * 2 * parts) * 4 // 256) * 256
+    # the work lists (64-int header + one int4 entry per possible (request,
+    # partition) + one merge-list slot per request, padded to 256 B), then
+    # rows * Hq * parts * (D + 2) fp32 partials
+    plan = -(-(64 + 4 * 2 * parts + 2) * 4 // 256) * 256
     assert need == plan + 2 * 8 * parts * (128 + 2) * 4
     assert L.pa_attention_varlen(None, 16, 16, 16, 16, 16, 16, ctypes.byref(p), None, 0, None) == -1
     assert L.pa_attention_varlen(16, 16, 16, 16, 16, 16, 16, ctypes.byref(p), 16, need - 1, None) == -5
