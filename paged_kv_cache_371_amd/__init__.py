@@ -209,7 +209,8 @@ def attention_varlen(out, q, k_cache, v_cache, cu_seqlens, seq_lens, block_table
                      stream=None):
     """Paged causal attention of packed rows; writes ``out`` [total_q, Hq, D] and returns it.
 
-    ``workspace`` (a uint8 device tensor) is allocated here when not given.
+    ``workspace`` (a contiguous device tensor of any dtype, at least
+    ``workspace_size`` bytes) is allocated here when not given.
     """
     torch = _torch()
     for t, nm in ((out, "out"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (cu_seqlens, "cu_seqlens"),
@@ -234,9 +235,13 @@ def attention_varlen(out, q, k_cache, v_cache, cu_seqlens, seq_lens, block_table
     need = workspace_size(p)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().pa_attention_varlen(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                      cu_seqlens.data_ptr(), seq_lens.data_ptr(), block_tables.data_ptr(),
-                                     ctypes.byref(p), workspace.data_ptr(), workspace.numel(), _stream(stream)))
+                                     ctypes.byref(p), workspace.data_ptr(), ws_bytes, _stream(stream)))
     return out
 
 

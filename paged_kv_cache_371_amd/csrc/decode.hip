@@ -350,42 +350,59 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a) {
 
 // Merge for the fast decode kernel's partials (bf16, D = 128): only the
 // requests on the work list's merge list, one wave per (request, query head).
-// Lanes read the partitions' (max, sum) in parallel and reduce them in a fixed
-// tree; then every lane combines its two d values over the partitions in
-// order, so the result is deterministic.
+// The list count and the wave's entry are read together; then partitions are
+// taken in chunks of kChunk, each chunk's (max, sum) (scalar loads) and
+// output slices (vector loads) issued at once, and folded into a running
+// log-sum-exp.  A request with up to kChunk partitions costs two memory round
+// trips.  Partitions are combined in order, so the result is deterministic.
 __global__ __launch_bounds__(256) void merge_list_kernel(DecodeArgs a) {
   constexpr int D = 128;
-  const int count = load_const(a.plan, kPlanMergeCountInt);
-  const int32_t* list = a.plan + kPlanHeaderInts + a.merge_off_ints;
+  constexpr int kChunk = 8;
+  const int4* list = reinterpret_cast<const int4*>(a.plan + kPlanHeaderInts + a.merge_off_ints);
   const int lane = threadIdx.x & 63;
   const int64_t NW = int64_t(gridDim.x) * 4;
-  const int64_t total = int64_t(count) * a.num_q_heads;
-  for (int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6); t < total; t += NW) {
+  const int64_t cap = int64_t(a.num_seqs) * a.num_q_heads;   // list capacity in (request, head) pairs
+  for (int64_t t = int64_t(blockIdx.x) * 4 + uni(threadIdx.x >> 6); t < cap; t += NW) {
     const int e = int(t / a.num_q_heads);
     const int h = int(t - int64_t(e) * a.num_q_heads);
-    const int b = load_const(list, e);
-    const int L = load_const(a.seq_lens, b);
-    const int q0 = load_const(a.cu_seqlens, b);
-    const int nparts = (L + a.part_size - 1) / a.part_size;
+    const int32_t* ep = reinterpret_cast<const int32_t*>(list + e);
+    const int b = load_const(ep, 0), q0 = load_const(ep, 1), nparts = load_const(ep, 2);
+    if (e >= load_const(a.plan, kPlanMergeCountInt)) break;
     const int64_t base = (int64_t(b) * a.num_q_heads + h) * a.max_parts;
-    const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + base;
-    float M = -__builtin_inff();
-    for (int p = lane; p < nparts; p += 64) M = fmaxf(M, ml[p].x);
-    M = group_max<64>(M);
-    float denom = 0.f;
-    for (int p = lane; p < nparts; p += 64) {
-      const float2 v = ml[p];
-      denom = fmaf(fast_exp2(v.x - M), v.y, denom);
-    }
-    denom = group_sum<64>(denom);
+    const int32_t* ml = reinterpret_cast<const int32_t*>(a.ws_ml + 2 * base);
     const float2* po = reinterpret_cast<const float2*>(a.ws_o + base * D) + lane;
-    float ox = 0.f, oy = 0.f;
-#pragma unroll 4
-    for (int p = 0; p < nparts; ++p) {
-      const float w = fast_exp2(ml[p].x - M);
-      const float2 v = po[int64_t(p) * (D / 2)];
-      ox = fmaf(w, v.x, ox);
-      oy = fmaf(w, v.y, oy);
+    float M = -__builtin_inff(), denom = 0.f, ox = 0.f, oy = 0.f;
+    for (int p0 = 0; p0 < nparts; p0 += kChunk) {
+      float m[kChunk], l[kChunk];
+      float2 o[kChunk];
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        m[j] = -__builtin_inff();
+        l[j] = 0.f;
+        o[j] = make_float2(0.f, 0.f);
+        if (p0 + j < nparts) {
+          m[j] = __builtin_bit_cast(float, load_const(ml, 2 * (p0 + j)));
+          l[j] = __builtin_bit_cast(float, load_const(ml, 2 * (p0 + j) + 1));
+          o[j] = po[int64_t(p0 + j) * (D / 2)];
+        }
+      }
+      float Mn = M;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) Mn = fmaxf(Mn, m[j]);
+      const float c = fast_exp2(M - Mn);   // 0 for the first chunk
+      denom *= c;
+      ox *= c;
+      oy *= c;
+      M = Mn;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        if (p0 + j < nparts) {
+          const float w = fast_exp2(m[j] - M);
+          denom = fmaf(w, l[j], denom);
+          ox = fmaf(w, o[j].x, ox);
+          oy = fmaf(w, o[j].y, oy);
+        }
+      }
     }
     const float inv = 1.f / denom;
     reinterpret_cast<uint32_t*>(static_cast<__bf16*>(a.out) + int64_t(q0) * a.o_row_stride + int64_t(h) * D)[lane] =

@@ -8,7 +8,7 @@
 //   [kPlanClaimInt]      claim counter of the decode kernel's dynamic rounds, zeroed here
 //   [kPlanHeaderInts ..)                   decode entries, int4 (request, partition, query row, context length)
 //   [kPlanHeaderInts + pref_off ..)        prefill entries, int4 (request, row tile, query row, query rows)
-//   [kPlanHeaderInts + merge_off ..)       merge list: request ids (any order)
+//   [kPlanHeaderInts + merge_off ..)       merge list, int4 (request, query row, partitions, 0), any order
 //
 // Decode list: one entry per non-empty context partition of every single-row
 // request -- all full partitions first, then the partial last partitions by
@@ -27,25 +27,41 @@ namespace {
 constexpr int kPrefBuckets = 512;   // key-tile counts are clamped into this many buckets
 
 // Exclusive positions of the buckets in decreasing bucket order, written over
-// hist[0..n); returns the total.  Hillis-Steele scan, n <= blockDim.x.
+// hist[0..n); returns base + the total.  n <= blockDim.x.  Each wave scans
+// its 64 buckets with lane shuffles, one wave scans the wave totals.
 __device__ int scan_desc(int* hist, int* tmp, int n, int base) {
   const int tid = threadIdx.x;
-  int x = tid < n ? hist[n - 1 - tid] : 0;
-  for (int off = 1; off < n; off <<= 1) {
-    if (tid < n) tmp[tid] = x;
-    __syncthreads();
-    if (tid < n && tid >= off) x += tmp[tid - off];
-    __syncthreads();
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int nw = blockDim.x >> 6;
+  const int x = tid < n ? hist[n - 1 - tid] : 0;
+  int v = x;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off);
+    if (lane >= off) v += y;
   }
-  if (tid == n - 1) tmp[0] = base + x;   // total
+  if (lane == 63) tmp[w] = v;
   __syncthreads();
-  const int total = tmp[0];
-  if (tid < n) hist[n - 1 - tid] = base + x - hist[n - 1 - tid];
+  if (w == 0) {
+    int t = lane < nw ? tmp[lane] : 0;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(t, off);
+      if (lane >= off) t += y;
+    }
+    if (lane < nw) tmp[64 + lane] = t;
+  }
   __syncthreads();
-  return total;
+  const int before = w > 0 ? tmp[64 + w - 1] : 0;
+  const int total = tmp[64 + nw - 1];
+  if (tid < n) hist[n - 1 - tid] = base + before + v - x;
+  __syncthreads();
+  return base + total;
 }
 
-__global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
+constexpr int kPlanThreads = 1024;
+constexpr int kPerThread = 4;   // requests whose lengths a thread keeps in registers
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int s_hist[kPrefBuckets > kMaxPartBuckets ? kPrefBuckets : kMaxPartBuckets];
   __shared__ int s_tmp[kPrefBuckets > kMaxPartBuckets ? kPrefBuckets : kMaxPartBuckets];
   __shared__ int s_full;
@@ -55,42 +71,65 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
   const int32_t* __restrict__ cu = a.cu_seqlens;
   const int32_t* __restrict__ seq_lens = a.seq_lens;
 
+  // (first row, rows, context) of the first kPerThread requests of this
+  // thread, read once; requests past kPerThread * kPlanThreads are re-read.
+  int rq0[kPerThread], rn[kPerThread], rl[kPerThread];
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    const int b = tid + k * kPlanThreads;
+    rq0[k] = 0;
+    rn[k] = 0;
+    rl[k] = 0;
+    if (b < a.num_seqs) {
+      rq0[k] = cu[b];
+      rn[k] = cu[b + 1] - rq0[k];
+      rl[k] = seq_lens[b];
+    }
+  }
+  auto for_each_request = [&](auto&& f) {
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+      const int b = tid + k * kPlanThreads;
+      if (b < a.num_seqs) f(b, rq0[k], rn[k], rl[k]);
+    }
+    for (int b = tid + kPerThread * kPlanThreads; b < a.num_seqs; b += kPlanThreads) {
+      const int q0 = cu[b];
+      f(b, q0, cu[b + 1] - q0, seq_lens[b]);
+    }
+  };
+
   if (a.decode) {
     const int P = a.part_size;
     const int nbk = P / kBlock;
-    for (int i = tid; i < nbk; i += blockDim.x) s_hist[i] = 0;
+    for (int i = tid; i < nbk; i += kPlanThreads) s_hist[i] = 0;
     if (tid == 0) {
       s_full = 0;
       s_cursor = 0;
       s_merge = 0;
     }
     __syncthreads();
-    for (int b = tid; b < a.num_seqs; b += blockDim.x) {
-      if (cu[b + 1] - cu[b] != 1) continue;
-      const int L = seq_lens[b];
-      if (L > a.max_seq_len) continue;
+    for_each_request([&](int, int, int n, int L) {
+      if (n != 1 || L > a.max_seq_len) return;
       const int nf = L / P;
       const int rem = L - nf * P;
       if (nf) atomicAdd(&s_full, nf);
       if (rem > 0) atomicAdd(&s_hist[(rem - 1) / kBlock], 1);
-    }
+    });
     __syncthreads();
     const int total = scan_desc(s_hist, s_tmp, nbk, s_full);
     if (tid == 0) a.plan[kPlanCountInt] = total;
     int4* entries = reinterpret_cast<int4*>(a.plan + kPlanHeaderInts);
-    int32_t* merge = a.plan + kPlanHeaderInts + a.merge_off_ints;
-    for (int b = tid; b < a.num_seqs; b += blockDim.x) {
-      const int q0 = cu[b];
-      if (cu[b + 1] - q0 != 1) continue;
-      const int L = seq_lens[b];
-      if (L > a.max_seq_len) continue;
+    int4* merge = reinterpret_cast<int4*>(a.plan + kPlanHeaderInts + a.merge_off_ints);
+    for_each_request([&](int b, int q0, int n, int L) {
+      if (n != 1 || L > a.max_seq_len) return;
       const int nf = L / P;
       const int rem = L - nf * P;
       int pos = nf ? atomicAdd(&s_cursor, nf) : 0;
       for (int p = 0; p < nf; ++p, ++pos) entries[pos] = make_int4(b, p, q0, L);
       if (rem > 0) entries[atomicAdd(&s_hist[(rem - 1) / kBlock], 1)] = make_int4(b, nf, q0, L);
-      if (nf + (rem > 0) > 1) merge[atomicAdd(&s_merge, 1)] = b;
-    }
+      const int parts = nf + (rem > 0);
+      if (parts > 1) merge[atomicAdd(&s_merge, 1)] = make_int4(b, q0, parts, 0);
+    });
     __syncthreads();
     if (tid == 0) {
       a.plan[kPlanMergeCountInt] = s_merge;
@@ -100,7 +139,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
 
   if (a.prefill) {
     const int rows = kPrefillPairs / a.group;   // query rows per tile
-    for (int i = tid; i < kPrefBuckets; i += blockDim.x) s_hist[i] = 0;
+    for (int i = tid; i < kPrefBuckets; i += kPlanThreads) s_hist[i] = 0;
     __syncthreads();
     // bucket of a tile = number of 64-key tiles its last row visits, clamped
     auto bucket = [&](int L, int n, int mt) {
@@ -108,36 +147,32 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
       const int keys = L - n + last;
       return min((keys + kPrefillKeys - 1) / kPrefillKeys, kPrefBuckets - 1);
     };
-    for (int b = tid; b < a.num_seqs; b += blockDim.x) {
-      const int n = cu[b + 1] - cu[b];
-      const int L = seq_lens[b];
-      if (n < 2 || n > a.max_query_len || L < n || L > a.max_seq_len) continue;
+    auto usable = [&](int n, int L) { return n >= 2 && n <= a.max_query_len && L >= n && L <= a.max_seq_len; };
+    for_each_request([&](int, int, int n, int L) {
+      if (!usable(n, L)) return;
       for (int mt = 0; mt * rows < n; ++mt) atomicAdd(&s_hist[bucket(L, n, mt)], 1);
-    }
+    });
     __syncthreads();
     const int total = scan_desc(s_hist, s_tmp, kPrefBuckets, 0);
     if (tid == 0) a.plan[kPlanPrefCountInt] = total;
     int4* entries = reinterpret_cast<int4*>(a.plan + kPlanHeaderInts + a.pref_off_ints);
-    for (int b = tid; b < a.num_seqs; b += blockDim.x) {
-      const int q0 = cu[b];
-      const int n = cu[b + 1] - q0;
-      const int L = seq_lens[b];
-      if (n < 2 || n > a.max_query_len || L < n || L > a.max_seq_len) continue;
+    for_each_request([&](int b, int q0, int n, int L) {
+      if (!usable(n, L)) return;
       for (int mt = 0; mt * rows < n; ++mt) entries[atomicAdd(&s_hist[bucket(L, n, mt)], 1)] = make_int4(b, mt, q0, n);
-    }
+    });
   }
 }
 
 }  // namespace
 
 size_t plan_bytes(int64_t decode_capacity, int64_t prefill_capacity, int64_t merge_capacity) {
-  const size_t ints =
-      size_t(kPlanHeaderInts) + 4 * size_t(decode_capacity) + 4 * size_t(prefill_capacity) + size_t(merge_capacity);
+  const size_t ints = size_t(kPlanHeaderInts) + 4 * size_t(decode_capacity) + 4 * size_t(prefill_capacity) +
+                      4 * size_t(merge_capacity);
   return (ints * sizeof(int32_t) + 255) / 256 * 256;
 }
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,102 @@
+"""White-box GPU check of the work lists the attention call builds in its
+workspace: every decode partition and prefill row tile appears exactly once,
+in non-increasing size order, and the merge list names exactly the
+single-row requests with more than one partition.
+
+Layout (int32 words of the workspace): [8] decode entries, [9] prefill
+entries, [10] merge entries; decode entries (request, partition, first row,
+context) from word 64; prefill entries (request, row tile, first row, rows)
+after the decode capacity; merge entries (request, first row, partitions, 0)
+after the prefill capacity.
+"""
+
+import collections
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_371_amd as pa
+from tests.gpu_util import DeviceCase, say
+from workloads import build_case
+
+pytestmark = pytest.mark.gpu
+
+HEADER = 64
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def _run_and_read(c, partition_size):
+    dc = DeviceCase(c)
+    dc.cache_write()
+    p = pa.make_params(dc.q, dc.k_cache, dc.cu, dc.tables, c.num_kv_heads, float(c.scale), c.max_query_len,
+                       c.max_seq_len, out=dc.out, partition_size=partition_size)
+    need = pa.workspace_size(p)
+    ps = pa.partition_size(p)
+    ws = torch.full((need // 4,), -7, dtype=torch.int32, device="cuda:0")
+    pa.attention_varlen(dc.out, dc.q, dc.k_cache, dc.v_cache, dc.cu, dc.seq_lens, dc.tables, float(c.scale),
+                        c.max_query_len, c.max_seq_len, workspace=ws, partition_size=partition_size)
+    torch.cuda.synchronize()
+    return ws.cpu().numpy(), ps
+
+
+@pytest.mark.parametrize("partition_size", [0, 256])
+def test_work_lists(partition_size):
+    rng = np.random.default_rng(11)
+    B = 300
+    n = np.ones(B, np.int64)
+    n[rng.choice(B, 12, replace=False)] = rng.integers(2, 300, 12)
+    L = np.maximum(n, rng.integers(1, 3000, B))
+    Hq, Hkv = 16, 4
+    c = build_case("plan", 3, "bf16", Hq, Hkv, 128, n, L, poison=False)
+    w, P = _run_and_read(c, partition_size)
+    say("partition", P)
+    G = Hq // Hkv
+    parts_max = -(-c.max_seq_len // P)
+    dec_cap = B * parts_max
+    rows = 128 // G
+    pref_cap = B * -(-c.max_query_len // rows)
+    pref_off = HEADER + 4 * dec_cap
+    merge_off = pref_off + 4 * pref_cap
+    cu = c.cu_seqlens.astype(np.int64)
+
+    # decode list
+    nd = int(w[8])
+    got = [tuple(int(v) for v in w[HEADER + 4 * i: HEADER + 4 * i + 4]) for i in range(nd)]
+    want = []
+    for b in range(B):
+        if n[b] == 1:
+            for part in range(-(-int(L[b]) // P)):
+                want.append((b, part, int(cu[b]), int(L[b])))
+    assert collections.Counter(got) == collections.Counter(want)
+    tiles = [-(-min(P, Lb - part * P) // 16) for (_, part, _, Lb) in got]
+    assert all(x >= y for x, y in zip(tiles, tiles[1:])), "decode list not sorted by size"
+
+    # merge list
+    nm = int(w[10])
+    got_m = {tuple(int(v) for v in w[merge_off + 4 * i: merge_off + 4 * i + 3]) for i in range(nm)}
+    want_m = {(b, int(cu[b]), -(-int(L[b]) // P)) for b in range(B) if n[b] == 1 and L[b] > P}
+    assert nm == len(want_m) and got_m == want_m
+
+    # prefill list
+    npf = int(w[9])
+    got_p = [tuple(int(v) for v in w[pref_off + 4 * i: pref_off + 4 * i + 4]) for i in range(npf)]
+    want_p = []
+    for b in range(B):
+        if n[b] >= 2:
+            for mt in range(-(-int(n[b]) // rows)):
+                want_p.append((b, mt, int(cu[b]), int(n[b])))
+    assert collections.Counter(got_p) == collections.Counter(want_p)
+
+    def key_tiles(e):
+        b, mt, _, nb = e
+        last = min(nb, (mt + 1) * rows)
+        return min(-(-(int(L[b]) - nb + last) // 64), 511)
+    kt = [key_tiles(e) for e in got_p]
+    assert all(x >= y for x, y in zip(kt, kt[1:])), "prefill list not sorted by size"
