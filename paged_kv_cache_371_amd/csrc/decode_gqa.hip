@@ -237,6 +237,17 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
     return t < total ? int(t) : total;
   };
   const int64_t dyn0 = int64_t(kStaticRounds) * NW;   // first item handed out by claims
+  // List entry of static round i (scalar loads).  The entry index is clamped
+  // into the list's capacity instead of checked against the count, so round
+  // 0's entry is fetched together with the count at kernel start; make_item
+  // discards it when the round has no item.
+  auto static_entry = [&](int i) -> int4 {
+    const int64_t t = int64_t(i) * NW + ((i & 1) ? NW - 1 - wid : wid);
+    const int e = int(min<int64_t>(t / a.num_kv_heads, a.plan_capacity - 1));
+    const int32_t* ep = a.plan + kPlanHeaderInts + 4 * int64_t(e);
+    return make_int4(load_const_early(ep, 0), load_const_early(ep, 1), load_const_early(ep, 2), load_const_early(ep, 3));
+  };
+  const int4 entry0 = static_entry(0);
   int* claim_counter = a.plan + kPlanClaimInt;
 
   // Queue of claimed items with their list entries.  Slot s receives queue
@@ -361,21 +372,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
     });
   };
 
-  // The list entries of this wave's static items are staged in its LDS slot
-  // once, so setting up an item costs an LDS read, not a scalar memory round
-  // trip on the critical path.
-  __shared__ int4 sitems[kWavesPerGroup][kStaticRounds];
-  {
-    const int t = item_of_round(lane);
-    if (lane < kStaticRounds && t < total) sitems[wave][lane] = entries[t / a.num_kv_heads];
-  }
-  auto static_entry = [&](int i) -> int4 {
-    const int t = item_of_round(i);
-    return t < total ? sitems[wave][i] : make_int4(0, 0, 0, 1);
-  };
-  auto item_for_round = [&](int i) { return make_item(a, total, item_of_round(i), static_entry(i)); };
-
-  Item cur = item_for_round(0);
+  Item cur = make_item(a, total, item_of_round(0), entry0);
   if (!cur.valid) return;
 
   auto load_q = [&](u32x4_t(&qreg)[G], const Item& it) {   // q slices, lane-relative order h(r ^ M_j)
@@ -386,9 +383,6 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
       const int hh = (r ^ q_mask<K>(j)) >> (4 - K);
       qreg[j] = *reinterpret_cast<const u32x4_t*>(qrow + hh * (kD * 2) + r * 16);
     });
-  };
-  auto tile_phys = [&](const Item& it, int j) -> int64_t {
-    return load_const(it.table, it.lb0 + min(j, it.nb - 1));
   };
   auto load_tile = [&](u32x4_t(&kb)[4], u32x4_t(&vb)[4], const char* kbase, const char* vbase, bool live,
                        int64_t phys) {
@@ -406,10 +400,15 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
   u32x4_t qreg[G];
   u32x4_t kr[kRing][4], vr[kRing][4];   // the ring: K and V of kRing tiles
   load_q(qreg, cur);
+  int ph0[kRing];   // block ids of the first tiles, all requested before any is used
+  static_for<kRing>([&](auto S) {
+    constexpr int st = decltype(S)::value;
+    ph0[st] = load_const_early(cur.table, cur.lb0 + min(st, cur.nb - 1));
+  });
   __builtin_amdgcn_sched_barrier(0);
   static_for<kRing>([&](auto S) {
     constexpr int st = decltype(S)::value;
-    load_tile(kr[st], vr[st], cur.kbase, cur.vbase, st < cur.nb, tile_phys(cur, st));
+    load_tile(kr[st], vr[st], cur.kbase, cur.vbase, st < cur.nb, ph0[st]);
     __builtin_amdgcn_sched_barrier(0);
   });
 

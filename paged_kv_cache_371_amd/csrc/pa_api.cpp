@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 
@@ -232,6 +233,7 @@ pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, con
   d.scale_log2 = scale_log2;
   d.plan = (pl.fast || pl.prefill) ? static_cast<int32_t*>(workspace) : nullptr;
   d.merge_off_ints = merge_off(p, pl);
+  d.plan_capacity = int32_t(std::max<int64_t>(1, pl.fast ? decode_capacity(p, pl) : 1));
 
   // Partials of a region: o [rows, Hq, parts, D] followed by (m, l) [rows, Hq, parts, 2].
   auto point_at = [&](float* region, int64_t rows) {

@@ -30,6 +30,7 @@ struct DecodeArgs {
   float scale_log2;       // softmax scale * log2(e)
   int32_t* plan;            // fast kernel's work list (header + items), in the workspace
   int64_t merge_off_ints;   // list of requests with more than one partition: plan + kPlanHeaderInts + this
+  int32_t plan_capacity;    // decode entries the work list has room for (>= 1)
   int32_t row_mode;         // which requests this launch serves (RowMode)
   int32_t partial_by_seq;   // 1: partials indexed by request, else by packed row
 };
