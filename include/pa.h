@@ -92,7 +92,7 @@ typedef struct {
   int32_t max_seq_len;         /* host bound: >= every L_b */
   int64_t q_row_stride;        /* elements between consecutive packed rows of q  (>= Hq*D) */
   int64_t o_row_stride;        /* elements between consecutive packed rows of out (>= Hq*D) */
-  float scale;                 /* softmax scale, usually 1/sqrt(D) */
+  float scale;                 /* softmax scale, finite and > 0, usually 1/sqrt(D) */
   pa_dtype dtype;
   int32_t partition_size;      /* tokens per split-K context partition, a multiple of 16
                                   in [16, 8192].  Given explicitly, a request's result

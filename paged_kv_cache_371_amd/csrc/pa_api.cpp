@@ -130,7 +130,7 @@ pa_status check_params(const pa_attn_params* p) {
   if (p->total_q > 0 && p->num_seqs == 0) return PA_ERR_SHAPE;
   const int64_t hd = int64_t(p->num_q_heads) * p->head_dim;
   if (p->q_row_stride < hd || p->o_row_stride < hd) return PA_ERR_SHAPE;
-  if (!std::isfinite(p->scale)) return PA_ERR_SHAPE;
+  if (!std::isfinite(p->scale) || !(p->scale > 0.f)) return PA_ERR_SHAPE;
   if (p->partition_size != 0 && (p->partition_size < 16 || p->partition_size > 8192 || p->partition_size % 16))
     return PA_ERR_SHAPE;
   const int eb = elem_bytes(p->dtype);

@@ -25,7 +25,11 @@
 // operand without moving data: inside each 32-key step the keys are taken in
 // the order the S^T accumulators hold them (lane row h owns keys 4h..4h+3 and
 // 16+4h..16+4h+3), and V^T is read from LDS in that same order.  P is rounded
-// to bf16 for the MFMA, and the softmax sum uses the rounded values.
+// to bf16 for the MFMA, and the softmax sum uses the rounded values.  The
+// running max is raised only when a tile's max exceeds it by more than 8
+// (log2 units), so most tiles neither rescale the accumulators nor spend a
+// multiply on scaling the scores: p = 2^(s * scale * log2(e) - m) is one
+// FMA and one exp2 per score.
 //
 // Positions past the context (the partial last block, clamped block ids)
 // are zeroed when staged and masked as keys, so NaN in unused slots cannot
@@ -50,6 +54,8 @@ constexpr int kStageBytes = kKBytes + kVBytes;
 constexpr int kLdsBytes = 2 * kStageBytes;
 constexpr unsigned kRsrcWord3 = 0x00020000u;
 constexpr float kMinusBig = -1e30f;
+constexpr float kRescaleThreshold = 8.f;      // log2 units
+constexpr uint32_t kBf16OnePair = 0x3F803F80u;
 
 static_assert(kKeys == 4 * kBlock, "a key tile is one paged block per wave");
 
@@ -159,15 +165,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       char* ks = smem + st * kStageBytes;
       char* vs = ks + kKBytes;
       const int key0 = kt * kKeys + wave * kBlock;   // first position of this wave's block
-      const u32x4_t z = {0u, 0u, 0u, 0u};
+      if (kt * kKeys + kKeys > L) {   // the context ends in this tile: zero what lies past it
+        const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const u32x4_t kv = key0 + kkey + kk < L ? rg.k[kk] : z;
-        *reinterpret_cast<u32x4_t*>(ks + kchunk * kKChunk + (wave * kBlock + kkey + kk) * 16) = kv;
+        for (int kk = 0; kk < 4; ++kk) {
+          if (key0 + kkey + kk >= L) rg.k[kk] = z;
+          if (key0 + vkey + kk >= L) rg.v[kk] = z;
+        }
       }
-      u32x4_t vv[4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) vv[kk] = key0 + vkey + kk < L ? rg.v[kk] : z;
+      for (int kk = 0; kk < 4; ++kk)
+        *reinterpret_cast<u32x4_t*>(ks + kchunk * kKChunk + (wave * kBlock + kkey + kk) * 16) = rg.k[kk];
+      const u32x4_t* vv = rg.v;
       // V^T: d rows 8*vchunk + 2w (+1) get this thread's 4 keys (8 bytes each)
       char* vcol = vs + (wave * kBlock + vkey) * 2;
 #pragma unroll
@@ -198,42 +207,54 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb) sacc[c][mb] = mfma16(ka, qb[mb][s], sacc[c][mb]);
         }
-      const bool diag = kt * kKeys + kKeys - 1 > P + j0;   // some key of the tile is past some row's limit
+      // Keys past a row's limit get a score of -inf (raw scores: the scale is
+      // positive, so the order and the masking survive scaling).  Only tiles
+      // that reach past the first row's limit need it.
+      if (kt * kKeys + kKeys - 1 > P + j0) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (kt * kKeys + 16 * c + 4 * h + r > limit[mb]) sacc[c][mb][r] = -__builtin_inff();
+      }
       u32x4_t pb[2][2];   // B operand P^T per (pair block, 32-key step)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        float sc[4][4];
         float tmax = -__builtin_inff();
 #pragma unroll
         for (int c = 0; c < 4; ++c)
+          tmax = fmaxf(fmaxf(tmax, fmaxf(sacc[c][mb][0], sacc[c][mb][1])), fmaxf(sacc[c][mb][2], sacc[c][mb][3]));
+        tmax = rows_max(tmax) * scale_log2;
+        // The reference max is raised only when the tile's max exceeds it by
+        // more than kRescaleThreshold (log2 units); otherwise p <= 2^8 is used
+        // as is.  Exact: the normalisation uses the same reference.
+        if (__builtin_amdgcn_ballot_w64(tmax > mrun[mb] + kRescaleThreshold)) {
+          const float mnew = fmaxf(mrun[mb], tmax);
+          const float alpha = fast_exp2(mrun[mb] - mnew);
+          mrun[mb] = mnew;
+          lrun[mb] *= alpha;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float v = sacc[c][mb][r] * scale_log2;
-            if (diag && kt * kKeys + 16 * c + 4 * h + r > limit[mb]) v = -__builtin_inff();
-            sc[c][r] = v;
-            tmax = fmaxf(tmax, v);
-          }
-        tmax = rows_max(tmax);
-        const float mnew = fmaxf(mrun[mb], tmax);
-        const float alpha = fast_exp2(mrun[mb] - mnew);
-        mrun[mb] = mnew;
-        float lsum = 0.f;
+          for (int db = 0; db < 8; ++db) acc[mb][db] *= alpha;
+        }
+        const float nm = -mrun[mb];
+        float lsum = lrun[mb];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           uint32_t w[4];
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
-            const int c = 2 * u + half;
-            w[2 * half] = pack_bf16x2(fast_exp2(sc[c][0] - mnew), fast_exp2(sc[c][1] - mnew));
-            w[2 * half + 1] = pack_bf16x2(fast_exp2(sc[c][2] - mnew), fast_exp2(sc[c][3] - mnew));
+            const f32x4_t& sv = sacc[2 * u + half][mb];
+            w[2 * half] = pack_bf16x2(fast_exp2(fmaf(sv[0], scale_log2, nm)), fast_exp2(fmaf(sv[1], scale_log2, nm)));
+            w[2 * half + 1] =
+                pack_bf16x2(fast_exp2(fmaf(sv[2], scale_log2, nm)), fast_exp2(fmaf(sv[3], scale_log2, nm)));
           }
 #pragma unroll
-          for (int x = 0; x < 4; ++x) lsum += bf16_lo(w[x]) + bf16_hi(w[x]);
+          for (int x = 0; x < 4; ++x) lsum = dot2_bf16(w[x], kBf16OnePair, lsum);
           pb[mb][u] = u32x4_t{w[0], w[1], w[2], w[3]};
         }
-        lrun[mb] = lrun[mb] * alpha + lsum;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) acc[mb][db] *= alpha;
+        lrun[mb] = lsum;
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u)

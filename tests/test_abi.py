@@ -85,6 +85,8 @@ def _params(**over):
     (dict(partition_size=24), -2),
     (dict(partition_size=8208), -2),                # above the 8192-token maximum
     (dict(scale=float("nan")), -2),
+    (dict(scale=0.0), -2),
+    (dict(scale=-0.088), -2),
     (dict(max_query_len=65), -2),
 ])
 def test_host_rejects_bad_params_before_any_launch(L, over, code):
