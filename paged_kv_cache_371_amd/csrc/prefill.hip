@@ -12,7 +12,7 @@
 // pairs packed as m = row * G + head over the G query heads of the KV head.
 // Four waves own 32 pairs each (two 16-column MFMA blocks).  Keys are visited
 // in tiles of 64 (four paged blocks; wave w fetches block w of the tile, so
-// every load has a wave-uniform base).  Tiles are fetched into registers two
+// every load has a wave-uniform base).  Tiles are fetched into registers one
 // ahead and written to one of two LDS stages: K as 16-byte d-chunks, chunk
 // major (a 16-lane MFMA read is 256 contiguous bytes), V transposed (V^T,
 // d-major, rows padded to 136 bytes) by a 4 x 8 register transpose.  Both
@@ -35,6 +35,7 @@
 // are zeroed when staged and masked as keys, so NaN in unused slots cannot
 // reach the output.
 #include <atomic>
+#include <utility>
 
 #include "pa_common.h"
 #include "pa_internal.h"
@@ -61,6 +62,15 @@ static_assert(kKeys == 4 * kBlock, "a key tile is one paged block per wave");
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 __device__ __forceinline__ f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
@@ -199,14 +209,26 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) sacc[c][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // K operands in groups of one 32-wide d step (4 reads), the next group
+      // requested before the current one's 8 MFMAs, so LDS latency overlaps
+      // matrix work.
+      u32x4_t kbuf[2][4];
+      auto read_k = [&](int s, u32x4_t(&kb)[4]) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+        for (int c = 0; c < 4; ++c)
+          kb[c] = *reinterpret_cast<const u32x4_t*>(ks + (4 * s + h) * kKChunk + (16 * c + lc) * 16);
+      };
+      read_k(0, kbuf[0]);
+      static_for<4>([&](auto S) {
+        constexpr int s = decltype(S)::value;
+        if constexpr (s + 1 < 4) read_k(s + 1, kbuf[(s + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(ks + (4 * s + h) * kKChunk + (16 * c + lc) * 16);
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb) sacc[c][mb] = mfma16(ka, qb[mb][s], sacc[c][mb]);
-        }
+          for (int mb = 0; mb < 2; ++mb) sacc[c][mb] = mfma16(kbuf[s & 1][c], qb[mb][s], sacc[c][mb]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
       // Keys past a row's limit get a score of -inf (raw scores: the scale is
       // positive, so the order and the masking survive scaling).  Only tiles
       // that reach past the first row's limit need it.
@@ -256,44 +278,49 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         }
         lrun[mb] = lsum;
       }
+      // V operands in groups of 4 d blocks, pipelined like K.
+      u32x4_t vbuf[2][4];
+      auto read_v = [&](int g, u32x4_t(&vb)[4]) {   // group g: u = g / 2, d blocks 4 (g % 2) ..
+        const int u = g >> 1;
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          const char* vrow = vs + (16 * db + lc) * kVRow;
+        for (int i = 0; i < 4; ++i) {
+          const char* vrow = vs + (16 * (4 * (g & 1) + i) + lc) * kVRow;
           const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow + (32 * u + 4 * h) * 2);
           const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + (32 * u + 16 + 4 * h) * 2);
-          const u32x4_t va = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) acc[mb][db] = mfma16(va, pb[mb][u], acc[mb][db]);
+          vb[i] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
         }
+      };
+      read_v(0, vbuf[0]);
+      static_for<4>([&](auto Gc) {
+        constexpr int g = decltype(Gc)::value;
+        if constexpr (g + 1 < 4) read_v(g + 1, vbuf[(g + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+            acc[mb][4 * (g & 1) + i] = mfma16(vbuf[g & 1][i], pb[mb][g >> 1], acc[mb][4 * (g & 1) + i]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
     };
 
-    // ---- tile pipeline: registers two tiles ahead, two LDS stages -------------------
-    // Each barrier separates the staging write of a stage from the computes
-    // that read it, before and after.
+    // ---- tile pipeline: registers one tile ahead, two LDS stages -------------------
+    // Tile kt+1 is fetched into registers while tile kt is computed from its
+    // stage, then written to the other stage.  Each barrier separates the
+    // staging write of a stage from the computes that read it, before and
+    // after.
     __syncthreads();   // the previous item is done with both stages
-    TileRegs ra, rb;
-    int pha = phys_of(0);
-    const int phb = phys_of(1);
-    int phc = phys_of(2);
-    fetch(ra, 0, pha);
-    fetch(rb, 1, phb);
-    stage_write(ra, 0, 0);
+    TileRegs rg;
+    int ph_next = phys_of(1);
+    fetch(rg, 0, phys_of(0));
+    stage_write(rg, 0, 0);
     __syncthreads();
-    for (int kt = 0; kt < KT; kt += 2) {
-      // tile kt (stage 0) computed; tile kt+2 fetched into ra; tile kt+1 staged
-      fetch(ra, kt + 2, phc);
-      pha = phys_of(kt + 3);
-      compute(kt, 0);
-      if (kt + 1 < KT) stage_write(rb, kt + 1, 1);
-      __syncthreads();
-      if (kt + 1 >= KT) break;
-      // tile kt+1 (stage 1) computed; tile kt+3 fetched into rb; tile kt+2 staged
-      fetch(rb, kt + 3, pha);
-      phc = phys_of(kt + 4);
-      compute(kt + 1, 1);
-      if (kt + 2 < KT) stage_write(ra, kt + 2, 0);
+    for (int kt = 0; kt < KT; ++kt) {
+      const int st = kt & 1;
+      fetch(rg, kt + 1, ph_next);
+      ph_next = phys_of(kt + 2);
+      compute(kt, st);
+      if (kt + 1 < KT) stage_write(rg, kt + 1, st ^ 1);
       __syncthreads();
     }
 
