@@ -230,6 +230,42 @@ def test_config_full_size_sampled(name):
 
 
 # ---------------------------------------------------------------------------
+# scale extremes: many requests, one very long context
+
+
+def test_many_requests_sampled():
+    """5000 requests (past the 4096 whose lengths the work-list kernel keeps in
+    registers), mostly short, a few multi-partition, some multi-row."""
+    rng = np.random.default_rng(21)
+    B = 5000
+    L = rng.integers(1, 200, B)
+    L[rng.choice(B, 40, replace=False)] = rng.integers(2049, 6000, 40)
+    n = np.ones(B, np.int64)
+    multi = rng.choice(B, 16, replace=False)
+    n[multi] = np.minimum(L[multi], rng.integers(2, 40, 16))
+    c = build_case("many", 21, "bf16", 16, 2, 128, n, L, poison=True)
+    rows = sorted(set(rng.choice(c.total_q, 300, replace=False).tolist())
+                  | {int(c.cu_seqlens[b]) for b in np.argsort(L)[-40:]}
+                  | {int(c.cu_seqlens[b + 1]) - 1 for b in multi})
+    say("case", c.name, "rows", len(rows))
+    mx, mean, ok, dc = run_and_compare(c, rows=rows, check_pool=False)
+    say(f"  max {mx:.3g} mean {mean:.3g}")
+    assert ok, (mx, mean)
+    assert torch.isfinite(dc.out.float()).all()
+
+
+@pytest.mark.parametrize("psize", [0, 512])
+def test_one_very_long_context(psize):
+    """One 131072-token decode row (up to 256 partitions: the merge folds them
+    in chunks) next to a short one."""
+    c = build_case("long", 22, "bf16", 64, 8, 128, [1, 1], [131072, 77], poison=True)
+    say("case", c.name, "psize", psize)
+    mx, mean, ok, _ = run_and_compare(c, partition_size=psize, check_pool=False)
+    say(f"  max {mx:.3g} mean {mean:.3g}")
+    assert ok, (mx, mean)
+
+
+# ---------------------------------------------------------------------------
 # device-side metadata validation
 
 
