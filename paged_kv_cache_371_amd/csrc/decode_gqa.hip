@@ -9,8 +9,9 @@
 // Work split: one wave per work item (request, KV head, context partition);
 // the wave streams the partition's 16-token tiles and serves ALL G query
 // heads of the KV head, so each K/V byte enters the chip once and is used G
-// times from registers.  Items come from a device-built list (largest first)
-// and are dealt to the persistent waves in a zig-zag order (see below).
+// times from registers.  Items come from a device-built list (largest first):
+// the first round is dealt statically, the rest is claimed at run time (see
+// below).
 //
 // Lane layout for one 16-token tile of one KV head (16 x 256 B, contiguous):
 // lane l = 16*tg + r loads 16 B at token 4*i + tg, d-slice [8r, 8r+8), for
@@ -215,7 +216,7 @@ __device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t,
 //
 // A wave sees its items as one stream of tiles: an item contributes nbr
 // stream slots (its nb tiles padded with empty ones to a multiple of kRing), so
-// the last load group of an item already fetches the next item's first three
+// the last load group of an item already fetches the next item's first kRing
 // tiles and the HBM queue of the wave never drains at item boundaries.  The
 // physical block id of the slot issued next is fetched one issue ahead.
 template <int G>

@@ -15,7 +15,8 @@
 // decreasing number of blocks.  Prefill list: one entry per tile of
 // kPrefillPairs (query row, head) pairs of every multi-row request, by
 // decreasing number of 64-key tiles the tile has to visit.  Both orders put
-// the largest items first, which the consumers' zig-zag assignment relies on.
+// the largest items first: the consumers deal or claim items in list order,
+// and handing out the small ones last keeps the workers' finish times close.
 // Requests whose lengths break the bounds the host sized the buffer for get no
 // entries (their output rows are left untouched).
 #include "pa_common.h"
