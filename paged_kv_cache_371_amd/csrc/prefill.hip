@@ -45,6 +45,9 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kPairs = kPrefillPairs;        // (row, head) pairs per work item
+constexpr int kMB = kPairs / 64;             // 16-column MFMA blocks per wave (4 waves)
+constexpr int kOccupancy = 2;                // workgroups per CU (256 registers per wave)
+static_assert(kMB == 2, "two 16-column blocks per wave fit the register budget of two workgroups per CU");
 constexpr int kKeys = kPrefillKeys;          // keys per tile = kBlock * waves
 constexpr int kTileBytes = kBlock * kD * 2;  // one (block, KV head) tile of bf16
 constexpr int kKChunk = kKeys * 16 + 16;     // LDS bytes per 8-wide d-chunk of K (64 keys + pad)
@@ -86,7 +89,7 @@ struct TileRegs {
 };
 
 template <int G>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, kOccupancy) void prefill_kernel(PrefillArgs a) {
   constexpr int kRows = kPairs / G;   // query rows per work item
   extern __shared__ __align__(16) char smem[];
 
@@ -127,12 +130,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const char* vbase = static_cast<const char*>(a.v_cache) + int64_t(kvh) * kTileBytes;
 
     // ---- this lane's two pairs: m = wave*32 + mb*16 + lc ----------------------
-    int jrow[2], hq[2], limit[2];
-    bool mvalid[2];
-    u32x4_t qb[2][4];   // B operand Q^T: pair lc, d = 32s + 8h .. +7
+    int jrow[kMB], hq[kMB], limit[kMB];
+    bool mvalid[kMB];
+    u32x4_t qb[kMB][4];   // B operand Q^T: pair lc, d = 32s + 8h .. +7
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int m = wave * 32 + mb * 16 + lc;
+    for (int mb = 0; mb < kMB; ++mb) {
+      const int m = wave * (16 * kMB) + mb * 16 + lc;
       jrow[mb] = j0 + m / G;
       hq[mb] = kvh * G + m % G;
       mvalid[mb] = jrow[mb] < j1;
@@ -146,13 +149,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       }
     }
 
-    f32x4_t acc[2][8];   // O^T blocks: d = 16*db + 4h + r, pair lc
+    f32x4_t acc[kMB][8];   // O^T blocks: d = 16*db + 4h + r, pair lc
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
       for (int db = 0; db < 8; ++db) acc[mb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float mrun[2] = {kMinusBig, kMinusBig};
-    float lrun[2] = {0.f, 0.f};
+    float mrun[kMB], lrun[kMB];
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
+      mrun[mb] = kMinusBig;
+      lrun[mb] = 0.f;
+    }
 
     // ---- K/V tile staging -----------------------------------------------------
     // Physical block of this wave's part of tile kt (clamped into the table;
@@ -204,46 +211,34 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     auto compute = [&](int kt, int st) {
       const char* ks = smem + st * kStageBytes;
       const char* vs = ks + kKBytes;
-      f32x4_t sacc[4][2];
+      f32x4_t sacc[4][kMB];
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) sacc[c][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      // K operands in groups of one 32-wide d step (4 reads), the next group
-      // requested before the current one's 8 MFMAs, so LDS latency overlaps
-      // matrix work.
-      u32x4_t kbuf[2][4];
-      auto read_k = [&](int s, u32x4_t(&kb)[4]) {
+        for (int mb = 0; mb < kMB; ++mb) sacc[c][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          kb[c] = *reinterpret_cast<const u32x4_t*>(ks + (4 * s + h) * kKChunk + (16 * c + lc) * 16);
-      };
-      read_k(0, kbuf[0]);
-      static_for<4>([&](auto S) {
-        constexpr int s = decltype(S)::value;
-        if constexpr (s + 1 < 4) read_k(s + 1, kbuf[(s + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < 4; ++c) {
+          const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(ks + (4 * s + h) * kKChunk + (16 * c + lc) * 16);
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb) sacc[c][mb] = mfma16(kbuf[s & 1][c], qb[mb][s], sacc[c][mb]);
-        __builtin_amdgcn_sched_barrier(0);
-      });
+          for (int mb = 0; mb < kMB; ++mb) sacc[c][mb] = mfma16(ka, qb[mb][s], sacc[c][mb]);
+        }
       // Keys past a row's limit get a score of -inf (raw scores: the scale is
       // positive, so the order and the masking survive scaling).  Only tiles
       // that reach past the first row's limit need it.
       if (kt * kKeys + kKeys - 1 > P + j0) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
           for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               if (kt * kKeys + 16 * c + 4 * h + r > limit[mb]) sacc[c][mb][r] = -__builtin_inff();
       }
-      u32x4_t pb[2][2];   // B operand P^T per (pair block, 32-key step)
+      u32x4_t pb[kMB][2];   // B operand P^T per (pair block, 32-key step)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < kMB; ++mb) {
         float tmax = -__builtin_inff();
 #pragma unroll
         for (int c = 0; c < 4; ++c)
@@ -278,30 +273,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         }
         lrun[mb] = lsum;
       }
-      // V operands in groups of 4 d blocks, pipelined like K.
-      u32x4_t vbuf[2][4];
-      auto read_v = [&](int g, u32x4_t(&vb)[4]) {   // group g: u = g / 2, d blocks 4 (g % 2) ..
-        const int u = g >> 1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const char* vrow = vs + (16 * (4 * (g & 1) + i) + lc) * kVRow;
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const char* vrow = vs + (16 * db + lc) * kVRow;
           const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow + (32 * u + 4 * h) * 2);
           const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + (32 * u + 16 + 4 * h) * 2);
-          vb[i] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+          const u32x4_t va = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+          for (int mb = 0; mb < kMB; ++mb) acc[mb][db] = mfma16(va, pb[mb][u], acc[mb][db]);
         }
-      };
-      read_v(0, vbuf[0]);
-      static_for<4>([&](auto Gc) {
-        constexpr int g = decltype(Gc)::value;
-        if constexpr (g + 1 < 4) read_v(g + 1, vbuf[(g + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-            acc[mb][4 * (g & 1) + i] = mfma16(vbuf[g & 1][i], pb[mb][g >> 1], acc[mb][4 * (g & 1) + i]);
-        __builtin_amdgcn_sched_barrier(0);
-      });
     };
 
     // ---- tile pipeline: registers one tile ahead, two LDS stages -------------------
@@ -326,7 +308,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 
     // ---- normalise and store ----------------------------------------------------
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < kMB; ++mb) {
       const float inv = 1.f / rows_sum(lrun[mb]);
       if (mvalid[mb]) {
         __bf16* orow = static_cast<__bf16*>(a.out) + int64_t(q0 + jrow[mb]) * a.o_row_stride + int64_t(hq[mb]) * kD;
