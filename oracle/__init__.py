@@ -26,6 +26,9 @@ written brute force.  What no pin reaches is said so in the function.
 from .paged_attention import (  # noqa: F401
     OracleError,
     compare_outputs,
+    fp8_e4m3_decode,
+    fp8_e4m3_encode,
+    fp8_quantize_rows,
     gather_request_kv,
     kv_head_of,
     last_visible_key,

@@ -39,7 +39,77 @@ def widen(x: np.ndarray, dtype: str) -> np.ndarray:
         return (np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
     if dtype == "f32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "fp8":
+        return fp8_e4m3_decode(x)
     raise OracleError(f"unknown dtype {dtype!r}")
+
+
+# ---------------------------------------------------------------------------
+# 8-bit float cache encoding (OCP FP8 E4M3, the "FN" variant)
+#
+# The pages name FP8 KV caches as the next step for memory (quant67 §8.8 and
+# §10.3) without fixing a format; the reading taken is the OCP 8-bit floating
+# point E4M3 format: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+# bits; exponent 0 holds the subnormals m * 2^-9; there are no infinities;
+# S.1111.111 is NaN, so the largest finite magnitude is 1.75 * 2^8 = 448.
+# Encoding rounds to nearest, ties to an even mantissa, and saturates
+# magnitudes beyond 448 to 448.
+
+FP8_MAX = 448.0
+
+
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """fp64 value of each E4M3 code (NaN for the two NaN codes)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def fp8_e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 code of each fp32 value: ties to even, saturating at 448, NaN to 0x7F."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    out = np.empty(x.shape, np.uint8)
+    flat_x, flat_o = x.reshape(-1), out.reshape(-1)
+    for i, v in enumerate(flat_x.tolist()):
+        if math.isnan(v):
+            flat_o[i] = 0x7F
+            continue
+        sign = 0x80 if math.copysign(1.0, v) < 0 else 0
+        a = abs(v)
+        if a >= FP8_MAX:
+            flat_o[i] = sign | 0x7E
+            continue
+        # the spacing of representable values around a: 2^-9 below 2^-6
+        # (subnormals), else 2^(floor(log2 a) - 3)
+        e = max(math.floor(math.log2(a)), -6) if a > 0 else -6
+        quantum = 2.0 ** (e - 3)
+        n = a / quantum                      # exact: a power-of-two scaling
+        r = math.floor(n)
+        frac = n - r
+        if frac > 0.5 or (frac == 0.5 and r % 2 == 1):
+            r += 1                           # round to nearest, ties to even
+        val = r * quantum
+        if val >= FP8_MAX:
+            flat_o[i] = sign | 0x7E
+        elif val < 2.0 ** -6:
+            flat_o[i] = sign | int(round(val / 2.0 ** -9))
+        else:
+            ev = math.floor(math.log2(val))
+            mant = int(round((val / 2.0 ** ev - 1.0) * 8))
+            flat_o[i] = sign | ((ev + 7) << 3) | mant
+    return out
+
+
+def fp8_quantize_rows(x_bf16, scale) -> np.ndarray:
+    """Cache codes of bf16 rows stored with a per-tensor scale: each value is
+    divided by the fp32 scale in fp32 (rounded to nearest), then encoded."""
+    xf = (np.asarray(x_bf16, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    y = (xf / np.float32(scale)).astype(np.float32)
+    return fp8_e4m3_encode(y)
 
 
 # ---------------------------------------------------------------------------
@@ -139,14 +209,17 @@ def gather_request_kv(cache, block_table_row, seq_len: int, dtype: str, block_si
 
 def oracle_attention_varlen(q, k_cache, v_cache, cu_seqlens, seq_lens, block_tables,
                             scale, num_kv_heads: int, dtype: str, block_size: int = 16,
-                            rows=None, validate: bool = True):
+                            rows=None, validate: bool = True, kv_dtype: str | None = None,
+                            k_scale: float = 1.0, v_scale: float = 1.0):
     """Causal softmax attention of packed query rows over a paged KV cache.
 
     q: [total_q, Hq, D]; returns fp64 [total_q, Hq, D] (rows not computed stay
     NaN).  ``rows`` optionally limits the work to a subset of packed rows.
     For request b with rows cu[b] .. cu[b+1]-1 and context L_b, each query
     head h and row j:  s = scale * K[0..p] q,  o = softmax(s) V[0..p],  with
-    p = L_b - n_b + j and K, V gathered through the block table.
+    p = L_b - n_b + j and K, V gathered through the block table.  The pools
+    hold ``kv_dtype`` (default: ``dtype``); with 8-bit codes the cached values
+    are the decoded codes times ``k_scale`` / ``v_scale`` (fp32, widened).
     """
     q = np.asarray(q)
     total_q, Hq, D = q.shape
@@ -159,6 +232,8 @@ def oracle_attention_varlen(q, k_cache, v_cache, cu_seqlens, seq_lens, block_tab
         raise OracleError("cu_seqlens[-1] must equal the number of packed rows")
     G = Hq // num_kv_heads
     scale64 = float(np.float32(scale))
+    kvd = dtype if kv_dtype is None else kv_dtype
+    ks64, vs64 = float(np.float32(k_scale)), float(np.float32(v_scale))
     out = np.full((total_q, Hq, D), np.nan, np.float64)
     want = None if rows is None else set(int(r) for r in rows)
 
@@ -170,8 +245,8 @@ def oracle_attention_varlen(q, k_cache, v_cache, cu_seqlens, seq_lens, block_tab
         my_rows = [r for r in range(q0, q1) if want is None or r in want]
         if not my_rows:
             continue
-        K = gather_request_kv(k_cache, bt[b], L, dtype, block_size)
-        V = gather_request_kv(v_cache, bt[b], L, dtype, block_size)
+        K = gather_request_kv(k_cache, bt[b], L, kvd, block_size) * ks64
+        V = gather_request_kv(v_cache, bt[b], L, kvd, block_size) * vs64
         for r in my_rows:
             j = r - q0
             p = last_visible_key(L, n, j)
