@@ -167,6 +167,40 @@ pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, con
                               const int32_t* block_tables, const pa_attn_params* p,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * 8-bit KV cache (OCP FP8 E4M3).  [Q67] §8.8 and §10.3 name 8-bit KV caches
+ * as the way to halve KV memory without fixing a format; the format taken is
+ * OCP E4M3: 1 sign, 4 exponent (bias 7) and 3 mantissa bits, subnormals
+ * m * 2^-9, largest finite 448, S.1111.111 = NaN, no infinities.  Each pool
+ * has one fp32 scale: a code c stands for decode(c) * scale.
+ *
+ * pa_cache_write_fp8 -- as pa_cache_write, but the new rows are bf16 and the
+ * pools [num_blocks, Hkv, 16, D] hold one byte per element: each value x is
+ * stored as the code nearest to x / scale (the fp32 quotient rounded to
+ * nearest), ties to the even code, magnitudes of 448 and beyond saturated to
+ * 448, NaN stored as 0x7F.  D in {64, 128}; scales finite and > 0.  Errors
+ * as pa_cache_write.
+ */
+pa_status pa_cache_write_fp8(const void* k_new, const void* v_new, int64_t kv_row_stride,
+                             void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                             int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int64_t num_blocks, float k_scale, float v_scale,
+                             void* stream);
+
+/*
+ * pa_attention_varlen_fp8 -- as pa_attention_varlen with 8-bit pools: the
+ * attention runs over K = decode(k_cache) * k_scale and V = decode(v_cache) *
+ * v_scale.  q and out are bf16 (p->dtype == PA_BF16); D = 128, Hq/Hkv in
+ * {1, 2, 4, 8}, single-row (decode) requests only (max_query_len <= 1),
+ * otherwise PA_ERR_UNSUPPORTED.  Scales finite and > 0.  The workspace is
+ * sized by pa_attention_workspace_size(p).
+ */
+pa_status pa_attention_varlen_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                                  const int32_t* block_tables, const pa_attn_params* p,
+                                  float k_scale, float v_scale, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* Bits of the result word written by pa_validate_metadata. */
 #define PA_BAD_CU_SEQLENS   1   /* cu[0] != 0, cu decreasing, or cu[B] != total_q */
 #define PA_BAD_LENGTHS      2   /* n_b > L_b, L_b < 0, n_b > max_query_len or L_b > max_seq_len */
@@ -191,7 +225,7 @@ pa_status pa_validate_metadata(const int32_t* cu_seqlens_q, const int32_t* seq_l
 /* Static, NUL-terminated description of a status code. */
 const char* pa_status_string(pa_status s);
 
-/* ABI version of this header: major*100 + minor. */
+/* ABI version of this header: major*100 + minor (101: the 8-bit cache calls). */
 int32_t pa_abi_version(void);
 
 #ifdef __cplusplus

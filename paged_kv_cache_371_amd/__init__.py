@@ -53,6 +53,12 @@ _SIGNATURES = {
                                                                  ctypes.c_size_t, ctypes.c_void_p]),
     "pa_validate_metadata": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "pa_cache_write_fp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                          ctypes.c_float, ctypes.c_void_p]),
+    "pa_attention_varlen_fp8": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_float, ctypes.c_float,
+                                                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_abi_version": (ctypes.c_int32, []),
 }
@@ -173,6 +179,37 @@ def cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None) -> No
                                 _dtype_code(k_cache), _stream(stream)))
 
 
+def cache_write_fp8(k_new, v_new, k_cache, v_cache, slot_mapping, k_scale: float, v_scale: float,
+                    stream=None) -> None:
+    """Quantise new bf16 K/V rows [N, Hkv, D] into 8-bit (OCP E4M3) pools
+    [NB, Hkv, 16, D] (uint8 tensors) with per-pool scales."""
+    torch = _torch()
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                  (slot_mapping, "slot_mapping")):
+        _dev(t, nm)
+    if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous():
+        raise TypeError("slot_mapping must be a contiguous int64 tensor")
+    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise TypeError("new rows must be bf16")
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise TypeError("8-bit pools must be uint8 tensors")
+    if k_new.shape != v_new.shape or k_new.stride() != v_new.stride():
+        raise ValueError("k_new and v_new must share shape and strides")
+    if k_cache.shape != v_cache.shape or not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("pools must be contiguous [NB, Hkv, 16, D] tensors of one shape")
+    N, Hkv, D = k_new.shape
+    if k_new.stride(2) != 1 or k_new.stride(1) != D:
+        raise ValueError("each new row must hold contiguous [Hkv, D]")
+    if slot_mapping.shape[0] != N:
+        raise ValueError("slot_mapping must have one entry per new row")
+    NB, Hc, bs, Dc = k_cache.shape
+    if Hc != Hkv or Dc != D:
+        raise ValueError("pool heads/head_dim differ from the new rows")
+    _check(lib().pa_cache_write_fp8(k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0), k_cache.data_ptr(),
+                                    v_cache.data_ptr(), slot_mapping.data_ptr(), N, Hkv, D, bs, NB, float(k_scale),
+                                    float(v_scale), _stream(stream)))
+
+
 def make_params(q, k_cache, cu_seqlens, block_tables, num_kv_heads: int, scale: float, max_query_len: int,
                 max_seq_len: int, out=None, partition_size: int = 0) -> AttnParams:
     total_q, Hq, D = q.shape
@@ -206,11 +243,13 @@ def partition_size(params: AttnParams) -> int:
 
 def attention_varlen(out, q, k_cache, v_cache, cu_seqlens, seq_lens, block_tables, scale: float,
                      max_query_len: int, max_seq_len: int, workspace=None, partition_size: int = 0,
-                     stream=None):
+                     stream=None, k_scale=None, v_scale=None):
     """Paged causal attention of packed rows; writes ``out`` [total_q, Hq, D] and returns it.
 
     ``workspace`` (a contiguous device tensor of any dtype, at least
-    ``workspace_size`` bytes) is allocated here when not given.
+    ``workspace_size`` bytes) is allocated here when not given.  uint8 pools
+    hold 8-bit (OCP E4M3) codes: q and out are then bf16 and ``k_scale`` /
+    ``v_scale`` give the pools' scales.
     """
     torch = _torch()
     for t, nm in ((out, "out"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (cu_seqlens, "cu_seqlens"),
@@ -225,7 +264,13 @@ def attention_varlen(out, q, k_cache, v_cache, cu_seqlens, seq_lens, block_table
         raise ValueError("q and out rows must hold contiguous [Hq, D]")
     if not (k_cache.is_contiguous() and v_cache.is_contiguous()) or k_cache.shape != v_cache.shape:
         raise ValueError("pools must be contiguous [NB, Hkv, 16, D] tensors of one shape")
-    if len({q.dtype, out.dtype, k_cache.dtype, v_cache.dtype}) != 1:
+    fp8 = k_cache.dtype == torch.uint8
+    if fp8:
+        if v_cache.dtype != torch.uint8 or q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+            raise TypeError("8-bit pools need uint8 K and V pools and bf16 q and out")
+        if k_scale is None or v_scale is None:
+            raise ValueError("8-bit pools need k_scale and v_scale")
+    elif len({q.dtype, out.dtype, k_cache.dtype, v_cache.dtype}) != 1:
         raise TypeError("q, out and the pools must share one dtype")
     if seq_lens.shape[0] != cu_seqlens.shape[0] - 1 or block_tables.shape[0] != seq_lens.shape[0]:
         raise ValueError("cu_seqlens [B+1], seq_lens [B] and block_tables [B, W] disagree on B")
@@ -239,9 +284,15 @@ def attention_varlen(out, q, k_cache, v_cache, cu_seqlens, seq_lens, block_table
     if not workspace.is_contiguous():
         raise ValueError("workspace must be contiguous")
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib().pa_attention_varlen(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                     cu_seqlens.data_ptr(), seq_lens.data_ptr(), block_tables.data_ptr(),
-                                     ctypes.byref(p), workspace.data_ptr(), ws_bytes, _stream(stream)))
+    if fp8:
+        _check(lib().pa_attention_varlen_fp8(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                             cu_seqlens.data_ptr(), seq_lens.data_ptr(), block_tables.data_ptr(),
+                                             ctypes.byref(p), float(k_scale), float(v_scale), workspace.data_ptr(),
+                                             ws_bytes, _stream(stream)))
+    else:
+        _check(lib().pa_attention_varlen(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                         cu_seqlens.data_ptr(), seq_lens.data_ptr(), block_tables.data_ptr(),
+                                         ctypes.byref(p), workspace.data_ptr(), ws_bytes, _stream(stream)))
     return out
 
 

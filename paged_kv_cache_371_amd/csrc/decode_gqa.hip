@@ -48,6 +48,7 @@
 // merge kernel combines them.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 #include <utility>
 
 #include "pa_common.h"
@@ -61,17 +62,51 @@ namespace pa {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kTileBytes = kBlock * kD * 2;   // one (block, KV head) tile of bf16
 constexpr int kWavesPerGroup = 4;
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
 constexpr float kRescaleThreshold = 8.f;      // log2 units
 constexpr float kMinusBig = -1e30f;           // finite "no token yet" max
 constexpr uint32_t kBf16OnePair = 0x3F803F80u;
 constexpr int kMaxDevices = 64;
-// Tiles in flight per wave.  One workgroup per CU (one wave per SIMD): a
-// second workgroup only competes for issue slots (its waves starve while the
-// first one runs), so its registers are better spent on a deeper ring.
-constexpr int kRing = PA_DECODE_RING;
+#ifndef PA_DECODE_RING_FP8
+#define PA_DECODE_RING_FP8 6
+#endif
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+// Cache element types.  bf16: a lane loads 16 bytes (8 elements) per load
+// slot.  OCP FP8 E4M3: a lane loads 8 bytes (the same 8 elements) and widens
+// them to bf16 pairs with v_cvt_scalef32_pk_bf16_fp8 (exact: every E4M3 value
+// is a bf16 value); the per-tensor scales are folded into the softmax scale
+// and the output normalisation.
+//
+// Tiles in flight per wave (kRing): one workgroup per CU (one worker wave per
+// SIMD), so registers go to a deep ring; an 8-bit tile is half the bytes, so
+// its ring is twice as deep for the same bytes in flight.
+template <bool F8>
+struct Kv {
+  static constexpr int kTileBytes = kBlock * kD * (F8 ? 1 : 2);   // one (block, KV head) tile
+  static constexpr int kLoadBytes = F8 ? 8 : 16;                    // per lane and load slot
+  static constexpr int kRing = F8 ? PA_DECODE_RING_FP8 : PA_DECODE_RING;
+  using Raw = typename std::conditional<F8, u32x2_t, u32x4_t>::type;
+  static __device__ __forceinline__ Raw load(__amdgpu_buffer_rsrc_t rsrc, int off) {
+    if constexpr (F8) {
+      return __builtin_amdgcn_raw_buffer_load_b64(rsrc, off, 0, 0);
+    } else {
+      return __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+    }
+  }
+  // 8 elements as 4 bf16 pairs
+  static __device__ __forceinline__ u32x4_t widen(const Raw& w) {
+    if constexpr (F8) {
+      return u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.f, true)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.f, true))};
+    } else {
+      return w;
+    }
+  }
+};
 #ifndef PA_DECODE_STATIC_ROUNDS
 #define PA_DECODE_STATIC_ROUNDS 1
 #endif
@@ -169,7 +204,10 @@ struct Item {
 // t % Hkv.  An index past the list gives a placeholder with in-range
 // addresses and no tiles.  Every field goes through readfirstlane, so the descriptors and
 // table loads built from it stay scalar.
+template <bool F8>
 __device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t, int4 ent) {
+  constexpr int kRing = Kv<F8>::kRing;
+  constexpr int kTileBytes = Kv<F8>::kTileBytes;
   Item it;
   it.valid = t < total;
   int b = 0, part = 0, q0 = 0, L = 1, kvh = 0;
@@ -219,8 +257,12 @@ __device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t,
 // the last load group of an item already fetches the next item's first kRing
 // tiles and the HBM queue of the wave never drains at item boundaries.  The
 // physical block id of the slot issued next is fetched one issue ahead.
-template <int G>
+template <int G, bool F8>
 __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kernel(DecodeArgs a) {
+  using T = Kv<F8>;
+  constexpr int kRing = T::kRing;
+  constexpr int kTileBytes = T::kTileBytes;
+  using Raw = typename T::Raw;
   constexpr int K = log2_of<G>();
   constexpr int kRot = 16 / G;          // lanes between consecutive heads in a row
   constexpr int kNV = G * 8;            // accumulators per lane
@@ -330,7 +372,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
   const int r = lane & 15;
   const int tg = lane >> 4;
   const int hr = r >> (4 - K);
-  const int voff = tg * (kD * 2) + r * 16;
+  const int voff = tg * kD * (F8 ? 1 : 2) + r * T::kLoadBytes;   // token tg of the slot, d-slice r
   const int64_t bstride = int64_t(a.num_kv_heads) * kTileBytes;
   const float scale_log2 = a.scale_log2;
   // direction of row_ror within a row: the head of accumulator slot j is (hr + dir*j) mod G
@@ -373,7 +415,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
     });
   };
 
-  Item cur = make_item(a, total, item_of_round(0), entry0);
+  Item cur = make_item<F8>(a, total, item_of_round(0), entry0);
   if (!cur.valid) return;
 
   auto load_q = [&](u32x4_t(&qreg)[G], const Item& it) {   // q slices, lane-relative order h(r ^ M_j)
@@ -385,7 +427,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
       qreg[j] = *reinterpret_cast<const u32x4_t*>(qrow + hh * (kD * 2) + r * 16);
     });
   };
-  auto load_tile = [&](u32x4_t(&kb)[4], u32x4_t(&vb)[4], const char* kbase, const char* vbase, bool live,
+  auto load_tile = [&](Raw(&kb)[4], Raw(&vb)[4], const char* kbase, const char* vbase, bool live,
                        int64_t phys) {
     const int nrec = live ? kTileBytes : 0;
     const __amdgpu_buffer_rsrc_t rk =
@@ -393,13 +435,13 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
     const __amdgpu_buffer_rsrc_t rv =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + phys * bstride), 0, nrec, kRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kb[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff + i * 1024, 0, 0);
+    for (int i = 0; i < 4; ++i) kb[i] = T::load(rk, voff + i * (kTileBytes / 4));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vb[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + i * 1024, 0, 0);
+    for (int i = 0; i < 4; ++i) vb[i] = T::load(rv, voff + i * (kTileBytes / 4));
   };
 
   u32x4_t qreg[G];
-  u32x4_t kr[kRing][4], vr[kRing][4];   // the ring: K and V of kRing tiles
+  Raw kr[kRing][4], vr[kRing][4];   // the ring: K and V of kRing tiles, as loaded
   load_q(qreg, cur);
   int ph0[kRing];   // block ids of the first tiles, all requested before any is used
   static_for<kRing>([&](auto S) {
@@ -419,7 +461,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
     // second-to-last load group, just before its first block ids are needed,
     // so it is handed out as late as the tile stream allows.
     const bool dyn = i + 1 >= kStaticRounds;
-    Item nxt = make_item(a, total, total, make_int4(0, 0, 0, 1));
+    Item nxt = make_item<F8>(a, total, total, make_int4(0, 0, 0, 1));
     uint32_t qt[kQDw];
     bool requested = false;
     auto get_next = [&]() {
@@ -428,11 +470,11 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
       int t;
       int4 e;
       take(t, e);
-      nxt = make_item(a, total, t, e);
+      nxt = make_item<F8>(a, total, t, e);
       if (nxt.valid) fetch_q(nxt, qt);
     };
     if (!dyn) {
-      nxt = make_item(a, total, item_of_round(i + 1), static_entry(i + 1));
+      nxt = make_item<F8>(a, total, item_of_round(i + 1), static_entry(i + 1));
       if (nxt.valid) fetch_q(nxt, qt);
     } else if (cur.nb <= 2 * kRing) {
       get_next();
@@ -458,7 +500,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
       return load_const_early(tb, lb0 + max(min(jj, nbl - 1), 0));
     };
     int64_t pf = slot_phys(kRing);   // block id of the next slot to issue
-    auto issue = [&](u32x4_t(&kb)[4], u32x4_t(&vb)[4], int j) {
+    auto issue = [&](Raw(&kb)[4], Raw(&vb)[4], int j) {
       const int64_t phys = pf;
       pf = slot_phys(j + 1);
       const bool own = j < cur.nbr;
@@ -467,7 +509,13 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
       load_tile(kb, vb, own ? cur.kbase : nxt.kbase, own ? cur.vbase : nxt.vbase, jj < nbl, phys);
     };
 
-    auto process = [&](u32x4_t(&kb)[4], u32x4_t(&vb)[4], int k) {
+    auto process = [&](Raw(&kraw)[4], Raw(&vraw)[4], int k) {
+      u32x4_t kb[4], vb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kb[i] = T::widen(kraw[i]);
+        vb[i] = T::widen(vraw[i]);
+      }
       const int tb = (cur.lb0 + k) * kBlock;   // first token of the block
       float sc[4];
 #pragma unroll
@@ -557,7 +605,9 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
     // ---- combine the 4 token rows: common max, rescale, reduce-scatter -----------
     const float mw = rows_max(m);
     const float c = fast_exp2(m - mw);
-    const float lw = rows_sum(l * c);   // every lane: (max, sum) of head hr over the partition
+    // every lane: (max, sum) of head hr over the partition; the sum carries
+    // 1 / v_scale, so dividing by it also applies the V scale
+    const float lw = rows_sum(l * c) * a.lsum_scale;
     static_for<G>([&](auto J) {
       constexpr int j = decltype(J)::value;
       float cj = c;
@@ -632,7 +682,7 @@ bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size) {
 namespace {
 
 // Resident workgroups per device for kernel K: CUs x occupancy, queried once per device.
-template <int G>
+template <int G, bool F8>
 int persistent_groups() {
   static std::atomic<int> cache[kMaxDevices];
   int dev = 0;
@@ -641,7 +691,7 @@ int persistent_groups() {
   if (v > 0) return v;
   int cus = 0, occ = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_gqa_kernel<G>, 64 * (kWavesPerGroup + 1), 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_gqa_kernel<G, F8>, 64 * (kWavesPerGroup + 1), 0) !=
           hipSuccess ||
       occ <= 0)
     occ = 1;
@@ -650,12 +700,12 @@ int persistent_groups() {
   return v;
 }
 
-template <int G>
+template <int G, bool F8>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   const int64_t upper = int64_t(a.num_seqs) * a.max_parts * a.num_kv_heads;
-  const int64_t grid = std::min<int64_t>(upper, persistent_groups<G>());
+  const int64_t grid = std::min<int64_t>(upper, persistent_groups<G, F8>());
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_gqa_kernel<G>, dim3(grid), dim3(64 * (kWavesPerGroup + 1)), 0, stream, a);
+  hipLaunchKernelGGL((decode_gqa_kernel<G, F8>), dim3(grid), dim3(64 * (kWavesPerGroup + 1)), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -664,21 +714,30 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
 int decode_gqa_workers(int group) {
   int g = 0;
   switch (group) {
-    case 1: g = persistent_groups<1>(); break;
-    case 2: g = persistent_groups<2>(); break;
-    case 4: g = persistent_groups<4>(); break;
-    case 8: g = persistent_groups<8>(); break;
+    case 1: g = persistent_groups<1, false>(); break;
+    case 2: g = persistent_groups<2, false>(); break;
+    case 4: g = persistent_groups<4, false>(); break;
+    case 8: g = persistent_groups<8, false>(); break;
     default: g = 256;
   }
   return g * kWavesPerGroup;
 }
 
-hipError_t launch_decode_gqa(int group, const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode_gqa(int group, bool fp8_cache, const DecodeArgs& a, hipStream_t stream) {
+  if (fp8_cache) {
+    switch (group) {
+      case 1: return launch_g<1, true>(a, stream);
+      case 2: return launch_g<2, true>(a, stream);
+      case 4: return launch_g<4, true>(a, stream);
+      case 8: return launch_g<8, true>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (group) {
-    case 1: return launch_g<1>(a, stream);
-    case 2: return launch_g<2>(a, stream);
-    case 4: return launch_g<4>(a, stream);
-    case 8: return launch_g<8>(a, stream);
+    case 1: return launch_g<1, false>(a, stream);
+    case 2: return launch_g<2, false>(a, stream);
+    case 4: return launch_g<4, false>(a, stream);
+    case 8: return launch_g<8, false>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -142,7 +142,7 @@ pa_status check_params(const pa_attn_params* p) {
 
 extern "C" {
 
-int32_t pa_abi_version(void) { return 100; }
+int32_t pa_abi_version(void) { return 101; }
 
 const char* pa_status_string(pa_status s) {
   switch (s) {
@@ -190,11 +190,24 @@ int32_t pa_attention_partition_size(const pa_attn_params* p) {
   return effective_partition(p);
 }
 
-pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, const void* v_cache,
-                              const int32_t* cu_seqlens_q, const int32_t* seq_lens, const int32_t* block_tables,
-                              const pa_attn_params* p, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Both attention entry points.  fp8: the pools hold OCP FP8 E4M3 codes with
+// per-tensor scales (decode rows only; q and out are bf16).
+pa_status attention_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* cu_seqlens_q, const int32_t* seq_lens, const int32_t* block_tables,
+                         const pa_attn_params* p, void* workspace, size_t workspace_bytes, void* stream, bool fp8,
+                         float k_scale, float v_scale) {
   pa_status st = check_params(p);
   if (st != PA_OK) return st;
+  if (fp8) {
+    if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !(k_scale > 0.f) || !(v_scale > 0.f))
+      return PA_ERR_SHAPE;
+    const int g8 = p->num_q_heads / p->num_kv_heads;
+    if (p->dtype != PA_BF16 || p->max_query_len > 1 ||
+        !pa::decode_gqa_supported(1, p->head_dim, g8, effective_partition(p)))
+      return PA_ERR_UNSUPPORTED;
+  }
   if (p->num_seqs == 0 || p->total_q == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !cu_seqlens_q || !seq_lens || !block_tables) return PA_ERR_NULL;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
@@ -208,7 +221,7 @@ pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, con
   const Plan pl = make_plan(p);
   if (!pl.ok) return PA_ERR_UNSUPPORTED;
   if (pl.parts > 65535 || int64_t(p->num_seqs) * pl.parts * p->num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
-  const float scale_log2 = p->scale * kLog2e;
+  const float scale_log2 = p->scale * kLog2e * (fp8 ? k_scale : 1.f);
   const size_t pbytes = plan_bytes(p, pl);
   float* ws = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pbytes) : nullptr;
   float* region_a = ws;
@@ -231,6 +244,7 @@ pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, con
   d.part_size = effective_partition(p);
   d.max_parts = int32_t(pl.parts);
   d.scale_log2 = scale_log2;
+  d.lsum_scale = fp8 ? 1.f / v_scale : 1.f;
   d.plan = (pl.fast || pl.prefill) ? static_cast<int32_t*>(workspace) : nullptr;
   d.merge_off_ints = merge_off(p, pl);
   d.plan_capacity = int32_t(std::max<int64_t>(1, pl.fast ? decode_capacity(p, pl) : 1));
@@ -262,7 +276,7 @@ pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, con
     point_at(region_a, pl.rows_a);
     d.row_mode = pa::kSingleRowOnly;
     d.partial_by_seq = 1;
-    e = pa::launch_decode_gqa(g, d, s);
+    e = pa::launch_decode_gqa(g, fp8, d, s);
     if (e == hipSuccess && pl.parts > 1) e = pa::launch_merge_list(d, s);
     if (e != hipSuccess) return PA_ERR_LAUNCH;
   }
@@ -295,6 +309,41 @@ pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, con
     if (e != hipSuccess) return PA_ERR_LAUNCH;
   }
   return PA_OK;
+}
+
+}  // namespace
+
+pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* cu_seqlens_q, const int32_t* seq_lens, const int32_t* block_tables,
+                              const pa_attn_params* p, void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_impl(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, block_tables, p, workspace, workspace_bytes,
+                        stream, false, 1.f, 1.f);
+}
+
+pa_status pa_attention_varlen_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* cu_seqlens_q, const int32_t* seq_lens, const int32_t* block_tables,
+                                  const pa_attn_params* p, float k_scale, float v_scale, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return attention_impl(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, block_tables, p, workspace, workspace_bytes,
+                        stream, true, k_scale, v_scale);
+}
+
+pa_status pa_cache_write_fp8(const void* k_new, const void* v_new, int64_t kv_row_stride, void* k_cache,
+                             void* v_cache, const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int64_t num_blocks, float k_scale, float v_scale,
+                             void* stream) {
+  if (block_size != PA_BLOCK_SIZE) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+  if (kv_row_stride < int64_t(num_kv_heads) * head_dim) return PA_ERR_SHAPE;
+  if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !(k_scale > 0.f) || !(v_scale > 0.f)) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) || (kv_row_stride * 2) % 16)
+    return PA_ERR_ALIGN;
+  hipError_t e = pa::launch_cache_write_fp8(k_new, v_new, kv_row_stride * 2, k_cache, v_cache, slot_mapping, num_tokens,
+                                            num_kv_heads, head_dim, k_scale, v_scale, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 pa_status pa_validate_metadata(const int32_t* cu_seqlens_q, const int32_t* seq_lens, const int32_t* block_tables,

@@ -31,6 +31,7 @@ struct DecodeArgs {
   int32_t* plan;            // fast kernel's work list (header + items), in the workspace
   int64_t merge_off_ints;   // list of requests with more than one partition: plan + kPlanHeaderInts + this
   int32_t plan_capacity;    // decode entries the work list has room for (>= 1)
+  float lsum_scale;         // the softmax sum is multiplied by this (1 / v_scale for 8-bit pools, else 1)
   int32_t row_mode;         // which requests this launch serves (RowMode)
   int32_t partial_by_seq;   // 1: partials indexed by request, else by packed row
 };
@@ -62,6 +63,10 @@ struct PrefillArgs {
 hipError_t launch_cache_write(const void* k_new, const void* v_new, int64_t kv_row_stride_bytes, void* k_cache,
                               void* v_cache, const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
                               int32_t head_bytes, hipStream_t stream);
+// bf16 rows quantised to OCP FP8 E4M3 codes with per-tensor scales (D = 64 or 128).
+hipError_t launch_cache_write_fp8(const void* k_new, const void* v_new, int64_t kv_row_stride_bytes, void* k_cache,
+                                  void* v_cache, const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                                  int32_t head_dim, float k_scale, float v_scale, hipStream_t stream);
 
 // dtype: 0 fp32, 1 bf16.  Returns hipErrorInvalidValue for shapes not built.
 hipError_t launch_decode(int dtype, int head_dim, int group, const DecodeArgs& a, int64_t partial_rows,
@@ -101,7 +106,8 @@ size_t plan_bytes(int64_t decode_capacity, int64_t prefill_capacity, int64_t mer
 bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size);
 // Waves of the persistent fast decode kernel on the current device.
 int decode_gqa_workers(int group);
-hipError_t launch_decode_gqa(int group, const DecodeArgs& a, hipStream_t stream);
+// fp8_cache: the pools hold OCP FP8 E4M3 codes (scales folded into scale_log2 and lsum_scale).
+hipError_t launch_decode_gqa(int group, bool fp8_cache, const DecodeArgs& a, hipStream_t stream);
 // Partition merge alone (for a DecodeArgs whose partials are already written).
 hipError_t launch_merge(int dtype, int head_dim, const DecodeArgs& a, int64_t partial_rows, hipStream_t stream);
 // Merge for the fast decode kernel's partials (bf16, D = 128): only the

@@ -19,7 +19,7 @@ HEADER = os.path.join(ROOT, "include", "pa.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -55,7 +55,7 @@ def test_struct_layout_matches_c(tmp_path):
 
 
 def test_status_strings_and_version(L):
-    assert L.pa_abi_version() == 100
+    assert L.pa_abi_version() == 101
     for code in range(0, -8, -1):
         s = L.pa_status_string(code).decode()
         assert s.startswith("PA_")
@@ -136,6 +136,22 @@ def test_cache_write_host_errors(L):
     assert f(None, 16, 1024, 16, 16, 16, 4, 8, 128, 16, 10, pa.PA_BF16, None) == -1
     assert f(16, 16, 1028, 16, 16, 16, 4, 1, 128, 16, 10, pa.PA_BF16, None) == -4      # unaligned stride
     assert f(8, 16, 1024, 16, 16, 16, 4, 8, 128, 16, 10, pa.PA_BF16, None) == -4       # unaligned pointer
+
+
+def test_fp8_host_errors(L):
+    f = L.pa_cache_write_fp8
+    assert f(16, 16, 1024, 16, 16, 16, 0, 8, 128, 16, 10, 1.0, 1.0, None) == 0      # no rows: no-op
+    assert f(16, 16, 1024, 16, 16, 16, 4, 8, 128, 16, 10, 0.0, 1.0, None) == -2     # scale must be > 0
+    assert f(16, 16, 1024, 16, 16, 16, 4, 8, 128, 16, 10, 1.0, float("inf"), None) == -2
+    assert f(16, 16, 1024, 16, 16, 16, 4, 8, 96, 16, 10, 1.0, 1.0, None) == -3      # head dim
+    assert f(None, 16, 1024, 16, 16, 16, 4, 8, 128, 16, 10, 1.0, 1.0, None) == -1
+    a = L.pa_attention_varlen_fp8
+    p = _params()
+    assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(p), 1.0, -1.0, None, 0, None) == -2
+    assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(max_query_len=4)), 1.0, 1.0, None, 0, None) == -3
+    assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(dtype=pa.PA_F32)), 1.0, 1.0, None, 0, None) == -3
+    assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(head_dim=64, q_row_stride=512, o_row_stride=512)),
+             1.0, 1.0, None, 0, None) == -3
 
 
 def test_validate_host_errors(L):

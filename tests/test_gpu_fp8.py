@@ -1,0 +1,159 @@
+"""GPU parity of the 8-bit (OCP FP8 E4M3) KV cache path against the oracle.
+
+Bars: the quantising cache write is bit-exact over the whole pool (the
+oracle divides by the scale in fp32 and encodes with ties to even and
+saturation); attention over 8-bit pools is within the bf16 bounds (max-abs
+2e-2, mean-abs 2e-3) of the fp64 oracle attending over decode(code) *
+scale.  Slots that hold no token keep the NaN code, so a read outside a
+context shows up in the output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_371_amd as pa
+from tests.gpu_util import say, to_dev, to_host
+from workloads import build_case, make_config
+
+pytestmark = pytest.mark.gpu
+
+NAN_CODE = 0x7F
+BF16_NAN = 0x7FC0
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def fp8_pools(c, seed, max_exp=10):
+    """8-bit pools shaped like the case's: random finite codes of magnitude
+    below 2^(max_exp - 7), NaN codes wherever the case left a poisoned slot."""
+    rng = np.random.default_rng(seed)
+    pools = []
+    for bf in (c.k_cache, c.v_cache):
+        e = rng.integers(0, max_exp + 1, bf.shape)
+        m = rng.integers(0, 8, bf.shape)
+        s = rng.integers(0, 2, bf.shape)
+        codes = ((s << 7) | (e << 3) | m).astype(np.uint8)
+        codes[bf == BF16_NAN] = NAN_CODE
+        pools.append(codes)
+    return pools
+
+
+def to_dev_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+class Fp8Case:
+    def __init__(self, c, seed, k_scale, v_scale):
+        self.c, self.k_scale, self.v_scale = c, k_scale, v_scale
+        self.k_codes, self.v_codes = fp8_pools(c, seed)
+        self.q = to_dev(c.q, "bf16")
+        self.k_cache, self.v_cache = to_dev_u8(self.k_codes), to_dev_u8(self.v_codes)
+        self.k_new, self.v_new = to_dev(c.k_new, "bf16"), to_dev(c.v_new, "bf16")
+        self.slots = torch.from_numpy(c.slot_mapping).to("cuda:0")
+        self.cu = torch.from_numpy(c.cu_seqlens).to("cuda:0")
+        self.seq_lens = torch.from_numpy(c.seq_lens).to("cuda:0")
+        self.tables = torch.from_numpy(c.block_tables).to("cuda:0")
+        self.out = torch.empty_like(self.q)
+
+    def oracle_pools(self):
+        kq = oracle.fp8_quantize_rows(self.c.k_new, self.k_scale)
+        vq = oracle.fp8_quantize_rows(self.c.v_new, self.v_scale)
+        return oracle.oracle_cache_write(self.k_codes, self.v_codes, kq, vq, self.c.slot_mapping)
+
+    def write_and_attend(self, partition_size=0):
+        c = self.c
+        pa.cache_write_fp8(self.k_new, self.v_new, self.k_cache, self.v_cache, self.slots, self.k_scale, self.v_scale)
+        pa.attention_varlen(self.out, self.q, self.k_cache, self.v_cache, self.cu, self.seq_lens, self.tables,
+                            float(c.scale), c.max_query_len, c.max_seq_len, partition_size=partition_size,
+                            k_scale=self.k_scale, v_scale=self.v_scale)
+        torch.cuda.synchronize()
+
+    def compare(self, rows=None, check_pool=True):
+        c = self.c
+        kp, vp = self.oracle_pools()
+        if check_pool:
+            assert np.array_equal(self.k_cache.cpu().numpy(), kp), "K pool differs"
+            assert np.array_equal(self.v_cache.cpu().numpy(), vp), "V pool differs"
+        want = oracle.oracle_attention_varlen(c.q, kp, vp, c.cu_seqlens, c.seq_lens, c.block_tables, c.scale,
+                                              c.num_kv_heads, "bf16", rows=rows, kv_dtype="fp8",
+                                              k_scale=self.k_scale, v_scale=self.v_scale)
+        got = oracle.widen(to_host(self.out, "bf16"), "bf16")
+        if rows is not None:
+            idx = np.asarray(sorted(set(int(r) for r in rows)))
+            got, want = got[idx], want[idx]
+        return oracle.compare_outputs(got, want, "bf16")
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_cache_write_fp8_bitexact(D):
+    """Quantisation of new rows, including ties, saturation, tiny values and NaN."""
+    c = build_case(f"cw8_{D}", 31, "bf16", 4, 2, D, [1, 16, 5, 1, 30], [1, 16, 40, 100, 33])
+    c.slot_mapping[2] = -1
+    rng = np.random.default_rng(2)
+    special = np.array([0x4700, 0xC700, 0x3F88, 0x3F98, 0x3400, 0x2F80, 0x0001, BF16_NAN, 0x7F80, 0xFF80, 0x8000],
+                       np.uint16)   # 32768, -32768, ties near 1, 2^-23, tiny, subnormal bf16, NaN, +-inf, -0
+    for arr in (c.k_new, c.v_new):
+        flat = arr.reshape(-1)
+        pos = rng.choice(flat.size, special.size * 6, replace=False)
+        flat[pos] = np.tile(special, 6)
+    fc = Fp8Case(c, 7, 0.0625, 0.3)
+    pa.cache_write_fp8(fc.k_new, fc.v_new, fc.k_cache, fc.v_cache, fc.slots, fc.k_scale, fc.v_scale)
+    torch.cuda.synchronize()
+    kp, vp = fc.oracle_pools()
+    assert np.array_equal(fc.k_cache.cpu().numpy(), kp)
+    assert np.array_equal(fc.v_cache.cpu().numpy(), vp)
+
+
+LENS = [1, 2, 15, 16, 17, 63, 64, 65, 129, 500, 513, 1025, 3000]
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (16, 4), (64, 8)])
+@pytest.mark.parametrize("psize", [0, 256])
+def test_decode_fp8_edge_lengths(Hq, Hkv, psize):
+    c = build_case(f"dec8_{Hq}_{Hkv}", 32, "bf16", Hq, Hkv, 128, [1] * len(LENS), LENS)
+    fc = Fp8Case(c, 8, 0.5, 0.25)
+    fc.write_and_attend(psize)
+    mx, mean, ok = fc.compare()
+    say(f"fp8 {Hq}/{Hkv} psize {psize}: max {mx:.3g} mean {mean:.3g}")
+    assert ok, (mx, mean)
+
+
+def test_decode_fp8_deterministic_bitwise():
+    c = build_case("det8", 33, "bf16", 64, 8, 128, [1] * 6, [3000, 17, 900, 2049, 1, 4500])
+    fc = Fp8Case(c, 9, 0.5, 0.25)
+    fc.write_and_attend(0)
+    a = fc.out.clone()
+    pa.attention_varlen(fc.out, fc.q, fc.k_cache, fc.v_cache, fc.cu, fc.seq_lens, fc.tables, float(c.scale),
+                        1, c.max_seq_len, k_scale=fc.k_scale, v_scale=fc.v_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), fc.out.view(torch.int16))
+
+
+def test_gqa_config_fp8_sampled():
+    """The Llama-3-70B-shaped GQA decode layer with 8-bit pools, in the launch
+    configuration the benchmark times (default partition), sampled rows."""
+    c = make_config("gqa_decode_bf16", 0)
+    fc = Fp8Case(c, 10, 0.5, 0.25)
+    fc.write_and_attend(0)
+    rng = np.random.default_rng(0)
+    L = c.seq_lens
+    rows = set(rng.choice(c.total_q, 24, replace=False).tolist()) | {int(np.argmax(L)), int(np.argmin(L))}
+    mx, mean, ok = fc.compare(rows=sorted(rows), check_pool=False)
+    say(f"gqa fp8 sampled: max {mx:.3g} mean {mean:.3g}")
+    assert ok, (mx, mean)
+    assert torch.isfinite(fc.out.float()).all()
+
+
+def test_fp8_multirow_is_rejected():
+    c = build_case("mr8", 34, "bf16", 8, 2, 128, [3, 1], [20, 30])
+    fc = Fp8Case(c, 11, 1.0, 1.0)
+    with pytest.raises(pa.PAError) as e:
+        fc.write_and_attend(0)
+    assert e.value.status == -3
