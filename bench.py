@@ -19,7 +19,9 @@ the digest recorded there (null otherwise).  ``cpu_baseline`` times the fp64
 CPU oracle on a bounded sample of the same requests.
 
 ``--calibrate-copy`` runs only a 1 GiB device-to-device copy (the counters'
-calibration run).  Parity of this exact
+calibration run).  ``--kv-dtype fp8`` runs the same workload on 8-bit (OCP
+E4M3) pools of random finite codes with per-tensor scales; KV bytes then
+count one byte per element.  Parity of this exact
 launch configuration against the oracle is the job of the GPU tests; the
 oracle is used here only for the CPU baseline.
 """
@@ -75,17 +77,30 @@ def measured_traffic(workload: str):
     return int(val.group(1))
 
 
-def algorithmic_bytes(c) -> dict:
+K_SCALE_FP8, V_SCALE_FP8 = 0.5, 0.25
+
+
+def fp8_codes(shape, seed: int) -> np.ndarray:
+    """Random finite OCP E4M3 codes of magnitude below 16 (the 8-bit pools' contents)."""
+    rng = np.random.default_rng(seed)
+    e = rng.integers(0, 11, shape)
+    m = rng.integers(0, 8, shape)
+    sgn = rng.integers(0, 2, shape)
+    return ((sgn << 7) | (e << 3) | m).astype(np.uint8)
+
+
+def algorithmic_bytes(c, kv_elem_bytes=None) -> dict:
     """Bytes the attention must move for this batch (no re-reads, no partial-block over-read)."""
     s = 2 if c.dtype == "bf16" else 4
+    kvs = s if kv_elem_bytes is None else kv_elem_bytes
     L = c.seq_lens.astype(np.int64)
     n = c.q_lens.astype(np.int64)
-    kv = int((L * c.num_kv_heads * c.head_dim * 2 * s).sum())
+    kv = int((L * c.num_kv_heads * c.head_dim * 2 * kvs).sum())
     q = int(n.sum() * c.num_q_heads * c.head_dim * s)
     o = q
     tables = int(4 * (-(-L // 16)).sum())
     meta = 4 * (2 * c.num_seqs + 1)
-    cw = int(2 * 2 * (c.slot_mapping >= 0).sum() * c.num_kv_heads * c.head_dim * s + 8 * c.total_q)
+    cw = int(2 * (s + kvs) * (c.slot_mapping >= 0).sum() * c.num_kv_heads * c.head_dim + 8 * c.total_q)
     return dict(kv=kv, q=q, o=o, tables=tables, meta=meta, attention=kv + q + o + tables + meta, cache_write=cw)
 
 
@@ -99,9 +114,10 @@ def attention_flops(c) -> float:
     return 4.0 * c.head_dim * c.num_q_heads * keys
 
 
-def cpu_baseline(c, budget_s: float = 12.0) -> dict:
+def cpu_baseline(c, budget_s: float = 12.0, fp8_pools=None) -> dict:
     """Time the fp64 oracle on whole requests, in passes over the batch in a
-    fixed shuffled order, until the budget is spent (one BLAS thread)."""
+    fixed shuffled order, until the budget is spent (one BLAS thread).  With
+    ``fp8_pools`` (K and V codes) the oracle attends over the 8-bit pools."""
     import oracle
 
     try:
@@ -109,9 +125,17 @@ def cpu_baseline(c, budget_s: float = 12.0) -> dict:
         limit = threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
         limit = None
-    kp, vp = oracle.oracle_cache_write(c.k_cache, c.v_cache, c.k_new, c.v_new, c.slot_mapping)
+    extra = {}
+    if fp8_pools is None:
+        kp, vp = oracle.oracle_cache_write(c.k_cache, c.v_cache, c.k_new, c.v_new, c.slot_mapping)
+        s = 2 if c.dtype == "bf16" else 4
+    else:
+        kp, vp = oracle.oracle_cache_write(fp8_pools[0], fp8_pools[1],
+                                           oracle.fp8_quantize_rows(c.k_new, K_SCALE_FP8),
+                                           oracle.fp8_quantize_rows(c.v_new, V_SCALE_FP8), c.slot_mapping)
+        extra = dict(kv_dtype="fp8", k_scale=K_SCALE_FP8, v_scale=V_SCALE_FP8)
+        s = 1
     order = np.random.default_rng(1).permutation(c.num_seqs)
-    s = 2 if c.dtype == "bf16" else 4
     done_rows = done_kv = reqs = 0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
@@ -120,7 +144,7 @@ def cpu_baseline(c, budget_s: float = 12.0) -> dict:
             if not rows:
                 continue
             oracle.oracle_attention_varlen(c.q, kp, vp, c.cu_seqlens, c.seq_lens, c.block_tables, c.scale,
-                                           c.num_kv_heads, c.dtype, rows=rows, validate=False)
+                                           c.num_kv_heads, c.dtype, rows=rows, validate=False, **extra)
             done_rows += len(rows)
             done_kv += int(c.seq_lens[b]) * c.num_kv_heads * c.head_dim * 2 * s
             reqs += 1
@@ -151,15 +175,21 @@ def calibrate_copy() -> None:
 class _DeviceBatch:
     """The workload's arrays in HBM, and the two ABI calls of one step."""
 
-    def __init__(self, c, torch, pa):
+    def __init__(self, c, torch, pa, fp8_pools=None):
         self.c, self.torch, self.pa = c, torch, pa
+        self.fp8 = fp8_pools is not None
 
         def dev(a):
             if c.dtype == "bf16":
                 return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda:0").view(torch.bfloat16)
             return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
 
-        self.q, self.k_cache, self.v_cache = dev(c.q), dev(c.k_cache), dev(c.v_cache)
+        self.q = dev(c.q)
+        if self.fp8:
+            self.k_cache = torch.from_numpy(fp8_pools[0]).to("cuda:0")
+            self.v_cache = torch.from_numpy(fp8_pools[1]).to("cuda:0")
+        else:
+            self.k_cache, self.v_cache = dev(c.k_cache), dev(c.v_cache)
         self.k_new, self.v_new = dev(c.k_new), dev(c.v_new)
         self.slots = torch.from_numpy(c.slot_mapping).to("cuda:0")
         self.cu = torch.from_numpy(c.cu_seqlens).to("cuda:0")
@@ -170,7 +200,11 @@ class _DeviceBatch:
         self.partition_size = None
 
     def cache_write(self):
-        self.pa.cache_write(self.k_new, self.v_new, self.k_cache, self.v_cache, self.slots)
+        if self.fp8:
+            self.pa.cache_write_fp8(self.k_new, self.v_new, self.k_cache, self.v_cache, self.slots, K_SCALE_FP8,
+                                    V_SCALE_FP8)
+        else:
+            self.pa.cache_write(self.k_new, self.v_new, self.k_cache, self.v_cache, self.slots)
 
     def attention(self, partition_size):
         c = self.c
@@ -181,7 +215,8 @@ class _DeviceBatch:
             self.partition_size = self.pa.partition_size(p)
         self.pa.attention_varlen(self.out, self.q, self.k_cache, self.v_cache, self.cu, self.seq_lens, self.tables,
                                  float(c.scale), c.max_query_len, c.max_seq_len, workspace=self.ws,
-                                 partition_size=partition_size)
+                                 partition_size=partition_size, k_scale=K_SCALE_FP8 if self.fp8 else None,
+                                 v_scale=V_SCALE_FP8 if self.fp8 else None)
 
 
 def main() -> None:
@@ -195,6 +230,8 @@ def main() -> None:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default="bf16",
+                    help="fp8: 8-bit (OCP E4M3) pools with per-tensor scales, bf16 q and out")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this framework runs the path on one GPU; --gpus must be 1 "
@@ -210,8 +247,13 @@ def main() -> None:
     from workloads import make_config
 
     c = make_config(args.workload, args.seed, poison=False)
-    dc = _DeviceBatch(c, torch, pa)
-    ab = algorithmic_bytes(c)
+    fp8 = args.kv_dtype == "fp8"
+    if fp8 and c.dtype != "bf16":
+        raise SystemExit("8-bit pools need a bf16 workload")
+    pools8 = (fp8_codes(c.k_cache.shape, 1000 + args.seed), fp8_codes(c.v_cache.shape, 2000 + args.seed)) if fp8 \
+        else None
+    dc = _DeviceBatch(c, torch, pa, pools8)
+    ab = algorithmic_bytes(c, 1 if fp8 else None)
     flops = attention_flops(c)
     stream = torch.cuda.current_stream()
 
@@ -270,6 +312,7 @@ def main() -> None:
             "num_blocks": c.num_blocks,
             "mean_context": float(c.seq_lens.mean()),
             "partition_size": dc.partition_size,
+            "kv_dtype": "fp8_e4m3" if fp8 else c.dtype,
             "step": "cache_write + attention_varlen",
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
@@ -285,13 +328,13 @@ def main() -> None:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(c.name),
+            "traffic": measured_traffic(c.name + ("_fp8kv" if fp8 else "")),
             "algorithmic_bytes_per_launch": ab["attention"],
             "attention_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 3),
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(c, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(c, args.cpu_budget, pools8)
     print(json.dumps(result), flush=True)
 
 
