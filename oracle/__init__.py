@@ -14,6 +14,8 @@ Sources (web pages, cited by title and section):
     softmax; the result equals ordinary attention), §3.7 (16 tokens per block),
     §4 (chunked prefill), §10.8 FAQ (shared-prefix reuse is mathematically
     identical up to rounding).
+    §3.8 (reference counts and copy-on-write), §3.9 (swap), §5.2 (prefix
+    keys and LRU eviction) for the block manager and block copies.
   * "推理优化与服务：从 PagedAttention 到分离式部署" (ice-wocker), latest
     developments: query tokens packed as [total_q, H, D] with cu_seqlens
     request boundaries in one mixed prefill/decode step.
@@ -37,4 +39,10 @@ from .paged_attention import (  # noqa: F401
     physical_location,
     validate_metadata,
     widen,
+)
+from .block_manager import (  # noqa: F401
+    OracleBlockManager,
+    OutOfBlocks,
+    oracle_copy_blocks,
+    oracle_swap_blocks,
 )
