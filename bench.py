@@ -19,7 +19,10 @@ the digest recorded there (null otherwise).  ``cpu_baseline`` times the fp64
 CPU oracle on a bounded sample of the same requests.
 
 ``--calibrate-copy`` runs only a 1 GiB device-to-device copy (the counters'
-calibration run).  ``--kv-dtype fp8`` runs the same workload on 8-bit (OCP
+calibration run).  ``--op copy_blocks`` times copy-on-write block copies
+(pa_copy_blocks) and ``--op swap_out`` / ``--op swap_in`` time swapping a
+sequence's blocks to and from pinned host memory (pa_swap_blocks); see
+``run_copy_blocks`` and ``run_swap`` for their workloads.  ``--kv-dtype fp8`` runs the same workload on 8-bit (OCP
 E4M3) pools of random finite codes with per-tensor scales; KV bytes then
 count one byte per element.  Parity of this exact
 launch configuration against the oracle is the job of the GPU tests; the
@@ -42,22 +45,28 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+HOST_LINK_PEAK_GBS = 64.0      # PCIe 5.0 x16, one direction
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "paged_kv_cache_371_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30
 
 
-def kernel_source_digest() -> str:
-    """sha256 over the HIP/C++ sources of the library (file names and bytes, sorted by name)."""
+# Sources that decide what one pa_attention_varlen call moves: its argument
+# checks and launch configuration, the kernels it runs, their shared headers.
+ATTENTION_SOURCES = ("decode.hip", "decode_gqa.hip", "pa_api.cpp", "pa_common.h", "pa_internal.h", "plan.hip",
+                     "prefill.hip")
+
+
+def kernel_source_digest(names=ATTENTION_SOURCES) -> str:
+    """sha256 over the named library sources (file names and bytes, in sorted order)."""
     import hashlib
 
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".cpp", ".h")):
-            h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+    for name in sorted(names):
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
@@ -219,6 +228,180 @@ class _DeviceBatch:
                                  v_scale=V_SCALE_FP8 if self.fp8 else None)
 
 
+def _timed_loop(torch, fn, steps, warmup, stream):
+    """Warm up, then time `steps` calls of fn with HIP events on `stream` and the host clock."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / steps, float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def _block_result(args, metric, value, ms_step, dtype, config, roofline, cpu):
+    out = {
+        "metric": metric, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype, "data": "synthetic", "config": config, "roofline": roofline,
+    }
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    print(json.dumps(out), flush=True)
+
+
+COW_BLOCKS, COW_PAIRS = 16384, 4096
+LAYER_SHAPE = (8, 16, 128)      # Hkv, tokens per block, D of the Llama-3-70B-shaped GQA layer
+
+
+def _oracle_block_rate(fn, block_bytes, pairs_per_call, budget_s):
+    calls = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        fn()
+        calls += 1
+    dt = time.perf_counter() - t0
+    return calls, dt, 2 * 2 * block_bytes * pairs_per_call * calls / dt / 1e9
+
+
+def run_copy_blocks(args) -> None:
+    """Copy-on-write copies of one parallel-sampling decode step: 4096 samples
+    each copy their shared, partly filled last block (K and V, 32 KiB each in
+    the GQA layer's bf16 pools of 16384 blocks) to a fresh block.  Moves
+    2 x 4096 x 64 KiB = 512 MiB of HBM per call (every byte read once and
+    written once)."""
+    import torch
+
+    import paged_kv_cache_371_amd as pa
+
+    rng = np.random.default_rng(args.seed)
+    perm = rng.permutation(COW_BLOCKS)
+    pairs = np.stack([perm[:COW_PAIRS], perm[COW_PAIRS:2 * COW_PAIRS]], 1).astype(np.int64)
+    shape = (COW_BLOCKS,) + LAYER_SHAPE
+    k = torch.randn(shape, dtype=torch.bfloat16, device="cuda:0")
+    v = torch.randn(shape, dtype=torch.bfloat16, device="cuda:0")
+    dpairs = torch.from_numpy(pairs).to("cuda:0")
+    L = pa.lib()
+    block_bytes = k[0].numel() * k.element_size()
+    stream = torch.cuda.current_stream()
+
+    def call():
+        pa._check(L.pa_copy_blocks(k.data_ptr(), v.data_ptr(), dpairs.data_ptr(), COW_PAIRS, block_bytes,
+                                   COW_BLOCKS, stream.cuda_stream))
+
+    call()
+    torch.cuda.synchronize()
+    src, dst = torch.from_numpy(pairs[:, 0]).to("cuda:0"), torch.from_numpy(pairs[:, 1]).to("cuda:0")
+    if not (torch.equal(k[dst], k[src]) and torch.equal(v[dst], v[src])):
+        raise SystemExit("block copy mismatch")
+    ms_step, kern_ms = _timed_loop(torch, call, args.steps, args.warmup, stream)
+    moved = 2 * 2 * COW_PAIRS * block_bytes
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        nb, npairs = 1024, 256
+        hk = np.zeros((nb,) + LAYER_SHAPE, np.uint16)
+        hv = np.zeros_like(hk)
+        small = _small_pairs(nb, npairs)
+        calls, dt, rate = _oracle_block_rate(lambda: oracle.oracle_copy_blocks(hk, hv, small), block_bytes, npairs,
+                                             args.cpu_budget)
+        cpu = {"value": round(rate, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{calls} calls of the oracle's block copy, {npairs} pairs over a {nb}-block pool of the "
+                         f"same block shape, in {dt:.1f} s"}
+    roof = {"bound": "hbm", "kernel": "pa::copy_blocks_kernel", "achieved": round(moved / (kern_ms * 1e-3) / 1e9, 2),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(moved / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": None, "algorithmic_bytes_per_launch": moved}
+    _block_result(args, "copy-on-write block copy GB/s (HBM read + write) at 1 MI355X", moved / (ms_step * 1e-3) / 1e9,
+                  ms_step, "bf16",
+                  {"workload": "cow_copy_gqa_layer", "num_blocks": COW_BLOCKS, "pairs_per_call": COW_PAIRS,
+                   "block_shape": list(LAYER_SHAPE), "block_bytes_per_pool": block_bytes,
+                   "step": "pa_copy_blocks (K and V)"}, roof, cpu)
+
+
+def _small_pairs(nb, n):
+    perm = np.random.default_rng(7).permutation(nb)
+    return np.stack([perm[:n], perm[n:2 * n]], 1).astype(np.int64)
+
+
+SWAP_LAYERS, SWAP_BLOCKS = 80, 512
+
+
+def run_swap(args, direction: str) -> None:
+    """Swap of one 8192-token sequence of an 80-layer Llama-3-70B-shaped cache
+    (GQA, 8 KV heads, D=128, bf16): 512 blocks per layer, K and V, 32 KiB each
+    -- 2.5 GiB per step, one pa_swap_blocks call per layer, between the
+    device pools and a pinned host pool."""
+    import torch
+
+    import paged_kv_cache_371_amd as pa
+
+    rng = np.random.default_rng(args.seed)
+    nb_dev = 2 * SWAP_BLOCKS
+    dshape = (SWAP_LAYERS, nb_dev) + LAYER_SHAPE
+    hshape = (SWAP_LAYERS, SWAP_BLOCKS) + LAYER_SHAPE
+    dk = torch.randn(dshape, dtype=torch.bfloat16, device="cuda:0")
+    dv = torch.randn(dshape, dtype=torch.bfloat16, device="cuda:0")
+    hk = torch.empty(hshape, dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty(hshape, dtype=torch.bfloat16, pin_memory=True)
+    dev_blocks = rng.permutation(nb_dev)[:SWAP_BLOCKS]
+    host_blocks = np.arange(SWAP_BLOCKS)
+    if direction == "swap_out":
+        pairs = np.stack([dev_blocks, host_blocks], 1).astype(np.int64)
+        layers = [(hk[l], hv[l], dk[l], dv[l], SWAP_BLOCKS, nb_dev) for l in range(SWAP_LAYERS)]
+    else:
+        pairs = np.stack([host_blocks, dev_blocks], 1).astype(np.int64)
+        layers = [(dk[l], dv[l], hk[l], hv[l], nb_dev, SWAP_BLOCKS) for l in range(SWAP_LAYERS)]
+    if direction == "swap_in":
+        hk.copy_(dk[:, dev_blocks].cpu())
+        hv.copy_(dv[:, dev_blocks].cpu())
+    dpairs = torch.from_numpy(pairs).to("cuda:0")
+    L = pa.lib()
+    block_bytes = dk[0, 0].numel() * dk.element_size()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for dst_k, dst_v, src_k, src_v, ndst, nsrc in layers:
+            pa._check(L.pa_swap_blocks(dst_k.data_ptr(), dst_v.data_ptr(), src_k.data_ptr(), src_v.data_ptr(),
+                                       dpairs.data_ptr(), SWAP_BLOCKS, block_bytes, nsrc, ndst, stream.cuda_stream))
+
+    step()
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(dev_blocks).to("cuda:0")
+    for l in (0, SWAP_LAYERS - 1):
+        a = dk[l, idx].cpu()
+        if not torch.equal(a.view(torch.int16), hk[l].view(torch.int16)):
+            raise SystemExit("swap mismatch")
+    ms_step, kern_ms = _timed_loop(torch, step, args.steps, args.warmup, stream)
+    per_step = SWAP_LAYERS * 2 * SWAP_BLOCKS * block_bytes
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        h1k, h1v = np.zeros((SWAP_BLOCKS,) + LAYER_SHAPE, np.uint16), np.zeros((SWAP_BLOCKS,) + LAYER_SHAPE, np.uint16)
+        d1k, d1v = np.zeros((nb_dev,) + LAYER_SHAPE, np.uint16), np.zeros((nb_dev,) + LAYER_SHAPE, np.uint16)
+        calls, dt, rate = _oracle_block_rate(lambda: oracle.oracle_swap_blocks(h1k, h1v, d1k, d1v,
+                                                                               np.stack([dev_blocks, host_blocks], 1)),
+                                             block_bytes, SWAP_BLOCKS, args.cpu_budget)
+        cpu = {"value": round(rate / 2, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{calls} calls of the oracle's block swap of one layer ({SWAP_BLOCKS} blocks, K and V) "
+                         f"between host arrays, in {dt:.1f} s; bytes counted once"}
+    achieved = per_step / SWAP_LAYERS / (kern_ms / SWAP_LAYERS * 1e-3) / 1e9
+    roof = {"bound": "host_link", "kernel": "pa::copy_blocks_kernel", "achieved": round(achieved, 2),
+            "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HOST_LINK_PEAK_GBS, 4),
+            "traffic": None, "algorithmic_bytes_per_launch": per_step // SWAP_LAYERS}
+    _block_result(args, f"KV {direction.replace('_', '-')} GB/s over the host link at 1 MI355X",
+                  per_step / (ms_step * 1e-3) / 1e9, ms_step, "bf16",
+                  {"workload": f"{direction}_8k_seq_70b", "layers": SWAP_LAYERS, "blocks_per_layer": SWAP_BLOCKS,
+                   "block_shape": list(LAYER_SHAPE), "bytes_per_step": per_step,
+                   "step": f"{SWAP_LAYERS} x pa_swap_blocks (K and V)"}, roof, cpu)
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,6 +415,7 @@ def main() -> None:
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default="bf16",
                     help="fp8: 8-bit (OCP E4M3) pools with per-tensor scales, bf16 q and out")
+    ap.add_argument("--op", choices=("attention", "copy_blocks", "swap_out", "swap_in"), default="attention")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this framework runs the path on one GPU; --gpus must be 1 "
@@ -239,6 +423,12 @@ def main() -> None:
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.op == "copy_blocks":
+        run_copy_blocks(args)
+        return
+    if args.op in ("swap_out", "swap_in"):
+        run_swap(args, args.op)
         return
 
     import torch

@@ -39,8 +39,9 @@
  *   - q, out, the pools and the new rows share one element type (pa_dtype).
  *     Accumulation is fp32; bf16 results are rounded to nearest even.
  *
- * Pointers are DEVICE pointers unless marked host.  The library allocates
- * nothing and keeps no state between calls; the caller owns every buffer.
+ * Pointers are DEVICE pointers unless marked host.  The device calls
+ * allocate nothing and keep no state between calls; the caller owns every
+ * buffer.  (The host block manager in pa_blocks.h is the one stateful part.)
  * Both hot calls only enqueue work on `stream` (a hipStream_t passed as
  * void*, NULL = the null stream) and return; they never synchronise, read
  * device memory from the host, or allocate, so they can be captured in a HIP
@@ -70,7 +71,10 @@ typedef enum {
   PA_ERR_ALIGN = -4,        /* pointer or row stride not 16-byte aligned */
   PA_ERR_WORKSPACE = -5,    /* workspace missing or smaller than required */
   PA_ERR_LAUNCH = -6,       /* the HIP runtime rejected a kernel launch */
-  PA_ERR_METADATA = -7      /* pa_validate_metadata found a bad entry */
+  PA_ERR_METADATA = -7,     /* pa_validate_metadata found a bad entry */
+  PA_ERR_NO_BLOCKS = -8,    /* block manager: not enough free blocks; nothing changed */
+  PA_ERR_STATE = -9,        /* block manager: unknown, existing or swapped-out sequence */
+  PA_ERR_HOST_MEMORY = -10  /* block manager: host allocation failed */
 } pa_status;
 
 typedef enum {
@@ -225,7 +229,8 @@ pa_status pa_validate_metadata(const int32_t* cu_seqlens_q, const int32_t* seq_l
 /* Static, NUL-terminated description of a status code. */
 const char* pa_status_string(pa_status s);
 
-/* ABI version of this header: major*100 + minor (101: the 8-bit cache calls). */
+/* ABI version of this header: major*100 + minor (101: the 8-bit cache calls;
+ * 102: block copies and the host block manager, pa_blocks.h). */
 int32_t pa_abi_version(void);
 
 #ifdef __cplusplus

@@ -1,4 +1,4 @@
-"""Python binding of the paged-attention C ABI (``include/pa.h``).
+"""Python binding of the paged-attention C ABI (``include/pa.h``, ``include/pa_blocks.h``).
 
 Argument marshalling only: torch tensors supply device pointers and the
 current HIP stream; every step of the computation runs in the HIP kernels of
@@ -23,6 +23,10 @@ __all__ = [
     "make_params",
     "workspace_size",
     "validate_metadata",
+    "copy_blocks",
+    "swap_blocks",
+    "BlockManager",
+    "OutOfBlocks",
     "PA_F32",
     "PA_BF16",
 ]
@@ -59,6 +63,30 @@ _SIGNATURES = {
                                           ctypes.c_float, ctypes.c_void_p]),
     "pa_attention_varlen_fp8": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_float, ctypes.c_float,
                                                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "pa_copy_blocks": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
+    "pa_swap_blocks": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [ctypes.c_void_p]),
+    "pa_bm_create": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]),
+    "pa_bm_destroy": (None, [ctypes.c_void_p]),
+    "pa_bm_add_sequence": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                          ctypes.c_void_p]),
+    "pa_bm_fork": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64]),
+    "pa_bm_append_slot": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p]),
+    "pa_bm_free": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64]),
+    "pa_bm_swap_out": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_void_p]),
+    "pa_bm_swap_in": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_void_p]),
+    "pa_bm_block_table": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_void_p]),
+    "pa_bm_block_tables": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_int32, ctypes.c_void_p]),
+    "pa_bm_slot_mapping": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_void_p]),
+    "pa_bm_seq_info": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
+    "pa_bm_refcount": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
+    "pa_bm_stats": (ctypes.c_int, [ctypes.c_void_p] * 5),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_abi_version": (ctypes.c_int32, []),
 }
@@ -70,6 +98,14 @@ class PAError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(message)
         self.status = status
+
+
+class OutOfBlocks(PAError):
+    """PA_ERR_NO_BLOCKS: the block manager lacks free blocks; nothing changed."""
+
+
+ERR_NO_BLOCKS = -8
+ERR_STATE = -9
 
 
 class AttnParams(ctypes.Structure):
@@ -121,7 +157,8 @@ def exported_symbols():
 def _check(status: int) -> None:
     if status != 0:
         msg = lib().pa_status_string(status)
-        raise PAError(status, msg.decode() if msg else f"pa_status {status}")
+        cls = OutOfBlocks if status == ERR_NO_BLOCKS else PAError
+        raise cls(status, msg.decode() if msg else f"pa_status {status}")
 
 
 def _torch():
@@ -313,3 +350,174 @@ def validate_metadata(cu_seqlens, seq_lens, block_tables, num_blocks: int, max_q
                                       slot_mapping.data_ptr() if slot_mapping is not None else None, n_slots,
                                       ctypes.byref(p), result.data_ptr(), _stream(stream)))
     return int(result.item())
+
+
+# ---------------------------------------------------------------------------
+# block copies and the host block manager (include/pa_blocks.h)
+
+
+def _pairs_arg(pairs, device):
+    """(src, dst) pairs as a contiguous int64 [n, 2] tensor on ``device``."""
+    torch = _torch()
+    if not torch.is_tensor(pairs):
+        pairs = torch.as_tensor(pairs, dtype=torch.int64).reshape(-1, 2)
+    if pairs.dtype != torch.int64:
+        raise TypeError("block pairs must be int64")
+    pairs = pairs.reshape(-1, 2)
+    if pairs.device != device:
+        pairs = pairs.to(device)
+    return pairs.contiguous()
+
+
+def _block_bytes(pool) -> int:
+    if not pool.is_contiguous():
+        raise ValueError("pools must be contiguous")
+    return pool[0].numel() * pool.element_size()
+
+
+def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
+    """Copy-on-write copies inside one layer's pools: block dst <- block src for
+    every (src, dst) pair, K and V, bit for bit (any pool dtype)."""
+    _dev(k_cache, "k_cache")
+    _dev(v_cache, "v_cache")
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
+        raise ValueError("K and V pools must share shape and dtype")
+    pairs = _pairs_arg(pairs, k_cache.device)
+    _check(lib().pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), pairs.data_ptr(), int(pairs.shape[0]),
+                                _block_bytes(k_cache), int(k_cache.shape[0]), _stream(stream)))
+    return pairs
+
+
+def swap_blocks(dst_k, dst_v, src_k, src_v, pairs, stream=None):
+    """dst[d] <- src[s] for every (s, d) pair between two pools of one block
+    shape; one side is usually a pinned host pool (swap out or swap in).
+    Returns the device copy of ``pairs``, which must stay alive until the
+    stream has run the copy."""
+    dev = next((t.device for t in (dst_k, src_k) if t.is_cuda), None)
+    if dev is None:
+        raise ValueError("one side of a swap must be a device pool")
+    for t, nm in ((dst_k, "dst_k"), (dst_v, "dst_v"), (src_k, "src_k"), (src_v, "src_v")):
+        if not t.is_cuda and not t.is_pinned():
+            raise ValueError(f"{nm}: host pools must be pinned (pin_memory=True)")
+    if dst_k.shape[1:] != src_k.shape[1:] or dst_k.dtype != src_k.dtype:
+        raise ValueError("pools must share block shape and dtype")
+    if dst_k.shape != dst_v.shape or src_k.shape != src_v.shape:
+        raise ValueError("K and V pools must share shapes")
+    pairs = _pairs_arg(pairs, dev)
+    _check(lib().pa_swap_blocks(dst_k.data_ptr(), dst_v.data_ptr(), src_k.data_ptr(), src_v.data_ptr(),
+                                pairs.data_ptr(), int(pairs.shape[0]), _block_bytes(dst_k), int(src_k.shape[0]),
+                                int(dst_k.shape[0]), _stream(stream)))
+    return pairs
+
+
+def _i64(v=0):
+    return ctypes.c_int64(v)
+
+
+class BlockManager:
+    """Host block manager (native): free pool, block tables, reference counts
+    with copy-on-write, prefix keys with LRU eviction, host pool for swap."""
+
+    def __init__(self, num_blocks: int, block_size: int = BLOCK_SIZE, num_host_blocks: int = 0,
+                 prefix_caching: bool = True):
+        h = ctypes.c_void_p()
+        _check(lib().pa_bm_create(int(num_blocks), int(block_size), int(num_host_blocks), int(bool(prefix_caching)),
+                                  ctypes.byref(h)))
+        self._h = h
+        self.block_size = int(block_size)
+        self.num_blocks = int(num_blocks)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _LIB is not None:
+            _LIB.pa_bm_destroy(h)
+            self._h = None
+
+    def add_sequence(self, seq_id: int, tokens) -> int:
+        arr = (ctypes.c_int32 * len(tokens))(*[int(t) for t in tokens])
+        cached = _i64()
+        _check(lib().pa_bm_add_sequence(self._h, int(seq_id), arr, len(tokens), ctypes.byref(cached)))
+        return cached.value
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(lib().pa_bm_fork(self._h, int(parent), int(child)))
+
+    def append_slot(self, seq_id: int, token: int):
+        slot, src, dst = _i64(), _i64(), _i64()
+        _check(lib().pa_bm_append_slot(self._h, int(seq_id), int(token), ctypes.byref(slot), ctypes.byref(src),
+                                       ctypes.byref(dst)))
+        return slot.value, src.value, dst.value
+
+    def free(self, seq_id: int) -> None:
+        _check(lib().pa_bm_free(self._h, int(seq_id)))
+
+    def _swap(self, fn, seq_id):
+        cap = len(self.table(seq_id))
+        buf = (ctypes.c_int64 * (2 * max(cap, 1)))()
+        n = _i64()
+        _check(fn(self._h, int(seq_id), buf, cap, ctypes.byref(n)))
+        return [(buf[2 * i], buf[2 * i + 1]) for i in range(n.value)]
+
+    def swap_out(self, seq_id: int):
+        return self._swap(lib().pa_bm_swap_out, seq_id)
+
+    def swap_in(self, seq_id: int):
+        return self._swap(lib().pa_bm_swap_in, seq_id)
+
+    def table(self, seq_id: int):
+        n = _i64()
+        st = lib().pa_bm_block_table(self._h, int(seq_id), None, 0, ctypes.byref(n))
+        if st not in (0, -2):
+            _check(st)
+        buf = (ctypes.c_int32 * max(n.value, 1))()
+        _check(lib().pa_bm_block_table(self._h, int(seq_id), buf, n.value, ctypes.byref(n)))
+        return list(buf[:n.value])
+
+    def block_tables(self, seq_ids, width: int):
+        """Padded [len(seq_ids), width] int32 tables and int32 lengths (numpy)."""
+        import numpy as np
+
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        tables = np.zeros((len(ids), max(width, 0)), np.int32)
+        lens = np.zeros(len(ids), np.int32)
+        _check(lib().pa_bm_block_tables(self._h, ids.ctypes.data, len(ids), tables.ctypes.data, int(width),
+                                        lens.ctypes.data))
+        return tables, lens
+
+    def slot_mapping(self, seq_id: int, start: int, count: int):
+        buf = (ctypes.c_int64 * max(count, 1))()
+        _check(lib().pa_bm_slot_mapping(self._h, int(seq_id), int(start), int(count), buf))
+        return list(buf[:count])
+
+    def _info(self, seq_id):
+        n, sw = _i64(), ctypes.c_int32()
+        _check(lib().pa_bm_seq_info(self._h, int(seq_id), ctypes.byref(n), ctypes.byref(sw)))
+        return n.value, bool(sw.value)
+
+    def seq_len(self, seq_id: int) -> int:
+        return self._info(seq_id)[0]
+
+    def is_swapped(self, seq_id: int) -> bool:
+        return self._info(seq_id)[1]
+
+    def refcount(self, block: int) -> int:
+        c = ctypes.c_int32()
+        _check(lib().pa_bm_refcount(self._h, int(block), ctypes.byref(c)))
+        return c.value
+
+    def _stats(self):
+        f, c, h, s = _i64(), _i64(), _i64(), _i64()
+        _check(lib().pa_bm_stats(self._h, ctypes.byref(f), ctypes.byref(c), ctypes.byref(h), ctypes.byref(s)))
+        return f.value, c.value, h.value, s.value
+
+    def num_free(self) -> int:
+        return self._stats()[0]
+
+    def num_cached(self) -> int:
+        return self._stats()[1]
+
+    def num_host_free(self) -> int:
+        return self._stats()[2]
+
+    def num_seqs(self) -> int:
+        return self._stats()[3]

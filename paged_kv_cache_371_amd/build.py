@@ -18,7 +18,10 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 
-SOURCES = ["pa_api.cpp", "cache_write.hip", "plan.hip", "decode.hip", "decode_gqa.hip", "prefill.hip", "validate.hip"]
+SOURCES = ["pa_api.cpp", "cache_write.hip", "plan.hip", "decode.hip", "decode_gqa.hip", "prefill.hip", "validate.hip",
+           "block_copy.hip"]
+# Host-only C++ (no device code): compiled as plain C++.
+HOST_SOURCES = ["block_manager.cpp"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -49,7 +52,11 @@ def _hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + FLAGS + EXTRA_FLAGS.get(src, [])
+    if src in HOST_SOURCES:
+        cmd = [_hipcc(), "-x", "c++", "-c", os.path.join(CSRC, src), "-o", obj, "-O3", "-std=c++17", "-fPIC", "-Wall",
+               f"-I{os.path.join(ROOT, 'include')}"]
+    else:
+        cmd = [_hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + FLAGS + EXTRA_FLAGS.get(src, [])
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")
@@ -63,9 +70,10 @@ def _compile(src: str) -> str:
 def build(verbose: bool = True) -> str:
     """Compile every source and link ``libpa.so``; return its path."""
     os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, min(16, os.cpu_count() or 1)))
+    sources = SOURCES + HOST_SOURCES
+    jobs = min(len(sources), max(1, min(16, os.cpu_count() or 1)))
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(_compile, sources))
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)

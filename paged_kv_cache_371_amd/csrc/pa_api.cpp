@@ -142,7 +142,7 @@ pa_status check_params(const pa_attn_params* p) {
 
 extern "C" {
 
-int32_t pa_abi_version(void) { return 101; }
+int32_t pa_abi_version(void) { return 102; }
 
 const char* pa_status_string(pa_status s) {
   switch (s) {
@@ -154,6 +154,9 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: kernel launch failed";
     case PA_ERR_METADATA: return "PA_ERR_METADATA: device metadata failed validation";
+    case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: not enough free blocks (nothing changed)";
+    case PA_ERR_STATE: return "PA_ERR_STATE: unknown, existing or swapped-out sequence";
+    case PA_ERR_HOST_MEMORY: return "PA_ERR_HOST_MEMORY: host allocation failed";
   }
   return "unknown pa_status";
 }

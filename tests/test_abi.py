@@ -1,7 +1,8 @@
-"""The C-ABI library loads, exports what include/pa.h declares, and rejects
+"""The C-ABI library loads, exports what include/*.h declares, and rejects
 bad arguments on the host before touching the GPU (CPU only)."""
 
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -17,9 +18,11 @@ HEADER = os.path.join(ROOT, "include", "pa.h")
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for path in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names |= set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -55,8 +58,8 @@ def test_struct_layout_matches_c(tmp_path):
 
 
 def test_status_strings_and_version(L):
-    assert L.pa_abi_version() == 101
-    for code in range(0, -8, -1):
+    assert L.pa_abi_version() == 102
+    for code in range(0, -11, -1):
         s = L.pa_status_string(code).decode()
         assert s.startswith("PA_")
     assert L.pa_status_string(-99).decode() == "unknown pa_status"

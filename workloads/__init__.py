@@ -12,4 +12,5 @@ from .generate import (  # noqa: F401
     bf16_bits_from_f32,
     build_case,
     make_config,
+    prefix_kv_rows,
 )

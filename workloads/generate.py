@@ -317,3 +317,29 @@ def make_config(name: str, seed: int = 0, *, poison: bool = True, threads: int |
     if name not in _CONFIGS:
         raise KeyError(f"unknown config {name!r}; known: {CONFIG_NAMES}")
     return _CONFIGS[name](seed, poison=poison, threads=threads)
+
+
+# ---------------------------------------------------------------------------
+# K/V rows that depend only on the token prefix (block-sharing workloads)
+
+
+def prefix_kv_rows(tokens, start, count, num_kv_heads, head_dim, seed):
+    """bf16 bits [count, 2, Hkv, D] of the K and V rows of positions start ..
+    start+count-1 of a token sequence.
+
+    Row i is drawn from a generator seeded by ``seed`` and the exact token
+    prefix ``tokens[:i+1]``, the way a model's K/V at position i depend only
+    on the tokens up to i.  Two sequences with equal prefixes therefore get
+    bit-identical rows there, which is what makes sharing a cached block (or
+    a forked one) valid.
+    """
+    import zlib
+
+    out = np.empty((count, 2, num_kv_heads, head_dim), np.uint16)
+    arr = np.asarray(tokens, dtype=np.int64)
+    for j in range(count):
+        i = start + j
+        digest = zlib.crc32(arr[:i + 1].tobytes())
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), i, digest])))
+        out[j] = bf16_bits_from_f32(g.standard_normal((2, num_kv_heads, head_dim), dtype=np.float32))
+    return out
