@@ -348,8 +348,10 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a) {
     store_out<E>(a.out, int64_t(row) * a.o_row_stride + int64_t(h) * D + e * 64 + threadIdx.x, o[e] * inv);
 }
 
-// Merge for the fast decode kernel's partials (bf16, D = 128): only the
-// requests on the work list's merge list, one wave per (request, query head).
+// Merge of the partials of the fast decode kernel and of split short prefill
+// requests (bf16, D = 128): only the rows on the work list's merge list, one
+// wave per (row, query head); an entry names the row, its partition count and
+// the partial row its partials were written under.
 // The list count and the wave's entry are read together; then partitions are
 // taken in chunks of kChunk, each chunk's (max, sum) (scalar loads) and
 // output slices (vector loads) issued at once, and folded into a running
@@ -361,14 +363,14 @@ __global__ __launch_bounds__(256) void merge_list_kernel(DecodeArgs a) {
   const int4* list = reinterpret_cast<const int4*>(a.plan + kPlanHeaderInts + a.merge_off_ints);
   const int lane = threadIdx.x & 63;
   const int64_t NW = int64_t(gridDim.x) * 4;
-  const int64_t cap = int64_t(a.num_seqs) * a.num_q_heads;   // list capacity in (request, head) pairs
+  const int64_t cap = int64_t(a.merge_capacity) * a.num_q_heads;   // list capacity in (row, head) pairs
   for (int64_t t = int64_t(blockIdx.x) * 4 + uni(threadIdx.x >> 6); t < cap; t += NW) {
     const int e = int(t / a.num_q_heads);
     const int h = int(t - int64_t(e) * a.num_q_heads);
     const int32_t* ep = reinterpret_cast<const int32_t*>(list + e);
-    const int b = load_const(ep, 0), q0 = load_const(ep, 1), nparts = load_const(ep, 2);
+    const int q0 = load_const(ep, 1), nparts = load_const(ep, 2), prow = load_const(ep, 3);
     if (e >= load_const(a.plan, kPlanMergeCountInt)) break;
-    const int64_t base = (int64_t(b) * a.num_q_heads + h) * a.max_parts;
+    const int64_t base = (int64_t(prow) * a.num_q_heads + h) * a.max_parts;
     const int32_t* ml = reinterpret_cast<const int32_t*>(a.ws_ml + 2 * base);
     const float2* po = reinterpret_cast<const float2*>(a.ws_o + base * D) + lane;
     float M = -__builtin_inff(), denom = 0.f, ox = 0.f, oy = 0.f;
@@ -411,7 +413,7 @@ __global__ __launch_bounds__(256) void merge_list_kernel(DecodeArgs a) {
 }
 
 hipError_t launch_merge_list(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t waves = int64_t(a.num_seqs) * a.num_q_heads;
+  const int64_t waves = int64_t(a.merge_capacity) * a.num_q_heads;
   const int64_t grid = std::min<int64_t>((waves + 3) / 4, 1024);
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(merge_list_kernel, dim3(grid), dim3(256), 0, stream, a);

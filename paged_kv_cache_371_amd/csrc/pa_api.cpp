@@ -56,6 +56,8 @@ struct Plan {
   int64_t parts;      // partitions per request, upper bound
   int64_t rows_a;     // partial rows in region A
   int64_t rows_b;     // partial rows in region B
+  int32_t split_rows; // short multi-row requests split over partitions (0: none)
+  int32_t tile_pairs; // (row, head) pairs per prefill work item
 };
 
 inline int64_t max_parts(const pa_attn_params* p) {
@@ -72,6 +74,14 @@ inline Plan make_plan(const pa_attn_params* p) {
   pl.fast = pa::decode_gqa_supported(dt, p->head_dim, g, ps);
   pl.prefill = dt == 1 && multi && pa::prefill_supported(p->head_dim, g);
   pl.parts = max_parts(p);
+  // Batches whose multi-row requests all fit 64 / G rows use 64-pair prefill
+  // tiles; such short requests (one row tile) are split over context
+  // partitions when the partition is a whole number of prefill key tiles.
+  pl.tile_pairs = p->max_query_len <= pa::kPrefillPairsShort / g ? pa::kPrefillPairsShort : pa::kPrefillPairs;
+  pl.split_rows = (pl.fast && pl.prefill && pl.parts > 1 && ps % pa::kPrefillKeys == 0 &&
+                   p->max_query_len <= pl.tile_pairs / g)
+                      ? pl.tile_pairs / g
+                      : 0;
   if (pl.fast) {
     pl.generic_mode = (multi && !pl.prefill) ? pa::kMultiRowOnly : -1;
     pl.generic_by_seq = false;
@@ -86,7 +96,7 @@ inline Plan make_plan(const pa_attn_params* p) {
   if (pl.parts > 1) {
     const bool a_used = pl.fast || (pl.generic_mode >= 0 && pl.generic_by_seq);
     const bool b_used = pl.generic_mode >= 0 && !pl.generic_by_seq;
-    pl.rows_a = a_used ? p->num_seqs : 0;
+    pl.rows_a = a_used ? p->num_seqs + (pl.split_rows ? p->total_q : 0) : 0;
     pl.rows_b = b_used ? p->total_q : 0;
   }
   return pl;
@@ -96,24 +106,30 @@ inline size_t region_floats(const pa_attn_params* p, int64_t rows, int64_t parts
   return size_t(rows) * p->num_q_heads * parts * (p->head_dim + 2);
 }
 
-// Entries the prefill work list can hold: tiles of kPrefillPairs (row, head) pairs.
-inline int64_t prefill_capacity(const pa_attn_params* p) {
+// Entries the prefill work list can hold: tiles of kPrefillPairs (row, head)
+// pairs, or one per partition of a split short request.
+inline int64_t prefill_capacity(const pa_attn_params* p, const Plan& pl) {
   const int g = p->num_q_heads / p->num_kv_heads;
-  const int64_t rows = pa::kPrefillPairs / g;
-  return int64_t(p->num_seqs) * ((int64_t(p->max_query_len) + rows - 1) / rows);
+  const int64_t rows = pl.tile_pairs / g;
+  const int64_t per_seq = (int64_t(p->max_query_len) + rows - 1) / rows;
+  return int64_t(p->num_seqs) * (pl.split_rows ? std::max<int64_t>(per_seq, pl.parts) : per_seq);
 }
 inline int64_t decode_capacity(const pa_attn_params* p, const Plan& pl) { return int64_t(p->num_seqs) * pl.parts; }
+// Merge entries: single-row requests, plus the rows of split short requests.
+inline int64_t merge_capacity(const pa_attn_params* p, const Plan& pl) {
+  return pl.fast ? int64_t(p->num_seqs) + (pl.split_rows ? p->total_q : 0) : 0;
+}
 
 // Workspace: [work lists of the persistent kernels][region A][region B].
 inline size_t plan_bytes(const pa_attn_params* p, const Plan& pl) {
   if (!pl.fast && !pl.prefill) return 0;
-  return pa::plan_bytes(pl.fast ? decode_capacity(p, pl) : 0, pl.prefill ? prefill_capacity(p) : 0,
-                        pl.fast ? p->num_seqs : 0);
+  return pa::plan_bytes(pl.fast ? decode_capacity(p, pl) : 0, pl.prefill ? prefill_capacity(p, pl) : 0,
+                        merge_capacity(p, pl));
 }
 // Offsets (ints after the header) of the prefill entries and the merge list.
 inline int64_t pref_off(const pa_attn_params* p, const Plan& pl) { return pl.fast ? 4 * decode_capacity(p, pl) : 0; }
 inline int64_t merge_off(const pa_attn_params* p, const Plan& pl) {
-  return pref_off(p, pl) + (pl.prefill ? 4 * prefill_capacity(p) : 0);
+  return pref_off(p, pl) + (pl.prefill ? 4 * prefill_capacity(p, pl) : 0);
 }
 
 pa_status check_params(const pa_attn_params* p) {
@@ -251,6 +267,7 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
   d.plan = (pl.fast || pl.prefill) ? static_cast<int32_t*>(workspace) : nullptr;
   d.merge_off_ints = merge_off(p, pl);
   d.plan_capacity = int32_t(std::max<int64_t>(1, pl.fast ? decode_capacity(p, pl) : 1));
+  d.merge_capacity = int32_t(merge_capacity(p, pl));
 
   // Partials of a region: o [rows, Hq, parts, D] followed by (m, l) [rows, Hq, parts, 2].
   auto point_at = [&](float* region, int64_t rows) {
@@ -273,6 +290,8 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
     pa_.prefill = pl.prefill ? 1 : 0;
     pa_.max_query_len = p->max_query_len;
     pa_.max_seq_len = p->max_seq_len;
+    pa_.split_rows = pl.split_rows;
+    pa_.tile_pairs = pl.tile_pairs;
     if (pa::launch_plan(pa_, s) != hipSuccess) return PA_ERR_LAUNCH;
   }
   if (pl.fast) {
@@ -280,7 +299,6 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
     d.row_mode = pa::kSingleRowOnly;
     d.partial_by_seq = 1;
     e = pa::launch_decode_gqa(g, fp8, d, s);
-    if (e == hipSuccess && pl.parts > 1) e = pa::launch_merge_list(d, s);
     if (e != hipSuccess) return PA_ERR_LAUNCH;
   }
   if (pl.generic_mode >= 0) {
@@ -308,8 +326,19 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
     f.plan = static_cast<const int32_t*>(workspace);
     f.pref_off_ints = pref_off(p, pl);
     f.scale_log2 = scale_log2;
+    f.split_rows = pl.split_rows;
+    f.tile_pairs = pl.tile_pairs;
+    f.part_size = d.part_size;
+    f.max_parts = d.max_parts;
+    f.ws_o = pl.split_rows ? region_a : nullptr;
+    f.ws_ml = pl.split_rows ? region_a + int64_t(pl.rows_a) * p->num_q_heads * pl.parts * p->head_dim : nullptr;
     e = pa::launch_prefill(p->head_dim, g, f, s);
     if (e != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  // partitions of single-row requests and of split short requests
+  if (pl.fast && pl.parts > 1) {
+    point_at(region_a, pl.rows_a);
+    if (pa::launch_merge_list(d, s) != hipSuccess) return PA_ERR_LAUNCH;
   }
   return PA_OK;
 }

@@ -34,6 +34,7 @@ struct DecodeArgs {
   float lsum_scale;         // the softmax sum is multiplied by this (1 / v_scale for 8-bit pools, else 1)
   int32_t row_mode;         // which requests this launch serves (RowMode)
   int32_t partial_by_seq;   // 1: partials indexed by request, else by packed row
+  int32_t merge_capacity;   // entries the merge list has room for
 };
 
 // Requests a decode launch serves: all of them, only those with exactly one
@@ -58,6 +59,16 @@ struct PrefillArgs {
   const int32_t* plan;    // work list (prefill entries at plan + kPlanHeaderInts + pref_off_ints)
   int64_t pref_off_ints;
   float scale_log2;
+  // Context split of short requests (see PlanArgs::split_rows): a request with
+  // n <= split_rows rows and more than one partition of part_size tokens is
+  // computed per partition into partials [partial row, Hq, max_parts, D] and
+  // (m, l), partial row = num_seqs + packed row; the merge list combines them.
+  int32_t split_rows;
+  int32_t part_size;
+  int32_t max_parts;
+  float* ws_o;
+  float* ws_ml;
+  int32_t tile_pairs;   // (query row, head) pairs per work item: 128, or 64 for short requests
 };
 
 hipError_t launch_cache_write(const void* k_new, const void* v_new, int64_t kv_row_stride_bytes, void* k_cache,
@@ -77,10 +88,11 @@ bool decode_supported(int dtype, int head_dim, int group, int part_size);
 constexpr int kPlanHeaderInts = 64;      // header words (256 bytes)
 constexpr int kPlanCountInt = 8;         // header slot: number of decode entries
 constexpr int kPlanPrefCountInt = 9;     // header slot: number of prefill entries
-constexpr int kPlanMergeCountInt = 10;   // header slot: number of decode requests with > 1 partition
+constexpr int kPlanMergeCountInt = 10;   // header slot: number of merge entries (rows with > 1 partition)
 constexpr int kPlanClaimInt = 11;        // header slot: claim counter of the fast decode kernel (zeroed by the plan)
 constexpr int kMaxPartBuckets = 512;     // partition_size / 16 of the fast kernel, at most
-constexpr int kPrefillPairs = 128;       // (query row, head) pairs per prefill work item
+constexpr int kPrefillPairs = 128;       // (query row, head) pairs per prefill work item (chunked prefill)
+constexpr int kPrefillPairsShort = 64;   // ... when every multi-row request fits 64 / G rows
 constexpr int kPrefillKeys = 64;         // keys per prefill K/V tile
 
 struct PlanArgs {
@@ -96,6 +108,11 @@ struct PlanArgs {
   int32_t prefill;         // build the prefill list
   int32_t max_query_len;   // requests beyond these bounds get no entries, so the
   int32_t max_seq_len;     // lists never outgrow the capacity the host sized
+  // Multi-row requests with at most this many rows (0: none; at most one row
+  // tile) get one prefill entry per context partition of part_size tokens when
+  // they span more than one, and one merge entry per row.
+  int32_t split_rows;
+  int32_t tile_pairs;      // (query row, head) pairs per prefill work item (64 or 128)
 };
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
 // Bytes of a plan buffer for these capacities (entries), rounded to 256.

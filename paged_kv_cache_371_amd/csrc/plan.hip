@@ -4,19 +4,26 @@
 // Layout of the plan buffer (int32 words):
 //   [kPlanCountInt]      number of decode entries
 //   [kPlanPrefCountInt]  number of prefill entries
-//   [kPlanMergeCountInt] number of single-row requests with more than one partition
+//   [kPlanMergeCountInt] number of merge entries
 //   [kPlanClaimInt]      claim counter of the decode kernel's dynamic rounds, zeroed here
 //   [kPlanHeaderInts ..)                   decode entries, int4 (request, partition, query row, context length)
-//   [kPlanHeaderInts + pref_off ..)        prefill entries, int4 (request, row tile, query row, query rows)
-//   [kPlanHeaderInts + merge_off ..)       merge list, int4 (request, query row, partitions, 0), any order
+//   [kPlanHeaderInts + pref_off ..)        prefill entries, int4 (request, row tile | partition << 16,
+//                                          first query row, query rows)
+//   [kPlanHeaderInts + merge_off ..)       merge list, int4 (request, query row, partitions, partial row),
+//                                          any order
 //
 // Decode list: one entry per non-empty context partition of every single-row
 // request -- all full partitions first, then the partial last partitions by
 // decreasing number of blocks.  Prefill list: one entry per tile of
-// kPrefillPairs (query row, head) pairs of every multi-row request, by
-// decreasing number of 64-key tiles the tile has to visit.  Both orders put
-// the largest items first: the consumers deal or claim items in list order,
-// and handing out the small ones last keeps the workers' finish times close.
+// tile_pairs (query row, head) pairs of every multi-row request, by
+// decreasing number of 64-key tiles the tile has to visit; a short request
+// (at most split_rows rows) whose context spans several partitions instead
+// gets one entry per partition, so no single work item has to stream a whole
+// long context.  Both orders put the largest items first: the consumers deal
+// or claim items in list order, and handing out the small ones last keeps the
+// workers' finish times close.  Merge list: one entry per query row whose
+// result is split over partitions -- single-row requests (partial row = the
+// request) and rows of split short requests (partial row = num_seqs + row).
 // Requests whose lengths break the bounds the host sized the buffer for get no
 // entries (their output rows are left untouched).
 #include "pa_common.h"
@@ -99,6 +106,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     }
   };
 
+  if (tid == 0) s_merge = 0;
   if (a.decode) {
     const int P = a.part_size;
     const int nbk = P / kBlock;
@@ -106,7 +114,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     if (tid == 0) {
       s_full = 0;
       s_cursor = 0;
-      s_merge = 0;
     }
     __syncthreads();
     for_each_request([&](int, int, int n, int L) {
@@ -129,17 +136,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       for (int p = 0; p < nf; ++p, ++pos) entries[pos] = make_int4(b, p, q0, L);
       if (rem > 0) entries[atomicAdd(&s_hist[(rem - 1) / kBlock], 1)] = make_int4(b, nf, q0, L);
       const int parts = nf + (rem > 0);
-      if (parts > 1) merge[atomicAdd(&s_merge, 1)] = make_int4(b, q0, parts, 0);
+      if (parts > 1) merge[atomicAdd(&s_merge, 1)] = make_int4(b, q0, parts, b);
     });
     __syncthreads();
-    if (tid == 0) {
-      a.plan[kPlanMergeCountInt] = s_merge;
-      a.plan[kPlanClaimInt] = 0;
-    }
+    if (tid == 0) a.plan[kPlanClaimInt] = 0;
   }
 
   if (a.prefill) {
-    const int rows = kPrefillPairs / a.group;   // query rows per tile
+    const int rows = a.tile_pairs / a.group;   // query rows per tile
     for (int i = tid; i < kPrefBuckets; i += kPlanThreads) s_hist[i] = 0;
     __syncthreads();
     // bucket of a tile = number of 64-key tiles its last row visits, clamped
@@ -149,19 +153,42 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       return min((keys + kPrefillKeys - 1) / kPrefillKeys, kPrefBuckets - 1);
     };
     auto usable = [&](int n, int L) { return n >= 2 && n <= a.max_query_len && L >= n && L <= a.max_seq_len; };
+    // partitions of a split short request (1: not split)
+    const int P = a.part_size;
+    auto split_parts = [&](int n, int L) { return n <= a.split_rows ? (L + P - 1) / P : 1; };
+    // bucket of partition p of a split request: its 64-key tiles
+    auto part_bucket = [&](int L, int p) {
+      return min((min(L, (p + 1) * P) - p * P + kPrefillKeys - 1) / kPrefillKeys, kPrefBuckets - 1);
+    };
     for_each_request([&](int, int, int n, int L) {
       if (!usable(n, L)) return;
-      for (int mt = 0; mt * rows < n; ++mt) atomicAdd(&s_hist[bucket(L, n, mt)], 1);
+      const int parts = split_parts(n, L);
+      if (parts > 1) {
+        for (int p = 0; p < parts; ++p) atomicAdd(&s_hist[part_bucket(L, p)], 1);
+      } else {
+        for (int mt = 0; mt * rows < n; ++mt) atomicAdd(&s_hist[bucket(L, n, mt)], 1);
+      }
     });
     __syncthreads();
     const int total = scan_desc(s_hist, s_tmp, kPrefBuckets, 0);
     if (tid == 0) a.plan[kPlanPrefCountInt] = total;
     int4* entries = reinterpret_cast<int4*>(a.plan + kPlanHeaderInts + a.pref_off_ints);
+    int4* merge = reinterpret_cast<int4*>(a.plan + kPlanHeaderInts + a.merge_off_ints);
     for_each_request([&](int b, int q0, int n, int L) {
       if (!usable(n, L)) return;
-      for (int mt = 0; mt * rows < n; ++mt) entries[atomicAdd(&s_hist[bucket(L, n, mt)], 1)] = make_int4(b, mt, q0, n);
+      const int parts = split_parts(n, L);
+      if (parts > 1) {
+        for (int p = 0; p < parts; ++p) entries[atomicAdd(&s_hist[part_bucket(L, p)], 1)] = make_int4(b, p << 16, q0, n);
+        const int m0 = atomicAdd(&s_merge, n);
+        for (int j = 0; j < n; ++j) merge[m0 + j] = make_int4(b, q0 + j, parts, a.num_seqs + q0 + j);
+      } else {
+        for (int mt = 0; mt * rows < n; ++mt)
+          entries[atomicAdd(&s_hist[bucket(L, n, mt)], 1)] = make_int4(b, mt, q0, n);
+      }
     });
   }
+  __syncthreads();
+  if (tid == 0) a.plan[kPlanMergeCountInt] = s_merge;
 }
 
 }  // namespace

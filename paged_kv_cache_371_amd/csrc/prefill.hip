@@ -8,10 +8,13 @@
 // are dense contractions and run on the matrix cores
 // (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
 //
-// Work item: (request, KV head, tile of 128 (query row, head) pairs), the
-// pairs packed as m = row * G + head over the G query heads of the KV head.
-// Four waves own 32 pairs each (two 16-column MFMA blocks).  Keys are visited
-// in tiles of 64 (four paged blocks; wave w fetches block w of the tile, so
+// Work item: (request, KV head, tile of 128 -- or, for batches of short
+// requests, 64 -- (query row, head) pairs), the pairs packed as m = row * G +
+// head over the G query heads of the KV head.  Four waves own 32 (16) pairs
+// each: two (one) 16-column MFMA blocks.  A short request whose context spans
+// several partitions is one item per partition (its key tiles only), and
+// leaves unnormalised partials and (max, sum) for the merge kernel.  Keys are
+// visited in tiles of 64 (four paged blocks; wave w fetches block w of the tile, so
 // every load has a wave-uniform base).  Tiles are fetched into registers one
 // ahead and written to one of two LDS stages: K as 16-byte d-chunks, chunk
 // major (a 16-lane MFMA read is 256 contiguous bytes), V transposed (V^T,
@@ -44,10 +47,7 @@ namespace pa {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kPairs = kPrefillPairs;        // (row, head) pairs per work item
-constexpr int kMB = kPairs / 64;             // 16-column MFMA blocks per wave (4 waves)
-constexpr int kOccupancy = 2;                // workgroups per CU (256 registers per wave)
-static_assert(kMB == 2, "two 16-column blocks per wave fit the register budget of two workgroups per CU");
+constexpr int kOccupancy = 2;                // workgroups per CU (256 registers per wave; LDS allows 2)
 constexpr int kKeys = kPrefillKeys;          // keys per tile = kBlock * waves
 constexpr int kTileBytes = kBlock * kD * 2;  // one (block, KV head) tile of bf16
 constexpr int kKChunk = kKeys * 16 + 16;     // LDS bytes per 8-wide d-chunk of K (64 keys + pad)
@@ -88,8 +88,16 @@ struct TileRegs {
   u32x4_t v[4];
 };
 
-template <int G>
+// MB: 16-column MFMA blocks per wave, so a work item covers 64 * MB (row,
+// head) pairs.  MB = 2 (128 pairs) for chunked prefill; MB = 1 (64 pairs)
+// for batches whose multi-row requests are short (speculative-decode
+// verification), where a 128-pair tile would be mostly empty and the
+// per-tile instruction cost, not HBM, would set the pace.
+template <int G, int MB>
 __global__ __launch_bounds__(256, kOccupancy) void prefill_kernel(PrefillArgs a) {
+  constexpr int kMB = MB;
+  constexpr int kPairs = 64 * MB;
+  static_assert(MB == 1 || MB == 2, "one or two 16-column blocks per wave");
   constexpr int kRows = kPairs / G;   // query rows per work item
   extern __shared__ __align__(16) char smem[];
 
@@ -115,15 +123,23 @@ __global__ __launch_bounds__(256, kOccupancy) void prefill_kernel(PrefillArgs a)
     const int e = t / hkv;
     const int kvh = t - e * hkv;
     const int b = load_const(entries, 4 * int64_t(e));
-    const int mt = load_const(entries, 4 * int64_t(e) + 1);
+    const int tile_part = load_const(entries, 4 * int64_t(e) + 1);
     const int q0 = load_const(entries, 4 * int64_t(e) + 2);
     const int n = load_const(entries, 4 * int64_t(e) + 3);
+    const int mt = tile_part & 0xffff;
+    const int part = tile_part >> 16;
     const int L = load_const(a.seq_lens, b);
     const int P = L - n;                  // cached tokens before this request's rows
     const int j0 = mt * kRows;            // rows [j0, j1) of the request
     const int j1 = min(n, j0 + kRows);
     const int kmax = P + j1;              // keys visible to the last row
     const int KT = (kmax + kKeys - 1) / kKeys;
+    // A split short request covers key tiles [kt0, kt1) of partition `part`
+    // and leaves partials for the merge; otherwise the item covers all tiles.
+    const bool split = n <= a.split_rows && L > a.part_size;
+    const int part_tiles = a.part_size / kKeys;
+    const int kt0 = split ? part * part_tiles : 0;
+    const int kt1 = split ? min(KT, kt0 + part_tiles) : KT;
     const int nblk = max(1, min((L + kBlock - 1) / kBlock, a.max_blocks_per_seq));
     const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks_per_seq;
     const char* kbase = static_cast<const char*>(a.k_cache) + int64_t(kvh) * kTileBytes;
@@ -166,7 +182,7 @@ __global__ __launch_bounds__(256, kOccupancy) void prefill_kernel(PrefillArgs a)
     // positions past the context are zeroed when staged).
     auto phys_of = [&](int kt) -> int { return load_const_early(table, min(kt * 4 + wave, nblk - 1)); };
     auto fetch = [&](TileRegs& rg, int kt, int phys) {
-      const int nrec = kt < KT ? kTileBytes : 0;
+      const int nrec = kt < kt1 ? kTileBytes : 0;
       const __amdgpu_buffer_rsrc_t rk =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + int64_t(phys) * bstride), 0, nrec, kRsrcWord3);
       const __amdgpu_buffer_rsrc_t rv =
@@ -293,17 +309,33 @@ __global__ __launch_bounds__(256, kOccupancy) void prefill_kernel(PrefillArgs a)
     // after.
     __syncthreads();   // the previous item is done with both stages
     TileRegs rg;
-    int ph_next = phys_of(1);
-    fetch(rg, 0, phys_of(0));
-    stage_write(rg, 0, 0);
+    int ph_next = phys_of(kt0 + 1);
+    fetch(rg, kt0, phys_of(kt0));
+    stage_write(rg, kt0, 0);
     __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      const int st = kt & 1;
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const int st = (kt - kt0) & 1;
       fetch(rg, kt + 1, ph_next);
       ph_next = phys_of(kt + 2);
       compute(kt, st);
-      if (kt + 1 < KT) stage_write(rg, kt + 1, st ^ 1);
+      if (kt + 1 < kt1) stage_write(rg, kt + 1, st ^ 1);
       __syncthreads();
+    }
+
+    if (split) {
+      // unnormalised partial output and (max, sum) of this partition
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) {
+        const float lsum = rows_sum(lrun[mb]);
+        if (mvalid[mb]) {
+          const int64_t idx = (int64_t(a.num_seqs + q0 + jrow[mb]) * a.num_q_heads + hq[mb]) * a.max_parts + part;
+          float* po = a.ws_o + idx * kD;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4_t*>(po + 16 * db + 4 * h) = acc[mb][db];
+          if (h == 0) *reinterpret_cast<float2*>(a.ws_ml + 2 * idx) = make_float2(mrun[mb], lsum);
+        }
+      }
+      continue;
     }
 
     // ---- normalise and store ----------------------------------------------------
@@ -323,7 +355,7 @@ __global__ __launch_bounds__(256, kOccupancy) void prefill_kernel(PrefillArgs a)
   }
 }
 
-template <int G>
+template <int G, int MB>
 int prefill_groups() {
   static std::atomic<int> cache{0};
   int v = cache.load(std::memory_order_relaxed);
@@ -331,20 +363,20 @@ int prefill_groups() {
   int dev = 0, cus = 0, occ = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, prefill_kernel<G>, 256, kLdsBytes) != hipSuccess || occ <= 0)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, prefill_kernel<G, MB>, 256, kLdsBytes) != hipSuccess || occ <= 0)
     occ = 1;
   v = cus * occ;
   cache.store(v, std::memory_order_relaxed);
   return v;
 }
 
-template <int G>
+template <int G, int MB>
 hipError_t launch_g(const PrefillArgs& a, hipStream_t stream) {
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<G>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<G, MB>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(prefill_kernel<G>, dim3(prefill_groups<G>()), dim3(256), kLdsBytes, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<G, MB>), dim3(prefill_groups<G, MB>()), dim3(256), kLdsBytes, stream, a);
   return hipGetLastError();
 }
 
@@ -354,15 +386,22 @@ bool prefill_supported(int head_dim, int group) {
   return head_dim == kD && (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
-hipError_t launch_prefill(int head_dim, int group, const PrefillArgs& a, hipStream_t stream) {
-  if (head_dim != kD) return hipErrorInvalidValue;
+template <int MB>
+hipError_t launch_mb(int group, const PrefillArgs& a, hipStream_t stream) {
   switch (group) {
-    case 1: return launch_g<1>(a, stream);
-    case 2: return launch_g<2>(a, stream);
-    case 4: return launch_g<4>(a, stream);
-    case 8: return launch_g<8>(a, stream);
+    case 1: return launch_g<1, MB>(a, stream);
+    case 2: return launch_g<2, MB>(a, stream);
+    case 4: return launch_g<4, MB>(a, stream);
+    case 8: return launch_g<8, MB>(a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_prefill(int head_dim, int group, const PrefillArgs& a, hipStream_t stream) {
+  if (head_dim != kD) return hipErrorInvalidValue;
+  if (a.tile_pairs == 64) return launch_mb<1>(group, a, stream);
+  if (a.tile_pairs == 128) return launch_mb<2>(group, a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa

@@ -190,7 +190,7 @@ def test_shared_prefix_shared_vs_private_bitwise():
 
 
 # ---------------------------------------------------------------------------
-# the five workloads
+# the named workloads
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2, 3, 4])
@@ -212,7 +212,8 @@ def _sample_rows(c, k=24, seed=0):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("name", ["mha_decode_bf16", "gqa_decode_bf16", "prefix_long_bf16", "mixed_prefill_bf16"])
+@pytest.mark.parametrize("name", ["mha_decode_bf16", "gqa_decode_bf16", "prefix_long_bf16", "mixed_prefill_bf16",
+                                  "spec_verify_bf16"])
 def test_config_full_size_sampled(name):
     c = make_config(name, 0)
     rows = _sample_rows(c)
@@ -289,3 +290,37 @@ def test_validate_metadata_flags():
     bad_cu[2] = 0
     assert pa.validate_metadata(bad_cu, dc.seq_lens, dc.tables, c.num_blocks, 3, 30) & pa.BAD_CU_SEQLENS
     assert pa.validate_metadata(dc.cu, dc.seq_lens, dc.tables, c.num_blocks, 3, 16) & pa.BAD_LENGTHS
+
+
+# ---------------------------------------------------------------------------
+# short multi-row requests (speculative-decode verify) split over partitions
+
+
+@pytest.mark.parametrize("Hq,Hkv,maxn", [(64, 8, 16), (64, 8, 8), (16, 8, 16), (8, 8, 16), (8, 8, 64)])
+@pytest.mark.parametrize("psize", [0, 512])
+def test_short_multirow_split_over_partitions(Hq, Hkv, maxn, psize):
+    """Requests of at most one row tile whose contexts span several partitions
+    are computed per partition and merged (64-pair tiles when every multi-row
+    request fits 64 / G rows, else 128-pair tiles).  Edge cases: the last
+    partition visible to the last rows only, a context of exactly one
+    partition, rows next to decode rows, the largest split row count."""
+    n = [2, min(8, maxn), maxn, 3, 1, 1, 5, maxn, 4]
+    L = [2049, 5000, 4100, 513, 3000, 7, 1030, 2048 + maxn, 512]
+    c = build_case(f"split_{Hq}_{Hkv}_{maxn}", 40 + maxn, "bf16", Hq, Hkv, 128, n, L)
+    mx, mean, ok, _ = run_and_compare(c, partition_size=psize)
+    say(f"split {Hq}/{Hkv} psize {psize}: max {mx:.3g} mean {mean:.3g}")
+    assert ok, (mx, mean)
+
+
+def test_short_multirow_split_deterministic_and_batch_invariant():
+    """With an explicit partition size a split request's rows do not depend on
+    the rest of the batch, bit for bit."""
+    c = build_case("split_a", 50, "bf16", 64, 8, 128, [6, 1, 3], [3000, 2000, 700])
+    _, _, ok, dc = run_and_compare(c, partition_size=1024)
+    assert ok
+    alone = torch.empty_like(dc.q[:6])
+    pa.attention_varlen(alone, dc.q[:6], dc.k_cache, dc.v_cache, dc.cu[:2].contiguous(),
+                        dc.seq_lens[:1].contiguous(), dc.tables[:1].contiguous(), float(c.scale), 6, 3000,
+                        partition_size=1024)
+    torch.cuda.synchronize()
+    assert torch.equal(dc.out[:6].view(torch.int16), alone.view(torch.int16))

@@ -6,8 +6,12 @@ single-row requests with more than one partition.
 Layout (int32 words of the workspace): [8] decode entries, [9] prefill
 entries, [10] merge entries; decode entries (request, partition, first row,
 context) from word 64; prefill entries (request, row tile, first row, rows)
-after the decode capacity; merge entries (request, first row, partitions, 0)
-after the prefill capacity.
+after the decode capacity; merge entries (request, first row, partitions,
+partial row) after the prefill capacity.  Short multi-row requests (at most
+one row tile, in a batch of only such requests and decode rows) whose
+contexts span several partitions get one prefill entry per partition
+(request, partition << 16, first row, rows) and one merge entry per row, with
+partial row = number of requests + packed row.
 """
 
 import collections
@@ -80,8 +84,8 @@ def test_work_lists(partition_size):
 
     # merge list
     nm = int(w[10])
-    got_m = {tuple(int(v) for v in w[merge_off + 4 * i: merge_off + 4 * i + 3]) for i in range(nm)}
-    want_m = {(b, int(cu[b]), -(-int(L[b]) // P)) for b in range(B) if n[b] == 1 and L[b] > P}
+    got_m = {tuple(int(v) for v in w[merge_off + 4 * i: merge_off + 4 * i + 4]) for i in range(nm)}
+    want_m = {(b, int(cu[b]), -(-int(L[b]) // P), b) for b in range(B) if n[b] == 1 and L[b] > P}
     assert nm == len(want_m) and got_m == want_m
 
     # prefill list
@@ -100,3 +104,54 @@ def test_work_lists(partition_size):
         return min(-(-(int(L[b]) - nb + last) // 64), 511)
     kt = [key_tiles(e) for e in got_p]
     assert all(x >= y for x, y in zip(kt, kt[1:])), "prefill list not sorted by size"
+
+
+@pytest.mark.parametrize("partition_size", [0, 512])
+@pytest.mark.parametrize("rows", [16, 8])
+def test_work_lists_split_short_requests(partition_size, rows):
+    """rows = 16: 128-pair tiles (some request has more than 8 rows); rows =
+    8: 64-pair tiles."""
+    rng = np.random.default_rng(12)
+    B = 200
+    Hq, Hkv = 64, 8
+    n = np.ones(B, np.int64)
+    multi = rng.choice(B, 60, replace=False)
+    n[multi] = rng.integers(2, rows + 1, 60)
+    n[multi[0]] = rows
+    L = np.maximum(n, rng.integers(1, 6000, B))
+    c = build_case("plan_split", 4, "bf16", Hq, Hkv, 128, n, L, poison=False)
+    w, P = _run_and_read(c, partition_size)
+    parts_max = -(-c.max_seq_len // P)
+    dec_cap = B * parts_max
+    pref_cap = B * max(1, parts_max)
+    pref_off = HEADER + 4 * dec_cap
+    merge_off = pref_off + 4 * pref_cap
+    cu = c.cu_seqlens.astype(np.int64)
+
+    npf = int(w[9])
+    got_p = [tuple(int(v) for v in w[pref_off + 4 * i: pref_off + 4 * i + 4]) for i in range(npf)]
+    want_p, want_m = [], set()
+    for b in range(B):
+        parts = -(-int(L[b]) // P)
+        if n[b] == 1:
+            if parts > 1:
+                want_m.add((b, int(cu[b]), parts, b))
+        elif parts > 1:
+            want_p += [(b, p << 16, int(cu[b]), int(n[b])) for p in range(parts)]
+            want_m |= {(b, int(cu[b]) + j, parts, B + int(cu[b]) + j) for j in range(int(n[b]))}
+        else:
+            want_p.append((b, 0, int(cu[b]), int(n[b])))
+    assert collections.Counter(got_p) == collections.Counter(want_p)
+    nm = int(w[10])
+    got_m = [tuple(int(v) for v in w[merge_off + 4 * i: merge_off + 4 * i + 4]) for i in range(nm)]
+    assert len(got_m) == len(set(got_m)) and set(got_m) == want_m
+
+    def size(e):
+        b, tp, _, nb = e
+        p = tp >> 16
+        if -(-int(L[b]) // P) > 1:
+            return -(-(min(int(L[b]), (p + 1) * P) - p * P) // 64)
+        return -(-int(L[b]) // 64)
+    sz = [size(e) for e in got_p]
+    assert all(x >= y for x, y in zip(sz, sz[1:])), "prefill list not sorted by size"
+    say(f"partition {P}: {npf} prefill entries, {nm} merge entries")

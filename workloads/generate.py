@@ -302,18 +302,27 @@ def _prefix_long_bf16(seed, **kw):
                       max_blocks_per_seq=2048, share_groups=[(list(range(128)), 128)], **kw)
 
 
+def _spec_verify_bf16(seed, **kw):
+    # the GQA decode layer's requests, each verifying 1-7 draft tokens (2-8 query rows)
+    g = _gen(seed, S_LENGTHS)
+    L = np.clip(np.rint(g.lognormal(math.log(1024.0), 1.0, size=256)), 16, 8192).astype(np.int64)
+    n = g.integers(2, 8, size=256, endpoint=True)
+    return build_case("spec_verify_bf16", seed, "bf16", 64, 8, 128, n, L, max_blocks_per_seq=512, **kw)
+
+
 _CONFIGS = {
     "tiny_decode_f32": _tiny_decode_f32,
     "mha_decode_bf16": _mha_decode_bf16,
     "gqa_decode_bf16": _gqa_decode_bf16,
     "mixed_prefill_bf16": _mixed_prefill_bf16,
     "prefix_long_bf16": _prefix_long_bf16,
+    "spec_verify_bf16": _spec_verify_bf16,
 }
 CONFIG_NAMES = tuple(_CONFIGS)
 
 
 def make_config(name: str, seed: int = 0, *, poison: bool = True, threads: int | None = None) -> Case:
-    """Build one of the five named workloads for ``seed``."""
+    """Build one of the named workloads for ``seed``."""
     if name not in _CONFIGS:
         raise KeyError(f"unknown config {name!r}; known: {CONFIG_NAMES}")
     return _CONFIGS[name](seed, poison=poison, threads=threads)
