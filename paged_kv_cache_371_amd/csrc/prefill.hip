@@ -47,21 +47,35 @@ namespace pa {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kOccupancy = 2;                // workgroups per CU (256 registers per wave; LDS allows 2)
-constexpr int kKeys = kPrefillKeys;          // keys per tile = kBlock * waves
 constexpr int kTileBytes = kBlock * kD * 2;  // one (block, KV head) tile of bf16
-constexpr int kKChunk = kKeys * 16 + 16;     // LDS bytes per 8-wide d-chunk of K (64 keys + pad)
-constexpr int kVRow = kKeys * 2 + 8;         // LDS bytes per d row of V^T (64 keys + pad)
-constexpr int kKBytes = (kD / 8) * kKChunk;
-constexpr int kVBytes = kD * kVRow;
-constexpr int kStageBytes = kKBytes + kVBytes;
-constexpr int kLdsBytes = 2 * kStageBytes;
 constexpr unsigned kRsrcWord3 = 0x00020000u;
 constexpr float kMinusBig = -1e30f;
 constexpr float kRescaleThreshold = 8.f;      // log2 units
 constexpr uint32_t kBf16OnePair = 0x3F803F80u;
+constexpr int kWavesPerSimd = 2;              // register budget: 256 per lane
 
-static_assert(kKeys == 4 * kBlock, "a key tile is one paged block per wave");
+// Workgroup shape: W waves, each fetching one paged block of every key tile
+// (so a tile holds 16 W keys) and owning 32 (row, head) pairs.  W = 4: 128
+// pairs, 64-key tiles, two workgroups per CU (the LDS holds two).  W = 2: 64
+// pairs, 32-key tiles, four workgroups per CU -- the same waves per SIMD,
+// half the LDS reads per pair (each wave reads the whole staged tile).
+template <int W>
+struct Shape {
+  static constexpr int kWaves = W;
+  static constexpr int kThreads = 64 * W;
+  static constexpr int kKeys = kBlock * W;           // keys per tile
+  static constexpr int kCB = kKeys / 16;             // 16-key column blocks of S^T
+  static constexpr int kU = kKeys / 32;              // 32-key MFMA steps of O^T
+  static constexpr int kKChunk = kKeys * 16 + 16;    // LDS bytes per 8-wide d-chunk of K (+ pad)
+  // LDS bytes per d row of V^T: keys + pad chosen so that the 16 rows x 4 row
+  // groups of a 32-lane 8-byte read land on distinct banks
+  static constexpr int kVRow = W == 4 ? kKeys * 2 + 8 : kKeys * 2 + 16;
+  static constexpr int kKBytes = (kD / 8) * kKChunk;
+  static constexpr int kVBytes = kD * kVRow;
+  static constexpr int kStageBytes = kKBytes + kVBytes;
+  static constexpr int kLdsBytes = 2 * kStageBytes;
+  static_assert(kKeys % 32 == 0, "whole 32-key MFMA steps");
+};
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
@@ -88,22 +102,27 @@ struct TileRegs {
   u32x4_t v[4];
 };
 
-// MB: 16-column MFMA blocks per wave, so a work item covers 64 * MB (row,
-// head) pairs.  MB = 2 (128 pairs) for chunked prefill; MB = 1 (64 pairs)
-// for batches whose multi-row requests are short (speculative-decode
-// verification), where a 128-pair tile would be mostly empty and the
-// per-tile instruction cost, not HBM, would set the pace.
-template <int G, int MB>
-__global__ __launch_bounds__(256, kOccupancy) void prefill_kernel(PrefillArgs a) {
-  constexpr int kMB = MB;
-  constexpr int kPairs = 64 * MB;
-  static_assert(MB == 1 || MB == 2, "one or two 16-column blocks per wave");
+// W = 4 for chunked prefill; W = 2 for batches whose multi-row requests are
+// short (speculative-decode verification), where a 128-pair tile would be
+// mostly empty and the LDS reads per tile, not HBM, would set the pace.
+template <int G, int W>
+__global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_kernel(PrefillArgs a) {
+  using S = Shape<W>;
+  constexpr int kMB = 2;                      // 16-column MFMA blocks per wave
+  constexpr int kPairs = 16 * kMB * W;
+  constexpr int kKeys = S::kKeys;
+  constexpr int kCB = S::kCB;
+  constexpr int kU = S::kU;
+  constexpr int kKChunk = S::kKChunk;
+  constexpr int kVRow = S::kVRow;
+  constexpr int kKBytes = S::kKBytes;
+  constexpr int kStageBytes = S::kStageBytes;
   constexpr int kRows = kPairs / G;   // query rows per work item
   extern __shared__ __align__(16) char smem[];
 
   const int hkv = a.num_kv_heads;
   const int total = load_const(a.plan, kPlanPrefCountInt) * hkv;
-  const int W = gridDim.x;
+  const int ngroups = gridDim.x;
   const int wg = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -117,8 +136,10 @@ __global__ __launch_bounds__(256, kOccupancy) void prefill_kernel(PrefillArgs a)
   const float scale_log2 = a.scale_log2;
   const int32_t* entries = a.plan + kPlanHeaderInts + a.pref_off_ints;
 
-  for (int i = 0, base = 0; base < total; ++i, base += W) {
-    const int t = base + ((i & 1) ? W - 1 - wg : wg);
+  // Items in list order (largest first), dealt out round-robin, every other
+  // round in reverse, so the large items spread over the workgroups.
+  for (int i = 0, base = 0; base < total; ++i, base += ngroups) {
+    const int t = base + ((i & 1) ? ngroups - 1 - wg : wg);
     if (t >= total) continue;
     const int e = t / hkv;
     const int kvh = t - e * hkv;
@@ -179,14 +200,22 @@ __global__ __launch_bounds__(256, kOccupancy) void prefill_kernel(PrefillArgs a)
 
     // ---- K/V tile staging -----------------------------------------------------
     // Physical block of this wave's part of tile kt (clamped into the table;
-    // positions past the context are zeroed when staged).
-    auto phys_of = [&](int kt) -> int { return load_const_early(table, min(kt * 4 + wave, nblk - 1)); };
-    auto fetch = [&](TileRegs& rg, int kt, int phys) {
+    // positions past the context are zeroed when staged).  Read with a vector
+    // load one tile ahead: a scalar load would share the LDS reads' wait
+    // counter, and every tile's first LDS wait would then also wait out a
+    // memory round trip for the table.
+    const __amdgpu_buffer_rsrc_t rtab =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(table), 0, nblk * 4, kRsrcWord3);
+    auto phys_of = [&](int kt) -> uint32_t {
+      return __builtin_amdgcn_raw_buffer_load_b32(rtab, min(kt * W + wave, nblk - 1) * 4, 0, 0);
+    };
+    auto fetch = [&](TileRegs& rg, int kt, uint32_t phys_v) {
+      const int64_t phys = uni(int(phys_v));
       const int nrec = kt < kt1 ? kTileBytes : 0;
       const __amdgpu_buffer_rsrc_t rk =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + int64_t(phys) * bstride), 0, nrec, kRsrcWord3);
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + phys * bstride), 0, nrec, kRsrcWord3);
       const __amdgpu_buffer_rsrc_t rv =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + int64_t(phys) * bstride), 0, nrec, kRsrcWord3);
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + phys * bstride), 0, nrec, kRsrcWord3);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
         rg.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, (kkey + kk) * (kD * 2) + kchunk * 16, 0, 0);
@@ -227,15 +256,15 @@ __global__ __launch_bounds__(256, kOccupancy) void prefill_kernel(PrefillArgs a)
     auto compute = [&](int kt, int st) {
       const char* ks = smem + st * kStageBytes;
       const char* vs = ks + kKBytes;
-      f32x4_t sacc[4][kMB];
+      f32x4_t sacc[kCB][kMB];
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < kCB; ++c)
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) sacc[c][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < kCB; ++c) {
           const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(ks + (4 * s + h) * kKChunk + (16 * c + lc) * 16);
 #pragma unroll
           for (int mb = 0; mb < kMB; ++mb) sacc[c][mb] = mfma16(ka, qb[mb][s], sacc[c][mb]);
@@ -247,17 +276,17 @@ __global__ __launch_bounds__(256, kOccupancy) void prefill_kernel(PrefillArgs a)
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
+          for (int c = 0; c < kCB; ++c)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               if (kt * kKeys + 16 * c + 4 * h + r > limit[mb]) sacc[c][mb][r] = -__builtin_inff();
       }
-      u32x4_t pb[kMB][2];   // B operand P^T per (pair block, 32-key step)
+      u32x4_t pb[kMB][kU];   // B operand P^T per (pair block, 32-key step)
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb) {
         float tmax = -__builtin_inff();
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < kCB; ++c)
           tmax = fmaxf(fmaxf(tmax, fmaxf(sacc[c][mb][0], sacc[c][mb][1])), fmaxf(sacc[c][mb][2], sacc[c][mb][3]));
         tmax = rows_max(tmax) * scale_log2;
         // The reference max is raised only when the tile's max exceeds it by
@@ -274,7 +303,7 @@ __global__ __launch_bounds__(256, kOccupancy) void prefill_kernel(PrefillArgs a)
         const float nm = -mrun[mb];
         float lsum = lrun[mb];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < kU; ++u) {
           uint32_t w[4];
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
@@ -290,7 +319,7 @@ __global__ __launch_bounds__(256, kOccupancy) void prefill_kernel(PrefillArgs a)
         lrun[mb] = lsum;
       }
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < kU; ++u)
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
           const char* vrow = vs + (16 * db + lc) * kVRow;
@@ -309,7 +338,7 @@ __global__ __launch_bounds__(256, kOccupancy) void prefill_kernel(PrefillArgs a)
     // after.
     __syncthreads();   // the previous item is done with both stages
     TileRegs rg;
-    int ph_next = phys_of(kt0 + 1);
+    uint32_t ph_next = phys_of(kt0 + 1);
     fetch(rg, kt0, phys_of(kt0));
     stage_write(rg, kt0, 0);
     __syncthreads();
@@ -335,27 +364,27 @@ __global__ __launch_bounds__(256, kOccupancy) void prefill_kernel(PrefillArgs a)
           if (h == 0) *reinterpret_cast<float2*>(a.ws_ml + 2 * idx) = make_float2(mrun[mb], lsum);
         }
       }
-      continue;
-    }
-
-    // ---- normalise and store ----------------------------------------------------
+    } else {
+      // ---- normalise and store --------------------------------------------------
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
-      const float inv = 1.f / rows_sum(lrun[mb]);
-      if (mvalid[mb]) {
-        __bf16* orow = static_cast<__bf16*>(a.out) + int64_t(q0 + jrow[mb]) * a.o_row_stride + int64_t(hq[mb]) * kD;
+      for (int mb = 0; mb < kMB; ++mb) {
+        const float inv = 1.f / rows_sum(lrun[mb]);
+        if (mvalid[mb]) {
+          __bf16* orow =
+              static_cast<__bf16*>(a.out) + int64_t(q0 + jrow[mb]) * a.o_row_stride + int64_t(hq[mb]) * kD;
 #pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          const u32x2_t o = {pack_bf16x2(acc[mb][db][0] * inv, acc[mb][db][1] * inv),
-                             pack_bf16x2(acc[mb][db][2] * inv, acc[mb][db][3] * inv)};
-          *reinterpret_cast<u32x2_t*>(orow + 16 * db + 4 * h) = o;
+          for (int db = 0; db < 8; ++db) {
+            const u32x2_t o = {pack_bf16x2(acc[mb][db][0] * inv, acc[mb][db][1] * inv),
+                               pack_bf16x2(acc[mb][db][2] * inv, acc[mb][db][3] * inv)};
+            *reinterpret_cast<u32x2_t*>(orow + 16 * db + 4 * h) = o;
+          }
         }
       }
     }
   }
 }
 
-template <int G, int MB>
+template <int G, int W>
 int prefill_groups() {
   static std::atomic<int> cache{0};
   int v = cache.load(std::memory_order_relaxed);
@@ -363,20 +392,23 @@ int prefill_groups() {
   int dev = 0, cus = 0, occ = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, prefill_kernel<G, MB>, 256, kLdsBytes) != hipSuccess || occ <= 0)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, prefill_kernel<G, W>, Shape<W>::kThreads,
+                                                   Shape<W>::kLdsBytes) != hipSuccess ||
+      occ <= 0)
     occ = 1;
   v = cus * occ;
   cache.store(v, std::memory_order_relaxed);
   return v;
 }
 
-template <int G, int MB>
+template <int G, int W>
 hipError_t launch_g(const PrefillArgs& a, hipStream_t stream) {
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<G, MB>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+      hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<G, W>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, Shape<W>::kLdsBytes);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((prefill_kernel<G, MB>), dim3(prefill_groups<G, MB>()), dim3(256), kLdsBytes, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<G, W>), dim3(prefill_groups<G, W>()), dim3(Shape<W>::kThreads),
+                     Shape<W>::kLdsBytes, stream, a);
   return hipGetLastError();
 }
 
@@ -386,21 +418,21 @@ bool prefill_supported(int head_dim, int group) {
   return head_dim == kD && (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
-template <int MB>
-hipError_t launch_mb(int group, const PrefillArgs& a, hipStream_t stream) {
+template <int W>
+hipError_t launch_w(int group, const PrefillArgs& a, hipStream_t stream) {
   switch (group) {
-    case 1: return launch_g<1, MB>(a, stream);
-    case 2: return launch_g<2, MB>(a, stream);
-    case 4: return launch_g<4, MB>(a, stream);
-    case 8: return launch_g<8, MB>(a, stream);
+    case 1: return launch_g<1, W>(a, stream);
+    case 2: return launch_g<2, W>(a, stream);
+    case 4: return launch_g<4, W>(a, stream);
+    case 8: return launch_g<8, W>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_prefill(int head_dim, int group, const PrefillArgs& a, hipStream_t stream) {
   if (head_dim != kD) return hipErrorInvalidValue;
-  if (a.tile_pairs == 64) return launch_mb<1>(group, a, stream);
-  if (a.tile_pairs == 128) return launch_mb<2>(group, a, stream);
+  if (a.tile_pairs == 64) return launch_w<2>(group, a, stream);
+  if (a.tile_pairs == 128) return launch_w<4>(group, a, stream);
   return hipErrorInvalidValue;
 }
 
