@@ -31,6 +31,7 @@ from .paged_attention import (  # noqa: F401
     fp8_e4m3_decode,
     fp8_e4m3_encode,
     fp8_quantize_rows,
+    first_visible_key,
     gather_request_kv,
     kv_head_of,
     last_visible_key,

@@ -131,6 +131,17 @@ def last_visible_key(seq_len: int, q_len: int, j: int) -> int:
     return seq_len - q_len + j
 
 
+def first_visible_key(seq_len: int, q_len: int, j: int, sliding_window: int = 0) -> int:
+    """First key position row j may attend to: 0, or with a sliding window of
+    W > 0 tokens the oldest of the last W positions up to its own (the pages
+    list the sliding-window mask among the kernel variants, quant67 §10.8 FAQ,
+    without defining it; the window is read as the row's own position and the
+    W - 1 before it)."""
+    if sliding_window <= 0:
+        return 0
+    return max(0, last_visible_key(seq_len, q_len, j) - sliding_window + 1)
+
+
 # ---------------------------------------------------------------------------
 # metadata
 
@@ -210,7 +221,7 @@ def gather_request_kv(cache, block_table_row, seq_len: int, dtype: str, block_si
 def oracle_attention_varlen(q, k_cache, v_cache, cu_seqlens, seq_lens, block_tables,
                             scale, num_kv_heads: int, dtype: str, block_size: int = 16,
                             rows=None, validate: bool = True, kv_dtype: str | None = None,
-                            k_scale: float = 1.0, v_scale: float = 1.0):
+                            k_scale: float = 1.0, v_scale: float = 1.0, sliding_window: int = 0):
     """Causal softmax attention of packed query rows over a paged KV cache.
 
     q: [total_q, Hq, D]; returns fp64 [total_q, Hq, D] (rows not computed stay
@@ -220,6 +231,8 @@ def oracle_attention_varlen(q, k_cache, v_cache, cu_seqlens, seq_lens, block_tab
     p = L_b - n_b + j and K, V gathered through the block table.  The pools
     hold ``kv_dtype`` (default: ``dtype``); with 8-bit codes the cached values
     are the decoded codes times ``k_scale`` / ``v_scale`` (fp32, widened).
+    With ``sliding_window`` W > 0 the keys are further limited to the last W
+    positions up to p (``first_visible_key``).
     """
     q = np.asarray(q)
     total_q, Hq, D = q.shape
@@ -250,12 +263,13 @@ def oracle_attention_varlen(q, k_cache, v_cache, cu_seqlens, seq_lens, block_tab
         for r in my_rows:
             j = r - q0
             p = last_visible_key(L, n, j)
+            lo = first_visible_key(L, n, j, sliding_window)
             qr = widen(q[r], dtype)  # [Hq, D]
             for h in range(Hq):
                 kvh = kv_head_of(h, G)
-                s = scale64 * (K[:p + 1, kvh, :] @ qr[h])
+                s = scale64 * (K[lo:p + 1, kvh, :] @ qr[h])
                 w = np.exp(s - s.max())
-                out[r, h] = (w @ V[:p + 1, kvh, :]) / w.sum()
+                out[r, h] = (w @ V[lo:p + 1, kvh, :]) / w.sum()
     return out
 
 

@@ -12,11 +12,12 @@ import math
 import numpy as np
 
 
-def brute_attention(q_rows, K, V, scale, group):
+def brute_attention(q_rows, K, V, scale, group, window=0):
     """Textbook causal softmax attention for one request.
 
     q_rows: [n, Hq, D]; K, V: [L, Hkv, D] (contiguous, logical order).
-    Row j is the token at position L - n + j and sees keys 0 .. L - n + j.
+    Row j is the token at position L - n + j and sees keys 0 .. L - n + j
+    (with window > 0 only the last `window` of them).
     Returns a nested list [n][Hq][D] of Python floats.
     """
     if len(q_rows) == 0:
@@ -26,11 +27,12 @@ def brute_attention(q_rows, K, V, scale, group):
     out = []
     for j in range(n):
         pos = L - n + j
+        keys = [t for t in range(pos + 1) if window <= 0 or pos - t < window]
         row = []
         for h in range(Hq):
             g = h // group
             scores = []
-            for t in range(pos + 1):
+            for t in keys:
                 acc = 0.0
                 for d in range(D):
                     acc += float(q_rows[j][h][d]) * float(K[t][g][d])
@@ -41,8 +43,8 @@ def brute_attention(q_rows, K, V, scale, group):
             o = []
             for d in range(D):
                 acc = 0.0
-                for t in range(pos + 1):
-                    acc += ws[t] * float(V[t][g][d])
+                for i, t in enumerate(keys):
+                    acc += ws[i] * float(V[t][g][d])
                 o.append(acc / tot)
             row.append(o)
         out.append(row)
