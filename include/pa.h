@@ -104,6 +104,11 @@ typedef struct {
                                   batch).  0 = library default: 512, 1024 or 2048 chosen
                                   from num_seqs, num_kv_heads and max_seq_len (results may
                                   then differ in the last bits between batch shapes). */
+  int32_t sliding_window;      /* 0: every row sees its whole causal context.  W > 0: row j
+                                  of request b sees only the last W positions up to its own,
+                                  keys max(0, p - W + 1) .. p with p = L_b - n_b + j ([Q67]
+                                  §10.8 lists the sliding-window mask among the kernel
+                                  variants; this is its reading).  Must be >= 0. */
 } pa_attn_params;
 
 /*
@@ -146,8 +151,9 @@ int32_t pa_attention_partition_size(const pa_attn_params* p);
 /*
  * pa_attention_varlen -- [Q67] §3.6 and [ICE]: for every request b, row j,
  * query head h:
- *   s_t = scale * <q[row, h, :], K_b[t, h/G, :]>       for t <= L_b - n_b + j
+ *   s_t = scale * <q[row, h, :], K_b[t, h/G, :]>       for lo_j <= t <= L_b - n_b + j
  *   out[row, h, :] = sum_t softmax(s)_t * V_b[t, h/G, :]
+ * with lo_j = 0, or max(0, L_b - n_b + j - W + 1) for a sliding window W > 0,
  * where K_b[t] = k_cache[block_tables[b][t/16]][h/G][t%16] (same for V) and
  * row = cu_seqlens_q[b] + j.
  *
@@ -230,7 +236,8 @@ pa_status pa_validate_metadata(const int32_t* cu_seqlens_q, const int32_t* seq_l
 const char* pa_status_string(pa_status s);
 
 /* ABI version of this header: major*100 + minor (101: the 8-bit cache calls;
- * 102: block copies and the host block manager, pa_blocks.h). */
+ * 102: block copies and the host block manager, pa_blocks.h; 200:
+ * pa_attn_params.sliding_window). */
 int32_t pa_abi_version(void);
 
 #ifdef __cplusplus

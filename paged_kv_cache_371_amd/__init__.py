@@ -127,6 +127,7 @@ class AttnParams(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("dtype", ctypes.c_int),
         ("partition_size", ctypes.c_int32),
+        ("sliding_window", ctypes.c_int32),
     ]
 
 
@@ -248,7 +249,7 @@ def cache_write_fp8(k_new, v_new, k_cache, v_cache, slot_mapping, k_scale: float
 
 
 def make_params(q, k_cache, cu_seqlens, block_tables, num_kv_heads: int, scale: float, max_query_len: int,
-                max_seq_len: int, out=None, partition_size: int = 0) -> AttnParams:
+                max_seq_len: int, out=None, partition_size: int = 0, sliding_window: int = 0) -> AttnParams:
     total_q, Hq, D = q.shape
     p = AttnParams()
     p.num_seqs = int(cu_seqlens.shape[0]) - 1
@@ -266,6 +267,7 @@ def make_params(q, k_cache, cu_seqlens, block_tables, num_kv_heads: int, scale: 
     p.scale = float(scale)
     p.dtype = _dtype_code(q)
     p.partition_size = int(partition_size)
+    p.sliding_window = int(sliding_window)
     return p
 
 
@@ -280,8 +282,11 @@ def partition_size(params: AttnParams) -> int:
 
 def attention_varlen(out, q, k_cache, v_cache, cu_seqlens, seq_lens, block_tables, scale: float,
                      max_query_len: int, max_seq_len: int, workspace=None, partition_size: int = 0,
-                     stream=None, k_scale=None, v_scale=None):
+                     stream=None, k_scale=None, v_scale=None, sliding_window: int = 0):
     """Paged causal attention of packed rows; writes ``out`` [total_q, Hq, D] and returns it.
+
+    ``sliding_window`` W > 0 limits each row to the last W positions up to
+    its own.
 
     ``workspace`` (a contiguous device tensor of any dtype, at least
     ``workspace_size`` bytes) is allocated here when not given.  uint8 pools
@@ -313,7 +318,7 @@ def attention_varlen(out, q, k_cache, v_cache, cu_seqlens, seq_lens, block_table
         raise ValueError("cu_seqlens [B+1], seq_lens [B] and block_tables [B, W] disagree on B")
     num_kv_heads = int(k_cache.shape[1])
     p = make_params(q, k_cache, cu_seqlens, block_tables, num_kv_heads, scale, max_query_len, max_seq_len,
-                    out=out, partition_size=partition_size)
+                    out=out, partition_size=partition_size, sliding_window=sliding_window)
     need = workspace_size(p)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)

@@ -137,13 +137,30 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int lane_off = tg * kRowBytes + dl * 16;
 
   for (int j = 0; j < n; ++j) {
-    const int ctx = L - n + j + 1;  // keys 0 .. ctx-1 are visible to row j
+    const int ctx = L - n + j + 1;  // keys lo .. ctx-1 are visible to row j
     if (tok0 >= ctx) continue;
+    const int lo = window_start(ctx - 1, a.sliding_window);
     const int tok1 = min(tok0 + a.part_size, ctx);
     const int nparts = (ctx + a.part_size - 1) / a.part_size;
     const int row = q0 + j;
     const int lb0 = tok0 / kBlock;
     const int nblk = (tok1 + kBlock - 1) / kBlock - lb0;
+    if (tok1 <= lo) {
+      // the partition lies wholly before the row's window: an empty partial
+      // (max -inf, sum 0) that the merge weighs by zero
+      const int64_t prow = a.partial_by_seq ? b : row;
+      for (int idx = tid; idx < G * D; idx += C::kThreads) {
+        const int g = idx / D;
+        const int d = idx - g * D;
+        const int64_t slot = (prow * a.num_q_heads + kvh * G + g) * a.max_parts + part;
+        a.ws_o[slot * D + d] = 0.f;
+        if (d == 0) {
+          a.ws_ml[2 * slot] = kNegInf;
+          a.ws_ml[2 * slot + 1] = 0.f;
+        }
+      }
+      continue;
+    }
 
     // q slice of this lane for the G heads of the group.
     u32x4_t qf[G];
@@ -176,7 +193,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
           for (int g = 0; g < G; ++g) s[g] = group_sum<kLpr>(dot16<E>(qf[g], cur[l]));
           const int tl = i * kBlock + l * kTpl + tg;     // token index within the partition
-          const bool valid = tok0 + tl < tok1;
+          const bool valid = tok0 + tl < tok1 && tok0 + tl >= lo;
           if constexpr (kLpr >= G) {
             float v = s[0];
 #pragma unroll

@@ -188,7 +188,9 @@ __device__ __forceinline__ float dot16_bf16(const u32x4_t& q, const u32x4_t& k) 
 // single-row request, served by one wave.  All fields are wave-uniform.
 struct Item {
   int valid;
-  int b, kvh, part, q0;
+  int b, kvh, q0;
+  int part;      // partition index among the request's visible partitions (partial slot)
+  int lo;        // first visible key (sliding window), 0 without one
   int tok1;      // end of the partition's tokens
   int lb0;       // first logical block of the partition
   int nb;        // blocks (tiles) in the partition; >= 1 for a valid item
@@ -219,19 +221,23 @@ __device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t,
     L = ent.w;
   }
   const int P = a.part_size;
-  const int tok0 = part * P;
-  const int tok1 = min(tok0 + P, L);
+  // keys [lo, L) are visible; partitions before lo's have no items
+  const int lo = window_start(L - 1, a.sliding_window);
+  const int p_lo = lo / P;
+  const int tok0 = max(part * P, lo);
+  const int tok1 = min(part * P + P, L);
   const int lb0 = tok0 / kBlock;
   const int nb = it.valid ? (tok1 + kBlock - 1) / kBlock - lb0 : 0;
   it.b = uni(b);
   it.kvh = uni(kvh);
-  it.part = uni(part);
+  it.part = uni(part - p_lo);
   it.q0 = uni(q0);
+  it.lo = uni(lo);
   it.tok1 = uni(tok1);
   it.lb0 = uni(lb0);
   it.nb = uni(nb);
   it.nbr = uni(kRing * ((nb + kRing - 1) / kRing));
-  it.nparts = uni((L + P - 1) / P);
+  it.nparts = uni((L + P - 1) / P - p_lo);
   it.valid = uni(it.valid);
   it.table = uni_ptr(a.block_tables + int64_t(b) * a.max_blocks_per_seq);
   it.kbase = uni_ptr(static_cast<const char*>(a.k_cache) + int64_t(kvh) * kTileBytes);
@@ -525,10 +531,10 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
         for (int j = 0; j < G; ++j) s[j] = dot16_bf16(qreg[j], kb[i]);
         sc[i] = row_reduce<G, 0>(s) * scale_log2;
       }
-      if (tb + kBlock > cur.tok1) {   // the context ends inside this block
+      if (tb + kBlock > cur.tok1 || tb < cur.lo) {   // the context ends, or the window starts, in this block
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool dead = tb + 4 * i + tg >= cur.tok1;
+          const bool dead = tb + 4 * i + tg >= cur.tok1 || tb + 4 * i + tg < cur.lo;
           sc[i] = dead ? -__builtin_inff() : sc[i];
 #pragma unroll
           for (int w = 0; w < 4; ++w) vb[i][w] = dead ? 0u : vb[i][w];

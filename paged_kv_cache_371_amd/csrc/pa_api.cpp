@@ -149,6 +149,7 @@ pa_status check_params(const pa_attn_params* p) {
   if (!std::isfinite(p->scale) || !(p->scale > 0.f)) return PA_ERR_SHAPE;
   if (p->partition_size != 0 && (p->partition_size < 16 || p->partition_size > 8192 || p->partition_size % 16))
     return PA_ERR_SHAPE;
+  if (p->sliding_window < 0) return PA_ERR_SHAPE;
   const int eb = elem_bytes(p->dtype);
   if ((p->q_row_stride * eb) % 16 || (p->o_row_stride * eb) % 16) return PA_ERR_ALIGN;
   return PA_OK;
@@ -158,7 +159,7 @@ pa_status check_params(const pa_attn_params* p) {
 
 extern "C" {
 
-int32_t pa_abi_version(void) { return 102; }
+int32_t pa_abi_version(void) { return 200; }
 
 const char* pa_status_string(pa_status s) {
   switch (s) {
@@ -268,6 +269,7 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
   d.merge_off_ints = merge_off(p, pl);
   d.plan_capacity = int32_t(std::max<int64_t>(1, pl.fast ? decode_capacity(p, pl) : 1));
   d.merge_capacity = int32_t(merge_capacity(p, pl));
+  d.sliding_window = p->sliding_window;
 
   // Partials of a region: o [rows, Hq, parts, D] followed by (m, l) [rows, Hq, parts, 2].
   auto point_at = [&](float* region, int64_t rows) {
@@ -292,6 +294,7 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
     pa_.max_seq_len = p->max_seq_len;
     pa_.split_rows = pl.split_rows;
     pa_.tile_pairs = pl.tile_pairs;
+    pa_.sliding_window = p->sliding_window;
     if (pa::launch_plan(pa_, s) != hipSuccess) return PA_ERR_LAUNCH;
   }
   if (pl.fast) {
@@ -328,6 +331,7 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
     f.scale_log2 = scale_log2;
     f.split_rows = pl.split_rows;
     f.tile_pairs = pl.tile_pairs;
+    f.sliding_window = p->sliding_window;
     f.part_size = d.part_size;
     f.max_parts = d.max_parts;
     f.ws_o = pl.split_rows ? region_a : nullptr;

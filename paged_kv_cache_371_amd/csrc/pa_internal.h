@@ -8,6 +8,12 @@ namespace pa {
 
 constexpr int kDefaultPartition = 512;
 
+// First key a row at position pos sees: 0, or the oldest of the last W
+// positions with a sliding window W > 0.
+__host__ __device__ inline int window_start(int pos, int window) {
+  return window > 0 ? (pos - window + 1 > 0 ? pos - window + 1 : 0) : 0;
+}
+
 // Arguments of the split-K decode kernel and its partition merge.
 struct DecodeArgs {
   void* out;
@@ -35,6 +41,7 @@ struct DecodeArgs {
   int32_t row_mode;         // which requests this launch serves (RowMode)
   int32_t partial_by_seq;   // 1: partials indexed by request, else by packed row
   int32_t merge_capacity;   // entries the merge list has room for
+  int32_t sliding_window;   // 0, or W > 0: a row sees only the last W positions up to its own
 };
 
 // Requests a decode launch serves: all of them, only those with exactly one
@@ -69,6 +76,7 @@ struct PrefillArgs {
   float* ws_o;
   float* ws_ml;
   int32_t tile_pairs;   // (query row, head) pairs per work item: 128, or 64 for short requests
+  int32_t sliding_window;
 };
 
 hipError_t launch_cache_write(const void* k_new, const void* v_new, int64_t kv_row_stride_bytes, void* k_cache,
@@ -113,6 +121,7 @@ struct PlanArgs {
   // they span more than one, and one merge entry per row.
   int32_t split_rows;
   int32_t tile_pairs;      // (query row, head) pairs per prefill work item (64 or 128)
+  int32_t sliding_window;  // partitions wholly before a request's window get no entries
 };
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
 // Bytes of a plan buffer for these capacities (entries), rounded to 256.

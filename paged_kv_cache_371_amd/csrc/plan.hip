@@ -116,12 +116,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       s_cursor = 0;
     }
     __syncthreads();
+    // Partitions [p_lo, p_end) of a request hold keys its row sees (a sliding
+    // window drops the ones wholly before it); partitions p_lo+1 .. p_end-2 are
+    // full, the first and the last are sized in blocks.
+    auto blocks_of = [&](int L, int lo, int p) {
+      return (min(L, (p + 1) * P) + kBlock - 1) / kBlock - max(p * P, lo) / kBlock;
+    };
     for_each_request([&](int, int, int n, int L) {
       if (n != 1 || L > a.max_seq_len) return;
-      const int nf = L / P;
-      const int rem = L - nf * P;
-      if (nf) atomicAdd(&s_full, nf);
-      if (rem > 0) atomicAdd(&s_hist[(rem - 1) / kBlock], 1);
+      const int lo = window_start(L - 1, a.sliding_window);
+      const int p_lo = lo / P, np = (L + P - 1) / P - p_lo;
+      int full = max(0, np - 2);
+      for (int k = 0; k < min(np, 2); ++k) {   // the first and the last partition
+        const int nb = blocks_of(L, lo, k ? p_lo + np - 1 : p_lo);
+        if (nb == nbk) ++full; else atomicAdd(&s_hist[nb - 1], 1);
+      }
+      if (full) atomicAdd(&s_full, full);
     });
     __syncthreads();
     const int total = scan_desc(s_hist, s_tmp, nbk, s_full);
@@ -130,13 +140,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     int4* merge = reinterpret_cast<int4*>(a.plan + kPlanHeaderInts + a.merge_off_ints);
     for_each_request([&](int b, int q0, int n, int L) {
       if (n != 1 || L > a.max_seq_len) return;
-      const int nf = L / P;
-      const int rem = L - nf * P;
-      int pos = nf ? atomicAdd(&s_cursor, nf) : 0;
-      for (int p = 0; p < nf; ++p, ++pos) entries[pos] = make_int4(b, p, q0, L);
-      if (rem > 0) entries[atomicAdd(&s_hist[(rem - 1) / kBlock], 1)] = make_int4(b, nf, q0, L);
-      const int parts = nf + (rem > 0);
-      if (parts > 1) merge[atomicAdd(&s_merge, 1)] = make_int4(b, q0, parts, b);
+      const int lo = window_start(L - 1, a.sliding_window);
+      const int p_lo = lo / P, p_end = (L + P - 1) / P;
+      int nfull = 0;
+      for (int p = p_lo; p < p_end; ++p) nfull += blocks_of(L, lo, p) == nbk;
+      int pos = nfull ? atomicAdd(&s_cursor, nfull) : 0;
+      for (int p = p_lo; p < p_end; ++p) {
+        const int nb = blocks_of(L, lo, p);
+        entries[nb == nbk ? pos++ : atomicAdd(&s_hist[nb - 1], 1)] = make_int4(b, p, q0, L);
+      }
+      if (p_end - p_lo > 1) merge[atomicAdd(&s_merge, 1)] = make_int4(b, q0, p_end - p_lo, b);
     });
     __syncthreads();
     if (tid == 0) a.plan[kPlanClaimInt] = 0;
@@ -146,25 +159,32 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     const int rows = a.tile_pairs / a.group;   // query rows per tile
     for (int i = tid; i < kPrefBuckets; i += kPlanThreads) s_hist[i] = 0;
     __syncthreads();
-    // bucket of a tile = number of 64-key tiles its last row visits, clamped
+    // key tiles (64 keys) in [k0, k1), clamped into the buckets
+    auto tiles = [&](int k0, int k1) {
+      return min((k1 + kPrefillKeys - 1) / kPrefillKeys - k0 / kPrefillKeys, kPrefBuckets - 1);
+    };
+    // bucket of row tile mt: the keys its rows see, from its first row's
+    // window start to its last row's position
     auto bucket = [&](int L, int n, int mt) {
       const int last = min(n, (mt + 1) * rows);   // rows [mt*rows, last)
-      const int keys = L - n + last;
-      return min((keys + kPrefillKeys - 1) / kPrefillKeys, kPrefBuckets - 1);
+      return tiles(window_start(L - n + mt * rows, a.sliding_window), L - n + last);
     };
     auto usable = [&](int n, int L) { return n >= 2 && n <= a.max_query_len && L >= n && L <= a.max_seq_len; };
-    // partitions of a split short request (1: not split)
+    // A short request is split over partitions [p_lo, p_end) of P tokens when
+    // its rows' keys span more than one (p_lo: the partition of its first
+    // row's window start).
     const int P = a.part_size;
-    auto split_parts = [&](int n, int L) { return n <= a.split_rows ? (L + P - 1) / P : 1; };
-    // bucket of partition p of a split request: its 64-key tiles
-    auto part_bucket = [&](int L, int p) {
-      return min((min(L, (p + 1) * P) - p * P + kPrefillKeys - 1) / kPrefillKeys, kPrefBuckets - 1);
+    auto first_part = [&](int n, int L) { return window_start(L - n, a.sliding_window) / P; };
+    auto split_parts = [&](int n, int L) { return n <= a.split_rows ? (L + P - 1) / P - first_part(n, L) : 1; };
+    auto part_bucket = [&](int n, int L, int p) {
+      return tiles(max(p * P, window_start(L - n, a.sliding_window)), min(L, (p + 1) * P));
     };
     for_each_request([&](int, int, int n, int L) {
       if (!usable(n, L)) return;
       const int parts = split_parts(n, L);
       if (parts > 1) {
-        for (int p = 0; p < parts; ++p) atomicAdd(&s_hist[part_bucket(L, p)], 1);
+        const int p_lo = first_part(n, L);
+        for (int p = p_lo; p < p_lo + parts; ++p) atomicAdd(&s_hist[part_bucket(n, L, p)], 1);
       } else {
         for (int mt = 0; mt * rows < n; ++mt) atomicAdd(&s_hist[bucket(L, n, mt)], 1);
       }
@@ -178,7 +198,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       if (!usable(n, L)) return;
       const int parts = split_parts(n, L);
       if (parts > 1) {
-        for (int p = 0; p < parts; ++p) entries[atomicAdd(&s_hist[part_bucket(L, p)], 1)] = make_int4(b, p << 16, q0, n);
+        const int p_lo = first_part(n, L);
+        for (int p = p_lo; p < p_lo + parts; ++p)
+          entries[atomicAdd(&s_hist[part_bucket(n, L, p)], 1)] = make_int4(b, p << 16, q0, n);
         const int m0 = atomicAdd(&s_merge, n);
         for (int j = 0; j < n; ++j) merge[m0 + j] = make_int4(b, q0 + j, parts, a.num_seqs + q0 + j);
       } else {

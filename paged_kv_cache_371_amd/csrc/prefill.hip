@@ -155,19 +155,25 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
     const int j1 = min(n, j0 + kRows);
     const int kmax = P + j1;              // keys visible to the last row
     const int KT = (kmax + kKeys - 1) / kKeys;
-    // A split short request covers key tiles [kt0, kt1) of partition `part`
-    // and leaves partials for the merge; otherwise the item covers all tiles.
-    const bool split = n <= a.split_rows && L > a.part_size;
+    // Keys from the first row's window start on.  A split short request
+    // covers the key tiles of partition `part` (partitions before p_lo get no
+    // item) and leaves partials for the merge; otherwise the item covers all
+    // its tiles.
+    const int lo_first = window_start(P + j0, a.sliding_window);
+    const int lo_last = window_start(P + j1 - 1, a.sliding_window);
+    const int p_lo = lo_first / a.part_size;
+    const bool split = n <= a.split_rows && (L + a.part_size - 1) / a.part_size - p_lo > 1;
     const int part_tiles = a.part_size / kKeys;
-    const int kt0 = split ? part * part_tiles : 0;
-    const int kt1 = split ? min(KT, kt0 + part_tiles) : KT;
+    const int kt_lo = lo_first / kKeys;
+    const int kt0 = split ? max(part * part_tiles, kt_lo) : kt_lo;
+    const int kt1 = split ? min(KT, (part + 1) * part_tiles) : KT;
     const int nblk = max(1, min((L + kBlock - 1) / kBlock, a.max_blocks_per_seq));
     const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks_per_seq;
     const char* kbase = static_cast<const char*>(a.k_cache) + int64_t(kvh) * kTileBytes;
     const char* vbase = static_cast<const char*>(a.v_cache) + int64_t(kvh) * kTileBytes;
 
     // ---- this lane's two pairs: m = wave*32 + mb*16 + lc ----------------------
-    int jrow[kMB], hq[kMB], limit[kMB];
+    int jrow[kMB], hq[kMB], limit[kMB], lolim[kMB];
     bool mvalid[kMB];
     u32x4_t qb[kMB][4];   // B operand Q^T: pair lc, d = 32s + 8h .. +7
 #pragma unroll
@@ -177,6 +183,7 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
       hq[mb] = kvh * G + m % G;
       mvalid[mb] = jrow[mb] < j1;
       limit[mb] = mvalid[mb] ? P + jrow[mb] : 0;
+      lolim[mb] = mvalid[mb] ? window_start(P + jrow[mb], a.sliding_window) : 0;
       const char* qrow = static_cast<const char*>(a.q) +
                          (int64_t(q0 + (mvalid[mb] ? jrow[mb] : 0)) * a.q_row_stride + int64_t(hq[mb]) * kD) * 2;
 #pragma unroll
@@ -269,17 +276,20 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
 #pragma unroll
           for (int mb = 0; mb < kMB; ++mb) sacc[c][mb] = mfma16(ka, qb[mb][s], sacc[c][mb]);
         }
-      // Keys past a row's limit get a score of -inf (raw scores: the scale is
-      // positive, so the order and the masking survive scaling).  Only tiles
-      // that reach past the first row's limit need it.
-      if (kt * kKeys + kKeys - 1 > P + j0) {
+      // Keys past a row's limit, or before its window, get a score of -inf
+      // (raw scores: the scale is positive, so the order and the masking
+      // survive scaling).  Only tiles that reach past the first row's limit or
+      // before the last row's window start need it.
+      if (kt * kKeys + kKeys - 1 > P + j0 || kt * kKeys < lo_last) {
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
           for (int c = 0; c < kCB; ++c)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (kt * kKeys + 16 * c + 4 * h + r > limit[mb]) sacc[c][mb][r] = -__builtin_inff();
+            for (int r = 0; r < 4; ++r) {
+              const int key = kt * kKeys + 16 * c + 4 * h + r;
+              if (key > limit[mb] || key < lolim[mb]) sacc[c][mb][r] = -__builtin_inff();
+            }
       }
       u32x4_t pb[kMB][kU];   // B operand P^T per (pair block, 32-key step)
 #pragma unroll
@@ -357,7 +367,8 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
       for (int mb = 0; mb < kMB; ++mb) {
         const float lsum = rows_sum(lrun[mb]);
         if (mvalid[mb]) {
-          const int64_t idx = (int64_t(a.num_seqs + q0 + jrow[mb]) * a.num_q_heads + hq[mb]) * a.max_parts + part;
+          const int64_t idx =
+              (int64_t(a.num_seqs + q0 + jrow[mb]) * a.num_q_heads + hq[mb]) * a.max_parts + (part - p_lo);
           float* po = a.ws_o + idx * kD;
 #pragma unroll
           for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4_t*>(po + 16 * db + 4 * h) = acc[mb][db];

@@ -50,11 +50,12 @@ class DeviceCase:
     def cache_write(self):
         pa.cache_write(self.k_new, self.v_new, self.k_cache, self.v_cache, self.slots)
 
-    def attention(self, partition_size=0, out=None):
+    def attention(self, partition_size=0, out=None, sliding_window=0):
         c = self.c
         out = self.out if out is None else out
         pa.attention_varlen(out, self.q, self.k_cache, self.v_cache, self.cu, self.seq_lens, self.tables,
-                            float(c.scale), c.max_query_len, c.max_seq_len, partition_size=partition_size)
+                            float(c.scale), c.max_query_len, c.max_seq_len, partition_size=partition_size,
+                            sliding_window=sliding_window)
         return out
 
 
@@ -62,22 +63,22 @@ def oracle_pools(c):
     return oracle.oracle_cache_write(c.k_cache, c.v_cache, c.k_new, c.v_new, c.slot_mapping)
 
 
-def oracle_out(c, k_pool, v_pool, rows=None):
+def oracle_out(c, k_pool, v_pool, rows=None, sliding_window=0):
     return oracle.oracle_attention_varlen(c.q, k_pool, v_pool, c.cu_seqlens, c.seq_lens, c.block_tables, c.scale,
-                                          c.num_kv_heads, c.dtype, rows=rows)
+                                          c.num_kv_heads, c.dtype, rows=rows, sliding_window=sliding_window)
 
 
-def run_and_compare(c, partition_size=0, rows=None, check_pool=True):
+def run_and_compare(c, partition_size=0, rows=None, check_pool=True, sliding_window=0):
     """Cache write + attention on the GPU; returns (max_abs, mean_abs, ok, dc)."""
     dc = DeviceCase(c)
     dc.cache_write()
-    dc.attention(partition_size)
+    dc.attention(partition_size, sliding_window=sliding_window)
     torch.cuda.synchronize()
     k_pool, v_pool = oracle_pools(c)
     if check_pool:
         assert np.array_equal(to_host(dc.k_cache, c.dtype).view(np.uint8), k_pool.view(np.uint8)), "K pool differs"
         assert np.array_equal(to_host(dc.v_cache, c.dtype).view(np.uint8), v_pool.view(np.uint8)), "V pool differs"
-    want = oracle_out(c, k_pool, v_pool, rows=rows)
+    want = oracle_out(c, k_pool, v_pool, rows=rows, sliding_window=sliding_window)
     got = oracle.widen(to_host(dc.out, c.dtype), c.dtype)
     if rows is not None:
         idx = np.asarray(sorted(set(int(r) for r in rows)))

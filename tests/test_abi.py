@@ -58,7 +58,7 @@ def test_struct_layout_matches_c(tmp_path):
 
 
 def test_status_strings_and_version(L):
-    assert L.pa_abi_version() == 102
+    assert L.pa_abi_version() == 200
     for code in range(0, -11, -1):
         s = L.pa_status_string(code).decode()
         assert s.startswith("PA_")
@@ -91,6 +91,7 @@ def _params(**over):
     (dict(scale=0.0), -2),
     (dict(scale=-0.088), -2),
     (dict(max_query_len=65), -2),
+    (dict(sliding_window=-1), -2),
 ])
 def test_host_rejects_bad_params_before_any_launch(L, over, code):
     p = _params(**over)
