@@ -19,7 +19,8 @@ the digest recorded there (null otherwise).  ``cpu_baseline`` times the fp64
 CPU oracle on a bounded sample of the same requests.
 
 ``--calibrate-copy`` runs only a 1 GiB device-to-device copy (the counters'
-calibration run).  ``--op copy_blocks`` times copy-on-write block copies
+calibration run).  ``--sliding-window W`` runs the workload with a sliding
+window of W tokens (KV bytes then count only the keys in some row's window).  ``--op copy_blocks`` times copy-on-write block copies
 (pa_copy_blocks) and ``--op swap_out`` / ``--op swap_in`` time swapping a
 sequence's blocks to and from pinned host memory (pa_swap_blocks); see
 ``run_copy_blocks`` and ``run_swap`` for their workloads.  ``--kv-dtype fp8`` runs the same workload on 8-bit (OCP
@@ -117,32 +118,38 @@ def fp8_codes(shape, seed: int) -> np.ndarray:
     return ((sgn << 7) | (e << 3) | m).astype(np.uint8)
 
 
-def algorithmic_bytes(c, kv_elem_bytes=None) -> dict:
-    """Bytes the attention must move for this batch (no re-reads, no partial-block over-read)."""
+def algorithmic_bytes(c, kv_elem_bytes=None, window: int = 0) -> dict:
+    """Bytes the attention must move for this batch (no re-reads, no partial-block over-read).
+
+    With a sliding window only the keys some row of the request sees count:
+    from its first row's window start to the end of its context."""
     s = 2 if c.dtype == "bf16" else 4
     kvs = s if kv_elem_bytes is None else kv_elem_bytes
     L = c.seq_lens.astype(np.int64)
     n = c.q_lens.astype(np.int64)
-    kv = int((L * c.num_kv_heads * c.head_dim * 2 * kvs).sum())
+    keys = L if window <= 0 else L - np.maximum(0, L - n - window + 1)
+    kv = int((keys * c.num_kv_heads * c.head_dim * 2 * kvs).sum())
     q = int(n.sum() * c.num_q_heads * c.head_dim * s)
     o = q
-    tables = int(4 * (-(-L // 16)).sum())
+    tables = int(4 * (-(-keys // 16)).sum())
     meta = 4 * (2 * c.num_seqs + 1)
     cw = int(2 * (s + kvs) * (c.slot_mapping >= 0).sum() * c.num_kv_heads * c.head_dim + 8 * c.total_q)
     return dict(kv=kv, q=q, o=o, tables=tables, meta=meta, attention=kv + q + o + tables + meta, cache_write=cw)
 
 
-def attention_flops(c) -> float:
+def attention_flops(c, window: int = 0) -> float:
     """4 * D * Hq per (row, visible key)."""
     L = c.seq_lens.astype(np.int64)
     n = c.q_lens.astype(np.int64)
     keys = 0
     for Lb, nb in zip(L, n):
-        keys += int(nb * (Lb - nb) + nb * (nb + 1) // 2)
+        for j in range(int(nb)):
+            p = int(Lb) - int(nb) + j
+            keys += p + 1 if window <= 0 else min(p + 1, window)
     return 4.0 * c.head_dim * c.num_q_heads * keys
 
 
-def cpu_baseline(c, budget_s: float = 12.0, fp8_pools=None) -> dict:
+def cpu_baseline(c, budget_s: float = 12.0, fp8_pools=None, window: int = 0) -> dict:
     """Time the fp64 oracle on whole requests, in passes over the batch in a
     fixed shuffled order, until the budget is spent (one BLAS thread).  With
     ``fp8_pools`` (K and V codes) the oracle attends over the 8-bit pools."""
@@ -153,7 +160,7 @@ def cpu_baseline(c, budget_s: float = 12.0, fp8_pools=None) -> dict:
         limit = threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
         limit = None
-    extra = {}
+    extra = dict(sliding_window=window)
     if fp8_pools is None:
         kp, vp = oracle.oracle_cache_write(c.k_cache, c.v_cache, c.k_new, c.v_new, c.slot_mapping)
         s = 2 if c.dtype == "bf16" else 4
@@ -161,7 +168,7 @@ def cpu_baseline(c, budget_s: float = 12.0, fp8_pools=None) -> dict:
         kp, vp = oracle.oracle_cache_write(fp8_pools[0], fp8_pools[1],
                                            oracle.fp8_quantize_rows(c.k_new, K_SCALE_FP8),
                                            oracle.fp8_quantize_rows(c.v_new, V_SCALE_FP8), c.slot_mapping)
-        extra = dict(kv_dtype="fp8", k_scale=K_SCALE_FP8, v_scale=V_SCALE_FP8)
+        extra.update(kv_dtype="fp8", k_scale=K_SCALE_FP8, v_scale=V_SCALE_FP8)
         s = 1
     order = np.random.default_rng(1).permutation(c.num_seqs)
     done_rows = done_kv = reqs = 0
@@ -174,7 +181,9 @@ def cpu_baseline(c, budget_s: float = 12.0, fp8_pools=None) -> dict:
             oracle.oracle_attention_varlen(c.q, kp, vp, c.cu_seqlens, c.seq_lens, c.block_tables, c.scale,
                                            c.num_kv_heads, c.dtype, rows=rows, validate=False, **extra)
             done_rows += len(rows)
-            done_kv += int(c.seq_lens[b]) * c.num_kv_heads * c.head_dim * 2 * s
+            Lb, nb = int(c.seq_lens[b]), len(rows)
+            keys = Lb if window <= 0 else Lb - max(0, Lb - nb - window + 1)
+            done_kv += keys * c.num_kv_heads * c.head_dim * 2 * s
             reqs += 1
             if time.perf_counter() - t0 > budget_s:
                 break
@@ -203,9 +212,10 @@ def calibrate_copy() -> None:
 class _DeviceBatch:
     """The workload's arrays in HBM, and the two ABI calls of one step."""
 
-    def __init__(self, c, torch, pa, fp8_pools=None):
+    def __init__(self, c, torch, pa, fp8_pools=None, window=0):
         self.c, self.torch, self.pa = c, torch, pa
         self.fp8 = fp8_pools is not None
+        self.window = window
 
         def dev(a):
             if c.dtype == "bf16":
@@ -238,12 +248,14 @@ class _DeviceBatch:
         c = self.c
         if self.ws is None:
             p = self.pa.make_params(self.q, self.k_cache, self.cu, self.tables, c.num_kv_heads, float(c.scale),
-                                    c.max_query_len, c.max_seq_len, out=self.out, partition_size=partition_size)
+                                    c.max_query_len, c.max_seq_len, out=self.out, partition_size=partition_size,
+                                    sliding_window=self.window)
             self.ws = self.torch.empty(max(16, self.pa.workspace_size(p)), dtype=self.torch.uint8, device="cuda:0")
             self.partition_size = self.pa.partition_size(p)
         self.pa.attention_varlen(self.out, self.q, self.k_cache, self.v_cache, self.cu, self.seq_lens, self.tables,
                                  float(c.scale), c.max_query_len, c.max_seq_len, workspace=self.ws,
-                                 partition_size=partition_size, k_scale=K_SCALE_FP8 if self.fp8 else None,
+                                 partition_size=partition_size, sliding_window=self.window,
+                                 k_scale=K_SCALE_FP8 if self.fp8 else None,
                                  v_scale=V_SCALE_FP8 if self.fp8 else None)
 
 
@@ -435,6 +447,8 @@ def main() -> None:
     ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default="bf16",
                     help="fp8: 8-bit (OCP E4M3) pools with per-tensor scales, bf16 q and out")
     ap.add_argument("--op", choices=("attention", "copy_blocks", "swap_out", "swap_in"), default="attention")
+    ap.add_argument("--sliding-window", type=int, default=0,
+                    help="W > 0: each row sees only the last W positions up to its own")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this framework runs the path on one GPU; --gpus must be 1 "
@@ -461,9 +475,10 @@ def main() -> None:
         raise SystemExit("8-bit pools need a bf16 workload")
     pools8 = (fp8_codes(c.k_cache.shape, 1000 + args.seed), fp8_codes(c.v_cache.shape, 2000 + args.seed)) if fp8 \
         else None
-    dc = _DeviceBatch(c, torch, pa, pools8)
-    ab = algorithmic_bytes(c, 1 if fp8 else None)
-    flops = attention_flops(c)
+    W = args.sliding_window
+    dc = _DeviceBatch(c, torch, pa, pools8, W)
+    ab = algorithmic_bytes(c, 1 if fp8 else None, W)
+    flops = attention_flops(c, W)
     stream = torch.cuda.current_stream()
 
     def step():
@@ -522,6 +537,7 @@ def main() -> None:
             "mean_context": float(c.seq_lens.mean()),
             "partition_size": dc.partition_size,
             "kv_dtype": "fp8_e4m3" if fp8 else c.dtype,
+            "sliding_window": W,
             "step": "cache_write + attention_varlen",
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
@@ -537,13 +553,13 @@ def main() -> None:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(c.name + ("_fp8kv" if fp8 else "")),
+            "traffic": measured_traffic(c.name + ("_fp8kv" if fp8 else "") + (f"_w{W}" if W else "")),
             "algorithmic_bytes_per_launch": ab["attention"],
             "attention_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 3),
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(c, args.cpu_budget, pools8)
+        result["cpu_baseline"] = cpu_baseline(c, args.cpu_budget, pools8, W)
     print(json.dumps(result), flush=True)
 
 

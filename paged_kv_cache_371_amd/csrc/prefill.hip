@@ -38,6 +38,8 @@
 // are zeroed when staged and masked as keys, so NaN in unused slots cannot
 // reach the output.
 #include <atomic>
+#include <cstddef>
+#include <type_traits>
 #include <utility>
 
 #include "pa_common.h"
@@ -88,6 +90,21 @@ template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
+
+// A kernel argument read from the kernel-argument segment where it is used,
+// with a volatile scalar load.  The arguments a work item needs once are read
+// this way, so they do not occupy scalar registers across the tile loop,
+// which needs most of them.  The argument block is the PrefillArgs value at
+// offset 0 of the segment.
+template <typename T>
+__device__ __forceinline__ T karg(size_t offset) {
+  typedef const volatile T __attribute__((address_space(4))) CT;
+  typedef const char __attribute__((address_space(4))) CC;
+  CC* base = (CC*)__builtin_amdgcn_kernarg_segment_ptr();
+  return *(CT*)(base + offset);
+}
+#define PA_KARG(field) karg<decltype(PrefillArgs::field)>(offsetof(PrefillArgs, field))
+static_assert(std::is_standard_layout<PrefillArgs>::value, "offsetof on the argument block");
 
 __device__ __forceinline__ f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
@@ -149,7 +166,7 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
     const int n = load_const(entries, 4 * int64_t(e) + 3);
     const int mt = tile_part & 0xffff;
     const int part = tile_part >> 16;
-    const int L = load_const(a.seq_lens, b);
+    const int L = load_const(PA_KARG(seq_lens), b);
     const int P = L - n;                  // cached tokens before this request's rows
     const int j0 = mt * kRows;            // rows [j0, j1) of the request
     const int j1 = min(n, j0 + kRows);
@@ -159,21 +176,25 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
     // covers the key tiles of partition `part` (partitions before p_lo get no
     // item) and leaves partials for the merge; otherwise the item covers all
     // its tiles.
-    const int lo_first = window_start(P + j0, a.sliding_window);
-    const int lo_last = window_start(P + j1 - 1, a.sliding_window);
-    const int p_lo = lo_first / a.part_size;
-    const bool split = n <= a.split_rows && (L + a.part_size - 1) / a.part_size - p_lo > 1;
-    const int part_tiles = a.part_size / kKeys;
+    const int window = PA_KARG(sliding_window);
+    const int part_size = PA_KARG(part_size);
+    const int lo_first = window_start(P + j0, window);
+    const int lo_last = window_start(P + j1 - 1, window);
+    const int p_lo = lo_first / part_size;
+    const bool split = n <= PA_KARG(split_rows) && (L + part_size - 1) / part_size - p_lo > 1;
+    const int part_tiles = part_size / kKeys;
     const int kt_lo = lo_first / kKeys;
     const int kt0 = split ? max(part * part_tiles, kt_lo) : kt_lo;
     const int kt1 = split ? min(KT, (part + 1) * part_tiles) : KT;
-    const int nblk = max(1, min((L + kBlock - 1) / kBlock, a.max_blocks_per_seq));
-    const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks_per_seq;
-    const char* kbase = static_cast<const char*>(a.k_cache) + int64_t(kvh) * kTileBytes;
-    const char* vbase = static_cast<const char*>(a.v_cache) + int64_t(kvh) * kTileBytes;
+    const int mbps = PA_KARG(max_blocks_per_seq);
+    const int nblk = max(1, min((L + kBlock - 1) / kBlock, mbps));
+    const int32_t* table = PA_KARG(block_tables) + int64_t(b) * mbps;
+    const char* kbase = static_cast<const char*>(PA_KARG(k_cache)) + int64_t(kvh) * kTileBytes;
+    const char* vbase = static_cast<const char*>(PA_KARG(v_cache)) + int64_t(kvh) * kTileBytes;
 
     // ---- this lane's two pairs: m = wave*32 + mb*16 + lc ----------------------
-    int jrow[kMB], hq[kMB], limit[kMB], lolim[kMB];
+    // visible keys of a pair: lolim .. lolim + span (one unsigned compare per score)
+    int jrow[kMB], hq[kMB], lolim[kMB], span[kMB];
     bool mvalid[kMB];
     u32x4_t qb[kMB][4];   // B operand Q^T: pair lc, d = 32s + 8h .. +7
 #pragma unroll
@@ -182,10 +203,10 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
       jrow[mb] = j0 + m / G;
       hq[mb] = kvh * G + m % G;
       mvalid[mb] = jrow[mb] < j1;
-      limit[mb] = mvalid[mb] ? P + jrow[mb] : 0;
-      lolim[mb] = mvalid[mb] ? window_start(P + jrow[mb], a.sliding_window) : 0;
-      const char* qrow = static_cast<const char*>(a.q) +
-                         (int64_t(q0 + (mvalid[mb] ? jrow[mb] : 0)) * a.q_row_stride + int64_t(hq[mb]) * kD) * 2;
+      lolim[mb] = mvalid[mb] ? window_start(P + jrow[mb], window) : 0;
+      span[mb] = mvalid[mb] ? P + jrow[mb] - lolim[mb] : 0;
+      const char* qrow = static_cast<const char*>(PA_KARG(q)) +
+                         (int64_t(q0 + (mvalid[mb] ? jrow[mb] : 0)) * PA_KARG(q_row_stride) + int64_t(hq[mb]) * kD) * 2;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qrow + (32 * s + 8 * h) * 2);
@@ -288,7 +309,7 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int key = kt * kKeys + 16 * c + 4 * h + r;
-              if (key > limit[mb] || key < lolim[mb]) sacc[c][mb][r] = -__builtin_inff();
+              if (uint32_t(key - lolim[mb]) > uint32_t(span[mb])) sacc[c][mb][r] = -__builtin_inff();
             }
       }
       u32x4_t pb[kMB][kU];   // B operand P^T per (pair block, 32-key step)
@@ -367,12 +388,13 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
       for (int mb = 0; mb < kMB; ++mb) {
         const float lsum = rows_sum(lrun[mb]);
         if (mvalid[mb]) {
-          const int64_t idx =
-              (int64_t(a.num_seqs + q0 + jrow[mb]) * a.num_q_heads + hq[mb]) * a.max_parts + (part - p_lo);
-          float* po = a.ws_o + idx * kD;
+          const int64_t idx = (int64_t(PA_KARG(num_seqs) + q0 + jrow[mb]) * PA_KARG(num_q_heads) + hq[mb]) *
+                                  PA_KARG(max_parts) +
+                              (part - p_lo);
+          float* po = PA_KARG(ws_o) + idx * kD;
 #pragma unroll
           for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4_t*>(po + 16 * db + 4 * h) = acc[mb][db];
-          if (h == 0) *reinterpret_cast<float2*>(a.ws_ml + 2 * idx) = make_float2(mrun[mb], lsum);
+          if (h == 0) *reinterpret_cast<float2*>(PA_KARG(ws_ml) + 2 * idx) = make_float2(mrun[mb], lsum);
         }
       }
     } else {
@@ -382,7 +404,7 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
         const float inv = 1.f / rows_sum(lrun[mb]);
         if (mvalid[mb]) {
           __bf16* orow =
-              static_cast<__bf16*>(a.out) + int64_t(q0 + jrow[mb]) * a.o_row_stride + int64_t(hq[mb]) * kD;
+              static_cast<__bf16*>(PA_KARG(out)) + int64_t(q0 + jrow[mb]) * PA_KARG(o_row_stride) + int64_t(hq[mb]) * kD;
 #pragma unroll
           for (int db = 0; db < 8; ++db) {
             const u32x2_t o = {pack_bf16x2(acc[mb][db][0] * inv, acc[mb][db][1] * inv),
