@@ -189,13 +189,13 @@ __device__ __forceinline__ float dot16_bf16(const u32x4_t& q, const u32x4_t& k) 
 struct Item {
   int valid;
   int b, kvh, q0;
-  int part;      // partition index among the request's visible partitions (partial slot)
+  int parts;     // partition index among the request's visible partitions (the partial
+                 // slot) | their count << 16
   int lo;        // first visible key (sliding window), 0 without one
   int tok1;      // end of the partition's tokens
   int lb0;       // first logical block of the partition
   int nb;        // blocks (tiles) in the partition; >= 1 for a valid item
   int nbr;       // nb rounded up to a multiple of kRing (the item's stream length)
-  int nparts;    // partitions of the request
   const int32_t* table;
   const char* kbase;
   const char* vbase;
@@ -230,14 +230,13 @@ __device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t,
   const int nb = it.valid ? (tok1 + kBlock - 1) / kBlock - lb0 : 0;
   it.b = uni(b);
   it.kvh = uni(kvh);
-  it.part = uni(part - p_lo);
+  it.parts = uni((part - p_lo) | (((L + P - 1) / P - p_lo) << 16));
   it.q0 = uni(q0);
   it.lo = uni(lo);
   it.tok1 = uni(tok1);
   it.lb0 = uni(lb0);
   it.nb = uni(nb);
   it.nbr = uni(kRing * ((nb + kRing - 1) / kRing));
-  it.nparts = uni((L + P - 1) / P - p_lo);
   it.valid = uni(it.valid);
   it.table = uni_ptr(a.block_tables + int64_t(b) * a.max_blocks_per_seq);
   it.kbase = uni_ptr(static_cast<const char*>(a.k_cache) + int64_t(kvh) * kTileBytes);
@@ -532,9 +531,10 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
         sc[i] = row_reduce<G, 0>(s) * scale_log2;
       }
       if (tb + kBlock > cur.tok1 || tb < cur.lo) {   // the context ends, or the window starts, in this block
+        const uint32_t span = uint32_t(cur.tok1 - cur.lo);   // visible keys: lo .. tok1 - 1
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool dead = tb + 4 * i + tg >= cur.tok1 || tb + 4 * i + tg < cur.lo;
+          const bool dead = uint32_t(tb + 4 * i + tg - cur.lo) >= span;
           sc[i] = dead ? -__builtin_inff() : sc[i];
 #pragma unroll
           for (int w = 0; w < 4; ++w) vb[i][w] = dead ? 0u : vb[i][w];
@@ -647,7 +647,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
       const int src = head * kRot;   // a lane of row 0 whose head is `head`
       const float Lh = __shfl(lw, src);
       const int hq = cur.kvh * G + head;
-      if (cur.nparts == 1) {
+      if ((cur.parts >> 16) == 1) {
         const float inv = 1.f / Lh;
         if constexpr (kRun == 8) {
           u32x4_t o;
@@ -662,14 +662,14 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
                 (__bf16)(flat[x0 + x] * inv);
         }
       } else {
-        const int64_t slot = (int64_t(cur.b) * a.num_q_heads + hq) * a.max_parts + cur.part;
+        const int64_t slot = (int64_t(cur.b) * a.num_q_heads + hq) * a.max_parts + (cur.parts & 0xffff);
         float* dst = a.ws_o + slot * kD + r * 8 + e0;
 #pragma unroll
         for (int x = 0; x < kRun; ++x) dst[x] = flat[x0 + x];
       }
     }
-    if (cur.nparts > 1 && tg == 0 && (r & (kRot - 1)) == 0) {   // one lane per head
-      const int64_t slot = (int64_t(cur.b) * a.num_q_heads + cur.kvh * G + hr) * a.max_parts + cur.part;
+    if ((cur.parts >> 16) > 1 && tg == 0 && (r & (kRot - 1)) == 0) {   // one lane per head
+      const int64_t slot = (int64_t(cur.b) * a.num_q_heads + cur.kvh * G + hr) * a.max_parts + (cur.parts & 0xffff);
       a.ws_ml[2 * slot] = mw;
       a.ws_ml[2 * slot + 1] = lw;
     }
