@@ -88,8 +88,11 @@ typedef struct {
   int64_t total_q;             /* packed query rows, = cu_seqlens_q[B] */
   int32_t num_q_heads;         /* Hq, a multiple of num_kv_heads */
   int32_t num_kv_heads;        /* Hkv */
-  int32_t head_dim;            /* D: 64 or 128 */
-  int32_t block_size;          /* must be 16 */
+  int32_t head_dim;            /* D: 64, 128 or 256 */
+  int32_t block_size;          /* tokens per physical block: 16 (the pages' default), 8 or 32.
+                                  The fast kernels (single-row decode, 8-bit pools, MFMA
+                                  prefill) take D = 128 and block size 16; every other
+                                  shape runs on the generic split-K kernel. */
   int64_t num_blocks;          /* physical blocks in each pool */
   int32_t max_blocks_per_seq;  /* row length of block_tables */
   int32_t max_query_len;       /* host bound: >= every n_b */
@@ -119,12 +122,13 @@ typedef struct {
  *   k_cache[s/16][h][s%16][:] = k_new[i*kv_row_stride + h*D + :]
  *   v_cache[s/16][h][s%16][:] = v_new[i*kv_row_stride + h*D + :]
  * with s = slot_mapping[i].  Rows with a negative slot are skipped.  The
- * copy is bit-exact.  Slots must be unique and < num_blocks*16 (not checked
+ * copy is bit-exact.  Slots must be unique and < num_blocks*bs (not checked
  * here).  k_new/v_new: [num_tokens, Hkv, D] rows kv_row_stride elements
- * apart (>= Hkv*D).  k_cache, v_cache: [num_blocks, Hkv, 16, D] in place.
- * num_tokens == 0 is a no-op.  Errors: NULL pointers (when num_tokens > 0),
- * non-positive sizes, block_size != 16, D not in {64, 128}, unaligned
- * pointers or stride.
+ * apart (>= Hkv*D).  k_cache, v_cache: [num_blocks, Hkv, bs, D] in place,
+ * bs = block_size (the formulas above are written for 16; slot s names block
+ * s / bs, offset s % bs).  num_tokens == 0 is a no-op.  Errors: NULL pointers
+ * (when num_tokens > 0), non-positive sizes, block_size not in {8, 16, 32},
+ * D not in {64, 128, 256}, unaligned pointers or stride.
  */
 pa_status pa_cache_write(const void* k_new, const void* v_new, int64_t kv_row_stride,
                          void* k_cache, void* v_cache, const int64_t* slot_mapping,
@@ -185,11 +189,11 @@ pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, con
  * has one fp32 scale: a code c stands for decode(c) * scale.
  *
  * pa_cache_write_fp8 -- as pa_cache_write, but the new rows are bf16 and the
- * pools [num_blocks, Hkv, 16, D] hold one byte per element: each value x is
+ * pools [num_blocks, Hkv, bs, D] hold one byte per element: each value x is
  * stored as the code nearest to x / scale (the fp32 quotient rounded to
  * nearest), ties to the even code, magnitudes of 448 and beyond saturated to
- * 448, NaN stored as 0x7F.  D in {64, 128}; scales finite and > 0.  Errors
- * as pa_cache_write.
+ * 448, NaN stored as 0x7F.  D in {64, 128, 256}; scales finite and > 0.
+ * Errors as pa_cache_write.
  */
 pa_status pa_cache_write_fp8(const void* k_new, const void* v_new, int64_t kv_row_stride,
                              void* k_cache, void* v_cache, const int64_t* slot_mapping,
@@ -200,9 +204,9 @@ pa_status pa_cache_write_fp8(const void* k_new, const void* v_new, int64_t kv_ro
 /*
  * pa_attention_varlen_fp8 -- as pa_attention_varlen with 8-bit pools: the
  * attention runs over K = decode(k_cache) * k_scale and V = decode(v_cache) *
- * v_scale.  q and out are bf16 (p->dtype == PA_BF16); D = 128, Hq/Hkv in
- * {1, 2, 4, 8}, single-row (decode) requests only (max_query_len <= 1),
- * otherwise PA_ERR_UNSUPPORTED.  Scales finite and > 0.  The workspace is
+ * v_scale.  q and out are bf16 (p->dtype == PA_BF16); D = 128, block size
+ * 16, Hq/Hkv in {1, 2, 4, 8}, single-row (decode) requests only
+ * (max_query_len <= 1), otherwise PA_ERR_UNSUPPORTED.  Scales finite and > 0.  The workspace is
  * sized by pa_attention_workspace_size(p).
  */
 pa_status pa_attention_varlen_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -214,9 +218,9 @@ pa_status pa_attention_varlen_fp8(void* out, const void* q, const void* k_cache,
 /* Bits of the result word written by pa_validate_metadata. */
 #define PA_BAD_CU_SEQLENS   1   /* cu[0] != 0, cu decreasing, or cu[B] != total_q */
 #define PA_BAD_LENGTHS      2   /* n_b > L_b, L_b < 0, n_b > max_query_len or L_b > max_seq_len */
-#define PA_BAD_TABLE_WIDTH  4   /* ceil(L_b/16) > max_blocks_per_seq */
+#define PA_BAD_TABLE_WIDTH  4   /* ceil(L_b/block_size) > max_blocks_per_seq */
 #define PA_BAD_BLOCK_ID     8   /* a used block-table entry outside [0, num_blocks) */
-#define PA_BAD_SLOT_RANGE  16   /* a slot >= num_blocks*16 */
+#define PA_BAD_SLOT_RANGE  16   /* a slot >= num_blocks*block_size */
 #define PA_BAD_SLOT_DUP    32   /* two rows share a non-negative slot */
 
 /*
@@ -237,7 +241,7 @@ const char* pa_status_string(pa_status s);
 
 /* ABI version of this header: major*100 + minor (101: the 8-bit cache calls;
  * 102: block copies and the host block manager, pa_blocks.h; 200:
- * pa_attn_params.sliding_window). */
+ * pa_attn_params.sliding_window; 201: block sizes 8 and 32, D = 256). */
 int32_t pa_abi_version(void);
 
 #ifdef __cplusplus

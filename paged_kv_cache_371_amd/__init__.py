@@ -339,13 +339,14 @@ def attention_varlen(out, q, k_cache, v_cache, cu_seqlens, seq_lens, block_table
 
 
 def validate_metadata(cu_seqlens, seq_lens, block_tables, num_blocks: int, max_query_len: int,
-                      max_seq_len: int, slot_mapping=None, stream=None) -> int:
+                      max_seq_len: int, slot_mapping=None, stream=None, block_size: int = BLOCK_SIZE) -> int:
     """Run the device checks and return the PA_BAD_* bitmask (0 = all pass).  Synchronises."""
     torch = _torch()
     p = AttnParams()
     p.num_seqs = int(seq_lens.shape[0])
     p.total_q = int(cu_seqlens[-1].item()) if p.num_seqs else 0
     p.num_blocks = int(num_blocks)
+    p.block_size = int(block_size)
     p.max_blocks_per_seq = int(block_tables.shape[1])
     p.max_query_len = int(max_query_len)
     p.max_seq_len = int(max_seq_len)

@@ -1,10 +1,11 @@
-// Cache write: scatter this step's new K/V rows into the 16-token block pool.
+// Cache write: scatter this step's new K/V rows into the block pool (8, 16 or
+// 32 tokens per block; 16 is the pages' default).
 //
 // quant67, "PagedAttention 与 Continuous Batching" §3.3: every decode step
 // computes the new token's K/V and appends it to the block that holds its
 // position; the scheduler hands the kernel one slot per row (slot_mapping).
-// Slot s names block s / 16, offset s % 16.  The pool layout is
-// [num_blocks, Hkv, 16, D], so one (row, head) is a contiguous run of D
+// Slot s names block s / bs, offset s % bs.  The pool layout is
+// [num_blocks, Hkv, bs, D], so one (row, head) is a contiguous run of D
 // elements both in the source and in the pool.
 //
 // One thread moves one 16-byte chunk; consecutive threads cover consecutive
@@ -21,7 +22,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const u32x4_t* __restr
                                                           int64_t row_stride_chunks, u32x4_t* __restrict__ k_cache,
                                                           u32x4_t* __restrict__ v_cache,
                                                           const int64_t* __restrict__ slot_mapping,
-                                                          int64_t num_tokens, int32_t num_kv_heads) {
+                                                          int64_t num_tokens, int32_t num_kv_heads, int bs_log2) {
   const int64_t per_row = int64_t(num_kv_heads) * ChunksPerHead;
   const int64_t total = num_tokens * per_row;
   for (int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
@@ -32,9 +33,9 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const u32x4_t* __restr
     if (slot < 0) continue;
     const int64_t head = rem / ChunksPerHead;
     const int64_t c = rem - head * ChunksPerHead;
-    const int64_t blk = slot >> 4;
-    const int64_t off = slot & 15;
-    const int64_t dst = ((blk * num_kv_heads + head) * kBlock + off) * ChunksPerHead + c;
+    const int64_t blk = slot >> bs_log2;
+    const int64_t off = slot & ((int64_t(1) << bs_log2) - 1);
+    const int64_t dst = (((blk * num_kv_heads + head) << bs_log2) + off) * ChunksPerHead + c;
     const int64_t src = row * row_stride_chunks + rem;
     const u32x4_t kv = k_new[src];
     const u32x4_t vv = v_new[src];
@@ -79,8 +80,8 @@ __global__ __launch_bounds__(256) void cache_write_fp8_kernel(const u32x4_t* __r
                                                               int64_t row_stride_chunks, uint2* __restrict__ k_cache,
                                                               uint2* __restrict__ v_cache,
                                                               const int64_t* __restrict__ slot_mapping,
-                                                              int64_t num_tokens, int32_t num_kv_heads, float k_scale,
-                                                              float v_scale) {
+                                                              int64_t num_tokens, int32_t num_kv_heads, int bs_log2,
+                                                              float k_scale, float v_scale) {
   const int64_t per_row = int64_t(num_kv_heads) * ChunksPerHead;
   const int64_t total = num_tokens * per_row;
   auto quantise = [](const u32x4_t& w, float scale) {
@@ -100,9 +101,9 @@ __global__ __launch_bounds__(256) void cache_write_fp8_kernel(const u32x4_t* __r
     if (slot < 0) continue;
     const int64_t head = rem / ChunksPerHead;
     const int64_t c = rem - head * ChunksPerHead;
-    const int64_t blk = slot >> 4;
-    const int64_t off = slot & 15;
-    const int64_t dst = ((blk * num_kv_heads + head) * kBlock + off) * ChunksPerHead + c;
+    const int64_t blk = slot >> bs_log2;
+    const int64_t off = slot & ((int64_t(1) << bs_log2) - 1);
+    const int64_t dst = (((blk * num_kv_heads + head) << bs_log2) + off) * ChunksPerHead + c;
     const int64_t src = row * row_stride_chunks + rem;
     const u32x4_t kv = k_new[src];
     const u32x4_t vv = v_new[src];
@@ -111,9 +112,15 @@ __global__ __launch_bounds__(256) void cache_write_fp8_kernel(const u32x4_t* __r
   }
 }
 
+namespace {
+int log2_block(int32_t block_size) { return block_size == 8 ? 3 : block_size == 32 ? 5 : 4; }
+}  // namespace
+
 hipError_t launch_cache_write_fp8(const void* k_new, const void* v_new, int64_t kv_row_stride_bytes, void* k_cache,
                                   void* v_cache, const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
-                                  int32_t head_dim, float k_scale, float v_scale, hipStream_t stream) {
+                                  int32_t head_dim, int32_t block_size, float k_scale, float v_scale,
+                                  hipStream_t stream) {
+  const int lb = log2_block(block_size);
   const int64_t chunks_per_head = head_dim / 8;   // 16 source bytes, 8 cache bytes per chunk
   const int64_t total = num_tokens * num_kv_heads * chunks_per_head;
   const int threads = 256;
@@ -127,11 +134,15 @@ hipError_t launch_cache_write_fp8(const void* k_new, const void* v_new, int64_t 
   switch (chunks_per_head) {
     case 8:   // D=64
       hipLaunchKernelGGL(cache_write_fp8_kernel<8>, dim3(blocks), dim3(threads), 0, stream, kn, vn, stride_chunks, kc,
-                         vc, slot_mapping, num_tokens, num_kv_heads, k_scale, v_scale);
+                         vc, slot_mapping, num_tokens, num_kv_heads, lb, k_scale, v_scale);
       break;
     case 16:  // D=128
       hipLaunchKernelGGL(cache_write_fp8_kernel<16>, dim3(blocks), dim3(threads), 0, stream, kn, vn, stride_chunks,
-                         kc, vc, slot_mapping, num_tokens, num_kv_heads, k_scale, v_scale);
+                         kc, vc, slot_mapping, num_tokens, num_kv_heads, lb, k_scale, v_scale);
+      break;
+    case 32:  // D=256
+      hipLaunchKernelGGL(cache_write_fp8_kernel<32>, dim3(blocks), dim3(threads), 0, stream, kn, vn, stride_chunks,
+                         kc, vc, slot_mapping, num_tokens, num_kv_heads, lb, k_scale, v_scale);
       break;
     default:
       return hipErrorInvalidValue;
@@ -141,7 +152,8 @@ hipError_t launch_cache_write_fp8(const void* k_new, const void* v_new, int64_t 
 
 hipError_t launch_cache_write(const void* k_new, const void* v_new, int64_t kv_row_stride_bytes, void* k_cache,
                               void* v_cache, const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
-                              int32_t head_bytes, hipStream_t stream) {
+                              int32_t head_bytes, int32_t block_size, hipStream_t stream) {
+  const int lb = log2_block(block_size);
   const int64_t chunks_per_head = head_bytes / 16;
   const int64_t total = num_tokens * num_kv_heads * chunks_per_head;
   const int threads = 256;
@@ -155,15 +167,19 @@ hipError_t launch_cache_write(const void* k_new, const void* v_new, int64_t kv_r
   switch (chunks_per_head) {
     case 8:   // D=64 bf16
       hipLaunchKernelGGL(cache_write_kernel<8>, dim3(blocks), dim3(threads), 0, stream, kn, vn, stride_chunks, kc, vc,
-                         slot_mapping, num_tokens, num_kv_heads);
+                         slot_mapping, num_tokens, num_kv_heads, lb);
       break;
     case 16:  // D=128 bf16, D=64 fp32
       hipLaunchKernelGGL(cache_write_kernel<16>, dim3(blocks), dim3(threads), 0, stream, kn, vn, stride_chunks, kc,
-                         vc, slot_mapping, num_tokens, num_kv_heads);
+                         vc, slot_mapping, num_tokens, num_kv_heads, lb);
       break;
-    case 32:  // D=128 fp32
+    case 32:  // D=256 bf16, D=128 fp32
       hipLaunchKernelGGL(cache_write_kernel<32>, dim3(blocks), dim3(threads), 0, stream, kn, vn, stride_chunks, kc,
-                         vc, slot_mapping, num_tokens, num_kv_heads);
+                         vc, slot_mapping, num_tokens, num_kv_heads, lb);
+      break;
+    case 64:  // D=256 fp32
+      hipLaunchKernelGGL(cache_write_kernel<64>, dim3(blocks), dim3(threads), 0, stream, kn, vn, stride_chunks, kc,
+                         vc, slot_mapping, num_tokens, num_kv_heads, lb);
       break;
     default:
       return hipErrorInvalidValue;

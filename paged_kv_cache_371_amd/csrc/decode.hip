@@ -42,7 +42,7 @@ struct DecodeCfg {
   static constexpr int kVec = 16 / E::bytes;   // elements per 16-byte lane load
   static constexpr int kLpr = D / kVec;        // lanes per token row
   static constexpr int kTpl = kWave / kLpr;    // token rows per load instruction
-  static constexpr int kLoads = kBlock / kTpl; // loads per lane per block
+  static constexpr int kLoads = kBlock / kTpl; // loads per lane per 16-token unit
   static constexpr int kWaves = 4;
   static constexpr int kThreads = kWaves * kWave;
   static_assert(kLpr >= 1 && kLpr <= kWave && kTpl <= kBlock, "layout");
@@ -106,8 +106,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   using C = DecodeCfg<E, D, G>;
   constexpr int kVec = C::kVec, kLpr = C::kLpr, kTpl = C::kTpl, kLoads = C::kLoads;
   constexpr int kRowBytes = D * E::bytes;
-  constexpr int kTileBytes = kBlock * kRowBytes;
   constexpr float kNegInf = -__builtin_inff();
+  const int bs = a.block_size;   // tokens per physical block: 8, 16 or 32
 
   const int part = blockIdx.x;
   const int kvh = blockIdx.y;
@@ -132,9 +132,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks_per_seq;
   const char* kpool = static_cast<const char*>(a.k_cache);
   const char* vpool = static_cast<const char*>(a.v_cache);
-  const int64_t head_tile = int64_t(kvh) * kTileBytes;
-  const int64_t block_stride = int64_t(a.num_kv_heads) * kTileBytes;
+  const int64_t head_tile = int64_t(kvh) * bs * kRowBytes;
+  const int64_t block_stride = int64_t(a.num_kv_heads) * bs * kRowBytes;
   const int lane_off = tg * kRowBytes + dl * 16;
+  // Rows tok .. tok + kTpl - 1 of one load instruction lie in one physical
+  // block (tok is a multiple of kTpl, and kTpl <= 8 divides the block size).
+  // A load wholly past tok_end (the partition's end) is never used: it reads
+  // the load group holding the last used row instead, so every address stays
+  // inside a block the context owns and no unused table entry is read.
+  auto row_addr = [&](const char* pool, int tok, int tok_end) {
+    const int tc = min(tok, (tok_end - 1) / kTpl * kTpl);
+    const int64_t blk = table[tc / bs];
+    return pool + blk * block_stride + head_tile + int64_t(tc - (tc / bs) * bs) * kRowBytes + lane_off;
+  };
 
   for (int j = 0; j < n; ++j) {
     const int ctx = L - n + j + 1;  // keys lo .. ctx-1 are visible to row j
@@ -175,17 +185,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       u32x4_t cur[kLoads];
       int i = wave;
       if (i < nblk) {
-        const char* tile = kpool + int64_t(table[lb0 + i]) * block_stride + head_tile + lane_off;
 #pragma unroll
-        for (int l = 0; l < kLoads; ++l) cur[l] = *reinterpret_cast<const u32x4_t*>(tile + l * kTpl * kRowBytes);
+        for (int l = 0; l < kLoads; ++l)
+          cur[l] = *reinterpret_cast<const u32x4_t*>(row_addr(kpool, (lb0 + i) * kBlock + l * kTpl, tok1));
       }
       for (; i < nblk; i += C::kWaves) {
         u32x4_t nxt[kLoads];
         const int in = i + C::kWaves;
         if (in < nblk) {
-          const char* tile = kpool + int64_t(table[lb0 + in]) * block_stride + head_tile + lane_off;
 #pragma unroll
-          for (int l = 0; l < kLoads; ++l) nxt[l] = *reinterpret_cast<const u32x4_t*>(tile + l * kTpl * kRowBytes);
+          for (int l = 0; l < kLoads; ++l)
+            nxt[l] = *reinterpret_cast<const u32x4_t*>(row_addr(kpool, (lb0 + in) * kBlock + l * kTpl, tok1));
         }
 #pragma unroll
         for (int l = 0; l < kLoads; ++l) {
@@ -244,17 +254,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       u32x4_t cur[kLoads];
       int i = wave;
       if (i < nblk) {
-        const char* tile = vpool + int64_t(table[lb0 + i]) * block_stride + head_tile + lane_off;
 #pragma unroll
-        for (int l = 0; l < kLoads; ++l) cur[l] = *reinterpret_cast<const u32x4_t*>(tile + l * kTpl * kRowBytes);
+        for (int l = 0; l < kLoads; ++l)
+          cur[l] = *reinterpret_cast<const u32x4_t*>(row_addr(vpool, (lb0 + i) * kBlock + l * kTpl, tok1));
       }
       for (; i < nblk; i += C::kWaves) {
         u32x4_t nxt[kLoads];
         const int in = i + C::kWaves;
         if (in < nblk) {
-          const char* tile = vpool + int64_t(table[lb0 + in]) * block_stride + head_tile + lane_off;
 #pragma unroll
-          for (int l = 0; l < kLoads; ++l) nxt[l] = *reinterpret_cast<const u32x4_t*>(tile + l * kTpl * kRowBytes);
+          for (int l = 0; l < kLoads; ++l)
+            nxt[l] = *reinterpret_cast<const u32x4_t*>(row_addr(vpool, (lb0 + in) * kBlock + l * kTpl, tok1));
         }
         const bool tail = (tok0 + (i + 1) * kBlock) > tok1;   // block holds tokens past the context
 #pragma unroll
@@ -476,7 +486,7 @@ static hipError_t dispatch_group(int group, const DecodeArgs& a, int64_t partial
 
 bool decode_supported(int dtype, int head_dim, int group, int part_size) {
   if (dtype != 0 && dtype != 1) return false;
-  if (head_dim != 64 && head_dim != 128) return false;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return false;
   if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16) return false;
   if (part_size < 16 || part_size > 8192 || part_size % 16) return false;
   return decode_lds_bytes(dtype, head_dim, group, part_size) <= 64 * 1024;
@@ -491,9 +501,11 @@ hipError_t launch_merge(int dtype, int head_dim, const DecodeArgs& a, int64_t pa
   if (dtype == 1) {
     if (head_dim == 128) return launch_merge_t<BF16, 128>(a, partial_rows, stream);
     if (head_dim == 64) return launch_merge_t<BF16, 64>(a, partial_rows, stream);
+    if (head_dim == 256) return launch_merge_t<BF16, 256>(a, partial_rows, stream);
   } else if (dtype == 0) {
     if (head_dim == 128) return launch_merge_t<F32, 128>(a, partial_rows, stream);
     if (head_dim == 64) return launch_merge_t<F32, 64>(a, partial_rows, stream);
+    if (head_dim == 256) return launch_merge_t<F32, 256>(a, partial_rows, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -503,9 +515,11 @@ hipError_t launch_decode(int dtype, int head_dim, int group, const DecodeArgs& a
   if (dtype == 1) {
     if (head_dim == 128) return dispatch_group<BF16, 128>(group, a, partial_rows, stream);
     if (head_dim == 64) return dispatch_group<BF16, 64>(group, a, partial_rows, stream);
+    if (head_dim == 256) return dispatch_group<BF16, 256>(group, a, partial_rows, stream);
   } else if (dtype == 0) {
     if (head_dim == 128) return dispatch_group<F32, 128>(group, a, partial_rows, stream);
     if (head_dim == 64) return dispatch_group<F32, 64>(group, a, partial_rows, stream);
+    if (head_dim == 256) return dispatch_group<F32, 256>(group, a, partial_rows, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -21,6 +21,10 @@ inline int elem_bytes(pa_dtype d) { return d == PA_BF16 ? 2 : 4; }
 
 inline bool dtype_ok(pa_dtype d) { return d == PA_F32 || d == PA_BF16; }
 
+// Block sizes built: 16 (the pages' default; every kernel) and 8 and 32 (the
+// cache writes and the generic decode kernel).
+inline bool block_size_ok(int32_t bs) { return bs == 8 || bs == 16 || bs == 32; }
+
 // Tokens per split-K partition.  An explicit partition_size is used as given;
 // then a request's result depends only on the request itself (bitwise the
 // same in any batch).  The default (0) picks, for the fast decode kernel, the
@@ -32,7 +36,8 @@ inline int effective_partition(const pa_attn_params* p) {
   if (p->partition_size > 0) return p->partition_size;
   const int g = p->num_kv_heads > 0 ? p->num_q_heads / p->num_kv_heads : 0;
   const int dt = p->dtype == PA_BF16 ? 1 : 0;
-  if (!pa::decode_gqa_supported(dt, p->head_dim, g, pa::kDefaultPartition)) return pa::kDefaultPartition;
+  if (p->block_size != PA_BLOCK_SIZE || !pa::decode_gqa_supported(dt, p->head_dim, g, pa::kDefaultPartition))
+    return pa::kDefaultPartition;
   const int64_t want = int64_t(8) * pa::decode_gqa_workers(g);
   for (int ps : {2048, 1024}) {
     const int64_t items = int64_t(p->num_seqs) * p->num_kv_heads * ((int64_t(p->max_seq_len) + ps - 1) / ps);
@@ -71,8 +76,9 @@ inline Plan make_plan(const pa_attn_params* p) {
   const int g = p->num_q_heads / p->num_kv_heads;
   const bool multi = p->max_query_len > 1;
   const int ps = effective_partition(p);
-  pl.fast = pa::decode_gqa_supported(dt, p->head_dim, g, ps);
-  pl.prefill = dt == 1 && multi && pa::prefill_supported(p->head_dim, g);
+  const bool bs16 = p->block_size == PA_BLOCK_SIZE;
+  pl.fast = bs16 && pa::decode_gqa_supported(dt, p->head_dim, g, ps);
+  pl.prefill = bs16 && dt == 1 && multi && pa::prefill_supported(p->head_dim, g);
   pl.parts = max_parts(p);
   // Batches whose multi-row requests all fit 64 / G rows use 64-pair prefill
   // tiles; such short requests (one row tile) are split over context
@@ -135,14 +141,14 @@ inline int64_t merge_off(const pa_attn_params* p, const Plan& pl) {
 pa_status check_params(const pa_attn_params* p) {
   if (!p) return PA_ERR_NULL;
   if (!dtype_ok(p->dtype)) return PA_ERR_UNSUPPORTED;
-  if (p->block_size != PA_BLOCK_SIZE) return PA_ERR_UNSUPPORTED;
+  if (!block_size_ok(p->block_size)) return PA_ERR_UNSUPPORTED;
   if (p->num_seqs < 0 || p->total_q < 0 || p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->head_dim <= 0 ||
       p->num_blocks <= 0 || p->max_blocks_per_seq <= 0 || p->max_query_len < 0 || p->max_seq_len < 0)
     return PA_ERR_SHAPE;
   if (p->num_q_heads % p->num_kv_heads) return PA_ERR_SHAPE;
   if (p->num_seqs > 65535) return PA_ERR_SHAPE;
   if (p->max_query_len > p->max_seq_len) return PA_ERR_SHAPE;
-  if (int64_t(p->max_blocks_per_seq) * PA_BLOCK_SIZE < p->max_seq_len) return PA_ERR_SHAPE;
+  if (int64_t(p->max_blocks_per_seq) * p->block_size < p->max_seq_len) return PA_ERR_SHAPE;
   if (p->total_q > 0 && p->num_seqs == 0) return PA_ERR_SHAPE;
   const int64_t hd = int64_t(p->num_q_heads) * p->head_dim;
   if (p->q_row_stride < hd || p->o_row_stride < hd) return PA_ERR_SHAPE;
@@ -159,7 +165,7 @@ pa_status check_params(const pa_attn_params* p) {
 
 extern "C" {
 
-int32_t pa_abi_version(void) { return 200; }
+int32_t pa_abi_version(void) { return 201; }
 
 const char* pa_status_string(pa_status s) {
   switch (s) {
@@ -182,8 +188,8 @@ pa_status pa_cache_write(const void* k_new, const void* v_new, int64_t kv_row_st
                          const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
                          int32_t block_size, int64_t num_blocks, pa_dtype dtype, void* stream) {
   if (!dtype_ok(dtype)) return PA_ERR_UNSUPPORTED;
-  if (block_size != PA_BLOCK_SIZE) return PA_ERR_UNSUPPORTED;
-  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PA_ERR_UNSUPPORTED;
   if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
   if (kv_row_stride < int64_t(num_kv_heads) * head_dim) return PA_ERR_SHAPE;
   if (num_tokens == 0) return PA_OK;
@@ -193,7 +199,7 @@ pa_status pa_cache_write(const void* k_new, const void* v_new, int64_t kv_row_st
       (kv_row_stride * eb) % 16)
     return PA_ERR_ALIGN;
   hipError_t e = pa::launch_cache_write(k_new, v_new, kv_row_stride * eb, k_cache, v_cache, slot_mapping, num_tokens,
-                                        num_kv_heads, head_dim * eb, static_cast<hipStream_t>(stream));
+                                        num_kv_heads, head_dim * eb, block_size, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -224,7 +230,7 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
     if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !(k_scale > 0.f) || !(v_scale > 0.f))
       return PA_ERR_SHAPE;
     const int g8 = p->num_q_heads / p->num_kv_heads;
-    if (p->dtype != PA_BF16 || p->max_query_len > 1 ||
+    if (p->dtype != PA_BF16 || p->max_query_len > 1 || p->block_size != PA_BLOCK_SIZE ||
         !pa::decode_gqa_supported(1, p->head_dim, g8, effective_partition(p)))
       return PA_ERR_UNSUPPORTED;
   }
@@ -270,6 +276,7 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
   d.plan_capacity = int32_t(std::max<int64_t>(1, pl.fast ? decode_capacity(p, pl) : 1));
   d.merge_capacity = int32_t(merge_capacity(p, pl));
   d.sliding_window = p->sliding_window;
+  d.block_size = p->block_size;
 
   // Partials of a region: o [rows, Hq, parts, D] followed by (m, l) [rows, Hq, parts, 2].
   auto point_at = [&](float* region, int64_t rows) {
@@ -368,8 +375,8 @@ pa_status pa_cache_write_fp8(const void* k_new, const void* v_new, int64_t kv_ro
                              void* v_cache, const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
                              int32_t head_dim, int32_t block_size, int64_t num_blocks, float k_scale, float v_scale,
                              void* stream) {
-  if (block_size != PA_BLOCK_SIZE) return PA_ERR_UNSUPPORTED;
-  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PA_ERR_UNSUPPORTED;
   if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
   if (kv_row_stride < int64_t(num_kv_heads) * head_dim) return PA_ERR_SHAPE;
   if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !(k_scale > 0.f) || !(v_scale > 0.f)) return PA_ERR_SHAPE;
@@ -378,7 +385,8 @@ pa_status pa_cache_write_fp8(const void* k_new, const void* v_new, int64_t kv_ro
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) || (kv_row_stride * 2) % 16)
     return PA_ERR_ALIGN;
   hipError_t e = pa::launch_cache_write_fp8(k_new, v_new, kv_row_stride * 2, k_cache, v_cache, slot_mapping, num_tokens,
-                                            num_kv_heads, head_dim, k_scale, v_scale, static_cast<hipStream_t>(stream));
+                                            num_kv_heads, head_dim, block_size, k_scale, v_scale,
+                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -386,13 +394,14 @@ pa_status pa_validate_metadata(const int32_t* cu_seqlens_q, const int32_t* seq_l
                                const int64_t* slot_mapping, int64_t num_slots, const pa_attn_params* p,
                                int32_t* result, void* stream) {
   if (!p || !result) return PA_ERR_NULL;
+  if (!block_size_ok(p->block_size)) return PA_ERR_UNSUPPORTED;
   if (p->num_seqs < 0 || p->total_q < 0 || p->num_blocks <= 0 || p->max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
   if (p->num_seqs > 0 && (!cu_seqlens_q || !seq_lens || !block_tables)) return PA_ERR_NULL;
   if (!slot_mapping) num_slots = 0;
   if (num_slots < 0) return PA_ERR_SHAPE;
   hipError_t e = pa::launch_validate(cu_seqlens_q, seq_lens, block_tables, slot_mapping, num_slots, p->num_seqs,
                                      p->total_q, p->max_query_len, p->max_seq_len, p->max_blocks_per_seq,
-                                     p->num_blocks, result, static_cast<hipStream_t>(stream));
+                                     p->num_blocks, p->block_size, result, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -42,6 +42,7 @@ struct DecodeArgs {
   int32_t partial_by_seq;   // 1: partials indexed by request, else by packed row
   int32_t merge_capacity;   // entries the merge list has room for
   int32_t sliding_window;   // 0, or W > 0: a row sees only the last W positions up to its own
+  int32_t block_size;       // tokens per physical block (the generic kernel takes 8, 16 or 32)
 };
 
 // Requests a decode launch serves: all of them, only those with exactly one
@@ -81,11 +82,12 @@ struct PrefillArgs {
 
 hipError_t launch_cache_write(const void* k_new, const void* v_new, int64_t kv_row_stride_bytes, void* k_cache,
                               void* v_cache, const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
-                              int32_t head_bytes, hipStream_t stream);
+                              int32_t head_bytes, int32_t block_size, hipStream_t stream);
 // bf16 rows quantised to OCP FP8 E4M3 codes with per-tensor scales (D = 64 or 128).
 hipError_t launch_cache_write_fp8(const void* k_new, const void* v_new, int64_t kv_row_stride_bytes, void* k_cache,
                                   void* v_cache, const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
-                                  int32_t head_dim, float k_scale, float v_scale, hipStream_t stream);
+                                  int32_t head_dim, int32_t block_size, float k_scale, float v_scale,
+                                  hipStream_t stream);
 
 // dtype: 0 fp32, 1 bf16.  Returns hipErrorInvalidValue for shapes not built.
 hipError_t launch_decode(int dtype, int head_dim, int group, const DecodeArgs& a, int64_t partial_rows,
@@ -147,7 +149,7 @@ bool prefill_supported(int head_dim, int group);
 
 hipError_t launch_validate(const int32_t* cu, const int32_t* seq_lens, const int32_t* bt, const int64_t* slots,
                            int64_t num_slots, int32_t num_seqs, int64_t total_q, int32_t max_query_len,
-                           int32_t max_seq_len, int32_t max_blocks_per_seq, int64_t num_blocks, int32_t* result,
-                           hipStream_t stream);
+                           int32_t max_seq_len, int32_t max_blocks_per_seq, int64_t num_blocks, int32_t block_size,
+                           int32_t* result, hipStream_t stream);
 
 }  // namespace pa

@@ -60,12 +60,13 @@ class DeviceCase:
 
 
 def oracle_pools(c):
-    return oracle.oracle_cache_write(c.k_cache, c.v_cache, c.k_new, c.v_new, c.slot_mapping)
+    return oracle.oracle_cache_write(c.k_cache, c.v_cache, c.k_new, c.v_new, c.slot_mapping, c.block_size)
 
 
 def oracle_out(c, k_pool, v_pool, rows=None, sliding_window=0):
     return oracle.oracle_attention_varlen(c.q, k_pool, v_pool, c.cu_seqlens, c.seq_lens, c.block_tables, c.scale,
-                                          c.num_kv_heads, c.dtype, rows=rows, sliding_window=sliding_window)
+                                          c.num_kv_heads, c.dtype, c.block_size, rows=rows,
+                                          sliding_window=sliding_window)
 
 
 def run_and_compare(c, partition_size=0, rows=None, check_pool=True, sliding_window=0):

@@ -58,7 +58,7 @@ def test_struct_layout_matches_c(tmp_path):
 
 
 def test_status_strings_and_version(L):
-    assert L.pa_abi_version() == 200
+    assert L.pa_abi_version() == 201
     for code in range(0, -11, -1):
         s = L.pa_status_string(code).decode()
         assert s.startswith("PA_")
@@ -77,7 +77,8 @@ def _params(**over):
 
 
 @pytest.mark.parametrize("over,code", [
-    (dict(block_size=8), -3),
+    (dict(block_size=12), -3),
+    (dict(block_size=64), -3),
     (dict(head_dim=96), -3),
     (dict(dtype=7), -3),
     (dict(num_q_heads=6, num_kv_heads=4), -2),
@@ -134,7 +135,8 @@ def test_partition_size_query(L):
 def test_cache_write_host_errors(L):
     f = L.pa_cache_write
     assert f(16, 16, 1024, 16, 16, 16, 0, 8, 128, 16, 10, pa.PA_BF16, None) == 0       # no rows: no-op
-    assert f(16, 16, 1024, 16, 16, 16, 4, 8, 128, 8, 10, pa.PA_BF16, None) == -3       # block size
+    assert f(16, 16, 1024, 16, 16, 16, 4, 8, 128, 12, 10, pa.PA_BF16, None) == -3      # block size
+    assert f(16, 16, 1024, 16, 16, 16, 4, 8, 128, 64, 10, pa.PA_BF16, None) == -3
     assert f(16, 16, 1024, 16, 16, 16, 4, 8, 96, 16, 10, pa.PA_BF16, None) == -3       # head dim
     assert f(16, 16, 1000, 16, 16, 16, 4, 8, 128, 16, 10, pa.PA_BF16, None) == -2      # stride < Hkv*D
     assert f(None, 16, 1024, 16, 16, 16, 4, 8, 128, 16, 10, pa.PA_BF16, None) == -1
@@ -148,12 +150,14 @@ def test_fp8_host_errors(L):
     assert f(16, 16, 1024, 16, 16, 16, 4, 8, 128, 16, 10, 0.0, 1.0, None) == -2     # scale must be > 0
     assert f(16, 16, 1024, 16, 16, 16, 4, 8, 128, 16, 10, 1.0, float("inf"), None) == -2
     assert f(16, 16, 1024, 16, 16, 16, 4, 8, 96, 16, 10, 1.0, 1.0, None) == -3      # head dim
+    assert f(16, 16, 1024, 16, 16, 16, 4, 8, 128, 24, 10, 1.0, 1.0, None) == -3     # block size
     assert f(None, 16, 1024, 16, 16, 16, 4, 8, 128, 16, 10, 1.0, 1.0, None) == -1
     a = L.pa_attention_varlen_fp8
     p = _params()
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(p), 1.0, -1.0, None, 0, None) == -2
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(max_query_len=4)), 1.0, 1.0, None, 0, None) == -3
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(dtype=pa.PA_F32)), 1.0, 1.0, None, 0, None) == -3
+    assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(block_size=32)), 1.0, 1.0, None, 0, None) == -3
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(head_dim=64, q_row_stride=512, o_row_stride=512)),
              1.0, 1.0, None, 0, None) == -3
 

@@ -153,6 +153,8 @@ def build_case(
     poison: bool = True,
     threads: int | None = None,
     info: dict | None = None,
+    block_size: int = BLOCK_SIZE,
+    rescale_tables: bool = False,
 ) -> Case:
     """Lay out a batch: block tables over a shuffled pool, history, new rows.
 
@@ -163,7 +165,14 @@ def build_case(
     With ``poison`` every slot that holds no history token, the slots the
     cache write will fill, and the padding block are set to NaN.
     """
-    bs = BLOCK_SIZE
+    bs = int(block_size)
+    if rescale_tables and bs != BLOCK_SIZE:
+        # sizes given in 16-token blocks: keep the same token capacities
+        def tok16(nb):
+            return -(-int(nb) * BLOCK_SIZE // bs)
+        max_blocks_per_seq = tok16(max_blocks_per_seq) if max_blocks_per_seq is not None else None
+        num_blocks = tok16(num_blocks) if num_blocks is not None else None
+        share_groups = [(m, int(nsh) * BLOCK_SIZE // bs) for m, nsh in share_groups]
     q_lens = np.asarray(q_lens, dtype=np.int64)
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
     B = int(seq_lens.shape[0])
@@ -321,11 +330,15 @@ _CONFIGS = {
 CONFIG_NAMES = tuple(_CONFIGS)
 
 
-def make_config(name: str, seed: int = 0, *, poison: bool = True, threads: int | None = None) -> Case:
-    """Build one of the named workloads for ``seed``."""
+def make_config(name: str, seed: int = 0, *, poison: bool = True, threads: int | None = None,
+                block_size: int = BLOCK_SIZE) -> Case:
+    """Build one of the named workloads for ``seed`` (``block_size`` tokens per block;
+    table widths scale so every context still fits)."""
     if name not in _CONFIGS:
         raise KeyError(f"unknown config {name!r}; known: {CONFIG_NAMES}")
-    return _CONFIGS[name](seed, poison=poison, threads=threads)
+    if block_size == BLOCK_SIZE:
+        return _CONFIGS[name](seed, poison=poison, threads=threads)
+    return _CONFIGS[name](seed, poison=poison, threads=threads, block_size=block_size, rescale_tables=True)
 
 
 # ---------------------------------------------------------------------------
