@@ -19,7 +19,8 @@ the digest recorded there (null otherwise).  ``cpu_baseline`` times the fp64
 CPU oracle on a bounded sample of the same requests.
 
 ``--calibrate-copy`` runs only a 1 GiB device-to-device copy (the counters'
-calibration run).  ``--sliding-window W`` runs the workload with a sliding
+calibration run).  ``--block-size 8|32`` builds the same workload on 8- or
+32-token blocks (served by the generic split-K kernel).  ``--sliding-window W`` runs the workload with a sliding
 window of W tokens (KV bytes then count only the keys in some row's window).  ``--op copy_blocks`` times copy-on-write block copies
 (pa_copy_blocks) and ``--op swap_out`` / ``--op swap_in`` time swapping a
 sequence's blocks to and from pinned host memory (pa_swap_blocks); see
@@ -131,7 +132,7 @@ def algorithmic_bytes(c, kv_elem_bytes=None, window: int = 0) -> dict:
     kv = int((keys * c.num_kv_heads * c.head_dim * 2 * kvs).sum())
     q = int(n.sum() * c.num_q_heads * c.head_dim * s)
     o = q
-    tables = int(4 * (-(-keys // 16)).sum())
+    tables = int(4 * (-(-keys // int(c.block_size))).sum())
     meta = 4 * (2 * c.num_seqs + 1)
     cw = int(2 * (s + kvs) * (c.slot_mapping >= 0).sum() * c.num_kv_heads * c.head_dim + 8 * c.total_q)
     return dict(kv=kv, q=q, o=o, tables=tables, meta=meta, attention=kv + q + o + tables + meta, cache_write=cw)
@@ -449,6 +450,8 @@ def main() -> None:
     ap.add_argument("--op", choices=("attention", "copy_blocks", "swap_out", "swap_in"), default="attention")
     ap.add_argument("--sliding-window", type=int, default=0,
                     help="W > 0: each row sees only the last W positions up to its own")
+    ap.add_argument("--block-size", type=int, default=16, choices=(8, 16, 32),
+                    help="tokens per physical block (8 and 32 run on the generic split-K kernel)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this framework runs the path on one GPU; --gpus must be 1 "
@@ -469,7 +472,7 @@ def main() -> None:
     import paged_kv_cache_371_amd as pa
     from workloads import make_config
 
-    c = make_config(args.workload, args.seed, poison=False)
+    c = make_config(args.workload, args.seed, poison=False, block_size=args.block_size)
     fp8 = args.kv_dtype == "fp8"
     if fp8 and c.dtype != "bf16":
         raise SystemExit("8-bit pools need a bf16 workload")
@@ -547,13 +550,16 @@ def main() -> None:
         "kv_bytes_per_step": ab["kv"],
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa_attention_varlen call: plan_kernel + decode_gqa_kernel + merge_kernel"
-                      + (" + prefill_kernel" if c.max_query_len > 1 else ""),
+            "kernel": ("pa_attention_varlen call: decode_kernel (generic split-K) + merge_kernel"
+                       if c.block_size != 16 else
+                       "pa_attention_varlen call: plan_kernel + decode_gqa_kernel + merge_list_kernel"
+                       + (" + prefill_kernel" if c.max_query_len > 1 else "")),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(c.name + ("_fp8kv" if fp8 else "") + (f"_w{W}" if W else "")),
+            "traffic": measured_traffic(c.name + ("_fp8kv" if fp8 else "") + (f"_w{W}" if W else "")
+                                        + (f"_bs{c.block_size}" if c.block_size != 16 else "")),
             "algorithmic_bytes_per_launch": ab["attention"],
             "attention_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 3),
         },

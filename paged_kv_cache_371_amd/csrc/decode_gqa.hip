@@ -118,7 +118,7 @@ static_assert(kStaticRounds >= 1, "round 0 is static");
 constexpr int kQueue = 16;                         // LDS queue slots of claimed items per workgroup
 constexpr int kClaimBatch = PA_DECODE_CLAIM_BATCH; // items per claim
 #ifndef PA_DECODE_REQUEST_TILES
-#define PA_DECODE_REQUEST_TILES 12
+#define PA_DECODE_REQUEST_TILES 6
 #endif
 constexpr int kRequestTiles = PA_DECODE_REQUEST_TILES;   // tiles before an item's end its worker asks for the next
 static_assert(kClaimBatch <= kWavesPerGroup && kWavesPerGroup <= kQueue, "one queued item per worker at most");

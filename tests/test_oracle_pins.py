@@ -125,6 +125,27 @@ def test_cache_write_bruteforce_bits():
     assert not np.shares_memory(k2, k)
 
 
+@pytest.mark.parametrize("bs", [8, 32])
+def test_cache_write_bruteforce_bits_other_block_sizes(bs):
+    """Block sizes 8 and 32 (quant67 §3.7 lists 8/16/32): slot s lands in block
+    s // bs at offset s % bs, every other slot keeps its bits."""
+    rng = np.random.default_rng(bs)
+    NB, Hkv, D, N = 7, 2, 4, 30
+    k = rng.integers(0, 65535, (NB, Hkv, bs, D), dtype=np.uint16)
+    kn = rng.integers(0, 65535, (N, Hkv, D), dtype=np.uint16)
+    slots = rng.choice(NB * bs, N, replace=False).astype(np.int64)
+    slots[::5] = -1
+    k2, _ = oracle_cache_write(k, k.copy(), kn, kn, slots, block_size=bs)
+    expect = k.copy()
+    for i, s in enumerate(slots):
+        if s >= 0:
+            for h in range(Hkv):
+                expect[s // bs, h, s % bs] = kn[i, h]
+    assert (k2 == expect).all()
+    with pytest.raises(OracleError):
+        oracle_cache_write(k, k, kn[:1], kn[:1], np.array([NB * bs]), block_size=bs)
+
+
 def test_cache_write_rejects_duplicates_and_range():
     k = np.zeros((2, 1, 16, 4), np.float32)
     row = np.ones((2, 1, 4), np.float32)
@@ -148,6 +169,19 @@ def test_attention_matches_unpaged_bruteforce(Hq, Hkv, D):
     out, _ = _run_oracle(K, V, Q, SEQS_MIXED, Hkv, scale, rng)
     ref = _brute_all(K, V, Q, SEQS_MIXED, scale, Hq // Hkv)
     assert out.shape == ref.shape
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_attention_matches_unpaged_bruteforce_other_block_sizes(bs):
+    """The paged result at block sizes 8 and 32 equals attention over the
+    contiguous (never paged) K/V of each request."""
+    rng = np.random.default_rng(300 + bs)
+    Hq, Hkv, D = 4, 2, 8
+    K, V, Q = _tiny(rng, SEQS_MIXED, Hq, Hkv, D)
+    scale = np.float32(1 / math.sqrt(D))
+    out, _ = _run_oracle(K, V, Q, SEQS_MIXED, Hkv, scale, rng, block_size=bs)
+    ref = _brute_all(K, V, Q, SEQS_MIXED, scale, Hq // Hkv)
     np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
 
 
