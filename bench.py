@@ -20,7 +20,7 @@ CPU oracle on a bounded sample of the same requests.
 
 ``--calibrate-copy`` runs only a 1 GiB device-to-device copy (the counters'
 calibration run).  ``--block-size 8|32`` builds the same workload on 8- or
-32-token blocks (served by the generic split-K kernel).  ``--sliding-window W`` runs the workload with a sliding
+32-token blocks.  ``--sliding-window W`` runs the workload with a sliding
 window of W tokens (KV bytes then count only the keys in some row's window).  ``--op copy_blocks`` times copy-on-write block copies
 (pa_copy_blocks) and ``--op swap_out`` / ``--op swap_in`` time swapping a
 sequence's blocks to and from pinned host memory (pa_swap_blocks); see
@@ -136,6 +136,14 @@ def algorithmic_bytes(c, kv_elem_bytes=None, window: int = 0) -> dict:
     meta = 4 * (2 * c.num_seqs + 1)
     cw = int(2 * (s + kvs) * (c.slot_mapping >= 0).sum() * c.num_kv_heads * c.head_dim + 8 * c.total_q)
     return dict(kv=kv, q=q, o=o, tables=tables, meta=meta, attention=kv + q + o + tables + meta, cache_write=cw)
+
+
+def attention_kernels(c) -> str:
+    """The kernels one pa_attention_varlen call runs for this batch (bf16, D = 128, G <= 8)."""
+    k = "pa_attention_varlen call: plan_kernel + decode_gqa_kernel + merge_list_kernel"
+    if c.max_query_len > 1:
+        k += " + prefill_kernel" if c.block_size == 16 else " + decode_kernel (multi-row requests) + merge_kernel"
+    return k
 
 
 def attention_flops(c, window: int = 0) -> float:
@@ -451,7 +459,7 @@ def main() -> None:
     ap.add_argument("--sliding-window", type=int, default=0,
                     help="W > 0: each row sees only the last W positions up to its own")
     ap.add_argument("--block-size", type=int, default=16, choices=(8, 16, 32),
-                    help="tokens per physical block (8 and 32 run on the generic split-K kernel)")
+                    help="tokens per physical block")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this framework runs the path on one GPU; --gpus must be 1 "
@@ -550,10 +558,7 @@ def main() -> None:
         "kv_bytes_per_step": ab["kv"],
         "roofline": {
             "bound": "hbm",
-            "kernel": ("pa_attention_varlen call: decode_kernel (generic split-K) + merge_kernel"
-                       if c.block_size != 16 else
-                       "pa_attention_varlen call: plan_kernel + decode_gqa_kernel + merge_list_kernel"
-                       + (" + prefill_kernel" if c.max_query_len > 1 else "")),
+            "kernel": attention_kernels(c),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

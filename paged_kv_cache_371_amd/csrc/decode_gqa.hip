@@ -107,6 +107,28 @@ struct Kv {
     }
   }
 };
+// Paging of the kernel's 16-token tiles onto blocks of BS tokens (8, 16 or
+// 32).  A tile's key, kept in scalar registers, names where it lives: BS =
+// 16: the block id; BS = 32: block id * 2 + which half of the block; BS = 8:
+// the ids of its two blocks (low and high 32 bits), the high one -1 when the
+// second block holds no token below tok1 (it may not be owned by the
+// request, so neither its table entry past the owned ones nor its memory is
+// read).  Tile T covers tokens [16 T, 16 T + 16) and starts below tok1.
+template <int BS>
+__device__ __forceinline__ int64_t tile_key(const int32_t* table, int T, int tok1) {
+  if constexpr (BS == 16) {
+    return load_const_early(table, T);
+  } else if constexpr (BS == 32) {
+    return int64_t(load_const_early(table, T >> 1)) * 2 + (T & 1);
+  } else {
+    static_assert(BS == 8, "block sizes 8, 16, 32");
+    const bool second = T * kBlock + 8 < tok1;
+    const int first_id = load_const_early(table, 2 * T);
+    const int second_id = load_const_early(table, second ? 2 * T + 1 : 2 * T);
+    return int64_t(uint64_t(uint32_t(first_id)) | (uint64_t(uint32_t(second ? second_id : -1)) << 32));
+  }
+}
+
 #ifndef PA_DECODE_STATIC_ROUNDS
 #define PA_DECODE_STATIC_ROUNDS 1
 #endif
@@ -206,10 +228,10 @@ struct Item {
 // t % Hkv.  An index past the list gives a placeholder with in-range
 // addresses and no tiles.  Every field goes through readfirstlane, so the descriptors and
 // table loads built from it stay scalar.
-template <bool F8>
+template <bool F8, int BS>
 __device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t, int4 ent) {
   constexpr int kRing = Kv<F8>::kRing;
-  constexpr int kTileBytes = Kv<F8>::kTileBytes;
+  constexpr int kHeadBytes = BS * kD * (F8 ? 1 : 2);   // one KV head's rows of a block
   Item it;
   it.valid = t < total;
   int b = 0, part = 0, q0 = 0, L = 1, kvh = 0;
@@ -239,8 +261,8 @@ __device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t,
   it.nbr = uni(kRing * ((nb + kRing - 1) / kRing));
   it.valid = uni(it.valid);
   it.table = uni_ptr(a.block_tables + int64_t(b) * a.max_blocks_per_seq);
-  it.kbase = uni_ptr(static_cast<const char*>(a.k_cache) + int64_t(kvh) * kTileBytes);
-  it.vbase = uni_ptr(static_cast<const char*>(a.v_cache) + int64_t(kvh) * kTileBytes);
+  it.kbase = uni_ptr(static_cast<const char*>(a.k_cache) + int64_t(kvh) * kHeadBytes);
+  it.vbase = uni_ptr(static_cast<const char*>(a.v_cache) + int64_t(kvh) * kHeadBytes);
   return it;
 }
 
@@ -262,11 +284,12 @@ __device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t,
 // the last load group of an item already fetches the next item's first kRing
 // tiles and the HBM queue of the wave never drains at item boundaries.  The
 // physical block id of the slot issued next is fetched one issue ahead.
-template <int G, bool F8>
+template <int G, bool F8, int BS>
 __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kernel(DecodeArgs a) {
   using T = Kv<F8>;
   constexpr int kRing = T::kRing;
   constexpr int kTileBytes = T::kTileBytes;
+  constexpr int kHeadBytes = BS * kD * (F8 ? 1 : 2);   // one KV head's rows of a block
   using Raw = typename T::Raw;
   constexpr int K = log2_of<G>();
   constexpr int kRot = 16 / G;          // lanes between consecutive heads in a row
@@ -378,7 +401,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
   const int tg = lane >> 4;
   const int hr = r >> (4 - K);
   const int voff = tg * kD * (F8 ? 1 : 2) + r * T::kLoadBytes;   // token tg of the slot, d-slice r
-  const int64_t bstride = int64_t(a.num_kv_heads) * kTileBytes;
+  const int64_t bstride = int64_t(a.num_kv_heads) * kHeadBytes;   // bytes per physical block
   const float scale_log2 = a.scale_log2;
   // direction of row_ror within a row: the head of accumulator slot j is (hr + dir*j) mod G
   int dir = 1;
@@ -420,7 +443,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
     });
   };
 
-  Item cur = make_item<F8>(a, total, item_of_round(0), entry0);
+  Item cur = make_item<F8, BS>(a, total, item_of_round(0), entry0);
   if (!cur.valid) return;
 
   auto load_q = [&](u32x4_t(&qreg)[G], const Item& it) {   // q slices, lane-relative order h(r ^ M_j)
@@ -432,26 +455,48 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
       qreg[j] = *reinterpret_cast<const u32x4_t*>(qrow + hh * (kD * 2) + r * 16);
     });
   };
-  auto load_tile = [&](Raw(&kb)[4], Raw(&vb)[4], const char* kbase, const char* vbase, bool live,
-                       int64_t phys) {
-    const int nrec = live ? kTileBytes : 0;
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + phys * bstride), 0, nrec, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + phys * bstride), 0, nrec, kRsrcWord3);
+  // Load slot i reads rows 4i .. 4i+3 of the tile.  With BS = 8 slots 0, 1
+  // read the first block and slots 2, 3 the second (rows 0..7 of each).
+  auto load_tile = [&](Raw(&kb)[4], Raw(&vb)[4], const char* kbase, const char* vbase, bool live, int64_t key) {
+    if constexpr (BS == 8) {
+      const int64_t id0 = int64_t(uint32_t(uint64_t(key)));
+      const int id1 = int(uint32_t(uint64_t(key) >> 32));
+      const int nrec0 = live ? kHeadBytes : 0;
+      const int nrec1 = live && id1 >= 0 ? kHeadBytes : 0;
+      const int64_t off1 = int64_t(id1 >= 0 ? id1 : 0) * bstride;
+      const __amdgpu_buffer_rsrc_t rk0 =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + id0 * bstride), 0, nrec0, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rk1 =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + off1), 0, nrec1, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv0 =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + id0 * bstride), 0, nrec0, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv1 =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + off1), 0, nrec1, kRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kb[i] = T::load(rk, voff + i * (kTileBytes / 4));
+      for (int i = 0; i < 4; ++i) kb[i] = T::load(i < 2 ? rk0 : rk1, voff + (i & 1) * (kTileBytes / 4));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vb[i] = T::load(rv, voff + i * (kTileBytes / 4));
+      for (int i = 0; i < 4; ++i) vb[i] = T::load(i < 2 ? rv0 : rv1, voff + (i & 1) * (kTileBytes / 4));
+    } else {
+      const int64_t off = BS == 32 ? (key >> 1) * bstride + (key & 1) * kTileBytes : key * bstride;
+      const int nrec = live ? kTileBytes : 0;
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + off), 0, nrec, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + off), 0, nrec, kRsrcWord3);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kb[i] = T::load(rk, voff + i * (kTileBytes / 4));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vb[i] = T::load(rv, voff + i * (kTileBytes / 4));
+    }
   };
 
   u32x4_t qreg[G];
   Raw kr[kRing][4], vr[kRing][4];   // the ring: K and V of kRing tiles, as loaded
   load_q(qreg, cur);
-  int ph0[kRing];   // block ids of the first tiles, all requested before any is used
+  int64_t ph0[kRing];   // keys of the first tiles, all requested before any is used
   static_for<kRing>([&](auto S) {
     constexpr int st = decltype(S)::value;
-    ph0[st] = load_const_early(cur.table, cur.lb0 + min(st, cur.nb - 1));
+    ph0[st] = tile_key<BS>(cur.table, cur.lb0 + min(st, cur.nb - 1), cur.tok1);
   });
   __builtin_amdgcn_sched_barrier(0);
   static_for<kRing>([&](auto S) {
@@ -466,7 +511,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
     // second-to-last load group, just before its first block ids are needed,
     // so it is handed out as late as the tile stream allows.
     const bool dyn = i + 1 >= kStaticRounds;
-    Item nxt = make_item<F8>(a, total, total, make_int4(0, 0, 0, 1));
+    Item nxt = make_item<F8, BS>(a, total, total, make_int4(0, 0, 0, 1));
     uint32_t qt[kQDw];
     bool requested = false;
     auto get_next = [&]() {
@@ -475,11 +520,11 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
       int t;
       int4 e;
       take(t, e);
-      nxt = make_item<F8>(a, total, t, e);
+      nxt = make_item<F8, BS>(a, total, t, e);
       if (nxt.valid) fetch_q(nxt, qt);
     };
     if (!dyn) {
-      nxt = make_item<F8>(a, total, item_of_round(i + 1), static_entry(i + 1));
+      nxt = make_item<F8, BS>(a, total, item_of_round(i + 1), static_entry(i + 1));
       if (nxt.valid) fetch_q(nxt, qt);
     } else if (cur.nb <= 2 * kRing) {
       get_next();
@@ -502,9 +547,9 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
       const int32_t* tb = own ? cur.table : nxt.table;
       const int lb0 = own ? cur.lb0 : nxt.lb0;
       const int nbl = own ? cur.nb : nxt.nb;
-      return load_const_early(tb, lb0 + max(min(jj, nbl - 1), 0));
+      return tile_key<BS>(tb, lb0 + max(min(jj, nbl - 1), 0), own ? cur.tok1 : nxt.tok1);
     };
-    int64_t pf = slot_phys(kRing);   // block id of the next slot to issue
+    int64_t pf = slot_phys(kRing);   // tile key of the next slot to issue
     auto issue = [&](Raw(&kb)[4], Raw(&vb)[4], int j) {
       const int64_t phys = pf;
       pf = slot_phys(j + 1);
@@ -680,15 +725,16 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
 
 }  // namespace
 
-bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size) {
+bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size, int block_size) {
   return dtype == 1 && head_dim == kD && (group == 1 || group == 2 || group == 4 || group == 8) &&
-         part_size % kBlock == 0 && part_size / kBlock <= kMaxPartBuckets;
+         (block_size == 8 || block_size == 16 || block_size == 32) && part_size % kBlock == 0 &&
+         part_size / kBlock <= kMaxPartBuckets;
 }
 
 namespace {
 
 // Resident workgroups per device for kernel K: CUs x occupancy, queried once per device.
-template <int G, bool F8>
+template <int G, bool F8, int BS>
 int persistent_groups() {
   static std::atomic<int> cache[kMaxDevices];
   int dev = 0;
@@ -697,8 +743,8 @@ int persistent_groups() {
   if (v > 0) return v;
   int cus = 0, occ = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_gqa_kernel<G, F8>, 64 * (kWavesPerGroup + 1), 0) !=
-          hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_gqa_kernel<G, F8, BS>, 64 * (kWavesPerGroup + 1),
+                                                   0) != hipSuccess ||
       occ <= 0)
     occ = 1;
   v = cus * std::min(occ, 1);
@@ -706,13 +752,34 @@ int persistent_groups() {
   return v;
 }
 
-template <int G, bool F8>
+template <int G, bool F8, int BS>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   const int64_t upper = int64_t(a.num_seqs) * a.max_parts * a.num_kv_heads;
-  const int64_t grid = std::min<int64_t>(upper, persistent_groups<G, F8>());
+  const int64_t grid = std::min<int64_t>(upper, persistent_groups<G, F8, BS>());
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_gqa_kernel<G, F8>), dim3(grid), dim3(64 * (kWavesPerGroup + 1)), 0, stream, a);
+  hipLaunchKernelGGL((decode_gqa_kernel<G, F8, BS>), dim3(grid), dim3(64 * (kWavesPerGroup + 1)), 0, stream, a);
   return hipGetLastError();
+}
+
+template <bool F8, int BS>
+hipError_t launch_bs(int group, const DecodeArgs& a, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_g<1, F8, BS>(a, stream);
+    case 2: return launch_g<2, F8, BS>(a, stream);
+    case 4: return launch_g<4, F8, BS>(a, stream);
+    case 8: return launch_g<8, F8, BS>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool F8>
+hipError_t launch_f(int group, const DecodeArgs& a, hipStream_t stream) {
+  switch (a.block_size) {
+    case 8: return launch_bs<F8, 8>(group, a, stream);
+    case 16: return launch_bs<F8, 16>(group, a, stream);
+    case 32: return launch_bs<F8, 32>(group, a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -720,32 +787,18 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
 int decode_gqa_workers(int group) {
   int g = 0;
   switch (group) {
-    case 1: g = persistent_groups<1, false>(); break;
-    case 2: g = persistent_groups<2, false>(); break;
-    case 4: g = persistent_groups<4, false>(); break;
-    case 8: g = persistent_groups<8, false>(); break;
+    case 1: g = persistent_groups<1, false, 16>(); break;
+    case 2: g = persistent_groups<2, false, 16>(); break;
+    case 4: g = persistent_groups<4, false, 16>(); break;
+    case 8: g = persistent_groups<8, false, 16>(); break;
     default: g = 256;
   }
   return g * kWavesPerGroup;
 }
 
+// a.block_size selects the paging (8, 16 or 32 tokens per block).
 hipError_t launch_decode_gqa(int group, bool fp8_cache, const DecodeArgs& a, hipStream_t stream) {
-  if (fp8_cache) {
-    switch (group) {
-      case 1: return launch_g<1, true>(a, stream);
-      case 2: return launch_g<2, true>(a, stream);
-      case 4: return launch_g<4, true>(a, stream);
-      case 8: return launch_g<8, true>(a, stream);
-      default: return hipErrorInvalidValue;
-    }
-  }
-  switch (group) {
-    case 1: return launch_g<1, false>(a, stream);
-    case 2: return launch_g<2, false>(a, stream);
-    case 4: return launch_g<4, false>(a, stream);
-    case 8: return launch_g<8, false>(a, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return fp8_cache ? launch_f<true>(group, a, stream) : launch_f<false>(group, a, stream);
 }
 
 }  // namespace pa

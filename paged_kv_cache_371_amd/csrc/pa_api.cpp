@@ -36,7 +36,7 @@ inline int effective_partition(const pa_attn_params* p) {
   if (p->partition_size > 0) return p->partition_size;
   const int g = p->num_kv_heads > 0 ? p->num_q_heads / p->num_kv_heads : 0;
   const int dt = p->dtype == PA_BF16 ? 1 : 0;
-  if (p->block_size != PA_BLOCK_SIZE || !pa::decode_gqa_supported(dt, p->head_dim, g, pa::kDefaultPartition))
+  if (!pa::decode_gqa_supported(dt, p->head_dim, g, pa::kDefaultPartition, p->block_size))
     return pa::kDefaultPartition;
   const int64_t want = int64_t(8) * pa::decode_gqa_workers(g);
   for (int ps : {2048, 1024}) {
@@ -77,7 +77,7 @@ inline Plan make_plan(const pa_attn_params* p) {
   const bool multi = p->max_query_len > 1;
   const int ps = effective_partition(p);
   const bool bs16 = p->block_size == PA_BLOCK_SIZE;
-  pl.fast = bs16 && pa::decode_gqa_supported(dt, p->head_dim, g, ps);
+  pl.fast = pa::decode_gqa_supported(dt, p->head_dim, g, ps, p->block_size);
   pl.prefill = bs16 && dt == 1 && multi && pa::prefill_supported(p->head_dim, g);
   pl.parts = max_parts(p);
   // Batches whose multi-row requests all fit 64 / G rows use 64-pair prefill
@@ -165,7 +165,7 @@ pa_status check_params(const pa_attn_params* p) {
 
 extern "C" {
 
-int32_t pa_abi_version(void) { return 201; }
+int32_t pa_abi_version(void) { return 202; }
 
 const char* pa_status_string(pa_status s) {
   switch (s) {
@@ -230,8 +230,8 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
     if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !(k_scale > 0.f) || !(v_scale > 0.f))
       return PA_ERR_SHAPE;
     const int g8 = p->num_q_heads / p->num_kv_heads;
-    if (p->dtype != PA_BF16 || p->max_query_len > 1 || p->block_size != PA_BLOCK_SIZE ||
-        !pa::decode_gqa_supported(1, p->head_dim, g8, effective_partition(p)))
+    if (p->dtype != PA_BF16 || p->max_query_len > 1 ||
+        !pa::decode_gqa_supported(1, p->head_dim, g8, effective_partition(p), p->block_size))
       return PA_ERR_UNSUPPORTED;
   }
   if (p->num_seqs == 0 || p->total_q == 0) return PA_OK;

@@ -129,9 +129,10 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
 // Bytes of a plan buffer for these capacities (entries), rounded to 256.
 size_t plan_bytes(int64_t decode_capacity, int64_t prefill_capacity, int64_t merge_capacity);
 
-// Fast single-row decode (bf16, D = 128, G in {1, 2, 4, 8}); partials by request.
-// Reads its work list from a.plan (built by launch_plan first).
-bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size);
+// Fast single-row decode (bf16, D = 128, G in {1, 2, 4, 8}, blocks of 8, 16 or
+// 32 tokens); partials by request.  Reads its work list from a.plan (built by
+// launch_plan first).
+bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size, int block_size);
 // Waves of the persistent fast decode kernel on the current device.
 int decode_gqa_workers(int group);
 // fp8_cache: the pools hold OCP FP8 E4M3 codes (scales folded into scale_log2 and lsum_scale).

@@ -58,7 +58,7 @@ def test_struct_layout_matches_c(tmp_path):
 
 
 def test_status_strings_and_version(L):
-    assert L.pa_abi_version() == 201
+    assert L.pa_abi_version() == 202
     for code in range(0, -11, -1):
         s = L.pa_status_string(code).decode()
         assert s.startswith("PA_")
@@ -157,7 +157,10 @@ def test_fp8_host_errors(L):
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(p), 1.0, -1.0, None, 0, None) == -2
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(max_query_len=4)), 1.0, 1.0, None, 0, None) == -3
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(dtype=pa.PA_F32)), 1.0, 1.0, None, 0, None) == -3
-    assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(block_size=32)), 1.0, 1.0, None, 0, None) == -3
+    assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(block_size=12)), 1.0, 1.0, None, 0, None) == -3
+    # 8- and 32-token blocks are served (here the missing workspace is the error)
+    assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(block_size=32)), 1.0, 1.0, None, 0, None) == -5
+    assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(block_size=8, max_blocks_per_seq=8)), 1.0, 1.0, None, 0, None) == -5
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(head_dim=64, q_row_stride=512, o_row_stride=512)),
              1.0, 1.0, None, 0, None) == -3
 

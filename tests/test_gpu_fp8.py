@@ -65,7 +65,7 @@ class Fp8Case:
     def oracle_pools(self):
         kq = oracle.fp8_quantize_rows(self.c.k_new, self.k_scale)
         vq = oracle.fp8_quantize_rows(self.c.v_new, self.v_scale)
-        return oracle.oracle_cache_write(self.k_codes, self.v_codes, kq, vq, self.c.slot_mapping)
+        return oracle.oracle_cache_write(self.k_codes, self.v_codes, kq, vq, self.c.slot_mapping, self.c.block_size)
 
     def write_and_attend(self, partition_size=0):
         c = self.c
@@ -82,7 +82,7 @@ class Fp8Case:
             assert np.array_equal(self.k_cache.cpu().numpy(), kp), "K pool differs"
             assert np.array_equal(self.v_cache.cpu().numpy(), vp), "V pool differs"
         want = oracle.oracle_attention_varlen(c.q, kp, vp, c.cu_seqlens, c.seq_lens, c.block_tables, c.scale,
-                                              c.num_kv_heads, "bf16", rows=rows, kv_dtype="fp8",
+                                              c.num_kv_heads, "bf16", c.block_size, rows=rows, kv_dtype="fp8",
                                               k_scale=self.k_scale, v_scale=self.v_scale)
         got = oracle.widen(to_host(self.out, "bf16"), "bf16")
         if rows is not None:
@@ -123,6 +123,20 @@ def test_decode_fp8_edge_lengths(Hq, Hkv, psize):
     mx, mean, ok = fc.compare()
     say(f"fp8 {Hq}/{Hkv} psize {psize}: max {mx:.3g} mean {mean:.3g}")
     assert ok, (mx, mean)
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (64, 8)])
+def test_decode_fp8_block_sizes(bs, Hq, Hkv):
+    """8-bit pools on 8- and 32-token blocks (the fast kernel's paging of
+    16-token tiles onto two blocks, or onto half a block)."""
+    c = build_case(f"dec8bs{bs}_{Hq}", 35 + bs, "bf16", Hq, Hkv, 128, [1] * len(LENS), LENS, block_size=bs)
+    fc = Fp8Case(c, 9, 0.5, 0.25)
+    for psize in (0, 48):
+        fc.write_and_attend(psize)
+        mx, mean, ok = fc.compare(check_pool=psize == 0)
+        say(f"fp8 bs {bs} {Hq}/{Hkv} psize {psize}: max {mx:.3g} mean {mean:.3g}")
+        assert ok, (psize, mx, mean)
 
 
 def test_decode_fp8_deterministic_bitwise():

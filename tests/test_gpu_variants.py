@@ -1,8 +1,10 @@
 """GPU parity of the block-size and head-dim variants against the oracle.
 
 Block sizes 8 and 32 (the pages list 8, 16 and 32 as selectable, quant67
-§3.7) and D = 256 run on the cache writes and the generic split-K kernel; D
-= 64 and 128 at block size 16 were covered before.  Bars: cache writes
+§3.7) run on the cache writes, on the fast decode kernel for bf16 D = 128
+(its 16-token tiles paged onto two 8-token blocks or half a 32-token block)
+and on the generic split-K kernel otherwise; D = 256 runs on the generic
+kernel; D = 64 and 128 at block size 16 were covered before.  Bars: cache writes
 bit-exact over the whole pool, attention within the fp32 / bf16 bounds of
 the oracle, with poisoned (NaN) slots outside every context, ragged contexts
 ending anywhere in a block, multi-row requests, partitions that start inside
@@ -15,7 +17,7 @@ import torch
 
 import oracle
 import paged_kv_cache_371_amd as pa
-from tests.gpu_util import run_and_compare, say, to_dev
+from tests.gpu_util import oracle_out, oracle_pools, run_and_compare, say, to_dev, to_host
 from workloads import build_case
 
 pytestmark = pytest.mark.gpu
@@ -89,3 +91,70 @@ def test_validate_metadata_block_size():
     assert pa.validate_metadata(cu, sl, bt, c.num_blocks, 1, 20, block_size=8) == 0
     narrow = torch.from_numpy(np.ascontiguousarray(c.block_tables[:, :2])).to("cuda:0")
     assert pa.validate_metadata(cu, sl, narrow, c.num_blocks, 1, 20, block_size=8) & pa.BAD_TABLE_WIDTH
+
+
+FAST_LENS = [1, 7, 8, 9, 15, 16, 17, 24, 31, 32, 33, 47, 100, 700, 2049, 3000]
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (64, 8), (16, 4)])
+def test_fast_decode_block_size(bs, Hq, Hkv):
+    """The fast decode kernel on 8- and 32-token blocks: contexts ending at
+    every offset class of a block, partitions of 16 and 48 tokens that start
+    inside 32-token blocks, NaN in every slot and table entry past a context."""
+    c = build_case(f"fbs{bs}_{Hq}_{Hkv}", 110 + bs, "bf16", Hq, Hkv, 128, [1] * len(FAST_LENS), FAST_LENS,
+                   block_size=bs)
+    for psize in (0, 16, 48, 256):
+        mx, mean, ok, _ = run_and_compare(c, partition_size=psize, check_pool=psize == 0)
+        say(f"fast bs {bs} {Hq}/{Hkv} psize {psize}: max {mx:.3g} mean {mean:.3g}")
+        assert ok, (psize, mx, mean)
+
+
+def _repage(pool_bits, tables, lens, bs, num_blocks, rng):
+    """Lay each request's contiguous rows (read from a 16-token-block pool) out
+    again on bs-token blocks in shuffled order; unused slots hold bf16 NaN."""
+    Hkv, D = pool_bits[0].shape[1], pool_bits[0].shape[3]
+    perm = rng.permutation(num_blocks)
+    width = max(-(-int(L) // bs) for L in lens)
+    new_tables = np.full((len(lens), width), num_blocks - 1, np.int32)
+    pools = [np.full((num_blocks, Hkv, bs, D), 0x7FC0, np.uint16) for _ in pool_bits]
+    nxt = 0
+    for b, L in enumerate(lens):
+        for j in range(-(-int(L) // bs)):
+            new_tables[b, j] = perm[nxt]
+            nxt += 1
+        for t in range(int(L)):
+            src_blk, src_off = tables[b, t // 16], t % 16
+            for src, dst in zip(pool_bits, pools):
+                dst[new_tables[b, t // bs], :, t % bs, :] = src[src_blk, :, src_off, :]
+    return pools, new_tables
+
+
+def test_fast_decode_bitwise_across_block_sizes():
+    """The same logical K/V paged on 8-, 16- and 32-token blocks gives the same
+    bits: the fast kernel visits the same 16-token tiles in the same order,
+    only their addresses change."""
+    lens = FAST_LENS
+    c = build_case("xbs", 120, "bf16", 64, 8, 128, [1] * len(lens), lens)
+    k16, v16 = oracle_pools(c)
+    outs = {}
+    rng = np.random.default_rng(5)
+    for bs in (16, 8, 32):
+        if bs == 16:
+            kp, vp, tables = k16, v16, c.block_tables
+        else:
+            nb = sum(-(-int(L) // bs) for L in lens) + 3
+            (kp, vp), tables = _repage((k16, v16), c.block_tables, lens, bs, nb, rng)
+        out = torch.empty_like(to_dev(c.q, "bf16"))
+        pa.attention_varlen(out, to_dev(c.q, "bf16"), to_dev(kp, "bf16"), to_dev(vp, "bf16"),
+                            torch.from_numpy(c.cu_seqlens).to("cuda:0"), torch.from_numpy(c.seq_lens).to("cuda:0"),
+                            torch.from_numpy(np.ascontiguousarray(tables)).to("cuda:0"), float(c.scale), 1,
+                            c.max_seq_len, partition_size=256)
+        torch.cuda.synchronize()
+        outs[bs] = to_host(out, "bf16")
+    assert np.array_equal(outs[8], outs[16]) and np.array_equal(outs[32], outs[16])
+    got = oracle.widen(outs[16], "bf16")
+    want = oracle_out(c, k16, v16)
+    mx, mean, ok = oracle.compare_outputs(got, want, "bf16")
+    say(f"across block sizes: bitwise equal; max {mx:.3g} mean {mean:.3g}")
+    assert ok
