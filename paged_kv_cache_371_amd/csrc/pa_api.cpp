@@ -38,10 +38,14 @@ inline int effective_partition(const pa_attn_params* p) {
   const int dt = p->dtype == PA_BF16 ? 1 : 0;
   if (!pa::decode_gqa_supported(dt, p->head_dim, g, pa::kDefaultPartition, p->block_size))
     return pa::kDefaultPartition;
+  // Multi-row requests that the MFMA kernel does not take run on the generic
+  // kernel, whose per-workgroup scores of one partition must fit its LDS.
+  const bool generic_rows =
+      p->max_query_len > 1 && !(dt == 1 && pa::prefill_supported(p->head_dim, g, p->block_size));
   const int64_t want = int64_t(8) * pa::decode_gqa_workers(g);
   for (int ps : {2048, 1024}) {
     const int64_t items = int64_t(p->num_seqs) * p->num_kv_heads * ((int64_t(p->max_seq_len) + ps - 1) / ps);
-    if (items >= want) return ps;
+    if (items >= want && (!generic_rows || pa::decode_supported(dt, p->head_dim, g, ps))) return ps;
   }
   return pa::kDefaultPartition;
 }
@@ -76,9 +80,8 @@ inline Plan make_plan(const pa_attn_params* p) {
   const int g = p->num_q_heads / p->num_kv_heads;
   const bool multi = p->max_query_len > 1;
   const int ps = effective_partition(p);
-  const bool bs16 = p->block_size == PA_BLOCK_SIZE;
   pl.fast = pa::decode_gqa_supported(dt, p->head_dim, g, ps, p->block_size);
-  pl.prefill = bs16 && dt == 1 && multi && pa::prefill_supported(p->head_dim, g);
+  pl.prefill = dt == 1 && multi && pa::prefill_supported(p->head_dim, g, p->block_size);
   pl.parts = max_parts(p);
   // Batches whose multi-row requests all fit 64 / G rows use 64-pair prefill
   // tiles; such short requests (one row tile) are split over context
@@ -339,6 +342,7 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
     f.split_rows = pl.split_rows;
     f.tile_pairs = pl.tile_pairs;
     f.sliding_window = p->sliding_window;
+    f.block_size = p->block_size;
     f.part_size = d.part_size;
     f.max_parts = d.max_parts;
     f.ws_o = pl.split_rows ? region_a : nullptr;

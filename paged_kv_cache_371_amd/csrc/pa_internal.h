@@ -78,6 +78,7 @@ struct PrefillArgs {
   float* ws_ml;
   int32_t tile_pairs;   // (query row, head) pairs per work item: 128, or 64 for short requests
   int32_t sliding_window;
+  int32_t block_size;   // tokens per physical block: 8, 16 or 32
 };
 
 hipError_t launch_cache_write(const void* k_new, const void* v_new, int64_t kv_row_stride_bytes, void* k_cache,
@@ -144,9 +145,9 @@ hipError_t launch_merge(int dtype, int head_dim, const DecodeArgs& a, int64_t pa
 hipError_t launch_merge_list(const DecodeArgs& a, hipStream_t stream);
 size_t decode_lds_bytes(int dtype, int head_dim, int group, int part_size);
 
-// MFMA kernel for multi-row requests (bf16, D = 128, G in {1, 2, 4, 8}).
+// MFMA kernel for multi-row requests (bf16, D = 128, G in {1, 2, 4, 8}, blocks of 8, 16 or 32 tokens).
 hipError_t launch_prefill(int head_dim, int group, const PrefillArgs& a, hipStream_t stream);
-bool prefill_supported(int head_dim, int group);
+bool prefill_supported(int head_dim, int group, int block_size);
 
 hipError_t launch_validate(const int32_t* cu, const int32_t* seq_lens, const int32_t* bt, const int64_t* slots,
                            int64_t num_slots, int32_t num_seqs, int64_t total_q, int32_t max_query_len,

@@ -122,7 +122,7 @@ struct TileRegs {
 // W = 4 for chunked prefill; W = 2 for batches whose multi-row requests are
 // short (speculative-decode verification), where a 128-pair tile would be
 // mostly empty and the LDS reads per tile, not HBM, would set the pace.
-template <int G, int W>
+template <int G, int W, int BS>
 __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_kernel(PrefillArgs a) {
   using S = Shape<W>;
   constexpr int kMB = 2;                      // 16-column MFMA blocks per wave
@@ -149,7 +149,8 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
   // staging coordinates (see TileRegs)
   const int kkey = 4 * (lane >> 4), kchunk = lane & 15;
   const int vkey = 4 * (lane & 3), vchunk = lane >> 2;
-  const int64_t bstride = int64_t(hkv) * kTileBytes;
+  constexpr int kHeadBytes = BS * kD * 2;   // one KV head's rows of a physical block
+  const int64_t bstride = int64_t(hkv) * kHeadBytes;
   const float scale_log2 = a.scale_log2;
   const int32_t* entries = a.plan + kPlanHeaderInts + a.pref_off_ints;
 
@@ -187,10 +188,12 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
     const int kt0 = split ? max(part * part_tiles, kt_lo) : kt_lo;
     const int kt1 = split ? min(KT, (part + 1) * part_tiles) : KT;
     const int mbps = PA_KARG(max_blocks_per_seq);
-    const int nblk = max(1, min((L + kBlock - 1) / kBlock, mbps));
+    // the request's table entries, and its 16-key units (a wave's share of a key tile)
+    const int nblk = max(1, min((L + BS - 1) / BS, mbps));
+    const int nunits = max(1, min((L + kBlock - 1) / kBlock, (mbps * BS + kBlock - 1) / kBlock));
     const int32_t* table = PA_KARG(block_tables) + int64_t(b) * mbps;
-    const char* kbase = static_cast<const char*>(PA_KARG(k_cache)) + int64_t(kvh) * kTileBytes;
-    const char* vbase = static_cast<const char*>(PA_KARG(v_cache)) + int64_t(kvh) * kTileBytes;
+    const char* kbase = static_cast<const char*>(PA_KARG(k_cache)) + int64_t(kvh) * kHeadBytes;
+    const char* vbase = static_cast<const char*>(PA_KARG(v_cache)) + int64_t(kvh) * kHeadBytes;
 
     // ---- this lane's two pairs: m = wave*32 + mb*16 + lc ----------------------
     // visible keys of a pair: lolim .. lolim + span (one unsigned compare per score)
@@ -232,24 +235,75 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
     // load one tile ahead: a scalar load would share the LDS reads' wait
     // counter, and every tile's first LDS wait would then also wait out a
     // memory round trip for the table.
+    //
+    // Unit u (keys 16u .. 16u+15) lives in block u of 16 tokens, in half u & 1
+    // of block u / 2 of 32 tokens, or in blocks 2u and 2u+1 of 8 tokens (the
+    // second read only when it holds a key below L: past the context it may
+    // not be the request's).  The ids travel packed in one 64-bit value.
     const __amdgpu_buffer_rsrc_t rtab =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(table), 0, nblk * 4, kRsrcWord3);
-    auto phys_of = [&](int kt) -> uint32_t {
-      return __builtin_amdgcn_raw_buffer_load_b32(rtab, min(kt * W + wave, nblk - 1) * 4, 0, 0);
+    auto unit_of = [&](int kt) { return min(kt * W + wave, nunits - 1); };
+    auto phys_of = [&](int kt) -> uint64_t {
+      const int u = unit_of(kt);
+      if constexpr (BS == 16) {
+        return __builtin_amdgcn_raw_buffer_load_b32(rtab, u * 4, 0, 0);
+      } else if constexpr (BS == 32) {
+        return __builtin_amdgcn_raw_buffer_load_b32(rtab, (u >> 1) * 4, 0, 0);
+      } else {
+        const uint32_t first = __builtin_amdgcn_raw_buffer_load_b32(rtab, 2 * u * 4, 0, 0);
+        const uint32_t second =
+            __builtin_amdgcn_raw_buffer_load_b32(rtab, (u * kBlock + 8 < L ? 2 * u + 1 : 2 * u) * 4, 0, 0);
+        return uint64_t(first) | (uint64_t(second) << 32);
+      }
     };
-    auto fetch = [&](TileRegs& rg, int kt, uint32_t phys_v) {
-      const int64_t phys = uni(int(phys_v));
-      const int nrec = kt < kt1 ? kTileBytes : 0;
-      const __amdgpu_buffer_rsrc_t rk =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + phys * bstride), 0, nrec, kRsrcWord3);
-      const __amdgpu_buffer_rsrc_t rv =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + phys * bstride), 0, nrec, kRsrcWord3);
+    auto fetch = [&](TileRegs& rg, int kt, uint64_t phys_v) {
+      const int u = unit_of(kt);
+      const int64_t phys = uni(int(uint32_t(phys_v)));
+      if constexpr (BS == 8) {
+        // keys 0..7 of the unit from the first block, 8..15 from the second
+        const int64_t phys2 = uni(int(uint32_t(phys_v >> 32)));
+        const int nrec = kt < kt1 ? kHeadBytes : 0;
+        const int nrec2 = kt < kt1 && u * kBlock + 8 < L ? kHeadBytes : 0;
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + phys * bstride), 0, nrec, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + phys * bstride), 0, nrec, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rk2 =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + phys2 * bstride), 0, nrec2, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rv2 =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + phys2 * bstride), 0, nrec2, kRsrcWord3);
+        if (kkey < 8) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        rg.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, (kkey + kk) * (kD * 2) + kchunk * 16, 0, 0);
+          for (int kk = 0; kk < 4; ++kk)
+            rg.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, (kkey + kk) * (kD * 2) + kchunk * 16, 0, 0);
+        } else {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        rg.v[kk] = __builtin_amdgcn_raw_buffer_load_b128(rv, (vkey + kk) * (kD * 2) + vchunk * 16, 0, 0);
+          for (int kk = 0; kk < 4; ++kk)
+            rg.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk2, (kkey - 8 + kk) * (kD * 2) + kchunk * 16, 0, 0);
+        }
+        if (vkey < 8) {
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            rg.v[kk] = __builtin_amdgcn_raw_buffer_load_b128(rv, (vkey + kk) * (kD * 2) + vchunk * 16, 0, 0);
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            rg.v[kk] = __builtin_amdgcn_raw_buffer_load_b128(rv2, (vkey - 8 + kk) * (kD * 2) + vchunk * 16, 0, 0);
+        }
+      } else {
+        const int64_t off = BS == 32 ? phys * bstride + (u & 1) * kTileBytes : phys * bstride;
+        const int nrec = kt < kt1 ? kTileBytes : 0;
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + off), 0, nrec, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + off), 0, nrec, kRsrcWord3);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          rg.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, (kkey + kk) * (kD * 2) + kchunk * 16, 0, 0);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          rg.v[kk] = __builtin_amdgcn_raw_buffer_load_b128(rv, (vkey + kk) * (kD * 2) + vchunk * 16, 0, 0);
+      }
     };
     auto stage_write = [&](TileRegs& rg, int kt, int st) {
       char* ks = smem + st * kStageBytes;
@@ -369,7 +423,7 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
     // after.
     __syncthreads();   // the previous item is done with both stages
     TileRegs rg;
-    uint32_t ph_next = phys_of(kt0 + 1);
+    uint64_t ph_next = phys_of(kt0 + 1);
     fetch(rg, kt0, phys_of(kt0));
     stage_write(rg, kt0, 0);
     __syncthreads();
@@ -417,7 +471,7 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
   }
 }
 
-template <int G, int W>
+template <int G, int W, int BS>
 int prefill_groups() {
   static std::atomic<int> cache{0};
   int v = cache.load(std::memory_order_relaxed);
@@ -425,7 +479,7 @@ int prefill_groups() {
   int dev = 0, cus = 0, occ = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, prefill_kernel<G, W>, Shape<W>::kThreads,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, prefill_kernel<G, W, BS>, Shape<W>::kThreads,
                                                    Shape<W>::kLdsBytes) != hipSuccess ||
       occ <= 0)
     occ = 1;
@@ -434,38 +488,49 @@ int prefill_groups() {
   return v;
 }
 
-template <int G, int W>
+template <int G, int W, int BS>
 hipError_t launch_g(const PrefillArgs& a, hipStream_t stream) {
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<G, W>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<G, W, BS>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, Shape<W>::kLdsBytes);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((prefill_kernel<G, W>), dim3(prefill_groups<G, W>()), dim3(Shape<W>::kThreads),
+  hipLaunchKernelGGL((prefill_kernel<G, W, BS>), dim3(prefill_groups<G, W, BS>()), dim3(Shape<W>::kThreads),
                      Shape<W>::kLdsBytes, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool prefill_supported(int head_dim, int group) {
-  return head_dim == kD && (group == 1 || group == 2 || group == 4 || group == 8);
+bool prefill_supported(int head_dim, int group, int block_size) {
+  return head_dim == kD && (group == 1 || group == 2 || group == 4 || group == 8) &&
+         (block_size == 8 || block_size == 16 || block_size == 32);
+}
+
+template <int W, int BS>
+hipError_t launch_w(int group, const PrefillArgs& a, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_g<1, W, BS>(a, stream);
+    case 2: return launch_g<2, W, BS>(a, stream);
+    case 4: return launch_g<4, W, BS>(a, stream);
+    case 8: return launch_g<8, W, BS>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int W>
-hipError_t launch_w(int group, const PrefillArgs& a, hipStream_t stream) {
-  switch (group) {
-    case 1: return launch_g<1, W>(a, stream);
-    case 2: return launch_g<2, W>(a, stream);
-    case 4: return launch_g<4, W>(a, stream);
-    case 8: return launch_g<8, W>(a, stream);
+hipError_t launch_b(int group, const PrefillArgs& a, hipStream_t stream) {
+  switch (a.block_size) {
+    case 8: return launch_w<W, 8>(group, a, stream);
+    case 16: return launch_w<W, 16>(group, a, stream);
+    case 32: return launch_w<W, 32>(group, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_prefill(int head_dim, int group, const PrefillArgs& a, hipStream_t stream) {
   if (head_dim != kD) return hipErrorInvalidValue;
-  if (a.tile_pairs == 64) return launch_w<2>(group, a, stream);
-  if (a.tile_pairs == 128) return launch_w<4>(group, a, stream);
+  if (a.tile_pairs == 64) return launch_b<2>(group, a, stream);
+  if (a.tile_pairs == 128) return launch_b<4>(group, a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -3,8 +3,9 @@
 Block sizes 8 and 32 (the pages list 8, 16 and 32 as selectable, quant67
 §3.7) run on the cache writes, on the fast decode kernel for bf16 D = 128
 (its 16-token tiles paged onto two 8-token blocks or half a 32-token block)
-and on the generic split-K kernel otherwise; D = 256 runs on the generic
-kernel; D = 64 and 128 at block size 16 were covered before.  Bars: cache writes
+and on the MFMA prefill kernel for multi-row requests (the same 16-key units
+per wave), on the generic split-K kernel otherwise; D = 256 runs on the
+generic kernel; D = 64 and 128 at block size 16 were covered before.  Bars: cache writes
 bit-exact over the whole pool, attention within the fp32 / bf16 bounds of
 the oracle, with poisoned (NaN) slots outside every context, ragged contexts
 ending anywhere in a block, multi-row requests, partitions that start inside
@@ -130,15 +131,13 @@ def _repage(pool_bits, tables, lens, bs, num_blocks, rng):
     return pools, new_tables
 
 
-def test_fast_decode_bitwise_across_block_sizes():
-    """The same logical K/V paged on 8-, 16- and 32-token blocks gives the same
-    bits: the fast kernel visits the same 16-token tiles in the same order,
-    only their addresses change."""
-    lens = FAST_LENS
-    c = build_case("xbs", 120, "bf16", 64, 8, 128, [1] * len(lens), lens)
+def _bitwise_across_block_sizes(name, seed, n, lens, Hq, Hkv, psize):
+    """Outputs for the same logical K/V paged on 8-, 16- and 32-token blocks;
+    asserts they are bitwise equal and match the oracle."""
+    c = build_case(name, seed, "bf16", Hq, Hkv, 128, n, lens)
     k16, v16 = oracle_pools(c)
     outs = {}
-    rng = np.random.default_rng(5)
+    rng = np.random.default_rng(seed)
     for bs in (16, 8, 32):
         if bs == 16:
             kp, vp, tables = k16, v16, c.block_tables
@@ -148,13 +147,65 @@ def test_fast_decode_bitwise_across_block_sizes():
         out = torch.empty_like(to_dev(c.q, "bf16"))
         pa.attention_varlen(out, to_dev(c.q, "bf16"), to_dev(kp, "bf16"), to_dev(vp, "bf16"),
                             torch.from_numpy(c.cu_seqlens).to("cuda:0"), torch.from_numpy(c.seq_lens).to("cuda:0"),
-                            torch.from_numpy(np.ascontiguousarray(tables)).to("cuda:0"), float(c.scale), 1,
-                            c.max_seq_len, partition_size=256)
+                            torch.from_numpy(np.ascontiguousarray(tables)).to("cuda:0"), float(c.scale),
+                            c.max_query_len, c.max_seq_len, partition_size=psize)
         torch.cuda.synchronize()
         outs[bs] = to_host(out, "bf16")
     assert np.array_equal(outs[8], outs[16]) and np.array_equal(outs[32], outs[16])
-    got = oracle.widen(outs[16], "bf16")
-    want = oracle_out(c, k16, v16)
-    mx, mean, ok = oracle.compare_outputs(got, want, "bf16")
-    say(f"across block sizes: bitwise equal; max {mx:.3g} mean {mean:.3g}")
+    mx, mean, ok = oracle.compare_outputs(oracle.widen(outs[16], "bf16"), oracle_out(c, k16, v16), "bf16")
+    say(f"{name}: bitwise equal across block sizes; max {mx:.3g} mean {mean:.3g}")
     assert ok
+
+
+def test_fast_decode_bitwise_across_block_sizes():
+    """Single-row requests: the fast decode kernel visits the same 16-token
+    tiles in the same order at every block size, only their addresses change."""
+    _bitwise_across_block_sizes("xbs", 120, [1] * len(FAST_LENS), FAST_LENS, 64, 8, 256)
+
+
+@pytest.mark.parametrize("n,lens,Hq", [
+    ([200, 1, 37, 1, 129, 5], [1000, 700, 37, 33, 700, 9], 32),   # chunked prefill, 128-pair tiles
+    ([4, 1, 8, 2, 1, 3], [3000, 2049, 1500, 700, 5, 4100], 64),  # short requests split over partitions
+])
+def test_prefill_bitwise_across_block_sizes(n, lens, Hq):
+    """Multi-row requests: the MFMA kernel's waves each stage one 16-key unit
+    of every key tile, from one 16-token block, half a 32-token block or two
+    8-token blocks; the staged tiles and so the results are the same."""
+    _bitwise_across_block_sizes(f"xpbs{Hq}", 121, n, lens, Hq, 8, 0)
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 8), (64, 8)])
+def test_prefill_block_size(bs, Hq, Hkv):
+    """Chunked-prefill rows with decode rows on 8- and 32-token blocks: prior
+    contexts ending anywhere in a block, chunks of 1..200 rows, partitions of
+    64 tokens, NaN in every unowned slot and table entry."""
+    n = [200, 1, 37, 1, 5, 129, 1, 2]
+    L = [1000, 700, 37, 33, 9, 700, 3000, 17]
+    c = build_case(f"pbs{bs}_{Hq}_{Hkv}", 130 + bs, "bf16", Hq, Hkv, 128, n, L, block_size=bs)
+    for psize in (0, 64):
+        mx, mean, ok, _ = run_and_compare(c, partition_size=psize, check_pool=psize == 0)
+        say(f"prefill bs {bs} {Hq}/{Hkv} psize {psize}: max {mx:.3g} mean {mean:.3g}")
+        assert ok, (psize, mx, mean)
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_split_short_requests_block_size(bs):
+    """Speculative-verify shape (2..8 rows, G = 8): short requests split over
+    context partitions on the MFMA kernel, merged per row."""
+    n = [4, 1, 8, 2, 1, 3, 7]
+    L = [3000, 2049, 1500, 700, 5, 4100, 8]
+    c = build_case(f"sbs{bs}", 140 + bs, "bf16", 64, 8, 128, n, L, block_size=bs)
+    for psize in (0, 512):
+        mx, mean, ok, _ = run_and_compare(c, partition_size=psize, check_pool=psize == 0)
+        say(f"split bs {bs} psize {psize}: max {mx:.3g} mean {mean:.3g}")
+        assert ok, (psize, mx, mean)
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_prefill_window_block_size(bs):
+    c = build_case(f"pwbs{bs}", 150 + bs, "bf16", 32, 8, 128, [100, 1, 9], [900, 400, 60], block_size=bs)
+    for W in (17, 300):
+        mx, mean, ok, _ = run_and_compare(c, partition_size=64, sliding_window=W)
+        say(f"prefill window {W} bs {bs}: max {mx:.3g} mean {mean:.3g}")
+        assert ok, (W, mx, mean)
