@@ -8,9 +8,14 @@ requests, 64 query / 8 KV heads, D=128, bf16, log-normal contexts with median
 
 Prints one JSON line.  ``value`` is KV GB/s: the attention's algorithmic
 K/V bytes per step divided by the step time (inputs resident in HBM).
-``roofline`` reports one pa_attention_varlen call (the work-list kernel, the
-split-K decode kernel and the partition merge; the prefill kernel too when the
-batch has multi-row requests), timed with HIP events on the launch stream.
+``roofline`` reports one layer's attention: pa_attention_run over the
+step's work lists (the split-K decode kernel and the partition merge; the
+prefill kernel too when the batch has multi-row requests), timed with HIP
+events on the launch stream.  The work lists (pa_attention_plan, one small
+kernel) depend only on the request lengths and are built once per step for
+every layer; ``attention_plan_ms`` times that stage and
+``call_frac_incl_plan`` the whole pa_attention_varlen call, and the whole
+step behind ``value`` includes it.
 Its ``traffic`` is the HBM bytes per call that rocprofv3's FETCH_SIZE and
 WRITE_SIZE counters measured, scaled by the same counters' reading for a
 plain copy of known size; it is read from the committed counter summary
@@ -139,10 +144,10 @@ def algorithmic_bytes(c, kv_elem_bytes=None, window: int = 0) -> dict:
 
 
 def attention_kernels(c) -> str:
-    """The kernels one pa_attention_varlen call runs for this batch (bf16, D = 128, G <= 8)."""
-    k = "pa_attention_varlen call: plan_kernel + decode_gqa_kernel + merge_list_kernel"
+    """The kernels one layer's pa_attention_run launches for this batch (bf16, D = 128, G <= 8)."""
+    k = "pa_attention_run (one layer over the step's work lists): decode_gqa_kernel + merge_list_kernel"
     if c.max_query_len > 1:
-        k += " + prefill_kernel" if c.block_size == 16 else " + decode_kernel (multi-row requests) + merge_kernel"
+        k += " + prefill_kernel"
     return k
 
 
@@ -253,7 +258,7 @@ class _DeviceBatch:
         else:
             self.pa.cache_write(self.k_new, self.v_new, self.k_cache, self.v_cache, self.slots)
 
-    def attention(self, partition_size):
+    def attention(self, partition_size, stage="all"):
         c = self.c
         if self.ws is None:
             p = self.pa.make_params(self.q, self.k_cache, self.cu, self.tables, c.num_kv_heads, float(c.scale),
@@ -265,7 +270,7 @@ class _DeviceBatch:
                                  float(c.scale), c.max_query_len, c.max_seq_len, workspace=self.ws,
                                  partition_size=partition_size, sliding_window=self.window,
                                  k_scale=K_SCALE_FP8 if self.fp8 else None,
-                                 v_scale=V_SCALE_FP8 if self.fp8 else None)
+                                 v_scale=V_SCALE_FP8 if self.fp8 else None, stage=stage)
 
 
 def _timed_loop(torch, fn, steps, warmup, stream):
@@ -520,8 +525,26 @@ def main() -> None:
     attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     ms_per_step = wall * 1e3 / args.steps
 
+    # The two stages of the call on their own: the work lists (pa_attention_plan,
+    # built once per step from the request lengths and shared by every layer)
+    # and one layer's attention over them (pa_attention_run), each timed with
+    # HIP events on the launch stream.
+    def stage_ms(stage):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a_, b_ in evs:
+            a_.record(stream)
+            dc.attention(partition_size=args.partition_size, stage=stage)
+            b_.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a_.elapsed_time(b_) for a_, b_ in evs]))
+
+    plan_ms = stage_ms("plan")
+    run_ms = stage_ms("run")
+
     value = ab["kv"] / (ms_per_step * 1e-3) / 1e9
-    achieved = ab["attention"] / (attn_ms * 1e-3) / 1e9
+    achieved = ab["attention"] / (run_ms * 1e-3) / 1e9
+    call_gbs = ab["attention"] / (attn_ms * 1e-3) / 1e9
     result = {
         "metric": "paged-attn decode KV GB/s (% of HBM peak) and query tokens/s at 1 MI355X",
         "value": round(value, 2),
@@ -554,6 +577,8 @@ def main() -> None:
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "query_tokens_per_s": round(c.total_q / (ms_per_step * 1e-3), 1),
         "attention_ms": round(attn_ms, 5),
+        "attention_run_ms": round(run_ms, 5),
+        "attention_plan_ms": round(plan_ms, 5),
         "cache_write_ms": round(cw_ms, 5),
         "kv_bytes_per_step": ab["kv"],
         "roofline": {
@@ -563,6 +588,7 @@ def main() -> None:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "call_frac_incl_plan": round(call_gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(c.name + ("_fp8kv" if fp8 else "") + (f"_w{W}" if W else "")
                                         + (f"_bs{c.block_size}" if c.block_size != 16 else "")),
             "algorithmic_bytes_per_launch": ab["attention"],

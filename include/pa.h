@@ -183,6 +183,33 @@ pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, con
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_attention_plan / pa_attention_run -- pa_attention_varlen in two stages.
+ * [Q67] §3.3: the scheduler builds the step's metadata (cu_seqlens, seq_lens,
+ * block tables) once, and every layer's attention reads it.  The work lists
+ * the kernels deal out depend only on cu_seqlens_q, seq_lens and *p, so
+ * pa_attention_plan builds them once per step into the workspace and
+ * pa_attention_run computes one layer from them, as often as there are
+ * layers.  pa_attention_varlen(...) == pa_attention_plan(...) followed by
+ * pa_attention_run(...), bit for bit.
+ *
+ * Preconditions of pa_attention_run (not checked on the device): the
+ * workspace holds the lists of a pa_attention_plan (or pa_attention_varlen)
+ * enqueued earlier with the same *p and the same cu_seqlens_q / seq_lens
+ * contents, and nothing else wrote the workspace since; runs on one
+ * workspace are serialised (same stream, or ordered by events), since each
+ * run hands out the list's items from a counter in the workspace and leaves
+ * it re-armed for the next run.  Arguments, layouts and host-side errors are
+ * those of pa_attention_varlen; pa_attention_plan reads only cu_seqlens_q,
+ * seq_lens, *p and the workspace.
+ */
+pa_status pa_attention_plan(const int32_t* cu_seqlens_q, const int32_t* seq_lens, const pa_attn_params* p,
+                            void* workspace, size_t workspace_bytes, void* stream);
+pa_status pa_attention_run(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                           const int32_t* block_tables, const pa_attn_params* p,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * 8-bit KV cache (OCP FP8 E4M3).  [Q67] §8.8 and §10.3 name 8-bit KV caches
  * as the way to halve KV memory without fixing a format; the format taken is
  * OCP E4M3: 1 sign, 4 exponent (bias 7) and 3 mantissa bits, subnormals
@@ -215,6 +242,13 @@ pa_status pa_attention_varlen_fp8(void* out, const void* q, const void* k_cache,
                                   const int32_t* block_tables, const pa_attn_params* p,
                                   float k_scale, float v_scale, void* workspace,
                                   size_t workspace_bytes, void* stream);
+/* The run stage of pa_attention_varlen_fp8 over lists from pa_attention_plan
+ * (same contract as pa_attention_run). */
+pa_status pa_attention_run_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                               const int32_t* block_tables, const pa_attn_params* p,
+                               float k_scale, float v_scale, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* Bits of the result word written by pa_validate_metadata. */
 #define PA_BAD_CU_SEQLENS   1   /* cu[0] != 0, cu decreasing, or cu[B] != total_q */
@@ -243,7 +277,7 @@ const char* pa_status_string(pa_status s);
 /* ABI version of this header: major*100 + minor (101: the 8-bit cache calls;
  * 102: block copies and the host block manager, pa_blocks.h; 200:
  * pa_attn_params.sliding_window; 201: block sizes 8 and 32, D = 256; 202:
- * 8-bit pools at block sizes 8 and 32). */
+ * 8-bit pools at block sizes 8 and 32; 203: pa_attention_plan / pa_attention_run). */
 int32_t pa_abi_version(void);
 
 #ifdef __cplusplus

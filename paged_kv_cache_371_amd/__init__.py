@@ -63,6 +63,11 @@ _SIGNATURES = {
                                           ctypes.c_float, ctypes.c_void_p]),
     "pa_attention_varlen_fp8": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_float, ctypes.c_float,
                                                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "pa_attention_plan": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "pa_attention_run": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_void_p,
+                                                              ctypes.c_size_t, ctypes.c_void_p]),
+    "pa_attention_run_fp8": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_float, ctypes.c_float,
+                                                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "pa_copy_blocks": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
     "pa_swap_blocks": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [ctypes.c_void_p]),
@@ -282,11 +287,13 @@ def partition_size(params: AttnParams) -> int:
 
 def attention_varlen(out, q, k_cache, v_cache, cu_seqlens, seq_lens, block_tables, scale: float,
                      max_query_len: int, max_seq_len: int, workspace=None, partition_size: int = 0,
-                     stream=None, k_scale=None, v_scale=None, sliding_window: int = 0):
+                     stream=None, k_scale=None, v_scale=None, sliding_window: int = 0, stage: str = "all"):
     """Paged causal attention of packed rows; writes ``out`` [total_q, Hq, D] and returns it.
 
     ``sliding_window`` W > 0 limits each row to the last W positions up to
-    its own.
+    its own.  ``stage``: "all" (pa_attention_varlen), "plan" (only the work
+    lists, pa_attention_plan: once per step, into ``workspace``) or "run" (one
+    layer over the lists already in ``workspace``, pa_attention_run).
 
     ``workspace`` (a contiguous device tensor of any dtype, at least
     ``workspace_size`` bytes) is allocated here when not given.  uint8 pools
@@ -321,20 +328,29 @@ def attention_varlen(out, q, k_cache, v_cache, cu_seqlens, seq_lens, block_table
                     out=out, partition_size=partition_size, sliding_window=sliding_window)
     need = workspace_size(p)
     if workspace is None:
+        if stage != "all":
+            raise ValueError("the plan and run stages share a workspace: pass one")
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _dev(workspace, "workspace")
     if not workspace.is_contiguous():
         raise ValueError("workspace must be contiguous")
     ws_bytes = workspace.numel() * workspace.element_size()
+    if stage not in ("all", "plan", "run"):
+        raise ValueError("stage must be 'all', 'plan' or 'run'")
+    if stage == "plan":
+        _check(lib().pa_attention_plan(cu_seqlens.data_ptr(), seq_lens.data_ptr(), ctypes.byref(p),
+                                       workspace.data_ptr(), ws_bytes, _stream(stream)))
+        return out
     if fp8:
-        _check(lib().pa_attention_varlen_fp8(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                             cu_seqlens.data_ptr(), seq_lens.data_ptr(), block_tables.data_ptr(),
-                                             ctypes.byref(p), float(k_scale), float(v_scale), workspace.data_ptr(),
-                                             ws_bytes, _stream(stream)))
+        fn = lib().pa_attention_run_fp8 if stage == "run" else lib().pa_attention_varlen_fp8
+        _check(fn(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cu_seqlens.data_ptr(),
+                  seq_lens.data_ptr(), block_tables.data_ptr(), ctypes.byref(p), float(k_scale), float(v_scale),
+                  workspace.data_ptr(), ws_bytes, _stream(stream)))
     else:
-        _check(lib().pa_attention_varlen(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                         cu_seqlens.data_ptr(), seq_lens.data_ptr(), block_tables.data_ptr(),
-                                         ctypes.byref(p), workspace.data_ptr(), ws_bytes, _stream(stream)))
+        fn = lib().pa_attention_run if stage == "run" else lib().pa_attention_varlen
+        _check(fn(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cu_seqlens.data_ptr(),
+                  seq_lens.data_ptr(), block_tables.data_ptr(), ctypes.byref(p), workspace.data_ptr(), ws_bytes,
+                  _stream(stream)))
     return out
 
 

@@ -320,6 +320,20 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
   };
   const int4 entry0 = static_entry(0);
   int* claim_counter = a.plan + kPlanClaimInt;
+  // Every wave counts itself out when it leaves; the last one re-arms the
+  // claim counter (and this count) for the next run on the same work list.
+  // Each scheduler's claims have returned their values before it counts out,
+  // so when the count completes no claim of this launch is still in flight.
+  int* done_counter = a.plan + kPlanDoneInt;
+  auto count_out = [&]() {
+    if ((threadIdx.x & 63) == 0) {
+      const int waves = int(gridDim.x) * (kWavesPerGroup + 1);
+      if (__hip_atomic_fetch_add(done_counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == waves - 1) {
+        __hip_atomic_store(claim_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(done_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  };
 
   // Queue of claimed items with their list entries.  Slot s receives queue
   // index p = s, s + kQueue, ...; s_qfree[s] is the index it may receive next
@@ -369,6 +383,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
       }
       lds_store(&s_qend, pushed);
     }
+    count_out();
     return;
   }
   // A worker asks for its next claimed item (once per item, before taking it).
@@ -444,7 +459,10 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
   };
 
   Item cur = make_item<F8, BS>(a, total, item_of_round(0), entry0);
-  if (!cur.valid) return;
+  if (!cur.valid) {
+    count_out();
+    return;
+  }
 
   auto load_q = [&](u32x4_t(&qreg)[G], const Item& it) {   // q slices, lane-relative order h(r ^ M_j)
     const char* qrow =
@@ -721,6 +739,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
     if (!nxt.valid) break;
     cur = nxt;
   }
+  count_out();
 }
 
 }  // namespace

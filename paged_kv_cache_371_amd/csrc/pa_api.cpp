@@ -168,7 +168,7 @@ pa_status check_params(const pa_attn_params* p) {
 
 extern "C" {
 
-int32_t pa_abi_version(void) { return 202; }
+int32_t pa_abi_version(void) { return 203; }
 
 const char* pa_status_string(pa_status s) {
   switch (s) {
@@ -221,12 +221,16 @@ int32_t pa_attention_partition_size(const pa_attn_params* p) {
 
 namespace {
 
-// Both attention entry points.  fp8: the pools hold OCP FP8 E4M3 codes with
+// Stages of an attention call: the work lists (from the request lengths
+// only, shared by every layer of a step) and the attention proper.
+enum Stage : int { kPlanStage = 1, kRunStage = 2 };
+
+// Every attention entry point.  fp8: the pools hold OCP FP8 E4M3 codes with
 // per-tensor scales (decode rows only; q and out are bf16).
 pa_status attention_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* cu_seqlens_q, const int32_t* seq_lens, const int32_t* block_tables,
                          const pa_attn_params* p, void* workspace, size_t workspace_bytes, void* stream, bool fp8,
-                         float k_scale, float v_scale) {
+                         float k_scale, float v_scale, int stages) {
   pa_status st = check_params(p);
   if (st != PA_OK) return st;
   if (fp8) {
@@ -238,8 +242,11 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
       return PA_ERR_UNSUPPORTED;
   }
   if (p->num_seqs == 0 || p->total_q == 0) return PA_OK;
-  if (!out || !q || !k_cache || !v_cache || !cu_seqlens_q || !seq_lens || !block_tables) return PA_ERR_NULL;
-  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
+  if (!cu_seqlens_q || !seq_lens) return PA_ERR_NULL;
+  if (stages & kRunStage) {
+    if (!out || !q || !k_cache || !v_cache || !block_tables) return PA_ERR_NULL;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
+  }
   const size_t need = pa_attention_workspace_size(p);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
   if (workspace && !aligned16(workspace)) return PA_ERR_ALIGN;
@@ -288,7 +295,7 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
   };
 
   hipError_t e = hipSuccess;
-  if (pl.fast || pl.prefill) {
+  if ((stages & kPlanStage) && (pl.fast || pl.prefill)) {
     pa::PlanArgs pa_{};
     pa_.cu_seqlens = cu_seqlens_q;
     pa_.seq_lens = seq_lens;
@@ -307,6 +314,7 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
     pa_.sliding_window = p->sliding_window;
     if (pa::launch_plan(pa_, s) != hipSuccess) return PA_ERR_LAUNCH;
   }
+  if (!(stages & kRunStage)) return PA_OK;
   if (pl.fast) {
     point_at(region_a, pl.rows_a);
     d.row_mode = pa::kSingleRowOnly;
@@ -364,7 +372,20 @@ pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, con
                               const int32_t* cu_seqlens_q, const int32_t* seq_lens, const int32_t* block_tables,
                               const pa_attn_params* p, void* workspace, size_t workspace_bytes, void* stream) {
   return attention_impl(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, block_tables, p, workspace, workspace_bytes,
-                        stream, false, 1.f, 1.f);
+                        stream, false, 1.f, 1.f, kPlanStage | kRunStage);
+}
+
+pa_status pa_attention_plan(const int32_t* cu_seqlens_q, const int32_t* seq_lens, const pa_attn_params* p,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_impl(nullptr, nullptr, nullptr, nullptr, cu_seqlens_q, seq_lens, nullptr, p, workspace,
+                        workspace_bytes, stream, false, 1.f, 1.f, kPlanStage);
+}
+
+pa_status pa_attention_run(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* cu_seqlens_q, const int32_t* seq_lens, const int32_t* block_tables,
+                           const pa_attn_params* p, void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_impl(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, block_tables, p, workspace, workspace_bytes,
+                        stream, false, 1.f, 1.f, kRunStage);
 }
 
 pa_status pa_attention_varlen_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -372,7 +393,15 @@ pa_status pa_attention_varlen_fp8(void* out, const void* q, const void* k_cache,
                                   const pa_attn_params* p, float k_scale, float v_scale, void* workspace,
                                   size_t workspace_bytes, void* stream) {
   return attention_impl(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, block_tables, p, workspace, workspace_bytes,
-                        stream, true, k_scale, v_scale);
+                        stream, true, k_scale, v_scale, kPlanStage | kRunStage);
+}
+
+pa_status pa_attention_run_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* cu_seqlens_q, const int32_t* seq_lens, const int32_t* block_tables,
+                               const pa_attn_params* p, float k_scale, float v_scale, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return attention_impl(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, block_tables, p, workspace, workspace_bytes,
+                        stream, true, k_scale, v_scale, kRunStage);
 }
 
 pa_status pa_cache_write_fp8(const void* k_new, const void* v_new, int64_t kv_row_stride, void* k_cache,

@@ -100,7 +100,9 @@ constexpr int kPlanHeaderInts = 64;      // header words (256 bytes)
 constexpr int kPlanCountInt = 8;         // header slot: number of decode entries
 constexpr int kPlanPrefCountInt = 9;     // header slot: number of prefill entries
 constexpr int kPlanMergeCountInt = 10;   // header slot: number of merge entries (rows with > 1 partition)
-constexpr int kPlanClaimInt = 11;        // header slot: claim counter of the fast decode kernel (zeroed by the plan)
+constexpr int kPlanClaimInt = 11;        // header slot: claim counter of the fast decode kernel (zeroed by the plan,
+                                         // re-armed by the last wave of each decode launch)
+constexpr int kPlanDoneInt = 12;         // header slot: waves of the fast decode launch that have finished
 constexpr int kMaxPartBuckets = 512;     // partition_size / 16 of the fast kernel, at most
 constexpr int kPrefillPairs = 128;       // (query row, head) pairs per prefill work item (chunked prefill)
 constexpr int kPrefillPairsShort = 64;   // ... when every multi-row request fits 64 / G rows

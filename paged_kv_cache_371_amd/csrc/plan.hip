@@ -6,6 +6,8 @@
 //   [kPlanPrefCountInt]  number of prefill entries
 //   [kPlanMergeCountInt] number of merge entries
 //   [kPlanClaimInt]      claim counter of the decode kernel's dynamic rounds, zeroed here
+//   [kPlanDoneInt]       finished waves of a decode launch, zeroed here (each launch's last wave
+//                        zeroes both again, so one list serves any number of launches)
 //   [kPlanHeaderInts ..)                   decode entries, int4 (request, partition, query row, context length)
 //   [kPlanHeaderInts + pref_off ..)        prefill entries, int4 (request, row tile | partition << 16,
 //                                          first query row, query rows)
@@ -152,7 +154,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       if (p_end - p_lo > 1) merge[atomicAdd(&s_merge, 1)] = make_int4(b, q0, p_end - p_lo, b);
     });
     __syncthreads();
-    if (tid == 0) a.plan[kPlanClaimInt] = 0;
+    if (tid == 0) {
+      a.plan[kPlanClaimInt] = 0;
+      a.plan[kPlanDoneInt] = 0;
+    }
   }
 
   if (a.prefill) {

@@ -155,3 +155,65 @@ def test_work_lists_split_short_requests(partition_size, rows):
     sz = [size(e) for e in got_p]
     assert all(x >= y for x, y in zip(sz, sz[1:])), "prefill list not sorted by size"
     say(f"partition {P}: {npf} prefill entries, {nm} merge entries")
+
+
+def _layers(dc, n, fp8):
+    """n layers' worth of inputs on one batch's metadata: fresh q and pools."""
+    g = torch.Generator(device="cuda:0").manual_seed(7)
+    out = []
+    for _ in range(n):
+        q = torch.randn(dc.q.shape, generator=g, device="cuda:0").to(dc.q.dtype)
+        if fp8:
+            k = torch.randint(0, 0x77, dc.k_cache.shape, generator=g, device="cuda:0", dtype=torch.uint8)
+            v = torch.randint(0, 0x77, dc.k_cache.shape, generator=g, device="cuda:0", dtype=torch.uint8)
+        else:
+            k = torch.randn(dc.k_cache.shape, generator=g, device="cuda:0").to(dc.k_cache.dtype)
+            v = torch.randn(dc.k_cache.shape, generator=g, device="cuda:0").to(dc.k_cache.dtype)
+        out.append((q, k, v))
+    return out
+
+
+@pytest.mark.parametrize("kind", ["decode", "decode_fp8", "mixed", "split"])
+def test_plan_once_run_many_layers_bitwise(kind):
+    """pa_attention_plan once, then pa_attention_run for several layers (new q
+    and pools, same metadata): every layer equals pa_attention_varlen bit for
+    bit, and the decode kernel leaves its claim and exit counters re-armed."""
+    rng = np.random.default_rng(21)
+    if kind.startswith("decode"):
+        B, Hq, Hkv = 300, 64, 8
+        n = np.ones(B, np.int64)
+        L = rng.integers(1, 3000, B)
+    elif kind == "mixed":
+        B, Hq, Hkv = 60, 32, 8
+        n = np.ones(B, np.int64)
+        n[:4] = [300, 64, 17, 2]
+        L = np.maximum(n, rng.integers(1, 3000, B))
+    else:
+        B, Hq, Hkv = 80, 64, 8
+        n = rng.integers(1, 9, B)
+        L = np.maximum(n, rng.integers(1, 5000, B))
+    fp8 = kind == "decode_fp8"
+    c = build_case(f"pr_{kind}", 22, "bf16", Hq, Hkv, 128, n, L, poison=False)
+    dc = DeviceCase(c)
+    kw = dict(k_scale=0.5, v_scale=0.25) if fp8 else {}
+    p = pa.make_params(dc.q, dc.k_cache, dc.cu, dc.tables, Hkv, float(c.scale), c.max_query_len, c.max_seq_len,
+                       out=dc.out)
+    ws = torch.empty(pa.workspace_size(p), dtype=torch.uint8, device="cuda:0")
+    layers = _layers(dc, 3, fp8)
+    want = []
+    for q, k, v in layers:
+        o = torch.empty_like(q)
+        pa.attention_varlen(o, q, k, v, dc.cu, dc.seq_lens, dc.tables, float(c.scale), c.max_query_len,
+                            c.max_seq_len, **kw)
+        want.append(o)
+    pa.attention_varlen(dc.out, dc.q, layers[0][1], layers[0][2], dc.cu, dc.seq_lens, dc.tables, float(c.scale),
+                        c.max_query_len, c.max_seq_len, workspace=ws, stage="plan", **kw)
+    for (q, k, v), w in zip(layers, want):
+        o = torch.empty_like(q)
+        pa.attention_varlen(o, q, k, v, dc.cu, dc.seq_lens, dc.tables, float(c.scale), c.max_query_len,
+                            c.max_seq_len, workspace=ws, stage="run", **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), w.view(torch.int16))
+    hdr = ws[:64 * 4].view(torch.int32).cpu().numpy()
+    say(f"{kind}: decode entries {hdr[8]}, prefill entries {hdr[9]}, counters {hdr[11]} {hdr[12]}")
+    assert hdr[11] == 0 and hdr[12] == 0
