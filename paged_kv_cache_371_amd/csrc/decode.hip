@@ -376,7 +376,7 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a) {
 }
 
 // Merge of the partials of the fast decode kernel and of split short prefill
-// requests (bf16, D = 128): only the rows on the work list's merge list, one
+// requests (bf16, D = 64 or 128): only the rows on the work list's merge list, one
 // wave per (row, query head); an entry names the row, its partition count and
 // the partial row its partials were written under.
 // The list count and the wave's entry are read together; then partitions are
@@ -384,8 +384,9 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a) {
 // output slices (vector loads) issued at once, and folded into a running
 // log-sum-exp.  A request with up to kChunk partitions costs two memory round
 // trips.  Partitions are combined in order, so the result is deterministic.
+template <int D>
 __global__ __launch_bounds__(256) void merge_list_kernel(DecodeArgs a) {
-  constexpr int D = 128;
+  constexpr int kPer = D / 64;   // d values per lane: 1 or 2
   constexpr int kChunk = 8;
   const int4* list = reinterpret_cast<const int4*>(a.plan + kPlanHeaderInts + a.merge_off_ints);
   const int lane = threadIdx.x & 63;
@@ -399,20 +400,26 @@ __global__ __launch_bounds__(256) void merge_list_kernel(DecodeArgs a) {
     if (e >= load_const(a.plan, kPlanMergeCountInt)) break;
     const int64_t base = (int64_t(prow) * a.num_q_heads + h) * a.max_parts;
     const int32_t* ml = reinterpret_cast<const int32_t*>(a.ws_ml + 2 * base);
-    const float2* po = reinterpret_cast<const float2*>(a.ws_o + base * D) + lane;
-    float M = -__builtin_inff(), denom = 0.f, ox = 0.f, oy = 0.f;
+    const float* po = a.ws_o + base * D + kPer * lane;
+    float M = -__builtin_inff(), denom = 0.f, acc[kPer] = {};
     for (int p0 = 0; p0 < nparts; p0 += kChunk) {
-      float m[kChunk], l[kChunk];
-      float2 o[kChunk];
+      float m[kChunk], l[kChunk], o[kChunk][kPer];
 #pragma unroll
       for (int j = 0; j < kChunk; ++j) {
         m[j] = -__builtin_inff();
         l[j] = 0.f;
-        o[j] = make_float2(0.f, 0.f);
+#pragma unroll
+        for (int x = 0; x < kPer; ++x) o[j][x] = 0.f;
         if (p0 + j < nparts) {
           m[j] = __builtin_bit_cast(float, load_const(ml, 2 * (p0 + j)));
           l[j] = __builtin_bit_cast(float, load_const(ml, 2 * (p0 + j) + 1));
-          o[j] = po[int64_t(p0 + j) * (D / 2)];
+          if constexpr (kPer == 2) {
+            const float2 v = *reinterpret_cast<const float2*>(po + int64_t(p0 + j) * D);
+            o[j][0] = v.x;
+            o[j][1] = v.y;
+          } else {
+            o[j][0] = po[int64_t(p0 + j) * D];
+          }
         }
       }
       float Mn = M;
@@ -420,30 +427,40 @@ __global__ __launch_bounds__(256) void merge_list_kernel(DecodeArgs a) {
       for (int j = 0; j < kChunk; ++j) Mn = fmaxf(Mn, m[j]);
       const float c = fast_exp2(M - Mn);   // 0 for the first chunk
       denom *= c;
-      ox *= c;
-      oy *= c;
+#pragma unroll
+      for (int x = 0; x < kPer; ++x) acc[x] *= c;
       M = Mn;
 #pragma unroll
       for (int j = 0; j < kChunk; ++j) {
         if (p0 + j < nparts) {
           const float w = fast_exp2(m[j] - M);
           denom = fmaf(w, l[j], denom);
-          ox = fmaf(w, o[j].x, ox);
-          oy = fmaf(w, o[j].y, oy);
+#pragma unroll
+          for (int x = 0; x < kPer; ++x) acc[x] = fmaf(w, o[j][x], acc[x]);
         }
       }
     }
     const float inv = 1.f / denom;
-    reinterpret_cast<uint32_t*>(static_cast<__bf16*>(a.out) + int64_t(q0) * a.o_row_stride + int64_t(h) * D)[lane] =
-        pack_bf16x2(ox * inv, oy * inv);
+    __bf16* orow = static_cast<__bf16*>(a.out) + int64_t(q0) * a.o_row_stride + int64_t(h) * D;
+    if constexpr (kPer == 2) {
+      reinterpret_cast<uint32_t*>(orow)[lane] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    } else {
+      orow[lane] = (__bf16)(acc[0] * inv);
+    }
   }
 }
 
-hipError_t launch_merge_list(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_merge_list(int head_dim, const DecodeArgs& a, hipStream_t stream) {
   const int64_t waves = int64_t(a.merge_capacity) * a.num_q_heads;
   const int64_t grid = std::min<int64_t>((waves + 3) / 4, 1024);
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_list_kernel, dim3(grid), dim3(256), 0, stream, a);
+  if (head_dim == 128) {
+    hipLaunchKernelGGL(merge_list_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
+  } else if (head_dim == 64) {
+    hipLaunchKernelGGL(merge_list_kernel<64>, dim3(grid), dim3(256), 0, stream, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -1,4 +1,4 @@
-// Split-K paged attention for single-row (decode) requests, bf16, D = 128.
+// Split-K paged attention for single-row (decode) requests, bf16, D = 64 or 128.
 //
 // quant67, "PagedAttention 与 Continuous Batching" §3.6: the kernel walks the
 // request's block table, loads each physical block's K/V and folds it into an
@@ -13,10 +13,11 @@
 // the first round is dealt statically, the rest is claimed at run time (see
 // below).
 //
-// Lane layout for one 16-token tile of one KV head (16 x 256 B, contiguous):
-// lane l = 16*tg + r loads 16 B at token 4*i + tg, d-slice [8r, 8r+8), for
-// load slots i = 0..3.  Every load instruction reads 1 KiB of consecutive
-// memory.  Loads are raw buffer loads whose descriptor spans exactly one tile;
+// Lane layout for one 16-token tile of one KV head (16 rows of D elements,
+// contiguous): lane l = 16*tg + r loads the E = D/16 elements of d-slice
+// [E r, E r + E) of token 4*i + tg, for load slots i = 0..3 (16 B per lane at
+// D = 128, 8 B at D = 64).  Every load instruction reads 64 E elements of
+// consecutive memory.  Loads are raw buffer loads whose descriptor spans exactly one tile;
 // a tile past the wave's range gets a zero-sized descriptor, so the pipeline
 // issues a fixed number of loads per step without touching memory for it.
 //
@@ -61,7 +62,6 @@
 namespace pa {
 namespace {
 
-constexpr int kD = 128;
 constexpr int kWavesPerGroup = 4;
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
 constexpr float kRescaleThreshold = 8.f;      // log2 units
@@ -80,30 +80,41 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 // and the output normalisation.
 //
 // Tiles in flight per wave (kRing): one workgroup per CU (one worker wave per
-// SIMD), so registers go to a deep ring; an 8-bit tile is half the bytes, so
-// its ring is twice as deep for the same bytes in flight.
-template <bool F8>
+// SIMD), so registers go to a deep ring; an 8-bit tile, or a tile of D = 64,
+// is half the bytes, so its ring is twice as deep for the same bytes in flight.
+template <bool F8, int D>
 struct Kv {
-  static constexpr int kTileBytes = kBlock * kD * (F8 ? 1 : 2);   // one (block, KV head) tile
-  static constexpr int kLoadBytes = F8 ? 8 : 16;                    // per lane and load slot
-  static constexpr int kRing = F8 ? PA_DECODE_RING_FP8 : PA_DECODE_RING;
-  using Raw = typename std::conditional<F8, u32x2_t, u32x4_t>::type;
+  static_assert(D == 64 || D == 128, "head dims 64 and 128");
+  static constexpr int kE = D / 16;                                  // elements of a row per lane
+  static constexpr int kW = kE / 2;                                  // the same as bf16 pairs
+  static constexpr int kTileBytes = kBlock * D * (F8 ? 1 : 2);       // 16 rows of one KV head
+  static constexpr int kLoadBytes = kE * (F8 ? 1 : 2);               // per lane and load slot
+  // the same bytes in flight for every tile size: twice the tiles at half the bytes
+  static constexpr int kRing = (F8 ? PA_DECODE_RING_FP8 : PA_DECODE_RING) * (128 / D);
+  using Raw = typename std::conditional<kLoadBytes == 16, u32x4_t,
+                                        typename std::conditional<kLoadBytes == 8, u32x2_t, uint32_t>::type>::type;
+  using Words = typename std::conditional<kW == 4, u32x4_t, u32x2_t>::type;   // kE elements as bf16 pairs
   static __device__ __forceinline__ Raw load(__amdgpu_buffer_rsrc_t rsrc, int off) {
-    if constexpr (F8) {
+    if constexpr (kLoadBytes == 16) {
+      return __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+    } else if constexpr (kLoadBytes == 8) {
       return __builtin_amdgcn_raw_buffer_load_b64(rsrc, off, 0, 0);
     } else {
-      return __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+      return __builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, 0);
     }
   }
-  // 8 elements as 4 bf16 pairs
-  static __device__ __forceinline__ u32x4_t widen(const Raw& w) {
-    if constexpr (F8) {
-      return u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.f, false)),
-                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.f, true)),
-                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.f, false)),
-                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.f, true))};
-    } else {
+  template <bool Hi>   // the low or high two codes of w as a bf16 pair
+  static __device__ __forceinline__ uint32_t cvt(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, Hi));
+  }
+  // the lane's kE elements as bf16 pairs
+  static __device__ __forceinline__ Words widen(const Raw& w) {
+    if constexpr (!F8) {
       return w;
+    } else if constexpr (kW == 4) {
+      return Words{cvt<false>(w[0]), cvt<true>(w[0]), cvt<false>(w[1]), cvt<true>(w[1])};
+    } else {
+      return Words{cvt<false>(w), cvt<true>(w)};
     }
   }
 };
@@ -197,11 +208,12 @@ __device__ __forceinline__ float row_reduce(const float* s) {
   }
 }
 
-__device__ __forceinline__ float dot16_bf16(const u32x4_t& q, const u32x4_t& k) {
+// Dot product of a lane's slices of q and k (N bf16 pairs each).
+template <int N, typename V>
+__device__ __forceinline__ float dot_bf16(const V& q, const V& k) {
   float s = dot2_bf16(q[0], k[0], 0.f);
-  s = dot2_bf16(q[1], k[1], s);
-  s = dot2_bf16(q[2], k[2], s);
-  s = dot2_bf16(q[3], k[3], s);
+#pragma unroll
+  for (int i = 1; i < N; ++i) s = dot2_bf16(q[i], k[i], s);
   return s;
 }
 
@@ -228,10 +240,10 @@ struct Item {
 // t % Hkv.  An index past the list gives a placeholder with in-range
 // addresses and no tiles.  Every field goes through readfirstlane, so the descriptors and
 // table loads built from it stay scalar.
-template <bool F8, int BS>
+template <bool F8, int BS, int D>
 __device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t, int4 ent) {
-  constexpr int kRing = Kv<F8>::kRing;
-  constexpr int kHeadBytes = BS * kD * (F8 ? 1 : 2);   // one KV head's rows of a block
+  constexpr int kRing = Kv<F8, D>::kRing;
+  constexpr int kHeadBytes = BS * D * (F8 ? 1 : 2);   // one KV head's rows of a block
   Item it;
   it.valid = t < total;
   int b = 0, part = 0, q0 = 0, L = 1, kvh = 0;
@@ -284,18 +296,21 @@ __device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t,
 // the last load group of an item already fetches the next item's first kRing
 // tiles and the HBM queue of the wave never drains at item boundaries.  The
 // physical block id of the slot issued next is fetched one issue ahead.
-template <int G, bool F8, int BS>
+template <int G, bool F8, int BS, int D>
 __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kernel(DecodeArgs a) {
-  using T = Kv<F8>;
+  using T = Kv<F8, D>;
   constexpr int kRing = T::kRing;
   constexpr int kTileBytes = T::kTileBytes;
-  constexpr int kHeadBytes = BS * kD * (F8 ? 1 : 2);   // one KV head's rows of a block
+  constexpr int kE = T::kE;             // elements of a row per lane
+  constexpr int kW = T::kW;
+  using Words = typename T::Words;
+  constexpr int kHeadBytes = BS * D * (F8 ? 1 : 2);   // one KV head's rows of a block
   using Raw = typename T::Raw;
   constexpr int K = log2_of<G>();
   constexpr int kRot = 16 / G;          // lanes between consecutive heads in a row
-  constexpr int kNV = G * 8;            // accumulators per lane
+  constexpr int kNV = G * kE;           // accumulators per lane
   constexpr int kNZ = kNV / 4;          // accumulators per lane after the row reduce-scatter
-  constexpr int kRun = kNZ < 8 ? kNZ : 8;   // consecutive d values per output run
+  constexpr int kRun = kNZ < kE ? kNZ : kE;   // consecutive d values per output run
 
   const int total = load_const(a.plan, kPlanCountInt) * a.num_kv_heads;
   const int lane = threadIdx.x & 63;
@@ -415,7 +430,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
   const int r = lane & 15;
   const int tg = lane >> 4;
   const int hr = r >> (4 - K);
-  const int voff = tg * kD * (F8 ? 1 : 2) + r * T::kLoadBytes;   // token tg of the slot, d-slice r
+  const int voff = tg * D * (F8 ? 1 : 2) + r * T::kLoadBytes;   // token tg of the slot, d-slice r
   const int64_t bstride = int64_t(a.num_kv_heads) * kHeadBytes;   // bytes per physical block
   const float scale_log2 = a.scale_log2;
   // direction of row_ror within a row: the head of accumulator slot j is (hr + dir*j) mod G
@@ -428,11 +443,12 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
   // Each wave stages the next item's q rows in its own LDS slot: fetched into a
   // few VGPRs when the item starts (not used by the tile loop, so the loop
   // never waits for them) and moved to qreg through LDS after the item.
-  constexpr int kQDw = G;   // q dwords per lane: G rows x 256 B over 64 lanes
+  constexpr int kQD = G * D / 2;                    // q dwords of an item: G rows of D bf16
+  constexpr int kQDw = kQD >= 64 ? kQD / 64 : 1;    // per lane (lanes >= kQD idle when kQD < 64)
   __shared__ uint32_t sq[kWavesPerGroup][64 * kQDw];
   auto fetch_q = [&](const Item& it, uint32_t(&qt)[kQDw]) {
     const uint32_t* src = reinterpret_cast<const uint32_t*>(
-        static_cast<const char*>(a.q) + (int64_t(it.q0) * a.q_row_stride + int64_t(it.kvh) * G * kD) * 2);
+        static_cast<const char*>(a.q) + (int64_t(it.q0) * a.q_row_stride + int64_t(it.kvh) * G * D) * 2);
     if constexpr (kQDw >= 4) {
 #pragma unroll
       for (int c = 0; c < kQDw / 4; ++c) {
@@ -442,35 +458,35 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
       }
     } else {
 #pragma unroll
-      for (int c = 0; c < kQDw; ++c) qt[c] = src[lane * kQDw + c];
+      for (int c = 0; c < kQDw; ++c) qt[c] = lane * kQDw + c < kQD ? src[lane * kQDw + c] : 0u;
     }
   };
   auto park_q = [&](const uint32_t(&qt)[kQDw]) {
 #pragma unroll
     for (int c = 0; c < kQDw; ++c) sq[wave][lane * kQDw + c] = qt[c];
   };
-  auto read_q = [&](u32x4_t(&qreg)[G]) {   // q slices, lane-relative order h(r ^ M_j)
+  auto read_q = [&](Words(&qreg)[G]) {   // q slices, lane-relative order h(r ^ M_j)
     const char* base = reinterpret_cast<const char*>(&sq[wave][0]);
     static_for<G>([&](auto J) {
       constexpr int j = decltype(J)::value;
       const int hh = (r ^ q_mask<K>(j)) >> (4 - K);
-      qreg[j] = *reinterpret_cast<const u32x4_t*>(base + hh * (kD * 2) + r * 16);
+      qreg[j] = *reinterpret_cast<const Words*>(base + hh * (D * 2) + r * (kE * 2));
     });
   };
 
-  Item cur = make_item<F8, BS>(a, total, item_of_round(0), entry0);
+  Item cur = make_item<F8, BS, D>(a, total, item_of_round(0), entry0);
   if (!cur.valid) {
     count_out();
     return;
   }
 
-  auto load_q = [&](u32x4_t(&qreg)[G], const Item& it) {   // q slices, lane-relative order h(r ^ M_j)
+  auto load_q = [&](Words(&qreg)[G], const Item& it) {   // q slices, lane-relative order h(r ^ M_j)
     const char* qrow =
-        static_cast<const char*>(a.q) + (int64_t(it.q0) * a.q_row_stride + int64_t(it.kvh) * G * kD) * 2;
+        static_cast<const char*>(a.q) + (int64_t(it.q0) * a.q_row_stride + int64_t(it.kvh) * G * D) * 2;
     static_for<G>([&](auto J) {
       constexpr int j = decltype(J)::value;
       const int hh = (r ^ q_mask<K>(j)) >> (4 - K);
-      qreg[j] = *reinterpret_cast<const u32x4_t*>(qrow + hh * (kD * 2) + r * 16);
+      qreg[j] = *reinterpret_cast<const Words*>(qrow + hh * (D * 2) + r * (kE * 2));
     });
   };
   // Load slot i reads rows 4i .. 4i+3 of the tile.  With BS = 8 slots 0, 1
@@ -508,7 +524,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
     }
   };
 
-  u32x4_t qreg[G];
+  Words qreg[G];
   Raw kr[kRing][4], vr[kRing][4];   // the ring: K and V of kRing tiles, as loaded
   load_q(qreg, cur);
   int64_t ph0[kRing];   // keys of the first tiles, all requested before any is used
@@ -529,7 +545,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
     // second-to-last load group, just before its first block ids are needed,
     // so it is handed out as late as the tile stream allows.
     const bool dyn = i + 1 >= kStaticRounds;
-    Item nxt = make_item<F8, BS>(a, total, total, make_int4(0, 0, 0, 1));
+    Item nxt = make_item<F8, BS, D>(a, total, total, make_int4(0, 0, 0, 1));
     uint32_t qt[kQDw];
     bool requested = false;
     auto get_next = [&]() {
@@ -538,22 +554,22 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
       int t;
       int4 e;
       take(t, e);
-      nxt = make_item<F8, BS>(a, total, t, e);
+      nxt = make_item<F8, BS, D>(a, total, t, e);
       if (nxt.valid) fetch_q(nxt, qt);
     };
     if (!dyn) {
-      nxt = make_item<F8, BS>(a, total, item_of_round(i + 1), static_entry(i + 1));
+      nxt = make_item<F8, BS, D>(a, total, item_of_round(i + 1), static_entry(i + 1));
       if (nxt.valid) fetch_q(nxt, qt);
     } else if (cur.nb <= 2 * kRing) {
       get_next();
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    float acc[G][8];
+    float acc[G][kE];
 #pragma unroll
     for (int j = 0; j < G; ++j)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+      for (int e = 0; e < kE; ++e) acc[j][e] = 0.f;
     float m = kMinusBig;   // reference max of this lane's (row, head), log2 units
     float l = 0.f;         // sum of rounded p relative to m
 
@@ -578,7 +594,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
     };
 
     auto process = [&](Raw(&kraw)[4], Raw(&vraw)[4], int k) {
-      u32x4_t kb[4], vb[4];
+      Words kb[4], vb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         kb[i] = T::widen(kraw[i]);
@@ -590,7 +606,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
       for (int i = 0; i < 4; ++i) {
         float s[G];
 #pragma unroll
-        for (int j = 0; j < G; ++j) s[j] = dot16_bf16(qreg[j], kb[i]);
+        for (int j = 0; j < G; ++j) s[j] = dot_bf16<kW>(qreg[j], kb[i]);
         sc[i] = row_reduce<G, 0>(s) * scale_log2;
       }
       if (tb + kBlock > cur.tok1 || tb < cur.lo) {   // the context ends, or the window starts, in this block
@@ -600,7 +616,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
           const bool dead = uint32_t(tb + 4 * i + tg - cur.lo) >= span;
           sc[i] = dead ? -__builtin_inff() : sc[i];
 #pragma unroll
-          for (int w = 0; w < 4; ++w) vb[i][w] = dead ? 0u : vb[i][w];
+          for (int w = 0; w < kW; ++w) vb[i][w] = dead ? 0u : vb[i][w];
         }
       }
       const float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
@@ -614,7 +630,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
           float c = alpha;
           if constexpr (j > 0) c = dpp_f32<0x120 + j * kRot>(alpha);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[j][e] *= c;
+          for (int e = 0; e < kE; ++e) acc[j][e] *= c;
         });
       }
       uint32_t p2[2];
@@ -630,16 +646,16 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
           if constexpr (j == 0) pg[j] = p2[kp];
           else pg[j] = dpp_u32<0x120 + j * kRot>(p2[kp]);
         });
-        uint32_t vp[8];
+        uint32_t vp[kE];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < kW; ++w) {
           vp[2 * w] = __builtin_amdgcn_perm(vb[2 * kp + 1][w], vb[2 * kp][w], 0x05040100u);
           vp[2 * w + 1] = __builtin_amdgcn_perm(vb[2 * kp + 1][w], vb[2 * kp][w], 0x07060302u);
         }
 #pragma unroll
         for (int j = 0; j < G; ++j)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[j][e] = dot2_bf16(pg[j], vp[e], acc[j][e]);
+          for (int e = 0; e < kE; ++e) acc[j][e] = dot2_bf16(pg[j], vp[e], acc[j][e]);
       }
     };
 
@@ -682,7 +698,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
       float cj = c;
       if constexpr (j > 0) cj = dpp_f32<0x120 + j * kRot>(c);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[j][e] *= cj;
+      for (int e = 0; e < kE; ++e) acc[j][e] *= cj;
     });
     // after the reduce-scatter, row rho holds accumulator x + rho*kNZ of d-slice r
     float* flat = &acc[0][0];
@@ -704,29 +720,32 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
 #pragma unroll
     for (int x0 = 0; x0 < kNZ; x0 += kRun) {
       const int v = x0 + tg * kNZ;
-      const int j = v >> 3;
-      const int e0 = v & 7;
+      const int j = v / kE;
+      const int e0 = v % kE;
       const int head = (hr + dir * j) & (G - 1);
       const int src = head * kRot;   // a lane of row 0 whose head is `head`
       const float Lh = __shfl(lw, src);
       const int hq = cur.kvh * G + head;
       if ((cur.parts >> 16) == 1) {
         const float inv = 1.f / Lh;
+        __bf16* orow = static_cast<__bf16*>(a.out) + int64_t(cur.q0) * a.o_row_stride + int64_t(hq) * D + r * kE + e0;
         if constexpr (kRun == 8) {
           u32x4_t o;
 #pragma unroll
           for (int w = 0; w < 4; ++w) o[w] = pack_bf16x2(flat[x0 + 2 * w] * inv, flat[x0 + 2 * w + 1] * inv);
-          *reinterpret_cast<u32x4_t*>(static_cast<__bf16*>(a.out) + int64_t(cur.q0) * a.o_row_stride +
-                                      int64_t(hq) * kD + r * 8 + e0) = o;
+          *reinterpret_cast<u32x4_t*>(orow) = o;
+        } else if constexpr (kRun == 4) {
+          u32x2_t o;
+#pragma unroll
+          for (int w = 0; w < 2; ++w) o[w] = pack_bf16x2(flat[x0 + 2 * w] * inv, flat[x0 + 2 * w + 1] * inv);
+          *reinterpret_cast<u32x2_t*>(orow) = o;
         } else {
 #pragma unroll
-          for (int x = 0; x < kRun; ++x)
-            static_cast<__bf16*>(a.out)[int64_t(cur.q0) * a.o_row_stride + int64_t(hq) * kD + r * 8 + e0 + x] =
-                (__bf16)(flat[x0 + x] * inv);
+          for (int x = 0; x < kRun; ++x) orow[x] = (__bf16)(flat[x0 + x] * inv);
         }
       } else {
         const int64_t slot = (int64_t(cur.b) * a.num_q_heads + hq) * a.max_parts + (cur.parts & 0xffff);
-        float* dst = a.ws_o + slot * kD + r * 8 + e0;
+        float* dst = a.ws_o + slot * D + r * kE + e0;
 #pragma unroll
         for (int x = 0; x < kRun; ++x) dst[x] = flat[x0 + x];
       }
@@ -745,7 +764,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
 }  // namespace
 
 bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size, int block_size) {
-  return dtype == 1 && head_dim == kD && (group == 1 || group == 2 || group == 4 || group == 8) &&
+  return dtype == 1 && (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8) &&
          (block_size == 8 || block_size == 16 || block_size == 32) && part_size % kBlock == 0 &&
          part_size / kBlock <= kMaxPartBuckets;
 }
@@ -753,7 +772,7 @@ bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size, int
 namespace {
 
 // Resident workgroups per device for kernel K: CUs x occupancy, queried once per device.
-template <int G, bool F8, int BS>
+template <int G, bool F8, int BS, int D>
 int persistent_groups() {
   static std::atomic<int> cache[kMaxDevices];
   int dev = 0;
@@ -762,7 +781,7 @@ int persistent_groups() {
   if (v > 0) return v;
   int cus = 0, occ = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_gqa_kernel<G, F8, BS>, 64 * (kWavesPerGroup + 1),
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_gqa_kernel<G, F8, BS, D>, 64 * (kWavesPerGroup + 1),
                                                    0) != hipSuccess ||
       occ <= 0)
     occ = 1;
@@ -771,32 +790,41 @@ int persistent_groups() {
   return v;
 }
 
-template <int G, bool F8, int BS>
+template <int G, bool F8, int BS, int D>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   const int64_t upper = int64_t(a.num_seqs) * a.max_parts * a.num_kv_heads;
-  const int64_t grid = std::min<int64_t>(upper, persistent_groups<G, F8, BS>());
+  const int64_t grid = std::min<int64_t>(upper, persistent_groups<G, F8, BS, D>());
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_gqa_kernel<G, F8, BS>), dim3(grid), dim3(64 * (kWavesPerGroup + 1)), 0, stream, a);
+  hipLaunchKernelGGL((decode_gqa_kernel<G, F8, BS, D>), dim3(grid), dim3(64 * (kWavesPerGroup + 1)), 0, stream, a);
   return hipGetLastError();
 }
 
-template <bool F8, int BS>
+template <bool F8, int BS, int D>
 hipError_t launch_bs(int group, const DecodeArgs& a, hipStream_t stream) {
   switch (group) {
-    case 1: return launch_g<1, F8, BS>(a, stream);
-    case 2: return launch_g<2, F8, BS>(a, stream);
-    case 4: return launch_g<4, F8, BS>(a, stream);
-    case 8: return launch_g<8, F8, BS>(a, stream);
+    case 1: return launch_g<1, F8, BS, D>(a, stream);
+    case 2: return launch_g<2, F8, BS, D>(a, stream);
+    case 4: return launch_g<4, F8, BS, D>(a, stream);
+    case 8: return launch_g<8, F8, BS, D>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool F8, int D>
+hipError_t launch_d(int group, const DecodeArgs& a, hipStream_t stream) {
+  switch (a.block_size) {
+    case 8: return launch_bs<F8, 8, D>(group, a, stream);
+    case 16: return launch_bs<F8, 16, D>(group, a, stream);
+    case 32: return launch_bs<F8, 32, D>(group, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <bool F8>
-hipError_t launch_f(int group, const DecodeArgs& a, hipStream_t stream) {
-  switch (a.block_size) {
-    case 8: return launch_bs<F8, 8>(group, a, stream);
-    case 16: return launch_bs<F8, 16>(group, a, stream);
-    case 32: return launch_bs<F8, 32>(group, a, stream);
+hipError_t launch_f(int group, int head_dim, const DecodeArgs& a, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_d<F8, 64>(group, a, stream);
+    case 128: return launch_d<F8, 128>(group, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -806,18 +834,18 @@ hipError_t launch_f(int group, const DecodeArgs& a, hipStream_t stream) {
 int decode_gqa_workers(int group) {
   int g = 0;
   switch (group) {
-    case 1: g = persistent_groups<1, false, 16>(); break;
-    case 2: g = persistent_groups<2, false, 16>(); break;
-    case 4: g = persistent_groups<4, false, 16>(); break;
-    case 8: g = persistent_groups<8, false, 16>(); break;
+    case 1: g = persistent_groups<1, false, 16, 128>(); break;
+    case 2: g = persistent_groups<2, false, 16, 128>(); break;
+    case 4: g = persistent_groups<4, false, 16, 128>(); break;
+    case 8: g = persistent_groups<8, false, 16, 128>(); break;
     default: g = 256;
   }
   return g * kWavesPerGroup;
 }
 
 // a.block_size selects the paging (8, 16 or 32 tokens per block).
-hipError_t launch_decode_gqa(int group, bool fp8_cache, const DecodeArgs& a, hipStream_t stream) {
-  return fp8_cache ? launch_f<true>(group, a, stream) : launch_f<false>(group, a, stream);
+hipError_t launch_decode_gqa(int group, int head_dim, bool fp8_cache, const DecodeArgs& a, hipStream_t stream) {
+  return fp8_cache ? launch_f<true>(group, head_dim, a, stream) : launch_f<false>(group, head_dim, a, stream);
 }
 
 }  // namespace pa

@@ -319,7 +319,7 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
     point_at(region_a, pl.rows_a);
     d.row_mode = pa::kSingleRowOnly;
     d.partial_by_seq = 1;
-    e = pa::launch_decode_gqa(g, fp8, d, s);
+    e = pa::launch_decode_gqa(g, p->head_dim, fp8, d, s);
     if (e != hipSuccess) return PA_ERR_LAUNCH;
   }
   if (pl.generic_mode >= 0) {
@@ -361,7 +361,7 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
   // partitions of single-row requests and of split short requests
   if (pl.fast && pl.parts > 1) {
     point_at(region_a, pl.rows_a);
-    if (pa::launch_merge_list(d, s) != hipSuccess) return PA_ERR_LAUNCH;
+    if (pa::launch_merge_list(p->head_dim, d, s) != hipSuccess) return PA_ERR_LAUNCH;
   }
   return PA_OK;
 }

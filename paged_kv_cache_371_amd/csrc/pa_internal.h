@@ -132,19 +132,19 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
 // Bytes of a plan buffer for these capacities (entries), rounded to 256.
 size_t plan_bytes(int64_t decode_capacity, int64_t prefill_capacity, int64_t merge_capacity);
 
-// Fast single-row decode (bf16, D = 128, G in {1, 2, 4, 8}, blocks of 8, 16 or
-// 32 tokens); partials by request.  Reads its work list from a.plan (built by
-// launch_plan first).
+// Fast single-row decode (bf16, D = 64 or 128, G in {1, 2, 4, 8}, blocks of 8,
+// 16 or 32 tokens); partials by request.  Reads its work list from a.plan
+// (built by launch_plan first).
 bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size, int block_size);
 // Waves of the persistent fast decode kernel on the current device.
 int decode_gqa_workers(int group);
 // fp8_cache: the pools hold OCP FP8 E4M3 codes (scales folded into scale_log2 and lsum_scale).
-hipError_t launch_decode_gqa(int group, bool fp8_cache, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_gqa(int group, int head_dim, bool fp8_cache, const DecodeArgs& a, hipStream_t stream);
 // Partition merge alone (for a DecodeArgs whose partials are already written).
 hipError_t launch_merge(int dtype, int head_dim, const DecodeArgs& a, int64_t partial_rows, hipStream_t stream);
-// Merge for the fast decode kernel's partials (bf16, D = 128): only the
+// Merge for the fast decode kernel's partials (bf16, D = 64 or 128): only the
 // requests on the plan's merge list, one wave per (request, query head).
-hipError_t launch_merge_list(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_merge_list(int head_dim, const DecodeArgs& a, hipStream_t stream);
 size_t decode_lds_bytes(int dtype, int head_dim, int group, int part_size);
 
 // MFMA kernel for multi-row requests (bf16, D = 128, G in {1, 2, 4, 8}, blocks of 8, 16 or 32 tokens).

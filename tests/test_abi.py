@@ -161,7 +161,10 @@ def test_fp8_host_errors(L):
     # 8- and 32-token blocks are served (here the missing workspace is the error)
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(block_size=32)), 1.0, 1.0, None, 0, None) == -5
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(block_size=8, max_blocks_per_seq=8)), 1.0, 1.0, None, 0, None) == -5
+    # D = 64 is served (the missing workspace is the error); D = 256 is not on the 8-bit path
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(head_dim=64, q_row_stride=512, o_row_stride=512)),
+             1.0, 1.0, None, 0, None) == -5
+    assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(head_dim=256, q_row_stride=2048, o_row_stride=2048)),
              1.0, 1.0, None, 0, None) == -3
 
 

@@ -131,10 +131,10 @@ def _repage(pool_bits, tables, lens, bs, num_blocks, rng):
     return pools, new_tables
 
 
-def _bitwise_across_block_sizes(name, seed, n, lens, Hq, Hkv, psize):
+def _bitwise_across_block_sizes(name, seed, n, lens, Hq, Hkv, psize, D=128):
     """Outputs for the same logical K/V paged on 8-, 16- and 32-token blocks;
     asserts they are bitwise equal and match the oracle."""
-    c = build_case(name, seed, "bf16", Hq, Hkv, 128, n, lens)
+    c = build_case(name, seed, "bf16", Hq, Hkv, D, n, lens)
     k16, v16 = oracle_pools(c)
     outs = {}
     rng = np.random.default_rng(seed)
@@ -209,3 +209,19 @@ def test_prefill_window_block_size(bs):
         mx, mean, ok, _ = run_and_compare(c, partition_size=64, sliding_window=W)
         say(f"prefill window {W} bs {bs}: max {mx:.3g} mean {mean:.3g}")
         assert ok, (W, mx, mean)
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (32, 8), (64, 8)])
+def test_fast_decode_head_dim_64(bs, Hq, Hkv):
+    """The fast decode kernel at D = 64 (8 bytes of a row per lane, a ring
+    twice as deep) for every group size and block size."""
+    c = build_case(f"d64_{bs}_{Hq}", 160 + bs, "bf16", Hq, Hkv, 64, [1] * len(FAST_LENS), FAST_LENS, block_size=bs)
+    for psize in (0, 48):
+        mx, mean, ok, _ = run_and_compare(c, partition_size=psize, check_pool=psize == 0)
+        say(f"D=64 bs {bs} {Hq}/{Hkv} psize {psize}: max {mx:.3g} mean {mean:.3g}")
+        assert ok, (psize, mx, mean)
+
+
+def test_fast_decode_head_dim_64_bitwise_across_block_sizes():
+    _bitwise_across_block_sizes("xbs64", 123, [1] * len(FAST_LENS), FAST_LENS, 32, 8, 256, D=64)
