@@ -386,7 +386,7 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a) {
 // trips.  Partitions are combined in order, so the result is deterministic.
 template <int D>
 __global__ __launch_bounds__(256) void merge_list_kernel(DecodeArgs a) {
-  constexpr int kPer = D / 64;   // d values per lane: 1 or 2
+  constexpr int kPer = D / 64;   // d values per lane: 1, 2 or 4
   constexpr int kChunk = 8;
   const int4* list = reinterpret_cast<const int4*>(a.plan + kPlanHeaderInts + a.merge_off_ints);
   const int lane = threadIdx.x & 63;
@@ -413,7 +413,13 @@ __global__ __launch_bounds__(256) void merge_list_kernel(DecodeArgs a) {
         if (p0 + j < nparts) {
           m[j] = __builtin_bit_cast(float, load_const(ml, 2 * (p0 + j)));
           l[j] = __builtin_bit_cast(float, load_const(ml, 2 * (p0 + j) + 1));
-          if constexpr (kPer == 2) {
+          if constexpr (kPer == 4) {
+            const float4 v = *reinterpret_cast<const float4*>(po + int64_t(p0 + j) * D);
+            o[j][0] = v.x;
+            o[j][1] = v.y;
+            o[j][2] = v.z;
+            o[j][3] = v.w;
+          } else if constexpr (kPer == 2) {
             const float2 v = *reinterpret_cast<const float2*>(po + int64_t(p0 + j) * D);
             o[j][0] = v.x;
             o[j][1] = v.y;
@@ -442,7 +448,10 @@ __global__ __launch_bounds__(256) void merge_list_kernel(DecodeArgs a) {
     }
     const float inv = 1.f / denom;
     __bf16* orow = static_cast<__bf16*>(a.out) + int64_t(q0) * a.o_row_stride + int64_t(h) * D;
-    if constexpr (kPer == 2) {
+    if constexpr (kPer == 4) {
+      reinterpret_cast<uint2*>(orow)[lane] =
+          make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv));
+    } else if constexpr (kPer == 2) {
       reinterpret_cast<uint32_t*>(orow)[lane] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
     } else {
       orow[lane] = (__bf16)(acc[0] * inv);
@@ -454,7 +463,9 @@ hipError_t launch_merge_list(int head_dim, const DecodeArgs& a, hipStream_t stre
   const int64_t waves = int64_t(a.merge_capacity) * a.num_q_heads;
   const int64_t grid = std::min<int64_t>((waves + 3) / 4, 1024);
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 128) {
+  if (head_dim == 256) {
+    hipLaunchKernelGGL(merge_list_kernel<256>, dim3(grid), dim3(256), 0, stream, a);
+  } else if (head_dim == 128) {
     hipLaunchKernelGGL(merge_list_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
   } else if (head_dim == 64) {
     hipLaunchKernelGGL(merge_list_kernel<64>, dim3(grid), dim3(256), 0, stream, a);

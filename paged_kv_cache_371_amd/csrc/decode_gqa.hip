@@ -1,4 +1,5 @@
-// Split-K paged attention for single-row (decode) requests, bf16, D = 64 or 128.
+// Split-K paged attention for single-row (decode) requests, bf16, D = 64, 128
+// or 256 (G <= 2).
 //
 // quant67, "PagedAttention 与 Continuous Batching" §3.6: the kernel walks the
 // request's block table, loads each physical block's K/V and folds it into an
@@ -16,7 +17,7 @@
 // Lane layout for one 16-token tile of one KV head (16 rows of D elements,
 // contiguous): lane l = 16*tg + r loads the E = D/16 elements of d-slice
 // [E r, E r + E) of token 4*i + tg, for load slots i = 0..3 (16 B per lane at
-// D = 128, 8 B at D = 64).  Every load instruction reads 64 E elements of
+// D = 128, 8 B at D = 64, 32 B as two loads at D = 256).  Every load instruction reads 64 E elements of
 // consecutive memory.  Loads are raw buffer loads whose descriptor spans exactly one tile;
 // a tile past the wave's range gets a zero-sized descriptor, so the pipeline
 // issues a fixed number of loads per step without touching memory for it.
@@ -72,6 +73,7 @@ constexpr int kMaxDevices = 64;
 #define PA_DECODE_RING_FP8 6
 #endif
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+typedef __attribute__((ext_vector_type(8))) uint32_t u32x8_t;
 
 // Cache element types.  bf16: a lane loads 16 bytes (8 elements) per load
 // slot.  OCP FP8 E4M3: a lane loads 8 bytes (the same 8 elements) and widens
@@ -84,18 +86,28 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 // is half the bytes, so its ring is twice as deep for the same bytes in flight.
 template <bool F8, int D>
 struct Kv {
-  static_assert(D == 64 || D == 128, "head dims 64 and 128");
+  static_assert(D == 64 || D == 128 || D == 256, "head dims 64, 128 and 256");
   static constexpr int kE = D / 16;                                  // elements of a row per lane
   static constexpr int kW = kE / 2;                                  // the same as bf16 pairs
   static constexpr int kTileBytes = kBlock * D * (F8 ? 1 : 2);       // 16 rows of one KV head
   static constexpr int kLoadBytes = kE * (F8 ? 1 : 2);               // per lane and load slot
-  // the same bytes in flight for every tile size: twice the tiles at half the bytes
-  static constexpr int kRing = (F8 ? PA_DECODE_RING_FP8 : PA_DECODE_RING) * (128 / D);
-  using Raw = typename std::conditional<kLoadBytes == 16, u32x4_t,
-                                        typename std::conditional<kLoadBytes == 8, u32x2_t, uint32_t>::type>::type;
-  using Words = typename std::conditional<kW == 4, u32x4_t, u32x2_t>::type;   // kE elements as bf16 pairs
+  // the same bytes in flight for every tile size: twice the tiles at half the
+  // bytes; a D = 256 tile (twice the bytes) keeps two in flight
+  static constexpr int kRing = D == 256 ? (F8 ? PA_DECODE_RING : 2)
+                                        : (F8 ? PA_DECODE_RING_FP8 : PA_DECODE_RING) * (128 / D);
+  using Raw = typename std::conditional<
+      kLoadBytes == 32, u32x8_t,
+      typename std::conditional<kLoadBytes == 16, u32x4_t,
+                                typename std::conditional<kLoadBytes == 8, u32x2_t, uint32_t>::type>::type>::type;
+  // kE elements as bf16 pairs
+  using Words = typename std::conditional<kW == 8, u32x8_t,
+                                          typename std::conditional<kW == 4, u32x4_t, u32x2_t>::type>::type;
   static __device__ __forceinline__ Raw load(__amdgpu_buffer_rsrc_t rsrc, int off) {
-    if constexpr (kLoadBytes == 16) {
+    if constexpr (kLoadBytes == 32) {
+      const u32x4_t lo = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+      const u32x4_t hi = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + 16, 0, 0);
+      return u32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else if constexpr (kLoadBytes == 16) {
       return __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
     } else if constexpr (kLoadBytes == 8) {
       return __builtin_amdgcn_raw_buffer_load_b64(rsrc, off, 0, 0);
@@ -111,6 +123,9 @@ struct Kv {
   static __device__ __forceinline__ Words widen(const Raw& w) {
     if constexpr (!F8) {
       return w;
+    } else if constexpr (kW == 8) {
+      return Words{cvt<false>(w[0]), cvt<true>(w[0]), cvt<false>(w[1]), cvt<true>(w[1]),
+                   cvt<false>(w[2]), cvt<true>(w[2]), cvt<false>(w[3]), cvt<true>(w[3])};
     } else if constexpr (kW == 4) {
       return Words{cvt<false>(w[0]), cvt<true>(w[0]), cvt<false>(w[1]), cvt<true>(w[1])};
     } else {
@@ -729,11 +744,15 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
       if ((cur.parts >> 16) == 1) {
         const float inv = 1.f / Lh;
         __bf16* orow = static_cast<__bf16*>(a.out) + int64_t(cur.q0) * a.o_row_stride + int64_t(hq) * D + r * kE + e0;
-        if constexpr (kRun == 8) {
-          u32x4_t o;
+        if constexpr (kRun >= 8) {
 #pragma unroll
-          for (int w = 0; w < 4; ++w) o[w] = pack_bf16x2(flat[x0 + 2 * w] * inv, flat[x0 + 2 * w + 1] * inv);
-          *reinterpret_cast<u32x4_t*>(orow) = o;
+          for (int c = 0; c < kRun / 8; ++c) {
+            u32x4_t o;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+              o[w] = pack_bf16x2(flat[x0 + 8 * c + 2 * w] * inv, flat[x0 + 8 * c + 2 * w + 1] * inv);
+            *reinterpret_cast<u32x4_t*>(orow + 8 * c) = o;
+          }
         } else if constexpr (kRun == 4) {
           u32x2_t o;
 #pragma unroll
@@ -764,7 +783,9 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
 }  // namespace
 
 bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size, int block_size) {
-  return dtype == 1 && (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8) &&
+  // at D = 256 the accumulators and q slices of G = 4 or 8 leave no registers for the ring
+  const bool dims = head_dim == 64 || head_dim == 128 || (head_dim == 256 && group <= 2);
+  return dtype == 1 && dims && (group == 1 || group == 2 || group == 4 || group == 8) &&
          (block_size == 8 || block_size == 16 || block_size == 32) && part_size % kBlock == 0 &&
          part_size / kBlock <= kMaxPartBuckets;
 }
@@ -820,11 +841,27 @@ hipError_t launch_d(int group, const DecodeArgs& a, hipStream_t stream) {
   }
 }
 
+template <bool F8, int BS>
+hipError_t launch_bs256(int group, const DecodeArgs& a, hipStream_t stream) {   // G <= 2 at D = 256
+  switch (group) {
+    case 1: return launch_g<1, F8, BS, 256>(a, stream);
+    case 2: return launch_g<2, F8, BS, 256>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <bool F8>
 hipError_t launch_f(int group, int head_dim, const DecodeArgs& a, hipStream_t stream) {
   switch (head_dim) {
     case 64: return launch_d<F8, 64>(group, a, stream);
     case 128: return launch_d<F8, 128>(group, a, stream);
+    case 256:
+      switch (a.block_size) {
+        case 8: return launch_bs256<F8, 8>(group, a, stream);
+        case 16: return launch_bs256<F8, 16>(group, a, stream);
+        case 32: return launch_bs256<F8, 32>(group, a, stream);
+        default: return hipErrorInvalidValue;
+      }
     default: return hipErrorInvalidValue;
   }
 }

@@ -168,7 +168,7 @@ pa_status check_params(const pa_attn_params* p) {
 
 extern "C" {
 
-int32_t pa_abi_version(void) { return 203; }
+int32_t pa_abi_version(void) { return 204; }
 
 const char* pa_status_string(pa_status s) {
   switch (s) {

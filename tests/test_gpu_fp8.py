@@ -139,15 +139,15 @@ def test_decode_fp8_block_sizes(bs, Hq, Hkv):
         assert ok, (psize, mx, mean)
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (32, 8), (64, 8)])
-def test_decode_fp8_head_dim_64(Hq, Hkv):
-    """8-bit pools at D = 64 (4 codes of a row per lane)."""
-    c = build_case(f"dec8d64_{Hq}", 37, "bf16", Hq, Hkv, 64, [1] * len(LENS), LENS)
+@pytest.mark.parametrize("D,Hq,Hkv", [(64, 8, 8), (64, 32, 8), (64, 64, 8), (256, 8, 8), (256, 16, 8)])
+def test_decode_fp8_head_dim_64(D, Hq, Hkv):
+    """8-bit pools at D = 64 (4 codes of a row per lane) and D = 256 (16 codes)."""
+    c = build_case(f"dec8d{D}_{Hq}", 37, "bf16", Hq, Hkv, D, [1] * len(LENS), LENS)
     fc = Fp8Case(c, 10, 0.5, 0.25)
     for psize in (0, 256):
         fc.write_and_attend(psize)
         mx, mean, ok = fc.compare(check_pool=psize == 0)
-        say(f"fp8 D=64 {Hq}/{Hkv} psize {psize}: max {mx:.3g} mean {mean:.3g}")
+        say(f"fp8 D={D} {Hq}/{Hkv} psize {psize}: max {mx:.3g} mean {mean:.3g}")
         assert ok, (psize, mx, mean)
 
 

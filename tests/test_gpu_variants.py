@@ -225,3 +225,19 @@ def test_fast_decode_head_dim_64(bs, Hq, Hkv):
 
 def test_fast_decode_head_dim_64_bitwise_across_block_sizes():
     _bitwise_across_block_sizes("xbs64", 123, [1] * len(FAST_LENS), FAST_LENS, 32, 8, 256, D=64)
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8)])
+def test_fast_decode_head_dim_256(bs, Hq, Hkv):
+    """The fast decode kernel at D = 256 for G = 1 and 2 (32 bytes of a row per
+    lane as two loads, two tiles in flight)."""
+    c = build_case(f"d256_{bs}_{Hq}", 170 + bs, "bf16", Hq, Hkv, 256, [1] * len(FAST_LENS), FAST_LENS, block_size=bs)
+    for psize in (0, 48):
+        mx, mean, ok, _ = run_and_compare(c, partition_size=psize, check_pool=psize == 0)
+        say(f"D=256 bs {bs} {Hq}/{Hkv} psize {psize}: max {mx:.3g} mean {mean:.3g}")
+        assert ok, (psize, mx, mean)
+
+
+def test_fast_decode_head_dim_256_bitwise_across_block_sizes():
+    _bitwise_across_block_sizes("xbs256", 124, [1] * len(FAST_LENS), FAST_LENS, 16, 8, 256, D=256)
