@@ -537,10 +537,11 @@ def main() -> None:
             dc.attention(partition_size=args.partition_size, stage=stage)
             b_.record(stream)
         torch.cuda.synchronize()
-        return float(np.mean([a_.elapsed_time(b_) for a_, b_ in evs]))
+        return np.array([a_.elapsed_time(b_) for a_, b_ in evs])
 
-    plan_ms = stage_ms("plan")
-    run_ms = stage_ms("run")
+    plan_ms = float(stage_ms("plan").mean())
+    run_all = stage_ms("run")
+    run_ms = float(run_all.mean())
 
     value = ab["kv"] / (ms_per_step * 1e-3) / 1e9
     achieved = ab["attention"] / (run_ms * 1e-3) / 1e9
@@ -578,6 +579,7 @@ def main() -> None:
         "query_tokens_per_s": round(c.total_q / (ms_per_step * 1e-3), 1),
         "attention_ms": round(attn_ms, 5),
         "attention_run_ms": round(run_ms, 5),
+        "attention_run_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(run_all, [10, 50, 90])],
         "attention_plan_ms": round(plan_ms, 5),
         "cache_write_ms": round(cw_ms, 5),
         "kv_bytes_per_step": ab["kv"],
