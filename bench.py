@@ -24,7 +24,11 @@ the digest recorded there (null otherwise).  ``cpu_baseline`` times the fp64
 CPU oracle on a bounded sample of the same requests.
 
 ``--calibrate-copy`` runs only a 1 GiB device-to-device copy (the counters'
-calibration run).  ``--block-size 8|32`` builds the same workload on 8- or
+calibration run).  ``--flush-cache`` reads a 1 GiB buffer before each
+timed plan and run call (a read, so no dirty lines are left to be written
+back during the call), so those times start with no part of the batch in
+the L2s or the Infinity Cache (for the shared-prefix workload, whose logical
+bytes count the shared blocks once per request).  ``--block-size 8|32`` builds the same workload on 8- or
 32-token blocks.  ``--sliding-window W`` runs the workload with a sliding
 window of W tokens (KV bytes then count only the keys in some row's window).  ``--op copy_blocks`` times copy-on-write block copies
 (pa_copy_blocks) and ``--op swap_out`` / ``--op swap_in`` time swapping a
@@ -141,6 +145,20 @@ def algorithmic_bytes(c, kv_elem_bytes=None, window: int = 0) -> dict:
     meta = 4 * (2 * c.num_seqs + 1)
     cw = int(2 * (s + kvs) * (c.slot_mapping >= 0).sum() * c.num_kv_heads * c.head_dim + 8 * c.total_q)
     return dict(kv=kv, q=q, o=o, tables=tables, meta=meta, attention=kv + q + o + tables + meta, cache_write=cw)
+
+
+def unique_kv_bytes(c, kv_elem_bytes=None) -> int:
+    """K/V bytes of the distinct physical blocks the batch reads (a block shared by
+    several requests counted once, each with the most tokens any of them reads)."""
+    s = 2 if c.dtype == "bf16" else 4
+    kvs = s if kv_elem_bytes is None else kv_elem_bytes
+    bs = int(c.block_size)
+    tokens = {}
+    for b, L in enumerate(c.seq_lens.astype(np.int64)):
+        for j in range(-(-int(L) // bs)):
+            blk = int(c.block_tables[b, j])
+            tokens[blk] = max(tokens.get(blk, 0), min(bs, int(L) - j * bs))
+    return int(sum(tokens.values()) * c.num_kv_heads * c.head_dim * 2 * kvs)
 
 
 def attention_kernels(c) -> str:
@@ -465,6 +483,9 @@ def main() -> None:
                     help="W > 0: each row sees only the last W positions up to its own")
     ap.add_argument("--block-size", type=int, default=16, choices=(8, 16, 32),
                     help="tokens per physical block")
+    ap.add_argument("--flush-cache", action="store_true",
+                    help="before each timed plan/run call, read a 1 GiB buffer (outside the events) so the "
+                         "L2s and the Infinity Cache hold none of the batch")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this framework runs the path on one GPU; --gpus must be 1 "
@@ -529,10 +550,14 @@ def main() -> None:
     # built once per step from the request lengths and shared by every layer)
     # and one layer's attention over them (pa_attention_run), each timed with
     # HIP events on the launch stream.
+    flush = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda:0") if args.flush_cache else None
+
     def stage_ms(stage):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
         torch.cuda.synchronize()
-        for a_, b_ in evs:
+        for i, (a_, b_) in enumerate(evs):
+            if flush is not None:   # a read of 1 GiB: evicts with clean lines, leaves nothing to write back
+                flush.sum()
             a_.record(stream)
             dc.attention(partition_size=args.partition_size, stage=stage)
             b_.record(stream)
@@ -573,6 +598,7 @@ def main() -> None:
             "partition_size": dc.partition_size,
             "kv_dtype": "fp8_e4m3" if fp8 else c.dtype,
             "sliding_window": W,
+            "caches_flushed_before_each_run": bool(args.flush_cache),
             "step": "cache_write + attention_varlen",
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
@@ -583,6 +609,8 @@ def main() -> None:
         "attention_plan_ms": round(plan_ms, 5),
         "cache_write_ms": round(cw_ms, 5),
         "kv_bytes_per_step": ab["kv"],
+        "kv_unique_bytes": unique_kv_bytes(c, 1 if fp8 else None),
+        "unique_kv_gbs_run": round(unique_kv_bytes(c, 1 if fp8 else None) / (run_ms * 1e-3) / 1e9, 1),
         "roofline": {
             "bound": "hbm",
             "kernel": attention_kernels(c),
