@@ -92,9 +92,9 @@ typedef struct {
   int32_t block_size;          /* tokens per physical block: 16 (the pages' default), 8 or 32.
                                   The fast single-row decode kernel (bf16 or 8-bit pools)
                                   takes D = 64 and 128, and 256 with Hq/Hkv <= 2, at all
-                                  three block sizes; the MFMA prefill kernel takes D = 128
-                                  at all three; every other shape runs on the generic
-                                  split-K kernel. */
+                                  three block sizes; the MFMA prefill kernel takes D = 64
+                                  and 128 at all three; every other shape runs on the
+                                  generic split-K kernel. */
   int64_t num_blocks;          /* physical blocks in each pool */
   int32_t max_blocks_per_seq;  /* row length of block_tables */
   int32_t max_query_len;       /* host bound: >= every n_b */

@@ -1,4 +1,4 @@
-// MFMA attention for multi-row (chunked-prefill) requests, bf16, D = 128.
+// MFMA attention for multi-row (chunked-prefill) requests, bf16, D = 64 or 128.
 //
 // quant67, "PagedAttention 与 Continuous Batching" §4.2: a long prompt is
 // processed in chunks batched with decode rows; a chunk's rows attend to the
@@ -48,8 +48,6 @@
 namespace pa {
 namespace {
 
-constexpr int kD = 128;
-constexpr int kTileBytes = kBlock * kD * 2;  // one (block, KV head) tile of bf16
 constexpr unsigned kRsrcWord3 = 0x00020000u;
 constexpr float kMinusBig = -1e30f;
 constexpr float kRescaleThreshold = 8.f;      // log2 units
@@ -61,7 +59,7 @@ constexpr int kWavesPerSimd = 2;              // register budget: 256 per lane
 // pairs, 64-key tiles, two workgroups per CU (the LDS holds two).  W = 2: 64
 // pairs, 32-key tiles, four workgroups per CU -- the same waves per SIMD,
 // half the LDS reads per pair (each wave reads the whole staged tile).
-template <int W>
+template <int W, int D>
 struct Shape {
   static constexpr int kWaves = W;
   static constexpr int kThreads = 64 * W;
@@ -72,8 +70,8 @@ struct Shape {
   // LDS bytes per d row of V^T: keys + pad chosen so that the 16 rows x 4 row
   // groups of a 32-lane 8-byte read land on distinct banks
   static constexpr int kVRow = W == 4 ? kKeys * 2 + 8 : kKeys * 2 + 16;
-  static constexpr int kKBytes = (kD / 8) * kKChunk;
-  static constexpr int kVBytes = kD * kVRow;
+  static constexpr int kKBytes = (D / 8) * kKChunk;
+  static constexpr int kVBytes = D * kVRow;
   static constexpr int kStageBytes = kKBytes + kVBytes;
   static constexpr int kLdsBytes = 2 * kStageBytes;
   static_assert(kKeys % 32 == 0, "whole 32-key MFMA steps");
@@ -122,9 +120,12 @@ struct TileRegs {
 // W = 4 for chunked prefill; W = 2 for batches whose multi-row requests are
 // short (speculative-decode verification), where a 128-pair tile would be
 // mostly empty and the LDS reads per tile, not HBM, would set the pace.
-template <int G, int W, int BS>
-__global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_kernel(PrefillArgs a) {
-  using S = Shape<W>;
+template <int G, int W, int BS, int D>
+__global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefill_kernel(PrefillArgs a) {
+  using S = Shape<W, D>;
+  constexpr int kTileBytes = kBlock * D * 2;   // one 16-key unit of one KV head, bf16
+  constexpr int kSteps = D / 32;               // 32-wide d steps of S^T = K Q^T
+  constexpr int kDB = D / 16;                  // 16-row d blocks of O^T
   constexpr int kMB = 2;                      // 16-column MFMA blocks per wave
   constexpr int kPairs = 16 * kMB * W;
   constexpr int kKeys = S::kKeys;
@@ -146,10 +147,13 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
   const int wave = uni(tid >> 6);
   const int h = lane >> 4;    // 16-lane row of the wave
   const int lc = lane & 15;   // MFMA column of the lane
-  // staging coordinates (see TileRegs)
-  const int kkey = 4 * (lane >> 4), kchunk = lane & 15;
+  // staging coordinates (see TileRegs): at D = 64 the unit's 8 d-chunks per key
+  // are staged by lanes 0..31 and lanes 32..63 stage nothing
+  const int kkey = D == 128 ? 4 * (lane >> 4) : 4 * ((lane >> 3) & 3);
+  const int kchunk = D == 128 ? lane & 15 : lane & 7;
   const int vkey = 4 * (lane & 3), vchunk = lane >> 2;
-  constexpr int kHeadBytes = BS * kD * 2;   // one KV head's rows of a physical block
+  const bool stager = D == 128 || lane < 32;
+  constexpr int kHeadBytes = BS * D * 2;   // one KV head's rows of a physical block
   const int64_t bstride = int64_t(hkv) * kHeadBytes;
   const float scale_log2 = a.scale_log2;
   const int32_t* entries = a.plan + kPlanHeaderInts + a.pref_off_ints;
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
     // visible keys of a pair: lolim .. lolim + span (one unsigned compare per score)
     int jrow[kMB], hq[kMB], lolim[kMB], span[kMB];
     bool mvalid[kMB];
-    u32x4_t qb[kMB][4];   // B operand Q^T: pair lc, d = 32s + 8h .. +7
+    u32x4_t qb[kMB][kSteps];   // B operand Q^T: pair lc, d = 32s + 8h .. +7
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
       const int m = wave * (16 * kMB) + mb * 16 + lc;
@@ -209,19 +213,19 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
       lolim[mb] = mvalid[mb] ? window_start(P + jrow[mb], window) : 0;
       span[mb] = mvalid[mb] ? P + jrow[mb] - lolim[mb] : 0;
       const char* qrow = static_cast<const char*>(PA_KARG(q)) +
-                         (int64_t(q0 + (mvalid[mb] ? jrow[mb] : 0)) * PA_KARG(q_row_stride) + int64_t(hq[mb]) * kD) * 2;
+                         (int64_t(q0 + (mvalid[mb] ? jrow[mb] : 0)) * PA_KARG(q_row_stride) + int64_t(hq[mb]) * D) * 2;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < kSteps; ++s) {
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qrow + (32 * s + 8 * h) * 2);
         qb[mb][s] = mvalid[mb] ? v : u32x4_t{0u, 0u, 0u, 0u};
       }
     }
 
-    f32x4_t acc[kMB][8];   // O^T blocks: d = 16*db + 4h + r, pair lc
+    f32x4_t acc[kMB][kDB];   // O^T blocks: d = 16*db + 4h + r, pair lc
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-      for (int db = 0; db < 8; ++db) acc[mb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int db = 0; db < kDB; ++db) acc[mb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float mrun[kMB], lrun[kMB];
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
@@ -257,6 +261,7 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
       }
     };
     auto fetch = [&](TileRegs& rg, int kt, uint64_t phys_v) {
+      if (!stager) return;
       const int u = unit_of(kt);
       const int64_t phys = uni(int(uint32_t(phys_v)));
       if constexpr (BS == 8) {
@@ -275,20 +280,20 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
         if (kkey < 8) {
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk)
-            rg.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, (kkey + kk) * (kD * 2) + kchunk * 16, 0, 0);
+            rg.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, (kkey + kk) * (D * 2) + kchunk * 16, 0, 0);
         } else {
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk)
-            rg.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk2, (kkey - 8 + kk) * (kD * 2) + kchunk * 16, 0, 0);
+            rg.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk2, (kkey - 8 + kk) * (D * 2) + kchunk * 16, 0, 0);
         }
         if (vkey < 8) {
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk)
-            rg.v[kk] = __builtin_amdgcn_raw_buffer_load_b128(rv, (vkey + kk) * (kD * 2) + vchunk * 16, 0, 0);
+            rg.v[kk] = __builtin_amdgcn_raw_buffer_load_b128(rv, (vkey + kk) * (D * 2) + vchunk * 16, 0, 0);
         } else {
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk)
-            rg.v[kk] = __builtin_amdgcn_raw_buffer_load_b128(rv2, (vkey - 8 + kk) * (kD * 2) + vchunk * 16, 0, 0);
+            rg.v[kk] = __builtin_amdgcn_raw_buffer_load_b128(rv2, (vkey - 8 + kk) * (D * 2) + vchunk * 16, 0, 0);
         }
       } else {
         const int64_t off = BS == 32 ? phys * bstride + (u & 1) * kTileBytes : phys * bstride;
@@ -299,13 +304,14 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
             __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + off), 0, nrec, kRsrcWord3);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-          rg.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, (kkey + kk) * (kD * 2) + kchunk * 16, 0, 0);
+          rg.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, (kkey + kk) * (D * 2) + kchunk * 16, 0, 0);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-          rg.v[kk] = __builtin_amdgcn_raw_buffer_load_b128(rv, (vkey + kk) * (kD * 2) + vchunk * 16, 0, 0);
+          rg.v[kk] = __builtin_amdgcn_raw_buffer_load_b128(rv, (vkey + kk) * (D * 2) + vchunk * 16, 0, 0);
       }
     };
     auto stage_write = [&](TileRegs& rg, int kt, int st) {
+      if (!stager) return;
       char* ks = smem + st * kStageBytes;
       char* vs = ks + kKBytes;
       const int key0 = kt * kKeys + wave * kBlock;   // first position of this wave's block
@@ -344,7 +350,7 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) sacc[c][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int s = 0; s < kSteps; ++s)
 #pragma unroll
         for (int c = 0; c < kCB; ++c) {
           const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(ks + (4 * s + h) * kKChunk + (16 * c + lc) * 16);
@@ -383,7 +389,7 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
           mrun[mb] = mnew;
           lrun[mb] *= alpha;
 #pragma unroll
-          for (int db = 0; db < 8; ++db) acc[mb][db] *= alpha;
+          for (int db = 0; db < kDB; ++db) acc[mb][db] *= alpha;
         }
         const float nm = -mrun[mb];
         float lsum = lrun[mb];
@@ -406,7 +412,7 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
 #pragma unroll
       for (int u = 0; u < kU; ++u)
 #pragma unroll
-        for (int db = 0; db < 8; ++db) {
+        for (int db = 0; db < kDB; ++db) {
           const char* vrow = vs + (16 * db + lc) * kVRow;
           const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow + (32 * u + 4 * h) * 2);
           const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + (32 * u + 16 + 4 * h) * 2);
@@ -445,9 +451,9 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
           const int64_t idx = (int64_t(PA_KARG(num_seqs) + q0 + jrow[mb]) * PA_KARG(num_q_heads) + hq[mb]) *
                                   PA_KARG(max_parts) +
                               (part - p_lo);
-          float* po = PA_KARG(ws_o) + idx * kD;
+          float* po = PA_KARG(ws_o) + idx * D;
 #pragma unroll
-          for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4_t*>(po + 16 * db + 4 * h) = acc[mb][db];
+          for (int db = 0; db < kDB; ++db) *reinterpret_cast<f32x4_t*>(po + 16 * db + 4 * h) = acc[mb][db];
           if (h == 0) *reinterpret_cast<float2*>(PA_KARG(ws_ml) + 2 * idx) = make_float2(mrun[mb], lsum);
         }
       }
@@ -458,9 +464,9 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
         const float inv = 1.f / rows_sum(lrun[mb]);
         if (mvalid[mb]) {
           __bf16* orow =
-              static_cast<__bf16*>(PA_KARG(out)) + int64_t(q0 + jrow[mb]) * PA_KARG(o_row_stride) + int64_t(hq[mb]) * kD;
+              static_cast<__bf16*>(PA_KARG(out)) + int64_t(q0 + jrow[mb]) * PA_KARG(o_row_stride) + int64_t(hq[mb]) * D;
 #pragma unroll
-          for (int db = 0; db < 8; ++db) {
+          for (int db = 0; db < kDB; ++db) {
             const u32x2_t o = {pack_bf16x2(acc[mb][db][0] * inv, acc[mb][db][1] * inv),
                                pack_bf16x2(acc[mb][db][2] * inv, acc[mb][db][3] * inv)};
             *reinterpret_cast<u32x2_t*>(orow + 16 * db + 4 * h) = o;
@@ -471,7 +477,7 @@ __global__ __launch_bounds__(Shape<W>::kThreads, kWavesPerSimd) void prefill_ker
   }
 }
 
-template <int G, int W, int BS>
+template <int G, int W, int BS, int D>
 int prefill_groups() {
   static std::atomic<int> cache{0};
   int v = cache.load(std::memory_order_relaxed);
@@ -479,8 +485,8 @@ int prefill_groups() {
   int dev = 0, cus = 0, occ = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, prefill_kernel<G, W, BS>, Shape<W>::kThreads,
-                                                   Shape<W>::kLdsBytes) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, prefill_kernel<G, W, BS, D>, Shape<W, D>::kThreads,
+                                                   Shape<W, D>::kLdsBytes) != hipSuccess ||
       occ <= 0)
     occ = 1;
   v = cus * occ;
@@ -488,49 +494,56 @@ int prefill_groups() {
   return v;
 }
 
-template <int G, int W, int BS>
+template <int G, int W, int BS, int D>
 hipError_t launch_g(const PrefillArgs& a, hipStream_t stream) {
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<G, W, BS>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, Shape<W>::kLdsBytes);
+      hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<G, W, BS, D>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, Shape<W, D>::kLdsBytes);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((prefill_kernel<G, W, BS>), dim3(prefill_groups<G, W, BS>()), dim3(Shape<W>::kThreads),
-                     Shape<W>::kLdsBytes, stream, a);
+  using Sh = Shape<W, D>;
+  const int groups = prefill_groups<G, W, BS, D>();
+  hipLaunchKernelGGL((prefill_kernel<G, W, BS, D>), dim3(groups), dim3(Sh::kThreads), Sh::kLdsBytes, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool prefill_supported(int head_dim, int group, int block_size) {
-  return head_dim == kD && (group == 1 || group == 2 || group == 4 || group == 8) &&
+  return (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8) &&
          (block_size == 8 || block_size == 16 || block_size == 32);
 }
 
-template <int W, int BS>
+template <int W, int BS, int D>
 hipError_t launch_w(int group, const PrefillArgs& a, hipStream_t stream) {
   switch (group) {
-    case 1: return launch_g<1, W, BS>(a, stream);
-    case 2: return launch_g<2, W, BS>(a, stream);
-    case 4: return launch_g<4, W, BS>(a, stream);
-    case 8: return launch_g<8, W, BS>(a, stream);
+    case 1: return launch_g<1, W, BS, D>(a, stream);
+    case 2: return launch_g<2, W, BS, D>(a, stream);
+    case 4: return launch_g<4, W, BS, D>(a, stream);
+    case 8: return launch_g<8, W, BS, D>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int W>
+template <int W, int D>
 hipError_t launch_b(int group, const PrefillArgs& a, hipStream_t stream) {
   switch (a.block_size) {
-    case 8: return launch_w<W, 8>(group, a, stream);
-    case 16: return launch_w<W, 16>(group, a, stream);
-    case 32: return launch_w<W, 32>(group, a, stream);
+    case 8: return launch_w<W, 8, D>(group, a, stream);
+    case 16: return launch_w<W, 16, D>(group, a, stream);
+    case 32: return launch_w<W, 32, D>(group, a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int D>
+hipError_t launch_d(int group, const PrefillArgs& a, hipStream_t stream) {
+  if (a.tile_pairs == 64) return launch_b<2, D>(group, a, stream);
+  if (a.tile_pairs == 128) return launch_b<4, D>(group, a, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill(int head_dim, int group, const PrefillArgs& a, hipStream_t stream) {
-  if (head_dim != kD) return hipErrorInvalidValue;
-  if (a.tile_pairs == 64) return launch_b<2>(group, a, stream);
-  if (a.tile_pairs == 128) return launch_b<4>(group, a, stream);
+  if (head_dim == 128) return launch_d<128>(group, a, stream);
+  if (head_dim == 64) return launch_d<64>(group, a, stream);
   return hipErrorInvalidValue;
 }
 

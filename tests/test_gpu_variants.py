@@ -241,3 +241,32 @@ def test_fast_decode_head_dim_256(bs, Hq, Hkv):
 
 def test_fast_decode_head_dim_256_bitwise_across_block_sizes():
     _bitwise_across_block_sizes("xbs256", 124, [1] * len(FAST_LENS), FAST_LENS, 16, 8, 256, D=256)
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (32, 8), (64, 8)])
+def test_prefill_head_dim_64(bs, Hq, Hkv):
+    """The MFMA kernel at D = 64 (two 32-wide d steps, four output blocks; the
+    unit's 8 d-chunks per key staged by half the lanes): chunked prefill with
+    decode rows, prior contexts ending anywhere in a block."""
+    n = [200, 1, 37, 1, 5, 129, 1, 2]
+    L = [1000, 700, 37, 33, 9, 700, 3000, 17]
+    c = build_case(f"p64_{bs}_{Hq}", 180 + bs, "bf16", Hq, Hkv, 64, n, L, block_size=bs)
+    for psize in (0, 64):
+        mx, mean, ok, _ = run_and_compare(c, partition_size=psize, check_pool=psize == 0)
+        say(f"prefill D=64 bs {bs} {Hq}/{Hkv} psize {psize}: max {mx:.3g} mean {mean:.3g}")
+        assert ok, (psize, mx, mean)
+
+
+def test_split_short_requests_head_dim_64():
+    n = [4, 1, 8, 2, 1, 3, 7]
+    L = [3000, 2049, 1500, 700, 5, 4100, 8]
+    c = build_case("s64", 190, "bf16", 64, 8, 64, n, L)
+    for psize in (0, 512):
+        mx, mean, ok, _ = run_and_compare(c, partition_size=psize, check_pool=psize == 0)
+        say(f"split D=64 psize {psize}: max {mx:.3g} mean {mean:.3g}")
+        assert ok, (psize, mx, mean)
+
+
+def test_prefill_head_dim_64_bitwise_across_block_sizes():
+    _bitwise_across_block_sizes("xpbs64", 125, [200, 1, 37, 1, 129, 5], [1000, 700, 37, 33, 700, 9], 32, 8, 0, D=64)
