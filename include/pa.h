@@ -92,8 +92,8 @@ typedef struct {
   int32_t block_size;          /* tokens per physical block: 16 (the pages' default), 8 or 32.
                                   The fast single-row decode kernel (bf16 or 8-bit pools)
                                   takes D = 64 and 128, and 256 with Hq/Hkv <= 2, at all
-                                  three block sizes; the MFMA prefill kernel takes D = 64
-                                  and 128 at all three; every other shape runs on the
+                                  three block sizes; the MFMA prefill kernel takes D = 64,
+                                  128 and 256 at all three; every other shape runs on the
                                   generic split-K kernel. */
   int64_t num_blocks;          /* physical blocks in each pool */
   int32_t max_blocks_per_seq;  /* row length of block_tables */
@@ -280,7 +280,8 @@ const char* pa_status_string(pa_status s);
  * 102: block copies and the host block manager, pa_blocks.h; 200:
  * pa_attn_params.sliding_window; 201: block sizes 8 and 32, D = 256; 202:
  * 8-bit pools at block sizes 8 and 32; 203: pa_attention_plan / pa_attention_run;
- * 204: the fast decode kernel and 8-bit pools at D = 64 and 256). */
+ * 204: the fast decode kernel and 8-bit pools at D = 64 and 256, the MFMA
+ * prefill kernel at D = 64 and 256). */
 int32_t pa_abi_version(void);
 
 #ifdef __cplusplus

@@ -86,7 +86,7 @@ inline Plan make_plan(const pa_attn_params* p) {
   // Batches whose multi-row requests all fit 64 / G rows use 64-pair prefill
   // tiles; such short requests (one row tile) are split over context
   // partitions when the partition is a whole number of prefill key tiles.
-  pl.tile_pairs = p->max_query_len <= pa::kPrefillPairsShort / g ? pa::kPrefillPairsShort : pa::kPrefillPairs;
+  pl.tile_pairs = pa::prefill_tile_pairs(p->head_dim, p->max_query_len <= pa::prefill_tile_pairs(p->head_dim, true) / g);
   pl.split_rows = (pl.fast && pl.prefill && pl.parts > 1 && ps % pa::kPrefillKeys == 0 &&
                    p->max_query_len <= pl.tile_pairs / g)
                       ? pl.tile_pairs / g

@@ -150,6 +150,9 @@ size_t decode_lds_bytes(int dtype, int head_dim, int group, int part_size);
 // MFMA kernel for multi-row requests (bf16, D = 128, G in {1, 2, 4, 8}, blocks of 8, 16 or 32 tokens).
 hipError_t launch_prefill(int head_dim, int group, const PrefillArgs& a, hipStream_t stream);
 bool prefill_supported(int head_dim, int group, int block_size);
+// (query row, head) pairs per prefill work item: 128 (64 at D = 256), or half
+// that when every multi-row request is short.
+int prefill_tile_pairs(int head_dim, bool short_rows);
 
 hipError_t launch_validate(const int32_t* cu, const int32_t* seq_lens, const int32_t* bt, const int64_t* slots,
                            int64_t num_slots, int32_t num_seqs, int64_t total_q, int32_t max_query_len,

@@ -1,4 +1,4 @@
-// MFMA attention for multi-row (chunked-prefill) requests, bf16, D = 64 or 128.
+// MFMA attention for multi-row (chunked-prefill) requests, bf16, D = 64, 128 or 256.
 //
 // quant67, "PagedAttention 与 Continuous Batching" §4.2: a long prompt is
 // processed in chunks batched with decode rows; a chunk's rows attend to the
@@ -109,12 +109,17 @@ __device__ __forceinline__ f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, co
                                                   0);
 }
 
-// One thread's share of a 64-key tile, both from block `wave` of the tile:
-//   k[kk]: key 4*(lane/16) + kk of the block, d-chunk lane%16
-//   v[kk]: key 4*(lane%4)  + kk of the block, d-chunk lane/4
+// One thread's share of a wave's 16-key unit of a tile (d-chunks of 8 values):
+//   D = 128: k[kk]: key 4*(lane/16) + kk, d-chunk lane%16;
+//            v[kk]: key 4*(lane%4) + kk, d-chunk lane/4
+//   D = 64:  the same for lanes 0..31 with d-chunk lane%8 for k
+//   D = 256: k[kk]: key 8*(lane/32) + kk, d-chunk lane%32 (kk < 8);
+//            v[4g + kk]: key 4*(lane%4) + kk, d-chunk lane/4 + 16g
+template <int D>
 struct TileRegs {
-  u32x4_t k[4];
-  u32x4_t v[4];
+  static constexpr int kN = D == 256 ? 8 : 4;
+  u32x4_t k[kN];
+  u32x4_t v[kN];
 };
 
 // W = 4 for chunked prefill; W = 2 for batches whose multi-row requests are
@@ -126,7 +131,8 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
   constexpr int kTileBytes = kBlock * D * 2;   // one 16-key unit of one KV head, bf16
   constexpr int kSteps = D / 32;               // 32-wide d steps of S^T = K Q^T
   constexpr int kDB = D / 16;                  // 16-row d blocks of O^T
-  constexpr int kMB = 2;                      // 16-column MFMA blocks per wave
+  constexpr int kMB = D == 256 ? 1 : 2;       // 16-column MFMA blocks per wave (registers at D = 256)
+  constexpr int kNK = TileRegs<D>::kN;        // 16-byte K (and V) chunks a lane stages per unit
   constexpr int kPairs = 16 * kMB * W;
   constexpr int kKeys = S::kKeys;
   constexpr int kCB = S::kCB;
@@ -149,10 +155,10 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
   const int lc = lane & 15;   // MFMA column of the lane
   // staging coordinates (see TileRegs): at D = 64 the unit's 8 d-chunks per key
   // are staged by lanes 0..31 and lanes 32..63 stage nothing
-  const int kkey = D == 128 ? 4 * (lane >> 4) : 4 * ((lane >> 3) & 3);
-  const int kchunk = D == 128 ? lane & 15 : lane & 7;
+  const int kkey = D == 256 ? 8 * (lane >> 5) : D == 128 ? 4 * (lane >> 4) : 4 * ((lane >> 3) & 3);
+  const int kchunk = D == 256 ? lane & 31 : D == 128 ? lane & 15 : lane & 7;
   const int vkey = 4 * (lane & 3), vchunk = lane >> 2;
-  const bool stager = D == 128 || lane < 32;
+  const bool stager = D != 64 || lane < 32;
   constexpr int kHeadBytes = BS * D * 2;   // one KV head's rows of a physical block
   const int64_t bstride = int64_t(hkv) * kHeadBytes;
   const float scale_log2 = a.scale_log2;
@@ -260,7 +266,7 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
         return uint64_t(first) | (uint64_t(second) << 32);
       }
     };
-    auto fetch = [&](TileRegs& rg, int kt, uint64_t phys_v) {
+    auto fetch = [&](TileRegs<D>& rg, int kt, uint64_t phys_v) {
       if (!stager) return;
       const int u = unit_of(kt);
       const int64_t phys = uni(int(uint32_t(phys_v)));
@@ -279,21 +285,23 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
             __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + phys2 * bstride), 0, nrec2, kRsrcWord3);
         if (kkey < 8) {
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
+          for (int kk = 0; kk < kNK; ++kk)
             rg.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, (kkey + kk) * (D * 2) + kchunk * 16, 0, 0);
         } else {
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
+          for (int kk = 0; kk < kNK; ++kk)
             rg.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk2, (kkey - 8 + kk) * (D * 2) + kchunk * 16, 0, 0);
         }
         if (vkey < 8) {
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-            rg.v[kk] = __builtin_amdgcn_raw_buffer_load_b128(rv, (vkey + kk) * (D * 2) + vchunk * 16, 0, 0);
+          for (int x = 0; x < kNK; ++x)
+            rg.v[x] = __builtin_amdgcn_raw_buffer_load_b128(
+                rv, (vkey + (x & 3)) * (D * 2) + (vchunk + 16 * (x >> 2)) * 16, 0, 0);
         } else {
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-            rg.v[kk] = __builtin_amdgcn_raw_buffer_load_b128(rv2, (vkey - 8 + kk) * (D * 2) + vchunk * 16, 0, 0);
+          for (int x = 0; x < kNK; ++x)
+            rg.v[x] = __builtin_amdgcn_raw_buffer_load_b128(
+                rv2, (vkey - 8 + (x & 3)) * (D * 2) + (vchunk + 16 * (x >> 2)) * 16, 0, 0);
         }
       } else {
         const int64_t off = BS == 32 ? phys * bstride + (u & 1) * kTileBytes : phys * bstride;
@@ -303,14 +311,15 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
         const __amdgpu_buffer_rsrc_t rv =
             __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + off), 0, nrec, kRsrcWord3);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+        for (int kk = 0; kk < kNK; ++kk)
           rg.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, (kkey + kk) * (D * 2) + kchunk * 16, 0, 0);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          rg.v[kk] = __builtin_amdgcn_raw_buffer_load_b128(rv, (vkey + kk) * (D * 2) + vchunk * 16, 0, 0);
+        for (int x = 0; x < kNK; ++x)
+          rg.v[x] = __builtin_amdgcn_raw_buffer_load_b128(rv, (vkey + (x & 3)) * (D * 2) + (vchunk + 16 * (x >> 2)) * 16,
+                                                          0, 0);
       }
     };
-    auto stage_write = [&](TileRegs& rg, int kt, int st) {
+    auto stage_write = [&](TileRegs<D>& rg, int kt, int st) {
       if (!stager) return;
       char* ks = smem + st * kStageBytes;
       char* vs = ks + kKBytes;
@@ -318,25 +327,29 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
       if (kt * kKeys + kKeys > L) {   // the context ends in this tile: zero what lies past it
         const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < kNK; ++kk) {   // v[kk] holds key vkey + kk % 4
           if (key0 + kkey + kk >= L) rg.k[kk] = z;
-          if (key0 + vkey + kk >= L) rg.v[kk] = z;
+          if (key0 + vkey + (kk & 3) >= L) rg.v[kk] = z;
         }
       }
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+      for (int kk = 0; kk < kNK; ++kk)
         *reinterpret_cast<u32x4_t*>(ks + kchunk * kKChunk + (wave * kBlock + kkey + kk) * 16) = rg.k[kk];
-      const u32x4_t* vv = rg.v;
-      // V^T: d rows 8*vchunk + 2w (+1) get this thread's 4 keys (8 bytes each)
+      // V^T: d rows 8*(vchunk + 16g) + 2w (+1) get this thread's 4 keys (8 bytes each)
       char* vcol = vs + (wave * kBlock + vkey) * 2;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t lo01 = __builtin_amdgcn_perm(vv[1][w], vv[0][w], 0x05040100u);
-        const uint32_t lo23 = __builtin_amdgcn_perm(vv[3][w], vv[2][w], 0x05040100u);
-        const uint32_t hi01 = __builtin_amdgcn_perm(vv[1][w], vv[0][w], 0x07060302u);
-        const uint32_t hi23 = __builtin_amdgcn_perm(vv[3][w], vv[2][w], 0x07060302u);
-        *reinterpret_cast<u32x2_t*>(vcol + (8 * vchunk + 2 * w) * kVRow) = u32x2_t{lo01, lo23};
-        *reinterpret_cast<u32x2_t*>(vcol + (8 * vchunk + 2 * w + 1) * kVRow) = u32x2_t{hi01, hi23};
+      for (int g = 0; g < kNK / 4; ++g) {
+        const u32x4_t* vv = rg.v + 4 * g;
+        const int dc = vchunk + 16 * g;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t lo01 = __builtin_amdgcn_perm(vv[1][w], vv[0][w], 0x05040100u);
+          const uint32_t lo23 = __builtin_amdgcn_perm(vv[3][w], vv[2][w], 0x05040100u);
+          const uint32_t hi01 = __builtin_amdgcn_perm(vv[1][w], vv[0][w], 0x07060302u);
+          const uint32_t hi23 = __builtin_amdgcn_perm(vv[3][w], vv[2][w], 0x07060302u);
+          *reinterpret_cast<u32x2_t*>(vcol + (8 * dc + 2 * w) * kVRow) = u32x2_t{lo01, lo23};
+          *reinterpret_cast<u32x2_t*>(vcol + (8 * dc + 2 * w + 1) * kVRow) = u32x2_t{hi01, hi23};
+        }
       }
     };
 
@@ -428,7 +441,7 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
     // staging write of a stage from the computes that read it, before and
     // after.
     __syncthreads();   // the previous item is done with both stages
-    TileRegs rg;
+    TileRegs<D> rg;
     uint64_t ph_next = phys_of(kt0 + 1);
     fetch(rg, kt0, phys_of(kt0));
     stage_write(rg, kt0, 0);
@@ -509,7 +522,7 @@ hipError_t launch_g(const PrefillArgs& a, hipStream_t stream) {
 }  // namespace
 
 bool prefill_supported(int head_dim, int group, int block_size) {
-  return (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8) &&
+  return (head_dim == 64 || head_dim == 128 || head_dim == 256) && (group == 1 || group == 2 || group == 4 || group == 8) &&
          (block_size == 8 || block_size == 16 || block_size == 32);
 }
 
@@ -534,17 +547,26 @@ hipError_t launch_b(int group, const PrefillArgs& a, hipStream_t stream) {
   }
 }
 
+// W waves of 16 * kMB pairs each: 128 / 64 pairs per item (32 per wave), or
+// 64 / 32 at D = 256 (16 per wave)
 template <int D>
 hipError_t launch_d(int group, const PrefillArgs& a, hipStream_t stream) {
-  if (a.tile_pairs == 64) return launch_b<2, D>(group, a, stream);
-  if (a.tile_pairs == 128) return launch_b<4, D>(group, a, stream);
+  const int per_wave = D == 256 ? 16 : 32;
+  if (a.tile_pairs == 2 * per_wave) return launch_b<2, D>(group, a, stream);
+  if (a.tile_pairs == 4 * per_wave) return launch_b<4, D>(group, a, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill(int head_dim, int group, const PrefillArgs& a, hipStream_t stream) {
   if (head_dim == 128) return launch_d<128>(group, a, stream);
   if (head_dim == 64) return launch_d<64>(group, a, stream);
+  if (head_dim == 256) return launch_d<256>(group, a, stream);
   return hipErrorInvalidValue;
+}
+
+int prefill_tile_pairs(int head_dim, bool short_rows) {
+  const int full = head_dim == 256 ? 64 : 128;
+  return short_rows ? full / 2 : full;
 }
 
 }  // namespace pa

@@ -270,3 +270,31 @@ def test_split_short_requests_head_dim_64():
 
 def test_prefill_head_dim_64_bitwise_across_block_sizes():
     _bitwise_across_block_sizes("xpbs64", 125, [200, 1, 37, 1, 129, 5], [1000, 700, 37, 33, 700, 9], 32, 8, 0, D=64)
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (64, 8)])
+def test_prefill_head_dim_256(bs, Hq, Hkv):
+    """The MFMA kernel at D = 256 (one 16-pair block per wave, 64-pair items;
+    8 K chunks and two V chunk groups staged per lane)."""
+    n = [200, 1, 37, 1, 5, 129, 1, 2]
+    L = [1000, 700, 37, 33, 9, 700, 3000, 17]
+    c = build_case(f"p256_{bs}_{Hq}", 200 + bs, "bf16", Hq, Hkv, 256, n, L, block_size=bs)
+    for psize in (0, 64):
+        mx, mean, ok, _ = run_and_compare(c, partition_size=psize, check_pool=psize == 0)
+        say(f"prefill D=256 bs {bs} {Hq}/{Hkv} psize {psize}: max {mx:.3g} mean {mean:.3g}")
+        assert ok, (psize, mx, mean)
+
+
+def test_split_short_requests_head_dim_256():
+    n = [4, 1, 8, 2, 1, 3, 7]
+    L = [3000, 2049, 1500, 700, 5, 4100, 8]
+    c = build_case("s256", 210, "bf16", 16, 8, 256, n, L)
+    for psize in (0, 512):
+        mx, mean, ok, _ = run_and_compare(c, partition_size=psize, check_pool=psize == 0)
+        say(f"split D=256 psize {psize}: max {mx:.3g} mean {mean:.3g}")
+        assert ok, (psize, mx, mean)
+
+
+def test_prefill_head_dim_256_bitwise_across_block_sizes():
+    _bitwise_across_block_sizes("xpbs256", 126, [200, 1, 37, 1, 129, 5], [1000, 700, 37, 33, 700, 9], 16, 8, 0, D=256)
