@@ -83,9 +83,10 @@ inline Plan make_plan(const pa_attn_params* p) {
   pl.fast = pa::decode_gqa_supported(dt, p->head_dim, g, ps, p->block_size);
   pl.prefill = dt == 1 && multi && pa::prefill_supported(p->head_dim, g, p->block_size);
   pl.parts = max_parts(p);
-  // Batches whose multi-row requests all fit 64 / G rows use 64-pair prefill
-  // tiles; such short requests (one row tile) are split over context
-  // partitions when the partition is a whole number of prefill key tiles.
+  // Batches whose multi-row requests all fit one half-size tile (64 / G rows;
+  // 32 / G at D = 256) use half-size prefill tiles; such short requests (one
+  // row tile) are split over context partitions when the partition is a
+  // whole number of prefill key tiles.
   pl.tile_pairs = pa::prefill_tile_pairs(p->head_dim, p->max_query_len <= pa::prefill_tile_pairs(p->head_dim, true) / g);
   pl.split_rows = (pl.fast && pl.prefill && pl.parts > 1 && ps % pa::kPrefillKeys == 0 &&
                    p->max_query_len <= pl.tile_pairs / g)
@@ -115,7 +116,7 @@ inline size_t region_floats(const pa_attn_params* p, int64_t rows, int64_t parts
   return size_t(rows) * p->num_q_heads * parts * (p->head_dim + 2);
 }
 
-// Entries the prefill work list can hold: tiles of kPrefillPairs (row, head)
+// Entries the prefill work list can hold: tiles of pl.tile_pairs (row, head)
 // pairs, or one per partition of a split short request.
 inline int64_t prefill_capacity(const pa_attn_params* p, const Plan& pl) {
   const int g = p->num_q_heads / p->num_kv_heads;

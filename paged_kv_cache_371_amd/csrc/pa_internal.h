@@ -104,8 +104,6 @@ constexpr int kPlanClaimInt = 11;        // header slot: claim counter of the fa
                                          // re-armed by the last wave of each decode launch)
 constexpr int kPlanDoneInt = 12;         // header slot: waves of the fast decode launch that have finished
 constexpr int kMaxPartBuckets = 512;     // partition_size / 16 of the fast kernel, at most
-constexpr int kPrefillPairs = 128;       // (query row, head) pairs per prefill work item (chunked prefill)
-constexpr int kPrefillPairsShort = 64;   // ... when every multi-row request fits 64 / G rows
 constexpr int kPrefillKeys = 64;         // keys per prefill K/V tile
 
 struct PlanArgs {
