@@ -490,8 +490,15 @@ static hipError_t launch_merge_t(const DecodeArgs& a, int64_t partial_rows, hipS
   return hipGetLastError();
 }
 
+// LDS a generic decode workgroup may take (its scores and partial outputs);
+// gfx950 gives a workgroup up to 160 KiB.
+constexpr size_t kGenericLdsMax = 128 * 1024;
+
 template <typename E, int D, int G>
 static hipError_t launch_one(const DecodeArgs& a, int64_t partial_rows, hipStream_t stream) {
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_kernel<E, D, G>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(kGenericLdsMax));
+  if (attr != hipSuccess) return attr;
   const size_t lds = lds_bytes<E, D, G>(a.part_size);
   dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
   hipLaunchKernelGGL((decode_kernel<E, D, G>), grid, dim3(256), lds, stream, a);
@@ -517,7 +524,7 @@ bool decode_supported(int dtype, int head_dim, int group, int part_size) {
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return false;
   if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16) return false;
   if (part_size < 16 || part_size > 8192 || part_size % 16) return false;
-  return decode_lds_bytes(dtype, head_dim, group, part_size) <= 64 * 1024;
+  return decode_lds_bytes(dtype, head_dim, group, part_size) <= kGenericLdsMax;
 }
 
 size_t decode_lds_bytes(int dtype, int head_dim, int group, int part_size) {
