@@ -91,10 +91,11 @@ typedef struct {
   int32_t head_dim;            /* D: 64, 128 or 256 */
   int32_t block_size;          /* tokens per physical block: 16 (the pages' default), 8 or 32.
                                   The fast single-row decode kernel (bf16 or 8-bit pools)
-                                  takes D = 64 and 128, and 256 with Hq/Hkv <= 2, at all
-                                  three block sizes; the MFMA prefill kernel takes D = 64,
-                                  128 and 256 at all three; every other shape runs on the
-                                  generic split-K kernel. */
+                                  takes D = 64, 128 and 256 with Hq/Hkv a power of two up
+                                  to 64 (16 at D = 256), at all three block sizes; the
+                                  MFMA prefill kernel takes D = 64, 128 and 256 with
+                                  Hq/Hkv in {1, 2, 4, 8} at all three; every other shape
+                                  runs on the generic split-K kernel. */
   int64_t num_blocks;          /* physical blocks in each pool */
   int32_t max_blocks_per_seq;  /* row length of block_tables */
   int32_t max_query_len;       /* host bound: >= every n_b */
@@ -234,8 +235,8 @@ pa_status pa_cache_write_fp8(const void* k_new, const void* v_new, int64_t kv_ro
  * pa_attention_varlen_fp8 -- as pa_attention_varlen with 8-bit pools: the
  * attention runs over K = decode(k_cache) * k_scale and V = decode(v_cache) *
  * v_scale.  q and out are bf16 (p->dtype == PA_BF16); D = 64 or 128 with
- * Hq/Hkv in {1, 2, 4, 8}, or D = 256 with Hq/Hkv in {1, 2}; block size 8,
- * 16 or 32; single-row (decode) requests only
+ * Hq/Hkv a power of two up to 64, or D = 256 with Hq/Hkv a power of two up to
+ * 16; block size 8, 16 or 32; single-row (decode) requests only
  * (max_query_len <= 1), otherwise PA_ERR_UNSUPPORTED.  Scales finite and > 0.  The workspace is
  * sized by pa_attention_workspace_size(p).
  */
@@ -281,7 +282,8 @@ const char* pa_status_string(pa_status s);
  * pa_attn_params.sliding_window; 201: block sizes 8 and 32, D = 256; 202:
  * 8-bit pools at block sizes 8 and 32; 203: pa_attention_plan / pa_attention_run;
  * 204: the fast decode kernel and 8-bit pools at D = 64 and 256, the MFMA
- * prefill kernel at D = 64 and 256). */
+ * prefill kernel at D = 64 and 256; 205: the fast decode kernel and 8-bit
+ * pools for Hq/Hkv above 8, and above 2 at D = 256). */
 int32_t pa_abi_version(void);
 
 #ifdef __cplusplus

@@ -170,6 +170,7 @@ constexpr int kClaimBatch = PA_DECODE_CLAIM_BATCH; // items per claim
 #endif
 constexpr int kRequestTiles = PA_DECODE_REQUEST_TILES;   // tiles before an item's end its worker asks for the next
 static_assert(kClaimBatch <= kWavesPerGroup && kWavesPerGroup <= kQueue, "one queued item per worker at most");
+static_assert(kStaticRounds * kWavesPerGroup % 4 == 0, "claims of up to 4 items start aligned");
 
 // Pairing masks of the 16-lane reduction steps and their DPP controls.
 constexpr int kStepMask[4] = {8, 7, 2, 1};
@@ -233,11 +234,11 @@ __device__ __forceinline__ float dot_bf16(const V& q, const V& k) {
 }
 
 
-// Geometry of one work item: (request b, KV head kvh, partition part) of a
+// Geometry of one work item: (request b, head group hg, partition part) of a
 // single-row request, served by one wave.  All fields are wave-uniform.
 struct Item {
   int valid;
-  int b, kvh, q0;
+  int b, hg, q0;   // hg: head group (query heads hg*G .. hg*G+G-1)
   int parts;     // partition index among the request's visible partitions (the partial
                  // slot) | their count << 16
   int lo;        // first visible key (sliding window), 0 without one
@@ -251,8 +252,9 @@ struct Item {
 };
 
 
-// Item t of the list plan_kernel built: entry t / Hkv (passed in), KV head
-// t % Hkv.  An index past the list gives a placeholder with in-range
+// Item t of the list plan_kernel built: entry t / H, head group t % H of the
+// H = Hkv * 2^head_split_log2 groups of G query heads; the group's KV head is
+// its index >> head_split_log2.  An index past the list gives a placeholder with in-range
 // addresses and no tiles.  Every field goes through readfirstlane, so the descriptors and
 // table loads built from it stay scalar.
 template <bool F8, int BS, int D>
@@ -261,9 +263,9 @@ __device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t,
   constexpr int kHeadBytes = BS * D * (F8 ? 1 : 2);   // one KV head's rows of a block
   Item it;
   it.valid = t < total;
-  int b = 0, part = 0, q0 = 0, L = 1, kvh = 0;
+  int b = 0, part = 0, q0 = 0, L = 1, hg = 0;
   if (it.valid) {
-    kvh = t % a.num_kv_heads;
+    hg = t % (a.num_kv_heads << a.head_split_log2);
     b = ent.x;
     part = ent.y;
     q0 = ent.z;
@@ -278,7 +280,7 @@ __device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t,
   const int lb0 = tok0 / kBlock;
   const int nb = it.valid ? (tok1 + kBlock - 1) / kBlock - lb0 : 0;
   it.b = uni(b);
-  it.kvh = uni(kvh);
+  it.hg = uni(hg);
   it.parts = uni((part - p_lo) | (((L + P - 1) / P - p_lo) << 16));
   it.q0 = uni(q0);
   it.lo = uni(lo);
@@ -288,8 +290,8 @@ __device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t,
   it.nbr = uni(kRing * ((nb + kRing - 1) / kRing));
   it.valid = uni(it.valid);
   it.table = uni_ptr(a.block_tables + int64_t(b) * a.max_blocks_per_seq);
-  it.kbase = uni_ptr(static_cast<const char*>(a.k_cache) + int64_t(kvh) * kHeadBytes);
-  it.vbase = uni_ptr(static_cast<const char*>(a.v_cache) + int64_t(kvh) * kHeadBytes);
+  it.kbase = uni_ptr(static_cast<const char*>(a.k_cache) + int64_t(hg >> a.head_split_log2) * kHeadBytes);
+  it.vbase = uni_ptr(static_cast<const char*>(a.v_cache) + int64_t(hg >> a.head_split_log2) * kHeadBytes);
   return it;
 }
 
@@ -327,7 +329,8 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
   constexpr int kNZ = kNV / 4;          // accumulators per lane after the row reduce-scatter
   constexpr int kRun = kNZ < kE ? kNZ : kE;   // consecutive d values per output run
 
-  const int total = load_const(a.plan, kPlanCountInt) * a.num_kv_heads;
+  const int nh = a.num_kv_heads << a.head_split_log2;   // head groups (work items per list entry)
+  const int total = load_const(a.plan, kPlanCountInt) * nh;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int NW = gridDim.x * kWavesPerGroup;
@@ -344,7 +347,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
   // discards it when the round has no item.
   auto static_entry = [&](int i) -> int4 {
     const int64_t t = int64_t(i) * NW + ((i & 1) ? NW - 1 - wid : wid);
-    const int e = int(min<int64_t>(t / a.num_kv_heads, a.plan_capacity - 1));
+    const int e = int(min<int64_t>(t / nh, a.plan_capacity - 1));
     const int32_t* ep = a.plan + kPlanHeaderInts + 4 * int64_t(e);
     return make_int4(load_const_early(ep, 0), load_const_early(ep, 1), load_const_early(ep, 2), load_const_early(ep, 3));
   };
@@ -391,17 +394,21 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
   if (wave == kWavesPerGroup) {   // the scheduler: one claim per batch of requests
     if (lane == 0) {
       const int64_t ndyn = int64_t(total) - dyn0;
+      // The items of one KV head's head groups are claimed together (up to
+      // one per worker, aligned), so this workgroup's workers stream the same
+      // tiles side by side and the repeated reads are served by L2.
+      const int unit = min(1 << a.head_split_log2, kWavesPerGroup);
       int pushed = 0, served = 0;
       for (bool more = ndyn > 0; more;) {
         int req;
         while ((req = lds_load(&s_qreq)) <= served) __builtin_amdgcn_s_sleep(1);
-        const int want = min(req - served, kClaimBatch);
+        const int want = (min(req - served, kClaimBatch) + unit - 1) / unit * unit;
         const int c = __hip_atomic_fetch_add(claim_counter, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int n = int(max<int64_t>(0, min<int64_t>(want, ndyn - c)));
         for (int j = 0; j < n; ++j) {
           const int q = pushed + j;
           const int t = int(dyn0 + c + j);
-          const int4 e = entries[t / a.num_kv_heads];
+          const int4 e = entries[t / nh];
           while (lds_load(&s_qfree[q % kQueue]) != q) __builtin_amdgcn_s_sleep(1);
           s_qitem[q % kQueue] = t;
           s_qent[q % kQueue] = e;
@@ -463,7 +470,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
   __shared__ uint32_t sq[kWavesPerGroup][64 * kQDw];
   auto fetch_q = [&](const Item& it, uint32_t(&qt)[kQDw]) {
     const uint32_t* src = reinterpret_cast<const uint32_t*>(
-        static_cast<const char*>(a.q) + (int64_t(it.q0) * a.q_row_stride + int64_t(it.kvh) * G * D) * 2);
+        static_cast<const char*>(a.q) + (int64_t(it.q0) * a.q_row_stride + int64_t(it.hg) * G * D) * 2);
     if constexpr (kQDw >= 4) {
 #pragma unroll
       for (int c = 0; c < kQDw / 4; ++c) {
@@ -497,7 +504,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
 
   auto load_q = [&](Words(&qreg)[G], const Item& it) {   // q slices, lane-relative order h(r ^ M_j)
     const char* qrow =
-        static_cast<const char*>(a.q) + (int64_t(it.q0) * a.q_row_stride + int64_t(it.kvh) * G * D) * 2;
+        static_cast<const char*>(a.q) + (int64_t(it.q0) * a.q_row_stride + int64_t(it.hg) * G * D) * 2;
     static_for<G>([&](auto J) {
       constexpr int j = decltype(J)::value;
       const int hh = (r ^ q_mask<K>(j)) >> (4 - K);
@@ -740,7 +747,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
       const int head = (hr + dir * j) & (G - 1);
       const int src = head * kRot;   // a lane of row 0 whose head is `head`
       const float Lh = __shfl(lw, src);
-      const int hq = cur.kvh * G + head;
+      const int hq = cur.hg * G + head;
       if ((cur.parts >> 16) == 1) {
         const float inv = 1.f / Lh;
         __bf16* orow = static_cast<__bf16*>(a.out) + int64_t(cur.q0) * a.o_row_stride + int64_t(hq) * D + r * kE + e0;
@@ -770,7 +777,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
       }
     }
     if ((cur.parts >> 16) > 1 && tg == 0 && (r & (kRot - 1)) == 0) {   // one lane per head
-      const int64_t slot = (int64_t(cur.b) * a.num_q_heads + cur.kvh * G + hr) * a.max_parts + (cur.parts & 0xffff);
+      const int64_t slot = (int64_t(cur.b) * a.num_q_heads + cur.hg * G + hr) * a.max_parts + (cur.parts & 0xffff);
       a.ws_ml[2 * slot] = mw;
       a.ws_ml[2 * slot + 1] = lw;
     }
@@ -782,10 +789,28 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
 
 }  // namespace
 
+// Query heads per work item.  At D = 256 the accumulators and q slices of
+// G = 4 or more leave no registers for the tile ring, so a KV head's heads are
+// served two at a time; above 8 heads (any D) eight at a time.  The items of
+// one KV head are adjacent in the list, so they are dealt to waves of one
+// workgroup and stream the same tiles at about the same time: the second
+// read of a tile is mostly served by L2.
+static int item_group(int head_dim, int group) {
+  const int cap = head_dim == 256 ? 2 : 8;
+  return group < cap ? group : cap;
+}
+
+constexpr int kMaxHeadSplit = 8;
+
+int decode_gqa_head_split(int head_dim, int group) {
+  const int gi = item_group(head_dim, group);
+  return gi > 0 ? group / gi : 1;
+}
+
 bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size, int block_size) {
-  // at D = 256 the accumulators and q slices of G = 4 or 8 leave no registers for the ring
-  const bool dims = head_dim == 64 || head_dim == 128 || (head_dim == 256 && group <= 2);
-  return dtype == 1 && dims && (group == 1 || group == 2 || group == 4 || group == 8) &&
+  const bool pow2 = group >= 1 && (group & (group - 1)) == 0;
+  return dtype == 1 && (head_dim == 64 || head_dim == 128 || head_dim == 256) && pow2 &&
+         decode_gqa_head_split(head_dim, group) <= kMaxHeadSplit &&
          (block_size == 8 || block_size == 16 || block_size == 32) && part_size % kBlock == 0 &&
          part_size / kBlock <= kMaxPartBuckets;
 }
@@ -813,7 +838,7 @@ int persistent_groups() {
 
 template <int G, bool F8, int BS, int D>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t upper = int64_t(a.num_seqs) * a.max_parts * a.num_kv_heads;
+  const int64_t upper = (int64_t(a.num_seqs) * a.max_parts * a.num_kv_heads) << a.head_split_log2;
   const int64_t grid = std::min<int64_t>(upper, persistent_groups<G, F8, BS, D>());
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL((decode_gqa_kernel<G, F8, BS, D>), dim3(grid), dim3(64 * (kWavesPerGroup + 1)), 0, stream, a);
@@ -870,7 +895,7 @@ hipError_t launch_f(int group, int head_dim, const DecodeArgs& a, hipStream_t st
 
 int decode_gqa_workers(int group) {
   int g = 0;
-  switch (group) {
+  switch (item_group(128, group)) {
     case 1: g = persistent_groups<1, false, 16, 128>(); break;
     case 2: g = persistent_groups<2, false, 16, 128>(); break;
     case 4: g = persistent_groups<4, false, 16, 128>(); break;
@@ -880,9 +905,16 @@ int decode_gqa_workers(int group) {
   return g * kWavesPerGroup;
 }
 
-// a.block_size selects the paging (8, 16 or 32 tokens per block).
+// a.block_size selects the paging (8, 16 or 32 tokens per block); the kernel
+// is instantiated for the item group, and a.head_split_log2 is set here.
 hipError_t launch_decode_gqa(int group, int head_dim, bool fp8_cache, const DecodeArgs& a, hipStream_t stream) {
-  return fp8_cache ? launch_f<true>(group, head_dim, a, stream) : launch_f<false>(group, head_dim, a, stream);
+  const int gi = item_group(head_dim, group);
+  const int split = decode_gqa_head_split(head_dim, group);
+  if (gi <= 0 || gi * split != group || split > kMaxHeadSplit) return hipErrorInvalidValue;
+  DecodeArgs b = a;
+  b.head_split_log2 = 0;
+  while ((1 << b.head_split_log2) < split) ++b.head_split_log2;
+  return fp8_cache ? launch_f<true>(gi, head_dim, b, stream) : launch_f<false>(gi, head_dim, b, stream);
 }
 
 }  // namespace pa

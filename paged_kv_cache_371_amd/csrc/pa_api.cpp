@@ -30,7 +30,8 @@ inline bool block_size_ok(int32_t bs) { return bs == 8 || bs == 16 || bs == 32; 
 // same in any batch).  The default (0) picks, for the fast decode kernel, the
 // largest of 2048 / 1024 / 512 tokens that still gives every wave of the
 // persistent grid about 8 work items by the host's upper bound
-// B * Hkv * ceil(max_seq_len / P): long partitions cost less per token (one
+// B * Hkv * S * ceil(max_seq_len / P) (S: work items per KV head, 1 unless a
+// KV head has more query heads than one item holds): long partitions cost less per token (one
 // merge per partition), but too few of them leave waves idle.
 inline int effective_partition(const pa_attn_params* p) {
   if (p->partition_size > 0) return p->partition_size;
@@ -44,7 +45,8 @@ inline int effective_partition(const pa_attn_params* p) {
       p->max_query_len > 1 && !(dt == 1 && pa::prefill_supported(p->head_dim, g, p->block_size));
   const int64_t want = int64_t(8) * pa::decode_gqa_workers(g);
   for (int ps : {2048, 1024}) {
-    const int64_t items = int64_t(p->num_seqs) * p->num_kv_heads * ((int64_t(p->max_seq_len) + ps - 1) / ps);
+    const int64_t items = int64_t(p->num_seqs) * p->num_kv_heads * pa::decode_gqa_head_split(p->head_dim, g) *
+                          ((int64_t(p->max_seq_len) + ps - 1) / ps);
     if (items >= want && (!generic_rows || pa::decode_supported(dt, p->head_dim, g, ps))) return ps;
   }
   return pa::kDefaultPartition;
@@ -169,7 +171,7 @@ pa_status check_params(const pa_attn_params* p) {
 
 extern "C" {
 
-int32_t pa_abi_version(void) { return 204; }
+int32_t pa_abi_version(void) { return 205; }
 
 const char* pa_status_string(pa_status s) {
   switch (s) {

@@ -43,6 +43,7 @@ struct DecodeArgs {
   int32_t merge_capacity;   // entries the merge list has room for
   int32_t sliding_window;   // 0, or W > 0: a row sees only the last W positions up to its own
   int32_t block_size;       // tokens per physical block (the generic kernel takes 8, 16 or 32)
+  int32_t head_split_log2;  // fast kernel: a KV head's query heads are served by 2^this work items
 };
 
 // Requests a decode launch serves: all of them, only those with exactly one
@@ -136,6 +137,9 @@ size_t plan_bytes(int64_t decode_capacity, int64_t prefill_capacity, int64_t mer
 bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size, int block_size);
 // Waves of the persistent fast decode kernel on the current device.
 int decode_gqa_workers(int group);
+// Work items per (KV head, partition) of the fast decode kernel: 1, or more
+// where one item cannot hold all of a KV head's query heads.
+int decode_gqa_head_split(int head_dim, int group);
 // fp8_cache: the pools hold OCP FP8 E4M3 codes (scales folded into scale_log2 and lsum_scale).
 hipError_t launch_decode_gqa(int group, int head_dim, bool fp8_cache, const DecodeArgs& a, hipStream_t stream);
 // Partition merge alone (for a DecodeArgs whose partials are already written).

@@ -58,7 +58,7 @@ def test_struct_layout_matches_c(tmp_path):
 
 
 def test_status_strings_and_version(L):
-    assert L.pa_abi_version() == 204
+    assert L.pa_abi_version() == 205
     for code in range(0, -11, -1):
         s = L.pa_status_string(code).decode()
         assert s.startswith("PA_")
@@ -161,10 +161,13 @@ def test_fp8_host_errors(L):
     # 8- and 32-token blocks are served (here the missing workspace is the error)
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(block_size=32)), 1.0, 1.0, None, 0, None) == -5
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(block_size=8, max_blocks_per_seq=8)), 1.0, 1.0, None, 0, None) == -5
-    # D = 64 is served (the missing workspace is the error); D = 256 is not on the 8-bit path
+    # D = 64 and 256 are served (the missing workspace is the error), D = 256 with G = 4 as two
+    # items of two heads per KV head; a group that is not a power of two is not
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(head_dim=64, q_row_stride=512, o_row_stride=512)),
              1.0, 1.0, None, 0, None) == -5
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(head_dim=256, q_row_stride=2048, o_row_stride=2048)),
+             1.0, 1.0, None, 0, None) == -5
+    assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(num_q_heads=6, q_row_stride=768, o_row_stride=768)),
              1.0, 1.0, None, 0, None) == -3
 
 

@@ -139,9 +139,11 @@ def test_decode_fp8_block_sizes(bs, Hq, Hkv):
         assert ok, (psize, mx, mean)
 
 
-@pytest.mark.parametrize("D,Hq,Hkv", [(64, 8, 8), (64, 32, 8), (64, 64, 8), (256, 8, 8), (256, 16, 8)])
+@pytest.mark.parametrize("D,Hq,Hkv", [(64, 8, 8), (64, 32, 8), (64, 64, 8), (256, 8, 8), (256, 16, 8),
+                                      (256, 64, 8), (128, 128, 8)])
 def test_decode_fp8_head_dim_64(D, Hq, Hkv):
-    """8-bit pools at D = 64 (4 codes of a row per lane) and D = 256 (16 codes)."""
+    """8-bit pools at D = 64 (4 codes of a row per lane) and D = 256 (16 codes),
+    and KV heads served by several items (G = 8 at D = 256, G = 16 at D = 128)."""
     c = build_case(f"dec8d{D}_{Hq}", 37, "bf16", Hq, Hkv, D, [1] * len(LENS), LENS)
     fc = Fp8Case(c, 10, 0.5, 0.25)
     for psize in (0, 256):

@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import paged_kv_cache_371_amd as pa
-from tests.gpu_util import oracle_out, oracle_pools, run_and_compare, say, to_dev, to_host
+from tests.gpu_util import DeviceCase, oracle_out, oracle_pools, run_and_compare, say, to_dev, to_host
 from workloads import build_case
 
 pytestmark = pytest.mark.gpu
@@ -298,3 +298,51 @@ def test_split_short_requests_head_dim_256():
 
 def test_prefill_head_dim_256_bitwise_across_block_sizes():
     _bitwise_across_block_sizes("xpbs256", 126, [200, 1, 37, 1, 129, 5], [1000, 700, 37, 33, 700, 9], 16, 8, 0, D=256)
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,bs", [(256, 32, 8, 16), (256, 64, 8, 8), (256, 16, 1, 32), (128, 64, 4, 16),
+                                         (128, 32, 1, 32), (64, 128, 4, 16)])
+def test_fast_decode_head_split(D, Hq, Hkv, bs):
+    """A KV head with more query heads than one work item holds (G > 2 at
+    D = 256, G > 8 otherwise) is served by several adjacent items of the fast
+    kernel that read the same tiles; the plan's decode list is filled, so the
+    fast kernel (not the generic one) ran."""
+    c = build_case(f"hs{D}_{Hq}_{Hkv}_{bs}", 200 + Hq // Hkv + D, "bf16", Hq, Hkv, D, [1] * len(FAST_LENS), FAST_LENS,
+                   block_size=bs)
+    for psize in (0, 48):
+        mx, mean, ok, dc = run_and_compare(c, partition_size=psize, check_pool=psize == 0)
+        say(f"split heads D={D} {Hq}/{Hkv} bs {bs} psize {psize}: max {mx:.3g} mean {mean:.3g}")
+        assert ok, (psize, mx, mean)
+    p = pa.make_params(dc.q, dc.k_cache, dc.cu, dc.tables, Hkv, float(c.scale), c.max_query_len, c.max_seq_len,
+                       out=dc.out)
+    ws = torch.zeros(pa.workspace_size(p), dtype=torch.uint8, device="cuda:0")
+    pa.attention_varlen(dc.out, dc.q, dc.k_cache, dc.v_cache, dc.cu, dc.seq_lens, dc.tables, float(c.scale),
+                        c.max_query_len, c.max_seq_len, workspace=ws)
+    torch.cuda.synchronize()
+    hdr = ws[:64 * 4].view(torch.int32).cpu().numpy()
+    P = pa.partition_size(p)
+    assert hdr[8] == sum(-(-int(L) // P) for L in FAST_LENS), (hdr[8], P)
+    assert hdr[11] == 0 and hdr[12] == 0
+
+
+def test_fast_decode_head_split_bitwise_per_head():
+    """Splitting a KV head's query heads over items does not change any head's
+    result: a 64/8-head layer at D = 128 (one item of 8 heads per KV head)
+    equals, head for head, the same heads served as a 128/8-head layer (two
+    items of 8), at one explicit partition size."""
+    c8 = build_case("hsb8", 240, "bf16", 64, 8, 128, [1] * len(FAST_LENS), FAST_LENS)
+    dc = DeviceCase(c8)
+    dc.cache_write()
+    dc.attention(512)
+    torch.cuda.synchronize()
+    T = dc.q.shape[0]
+    # heads 8j..8j+7 of KV head j, twice: 16 query heads per KV head
+    q2 = dc.q.view(T, 8, 8, 128).repeat(1, 1, 2, 1).reshape(T, 128, 128).contiguous()
+    out2 = torch.empty_like(q2)
+    pa.attention_varlen(out2, q2, dc.k_cache, dc.v_cache, dc.cu, dc.seq_lens, dc.tables, float(c8.scale),
+                        1, c8.max_seq_len, partition_size=512)
+    torch.cuda.synchronize()
+    o2 = out2.view(T, 8, 2, 8, 128)
+    f = dc.out.view(T, 8, 8, 128)
+    for half in range(2):
+        assert torch.equal(o2[:, :, half].contiguous().view(torch.int16), f.contiguous().view(torch.int16)), half
