@@ -213,7 +213,7 @@ def _sample_rows(c, k=24, seed=0):
 
 
 @pytest.mark.parametrize("name", ["mha_decode_bf16", "gqa_decode_bf16", "prefix_long_bf16", "mixed_prefill_bf16",
-                                  "spec_verify_bf16"])
+                                  "spec_verify_bf16", "gqa_decode_d256_bf16"])
 def test_config_full_size_sampled(name):
     c = make_config(name, 0)
     rows = _sample_rows(c)

@@ -75,7 +75,8 @@ def test_shared_prefix_tables_and_negative_slots():
     _check_structure(c)
 
 
-@pytest.mark.parametrize("name,lo,hi,B", [("mha_decode_bf16", 128, 2048, 64), ("gqa_decode_bf16", 16, 8192, 256)])
+@pytest.mark.parametrize("name,lo,hi,B", [("mha_decode_bf16", 128, 2048, 64), ("gqa_decode_bf16", 16, 8192, 256),
+                                          ("gqa_decode_d256_bf16", 16, 8192, 256)])
 def test_decode_config_lengths_and_pool(name, lo, hi, B):
     c = make_config(name, 0, poison=False)
     assert c.num_seqs == B and (c.q_lens == 1).all()
@@ -83,7 +84,7 @@ def test_decode_config_lengths_and_pool(name, lo, hi, B):
     need = int(np.sum(-(-c.seq_lens // 16)))
     assert c.num_blocks == int(np.ceil(1.25 * need))
     _check_structure(c)
-    if name == "gqa_decode_bf16":
+    if name.startswith("gqa_decode"):
         med = float(np.median(c.seq_lens))
         assert 700 < med < 1500     # log-normal, median 1024
 

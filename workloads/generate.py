@@ -268,7 +268,7 @@ def build_case(
 
 
 # ---------------------------------------------------------------------------
-# The five workload configurations.  Each draws its lengths from stream 0.
+# The workload configurations.  Each draws its lengths from stream 0.
 
 
 def _tiny_decode_f32(seed, **kw):
@@ -289,6 +289,14 @@ def _gqa_decode_bf16(seed, **kw):
     g = _gen(seed, S_LENGTHS)
     L = np.clip(np.rint(g.lognormal(math.log(1024.0), 1.0, size=256)), 16, 8192).astype(np.int64)
     return build_case("gqa_decode_bf16", seed, "bf16", 64, 8, 128, np.ones(256, np.int64), L,
+                      max_blocks_per_seq=512, **kw)
+
+
+def _gqa_decode_d256_bf16(seed, **kw):
+    # the GQA decode layer's requests and lengths at head dim 256, 32 query / 8 KV heads
+    g = _gen(seed, S_LENGTHS)
+    L = np.clip(np.rint(g.lognormal(math.log(1024.0), 1.0, size=256)), 16, 8192).astype(np.int64)
+    return build_case("gqa_decode_d256_bf16", seed, "bf16", 32, 8, 256, np.ones(256, np.int64), L,
                       max_blocks_per_seq=512, **kw)
 
 
@@ -323,6 +331,7 @@ _CONFIGS = {
     "tiny_decode_f32": _tiny_decode_f32,
     "mha_decode_bf16": _mha_decode_bf16,
     "gqa_decode_bf16": _gqa_decode_bf16,
+    "gqa_decode_d256_bf16": _gqa_decode_d256_bf16,
     "mixed_prefill_bf16": _mixed_prefill_bf16,
     "prefix_long_bf16": _prefix_long_bf16,
     "spec_verify_bf16": _spec_verify_bf16,
