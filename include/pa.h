@@ -94,8 +94,8 @@ typedef struct {
                                   takes D = 64, 128 and 256 with Hq/Hkv a power of two up
                                   to 64 (16 at D = 256), at all three block sizes; the
                                   MFMA prefill kernel takes D = 64, 128 and 256 with
-                                  Hq/Hkv in {1, 2, 4, 8} at all three; every other shape
-                                  runs on the generic split-K kernel. */
+                                  Hq/Hkv a power of two up to 64 at all three; every
+                                  other shape runs on the generic split-K kernel. */
   int64_t num_blocks;          /* physical blocks in each pool */
   int32_t max_blocks_per_seq;  /* row length of block_tables */
   int32_t max_query_len;       /* host bound: >= every n_b */
@@ -283,7 +283,8 @@ const char* pa_status_string(pa_status s);
  * 8-bit pools at block sizes 8 and 32; 203: pa_attention_plan / pa_attention_run;
  * 204: the fast decode kernel and 8-bit pools at D = 64 and 256, the MFMA
  * prefill kernel at D = 64 and 256; 205: the fast decode kernel and 8-bit
- * pools for Hq/Hkv above 8, and above 2 at D = 256). */
+ * pools for Hq/Hkv above 8, and above 2 at D = 256; the MFMA prefill kernel
+ * for Hq/Hkv above 8). */
 int32_t pa_abi_version(void);
 
 #ifdef __cplusplus

@@ -89,10 +89,11 @@ inline Plan make_plan(const pa_attn_params* p) {
   // 32 / G at D = 256) use half-size prefill tiles; such short requests (one
   // row tile) are split over context partitions when the partition is a
   // whole number of prefill key tiles.
-  pl.tile_pairs = pa::prefill_tile_pairs(p->head_dim, p->max_query_len <= pa::prefill_tile_pairs(p->head_dim, true) / g);
+  const int gp = pa::prefill_item_group(g);   // query heads per prefill work item
+  pl.tile_pairs = pa::prefill_tile_pairs(p->head_dim, p->max_query_len <= pa::prefill_tile_pairs(p->head_dim, true) / gp);
   pl.split_rows = (pl.fast && pl.prefill && pl.parts > 1 && ps % pa::kPrefillKeys == 0 &&
-                   p->max_query_len <= pl.tile_pairs / g)
-                      ? pl.tile_pairs / g
+                   p->max_query_len <= pl.tile_pairs / gp)
+                      ? pl.tile_pairs / gp
                       : 0;
   if (pl.fast) {
     pl.generic_mode = (multi && !pl.prefill) ? pa::kMultiRowOnly : -1;
@@ -121,8 +122,7 @@ inline size_t region_floats(const pa_attn_params* p, int64_t rows, int64_t parts
 // Entries the prefill work list can hold: tiles of pl.tile_pairs (row, head)
 // pairs, or one per partition of a split short request.
 inline int64_t prefill_capacity(const pa_attn_params* p, const Plan& pl) {
-  const int g = p->num_q_heads / p->num_kv_heads;
-  const int64_t rows = pl.tile_pairs / g;
+  const int64_t rows = pl.tile_pairs / pa::prefill_item_group(p->num_q_heads / p->num_kv_heads);
   const int64_t per_seq = (int64_t(p->max_query_len) + rows - 1) / rows;
   return int64_t(p->num_seqs) * (pl.split_rows ? std::max<int64_t>(per_seq, pl.parts) : per_seq);
 }
@@ -307,7 +307,7 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
     pa_.merge_off_ints = merge_off(p, pl);
     pa_.num_seqs = p->num_seqs;
     pa_.part_size = d.part_size;
-    pa_.group = g;
+    pa_.group = pa::prefill_item_group(g);
     pa_.decode = pl.fast ? 1 : 0;
     pa_.prefill = pl.prefill ? 1 : 0;
     pa_.max_query_len = p->max_query_len;

@@ -80,6 +80,7 @@ struct PrefillArgs {
   int32_t tile_pairs;   // (query row, head) pairs per work item: 128, or 64 for short requests
   int32_t sliding_window;
   int32_t block_size;   // tokens per physical block: 8, 16 or 32
+  int32_t head_split_log2;   // a KV head's query heads are served by 2^this items (set by launch_prefill)
 };
 
 hipError_t launch_cache_write(const void* k_new, const void* v_new, int64_t kv_row_stride_bytes, void* k_cache,
@@ -152,6 +153,9 @@ size_t decode_lds_bytes(int dtype, int head_dim, int group, int part_size);
 // MFMA kernel for multi-row requests (bf16, D = 128, G in {1, 2, 4, 8}, blocks of 8, 16 or 32 tokens).
 hipError_t launch_prefill(int head_dim, int group, const PrefillArgs& a, hipStream_t stream);
 bool prefill_supported(int head_dim, int group, int block_size);
+// Query heads per prefill work item: the group, at most 8 (larger groups are
+// served by several items per KV head; the work list's row tiles use this).
+int prefill_item_group(int group);
 // (query row, head) pairs per prefill work item: 128 (64 at D = 256), or half
 // that when every multi-row request is short.
 int prefill_tile_pairs(int head_dim, bool short_rows);

@@ -145,7 +145,9 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
   extern __shared__ __align__(16) char smem[];
 
   const int hkv = a.num_kv_heads;
-  const int total = load_const(a.plan, kPlanPrefCountInt) * hkv;
+  const int split_log2 = PA_KARG(head_split_log2);
+  const int nh = hkv << split_log2;   // head groups of G query heads; group hg reads KV head hg >> split_log2
+  const int total = load_const(a.plan, kPlanPrefCountInt) * nh;
   const int ngroups = gridDim.x;
   const int wg = blockIdx.x;
   const int tid = threadIdx.x;
@@ -169,8 +171,9 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
   for (int i = 0, base = 0; base < total; ++i, base += ngroups) {
     const int t = base + ((i & 1) ? ngroups - 1 - wg : wg);
     if (t >= total) continue;
-    const int e = t / hkv;
-    const int kvh = t - e * hkv;
+    const int e = t / nh;
+    const int hg = t - e * nh;
+    const int kvh = hg >> split_log2;
     const int b = load_const(entries, 4 * int64_t(e));
     const int tile_part = load_const(entries, 4 * int64_t(e) + 1);
     const int q0 = load_const(entries, 4 * int64_t(e) + 2);
@@ -214,7 +217,7 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
     for (int mb = 0; mb < kMB; ++mb) {
       const int m = wave * (16 * kMB) + mb * 16 + lc;
       jrow[mb] = j0 + m / G;
-      hq[mb] = kvh * G + m % G;
+      hq[mb] = hg * G + m % G;
       mvalid[mb] = jrow[mb] < j1;
       lolim[mb] = mvalid[mb] ? window_start(P + jrow[mb], window) : 0;
       span[mb] = mvalid[mb] ? P + jrow[mb] - lolim[mb] : 0;
@@ -521,8 +524,11 @@ hipError_t launch_g(const PrefillArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+int prefill_item_group(int group) { return group < 8 ? group : 8; }
+
 bool prefill_supported(int head_dim, int group, int block_size) {
-  return (head_dim == 64 || head_dim == 128 || head_dim == 256) && (group == 1 || group == 2 || group == 4 || group == 8) &&
+  const bool pow2 = group >= 1 && group <= 64 && (group & (group - 1)) == 0;
+  return (head_dim == 64 || head_dim == 128 || head_dim == 256) && pow2 &&
          (block_size == 8 || block_size == 16 || block_size == 32);
 }
 
@@ -558,10 +564,14 @@ hipError_t launch_d(int group, const PrefillArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_prefill(int head_dim, int group, const PrefillArgs& a, hipStream_t stream) {
-  if (head_dim == 128) return launch_d<128>(group, a, stream);
-  if (head_dim == 64) return launch_d<64>(group, a, stream);
-  if (head_dim == 256) return launch_d<256>(group, a, stream);
-  return hipErrorInvalidValue;
+  if (!prefill_supported(head_dim, group, a.block_size)) return hipErrorInvalidValue;
+  const int gi = prefill_item_group(group);
+  PrefillArgs b = a;
+  b.head_split_log2 = 0;
+  while ((gi << b.head_split_log2) < group) ++b.head_split_log2;
+  if (head_dim == 128) return launch_d<128>(gi, b, stream);
+  if (head_dim == 64) return launch_d<64>(gi, b, stream);
+  return launch_d<256>(gi, b, stream);
 }
 
 int prefill_tile_pairs(int head_dim, bool short_rows) {

@@ -346,3 +346,26 @@ def test_fast_decode_head_split_bitwise_per_head():
     f = dc.out.view(T, 8, 8, 128)
     for half in range(2):
         assert torch.equal(o2[:, :, half].contiguous().view(torch.int16), f.contiguous().view(torch.int16)), half
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,bs", [(128, 64, 4, 16), (128, 128, 4, 8), (64, 128, 8, 32), (256, 32, 2, 16),
+                                         (256, 64, 4, 8)])
+def test_prefill_head_split(D, Hq, Hkv, bs):
+    """Multi-row requests of a KV head with more than 8 query heads: the MFMA
+    kernel serves the heads 8 at a time (adjacent items on the same K/V), with
+    chunked prefill, decode rows and short requests in one batch; and a batch
+    of short requests only, which takes the split-over-partitions path."""
+    n = [200, 1, 37, 1, 5, 129, 1, 2]
+    L = [1000, 700, 37, 33, 9, 700, 3000, 17]
+    c = build_case(f"phs{D}_{Hq}_{Hkv}_{bs}", 260 + Hq // Hkv + D, "bf16", Hq, Hkv, D, n, L, block_size=bs)
+    for psize in (0, 64):
+        mx, mean, ok, _ = run_and_compare(c, partition_size=psize, check_pool=psize == 0)
+        say(f"prefill split heads D={D} {Hq}/{Hkv} bs {bs} psize {psize}: max {mx:.3g} mean {mean:.3g}")
+        assert ok, (psize, mx, mean)
+    n = [4, 1, 3, 2, 1, 3, 2]
+    L = [3000, 2049, 1500, 700, 5, 4100, 8]
+    c = build_case(f"shs{D}_{Hq}_{Hkv}_{bs}", 270 + Hq // Hkv + D, "bf16", Hq, Hkv, D, n, L, block_size=bs)
+    for psize in (0, 512):
+        mx, mean, ok, _ = run_and_compare(c, partition_size=psize, check_pool=psize == 0)
+        say(f"short split heads D={D} {Hq}/{Hkv} bs {bs} psize {psize}: max {mx:.3g} mean {mean:.3g}")
+        assert ok, (psize, mx, mean)
