@@ -1,7 +1,8 @@
 """GPU parity on seeded random shapes: every dispatch path of the attention
 call against the oracle in one sweep.
 
-Each case draws a head dim (64, 128, 256), a group size (1 to 16), a block
+Each case draws a head dim (64, 128, 256), a group size (1 to 16; 4 to 32
+in the large-group cases, where a KV head's heads span several work items), a block
 size (8, 16, 32), a dtype (bf16 mostly, fp32 sometimes), a batch mixing
 single-row requests with chunked-prefill and short multi-row requests, ragged
 contexts (some a single token), an optional sliding window and an optional
@@ -29,11 +30,14 @@ def _gpu():
     yield
 
 
-def _draw(seed):
+def _draw(seed, large_groups=False):
     rng = np.random.default_rng(1000 + seed)
     dtype = "f32" if rng.random() < 0.2 else "bf16"
     D = int(rng.choice([64, 128, 256]))
     G = int(rng.choice([1, 2, 4, 8, 16]))
+    if large_groups:   # several work items per KV head in the decode and MFMA kernels
+        dtype = "bf16"
+        G = int(rng.choice([16, 32])) if D < 256 else int(rng.choice([4, 8, 16]))
     Hkv = int(rng.choice([1, 2, 4]))
     bs = int(rng.choice([8, 16, 32]))
     B = int(rng.integers(1, 24))
@@ -61,7 +65,15 @@ def _draw(seed):
 
 @pytest.mark.parametrize("seed", range(24))
 def test_random_shape(seed):
-    s = _draw(seed)
+    _check(seed, _draw(seed))
+
+
+@pytest.mark.parametrize("seed", range(24, 32))
+def test_random_shape_large_groups(seed):
+    _check(seed, _draw(seed, large_groups=True))
+
+
+def _check(seed, s):
     c = build_case(f"rand{seed}", 300 + seed, s["dtype"], s["G"] * s["Hkv"], s["Hkv"], s["D"], s["n"], s["L"],
                    block_size=s["bs"])
     say(f"seed {seed}: {s['dtype']} D={s['D']} G={s['G']} Hkv={s['Hkv']} bs={s['bs']} B={len(s['n'])} "
