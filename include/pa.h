@@ -92,7 +92,7 @@ typedef struct {
   int32_t block_size;          /* tokens per physical block: 16 (the pages' default), 8 or 32.
                                   The fast single-row decode kernel (bf16 or 8-bit pools)
                                   takes D = 64, 128 and 256 with Hq/Hkv a power of two up
-                                  to 64 (16 at D = 256), at all three block sizes; the
+                                  to 64, at all three block sizes; the
                                   MFMA prefill kernel takes D = 64, 128 and 256 with
                                   Hq/Hkv a power of two up to 64 at all three; every
                                   other shape runs on the generic split-K kernel. */
@@ -234,9 +234,9 @@ pa_status pa_cache_write_fp8(const void* k_new, const void* v_new, int64_t kv_ro
 /*
  * pa_attention_varlen_fp8 -- as pa_attention_varlen with 8-bit pools: the
  * attention runs over K = decode(k_cache) * k_scale and V = decode(v_cache) *
- * v_scale.  q and out are bf16 (p->dtype == PA_BF16); D = 64 or 128 with
- * Hq/Hkv a power of two up to 64, or D = 256 with Hq/Hkv a power of two up to
- * 16; block size 8, 16 or 32; single-row (decode) requests only
+ * v_scale.  q and out are bf16 (p->dtype == PA_BF16); D = 64, 128 or 256 with
+ * Hq/Hkv a power of two up to 64; block size 8, 16 or 32; single-row (decode)
+ * requests only
  * (max_query_len <= 1), otherwise PA_ERR_UNSUPPORTED.  Scales finite and > 0.  The workspace is
  * sized by pa_attention_workspace_size(p).
  */

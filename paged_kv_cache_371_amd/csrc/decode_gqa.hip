@@ -800,7 +800,7 @@ static int item_group(int head_dim, int group) {
   return group < cap ? group : cap;
 }
 
-constexpr int kMaxHeadSplit = 8;
+constexpr int kMaxGroup = 64;   // query heads per KV head served by this kernel, at most
 
 int decode_gqa_head_split(int head_dim, int group) {
   const int gi = item_group(head_dim, group);
@@ -808,9 +808,8 @@ int decode_gqa_head_split(int head_dim, int group) {
 }
 
 bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size, int block_size) {
-  const bool pow2 = group >= 1 && (group & (group - 1)) == 0;
+  const bool pow2 = group >= 1 && group <= kMaxGroup && (group & (group - 1)) == 0;
   return dtype == 1 && (head_dim == 64 || head_dim == 128 || head_dim == 256) && pow2 &&
-         decode_gqa_head_split(head_dim, group) <= kMaxHeadSplit &&
          (block_size == 8 || block_size == 16 || block_size == 32) && part_size % kBlock == 0 &&
          part_size / kBlock <= kMaxPartBuckets;
 }
@@ -910,7 +909,7 @@ int decode_gqa_workers(int group) {
 hipError_t launch_decode_gqa(int group, int head_dim, bool fp8_cache, const DecodeArgs& a, hipStream_t stream) {
   const int gi = item_group(head_dim, group);
   const int split = decode_gqa_head_split(head_dim, group);
-  if (gi <= 0 || gi * split != group || split > kMaxHeadSplit) return hipErrorInvalidValue;
+  if (gi <= 0 || gi * split != group || group > kMaxGroup) return hipErrorInvalidValue;
   DecodeArgs b = a;
   b.head_split_log2 = 0;
   while ((1 << b.head_split_log2) < split) ++b.head_split_log2;

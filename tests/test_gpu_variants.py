@@ -301,7 +301,7 @@ def test_prefill_head_dim_256_bitwise_across_block_sizes():
 
 
 @pytest.mark.parametrize("D,Hq,Hkv,bs", [(256, 32, 8, 16), (256, 64, 8, 8), (256, 16, 1, 32), (128, 64, 4, 16),
-                                         (128, 32, 1, 32), (64, 128, 4, 16)])
+                                         (128, 32, 1, 32), (64, 128, 4, 16), (256, 64, 1, 8), (128, 128, 2, 16)])
 def test_fast_decode_head_split(D, Hq, Hkv, bs):
     """A KV head with more query heads than one work item holds (G > 2 at
     D = 256, G > 8 otherwise) is served by several adjacent items of the fast
@@ -349,7 +349,7 @@ def test_fast_decode_head_split_bitwise_per_head():
 
 
 @pytest.mark.parametrize("D,Hq,Hkv,bs", [(128, 64, 4, 16), (128, 128, 4, 8), (64, 128, 8, 32), (256, 32, 2, 16),
-                                         (256, 64, 4, 8)])
+                                         (256, 64, 4, 8), (256, 64, 1, 8)])
 def test_prefill_head_split(D, Hq, Hkv, bs):
     """Multi-row requests of a KV head with more than 8 query heads: the MFMA
     kernel serves the heads 8 at a time (adjacent items on the same K/V), with
