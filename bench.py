@@ -181,52 +181,104 @@ def attention_flops(c, window: int = 0) -> float:
     return 4.0 * c.head_dim * c.num_q_heads * keys
 
 
-def cpu_baseline(c, budget_s: float = 12.0, fp8_pools=None, window: int = 0) -> dict:
-    """Time the fp64 oracle on whole requests, in passes over the batch in a
-    fixed shuffled order, until the budget is spent (one BLAS thread).  With
-    ``fp8_pools`` (K and V codes) the oracle attends over the 8-bit pools."""
+def cpu_model() -> str:
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def cpu_baseline(c, budget_s: float = 12.0, fp8_pools=None, window: int = 0, pool=None) -> dict:
+    """Time the fp64 oracle on the batch's rows, on one core and on all cores.
+
+    The batch's rows are cut into pieces of about equal cost (a piece is some
+    rows of one request; a decode request is one piece), taken in a fixed
+    shuffled order.  Each piece is one call of the oracle over its request.
+    One core: pieces in order, in passes over the batch, until half the
+    budget is spent (one BLAS thread).  All cores (``pool``: one worker
+    process per core, one BLAS thread each, the inputs memory-mapped from
+    files written beforehand): the next pieces in the same order, as many as
+    take about half the budget at the one-core rate times the workers.  KV
+    bytes of a piece are its request's K/V bytes times its share of the
+    request's rows.  With ``fp8_pools`` (K and V codes) the oracle attends
+    over the 8-bit pools."""
     import oracle
+    from oracle.sharded import SharedBatch, run_piece, run_pieces, split_rows
 
     try:
         from threadpoolctl import threadpool_limits
         limit = threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
         limit = None
-    extra = dict(sliding_window=window)
+    meta = dict(scale=c.scale, num_kv_heads=c.num_kv_heads, dtype=c.dtype, block_size=c.block_size,
+                sliding_window=window)
     if fp8_pools is None:
-        kp, vp = oracle.oracle_cache_write(c.k_cache, c.v_cache, c.k_new, c.v_new, c.slot_mapping)
+        kp, vp = oracle.oracle_cache_write(c.k_cache, c.v_cache, c.k_new, c.v_new, c.slot_mapping, c.block_size)
         s = 2 if c.dtype == "bf16" else 4
     else:
         kp, vp = oracle.oracle_cache_write(fp8_pools[0], fp8_pools[1],
                                            oracle.fp8_quantize_rows(c.k_new, K_SCALE_FP8),
-                                           oracle.fp8_quantize_rows(c.v_new, V_SCALE_FP8), c.slot_mapping)
-        extra.update(kv_dtype="fp8", k_scale=K_SCALE_FP8, v_scale=V_SCALE_FP8)
+                                           oracle.fp8_quantize_rows(c.v_new, V_SCALE_FP8), c.slot_mapping,
+                                           c.block_size)
+        meta.update(kv_dtype="fp8", k_scale=K_SCALE_FP8, v_scale=V_SCALE_FP8)
         s = 1
-    order = np.random.default_rng(1).permutation(c.num_seqs)
-    done_rows = done_kv = reqs = 0
+
+    def kv_of(b, rows):
+        Lb, nb = int(c.seq_lens[b]), int(c.cu_seqlens[b + 1] - c.cu_seqlens[b])
+        keys = Lb if window <= 0 else Lb - max(0, Lb - nb - window + 1)
+        return keys * c.num_kv_heads * c.head_dim * 2 * s * rows / nb
+
+    pieces = split_rows(c.cu_seqlens, c.seq_lens, pieces=max(1024, 4 * c.num_seqs), window=window)
+    pieces = [pieces[i] for i in np.random.default_rng(1).permutation(len(pieces))]
+    arrays = dict(q=c.q, k=kp, v=vp, cu=c.cu_seqlens, lens=c.seq_lens, tables=c.block_tables)
+    one_budget = budget_s / 2 if pool is not None else budget_s
+    done_rows = done_kv = done = 0
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        for b in order:
-            rows = list(range(int(c.cu_seqlens[b]), int(c.cu_seqlens[b + 1])))
-            if not rows:
-                continue
-            oracle.oracle_attention_varlen(c.q, kp, vp, c.cu_seqlens, c.seq_lens, c.block_tables, c.scale,
-                                           c.num_kv_heads, c.dtype, rows=rows, validate=False, **extra)
-            done_rows += len(rows)
-            Lb, nb = int(c.seq_lens[b]), len(rows)
-            keys = Lb if window <= 0 else Lb - max(0, Lb - nb - window + 1)
-            done_kv += keys * c.num_kv_heads * c.head_dim * 2 * s
-            reqs += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
+    while time.perf_counter() - t0 < one_budget:
+        b, js = pieces[done % len(pieces)]
+        run_piece(arrays, meta, b, js)
+        done_rows += len(js)
+        done_kv += kv_of(b, len(js))
+        done += 1
     dt = time.perf_counter() - t0
     if limit is not None and hasattr(limit, "unregister"):
         limit.unregister()
-    return {"value": done_kv / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reqs} requests of the {c.num_seqs}-request batch in passes over it "
-                      f"({done_rows} query rows, {done_kv / 1e9:.3f} GB of KV) in {dt:.1f} s, "
-                      f"fp64 NumPy, one BLAS thread",
-            "query_tokens_per_s": done_rows / dt}
+    model = cpu_model()
+    one = {"value": done_kv / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{done} pieces ({done_rows} query rows, {done_kv / 1e9:.3f} GB of KV) of the "
+                     f"{c.num_seqs}-request batch in passes over it, in {dt:.1f} s, fp64 NumPy, one process, "
+                     f"one BLAS thread",
+           "query_tokens_per_s": done_rows / dt}
+    if pool is None:
+        one["cpu_model"] = model
+        return one
+
+    workers = pool._max_workers  # noqa: SLF001
+    want_kv = one["value"] * 1e9 * workers * (budget_s / 2)
+    sample, kv, rows = [], 0.0, 0
+    for i in range(len(pieces)):
+        if sample and kv >= want_kv:
+            break
+        b, js = pieces[(done + i) % len(pieces)]
+        sample.append((b, js))
+        kv += kv_of(b, len(js))
+        rows += len(js)
+    with SharedBatch(c.q, kp, vp, c.cu_seqlens, c.seq_lens, c.block_tables, **meta) as batch:
+        t0 = time.perf_counter()
+        run_pieces(batch, sample, pool)
+        dt_all = time.perf_counter() - t0
+    return {"value": kv / dt_all / 1e9, "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "sample": f"{len(sample)} pieces ({rows} query rows, {kv / 1e9:.3f} GB of KV) of the "
+                      f"{c.num_seqs}-request batch in {dt_all:.1f} s wall on a pool of {workers} worker processes "
+                      f"(one BLAS thread each, inputs memory-mapped), fp64 NumPy",
+            "query_tokens_per_s": rows / dt_all,
+            "cpu_model": model,
+            "one_core": one}
 
 
 def calibrate_copy() -> None:
@@ -474,7 +526,11 @@ def main() -> None:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of CPU baseline: half on one core, half on all cores")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="worker processes of the all-core CPU baseline (0: the host cores, at most 16; "
+                         "1: one-core baseline only)")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default="bf16",
                     help="fp8: 8-bit (OCP E4M3) pools with per-tensor scales, bf16 q and out")
@@ -500,6 +556,13 @@ def main() -> None:
     if args.op in ("swap_out", "swap_in"):
         run_swap(args, args.op)
         return
+
+    # The CPU baseline's worker processes start before anything touches the GPU.
+    cpu_pool = None
+    if not args.no_cpu_baseline and args.cpu_workers != 1:
+        from oracle.sharded import host_workers, make_pool
+
+        cpu_pool = make_pool(args.cpu_workers or host_workers())
 
     import torch
 
@@ -626,7 +689,9 @@ def main() -> None:
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(c, args.cpu_budget, pools8, W)
+        result["cpu_baseline"] = cpu_baseline(c, args.cpu_budget, pools8, W, pool=cpu_pool)
+    if cpu_pool is not None:
+        cpu_pool.shutdown()
     print(json.dumps(result), flush=True)
 
 

@@ -12,9 +12,9 @@
  *          (full blocks keyed by a hash of their tokens and of the previous
  *          block's key; a hit shares the block and adds a reference; blocks
  *          nobody references are evicted least recently used first).
- *   [ICE]  ice-wocker, "推理优化与服务：从 PagedAttention 到分离式部署",
- *          §2.2: blocks are allocated on demand and return to a global pool
- *          when the request finishes.
+ *   [LPNH] lpnh.cn, "大模型推理架构演进：从 PagedAttention 到 Prefill-Decode
+ *          分离的深度解析", §二 2.2, third step: blocks are allocated on
+ *          demand and return to a global pool when the request finishes.
  *
  * Status codes are those of pa.h.  No C++ exception crosses this interface.
  */

@@ -7,7 +7,8 @@ Batching"):
   * §3.3: a decode step appends the new token's K/V to the last block of the
     sequence if that block has room, else takes a physical block from the
     free pool; a request's blocks return to the pool when it finishes
-    (ice-wocker §2.2, third step).
+    (lpnh.cn "大模型推理架构演进：从 PagedAttention 到 Prefill-Decode 分离的
+    深度解析", §二 2.2, third step).
   * §3.5 / §3.8: parallel sampling shares the prompt's blocks among the
     samples (each share adds one to the block's reference count); a sample
     that must write into a block whose count is above one first copies it

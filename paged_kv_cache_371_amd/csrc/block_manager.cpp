@@ -4,8 +4,9 @@
 // quant67 "PagedAttention 与 Continuous Batching" §3.3 (append into the last
 // block, else take a free block), §3.5 / §3.8 (shared prompt blocks and
 // copy-on-write), §3.9 / §6.1 (swap), §5.2 (chained block keys, shared hits,
-// LRU eviction of unreferenced blocks); ice-wocker §2.2 (blocks go back to
-// the global pool when a request ends).  The rules where the pages leave a
+// LRU eviction of unreferenced blocks); lpnh.cn "大模型推理架构演进：从
+// PagedAttention 到 Prefill-Decode 分离的深度解析" §二 2.2, third step (blocks
+// go back to the global pool when a request ends).  The rules where the pages leave a
 // step open are listed in pa_blocks.h.
 //
 // Every operation checks that it can complete before it changes anything,

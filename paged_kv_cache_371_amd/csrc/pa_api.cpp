@@ -144,6 +144,24 @@ inline int64_t merge_off(const pa_attn_params* p, const Plan& pl) {
   return pref_off(p, pl) + (pl.prefill ? 4 * prefill_capacity(p, pl) : 0);
 }
 
+// Limits of the kernels' index arithmetic: a request's partition count sits
+// in the upper 16 bits of a signed int (count << 16) and a prefill entry's
+// row tile in the lower 16 bits; work items are indexed as int (list entries
+// x head groups).
+inline bool plan_fits(const pa_attn_params* p, const Plan& pl) {
+  const int g = p->num_q_heads / p->num_kv_heads;
+  if (pl.parts > 32767) return false;
+  if (int64_t(p->num_seqs) * pl.parts * p->num_kv_heads * pa::decode_gqa_head_split(p->head_dim, g) > INT32_MAX)
+    return false;
+  if (pl.prefill) {
+    const int gp = pa::prefill_item_group(g);
+    const int64_t rows = pl.tile_pairs / gp;
+    if ((int64_t(p->max_query_len) + rows - 1) / rows > 65535) return false;
+    if (prefill_capacity(p, pl) * p->num_kv_heads * (g / gp) > INT32_MAX) return false;
+  }
+  return true;
+}
+
 pa_status check_params(const pa_attn_params* p) {
   if (!p) return PA_ERR_NULL;
   if (!dtype_ok(p->dtype)) return PA_ERR_UNSUPPORTED;
@@ -212,7 +230,7 @@ pa_status pa_cache_write(const void* k_new, const void* v_new, int64_t kv_row_st
 size_t pa_attention_workspace_size(const pa_attn_params* p) {
   if (check_params(p) != PA_OK) return 0;
   const Plan pl = make_plan(p);
-  if (!pl.ok) return 0;
+  if (!pl.ok || !plan_fits(p, pl)) return 0;
   return plan_bytes(p, pl) +
          (region_floats(p, pl.rows_a, pl.parts) + region_floats(p, pl.rows_b, pl.parts)) * sizeof(float);
 }
@@ -259,7 +277,7 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
   const int g = p->num_q_heads / p->num_kv_heads;
   const Plan pl = make_plan(p);
   if (!pl.ok) return PA_ERR_UNSUPPORTED;
-  if (pl.parts > 65535 || int64_t(p->num_seqs) * pl.parts * p->num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
+  if (!plan_fits(p, pl)) return PA_ERR_SHAPE;
   const float scale_log2 = p->scale * kLog2e * (fp8 ? k_scale : 1.f);
   const size_t pbytes = plan_bytes(p, pl);
   float* ws = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pbytes) : nullptr;

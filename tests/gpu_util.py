@@ -63,14 +63,36 @@ def oracle_pools(c):
     return oracle.oracle_cache_write(c.k_cache, c.v_cache, c.k_new, c.v_new, c.slot_mapping, c.block_size)
 
 
-def oracle_out(c, k_pool, v_pool, rows=None, sliding_window=0):
-    return oracle.oracle_attention_varlen(c.q, k_pool, v_pool, c.cu_seqlens, c.seq_lens, c.block_tables, c.scale,
-                                          c.num_kv_heads, c.dtype, c.block_size, rows=rows,
-                                          sliding_window=sliding_window)
+_POOL = None
 
 
-def run_and_compare(c, partition_size=0, rows=None, check_pool=True, sliding_window=0):
-    """Cache write + attention on the GPU; returns (max_abs, mean_abs, ok, dc)."""
+def oracle_pool():
+    """One process pool per test process for the sharded oracle (spawn-started workers
+    that import only NumPy and the oracle)."""
+    global _POOL
+    if _POOL is None:
+        import atexit
+
+        from oracle.sharded import make_pool
+
+        _POOL = make_pool()
+        atexit.register(_POOL.shutdown)
+    return _POOL
+
+
+def oracle_out(c, k_pool, v_pool, rows=None, sliding_window=0, sharded=False):
+    args = (c.q, k_pool, v_pool, c.cu_seqlens, c.seq_lens, c.block_tables, c.scale, c.num_kv_heads, c.dtype,
+            c.block_size)
+    if sharded:
+        from oracle.sharded import oracle_attention_sharded
+
+        return oracle_attention_sharded(*args, rows=rows, sliding_window=sliding_window, pool=oracle_pool())
+    return oracle.oracle_attention_varlen(*args, rows=rows, sliding_window=sliding_window)
+
+
+def run_and_compare(c, partition_size=0, rows=None, check_pool=True, sliding_window=0, sharded=False):
+    """Cache write + attention on the GPU; returns (max_abs, mean_abs, ok, dc).
+    ``sharded``: compute the oracle's rows on the process pool (same result)."""
     dc = DeviceCase(c)
     dc.cache_write()
     dc.attention(partition_size, sliding_window=sliding_window)
@@ -79,7 +101,7 @@ def run_and_compare(c, partition_size=0, rows=None, check_pool=True, sliding_win
     if check_pool:
         assert np.array_equal(to_host(dc.k_cache, c.dtype).view(np.uint8), k_pool.view(np.uint8)), "K pool differs"
         assert np.array_equal(to_host(dc.v_cache, c.dtype).view(np.uint8), v_pool.view(np.uint8)), "V pool differs"
-    want = oracle_out(c, k_pool, v_pool, rows=rows, sliding_window=sliding_window)
+    want = oracle_out(c, k_pool, v_pool, rows=rows, sliding_window=sliding_window, sharded=sharded)
     got = oracle.widen(to_host(dc.out, c.dtype), c.dtype)
     if rows is not None:
         idx = np.asarray(sorted(set(int(r) for r in rows)))

@@ -93,6 +93,10 @@ def _params(**over):
     (dict(scale=-0.088), -2),
     (dict(max_query_len=65), -2),
     (dict(sliding_window=-1), -2),
+    # 32768 partitions: the kernels pack a request's partition count as count << 16 in an int
+    (dict(partition_size=16, max_seq_len=32768 * 16, max_blocks_per_seq=32768), -2),
+    # 65536 prefill row tiles of one request (16 rows per tile at G = 4... 8): the tile index takes 16 bits
+    (dict(max_query_len=65536 * 32, max_seq_len=65536 * 32, max_blocks_per_seq=65536 * 2), -2),
 ])
 def test_host_rejects_bad_params_before_any_launch(L, over, code):
     p = _params(**over)
@@ -119,6 +123,15 @@ def test_host_null_and_workspace_errors(L):
     # an empty batch is a no-op
     assert L.pa_attention_varlen(None, None, None, None, None, None, None,
                                  ctypes.byref(_params(num_seqs=0, total_q=0)), None, 0, None) == 0
+
+
+def test_partition_count_limit(L):
+    """32767 partitions is the largest count the kernels' packed fields hold."""
+    ok = _params(num_seqs=1, total_q=1, partition_size=16, max_seq_len=32767 * 16, max_blocks_per_seq=32767)
+    assert L.pa_attention_workspace_size(ctypes.byref(ok)) > 0
+    bad = _params(num_seqs=1, total_q=1, partition_size=16, max_seq_len=32767 * 16 + 1, max_blocks_per_seq=32768)
+    assert L.pa_attention_workspace_size(ctypes.byref(bad)) == 0
+    assert L.pa_attention_varlen(16, 16, 16, 16, 16, 16, 16, ctypes.byref(bad), 16, 1 << 40, None) == -2
 
 
 def test_partition_size_query(L):
