@@ -253,6 +253,28 @@ pa_status pa_attention_run_fp8(void* out, const void* q, const void* k_cache, co
                                float k_scale, float v_scale, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/*
+ * pa_attention_varlen_noalloc -- pa_attention_varlen for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, layouts, result and
+ * host-side errors as pa_attention_varlen, without the workspace: the work
+ * lists and split-K partials live in a static scratch of
+ * PA_NOALLOC_SCRATCH_BYTES in the library's device memory, one copy per GPU,
+ * held from the first call on that GPU until the process ends.  The call
+ * uses the scratch of the current device (the stream must belong to it),
+ * whose address it looks up on its first call there; it allocates nothing.
+ * Parameters whose pa_attention_workspace_size exceeds
+ * PA_NOALLOC_SCRATCH_BYTES return PA_ERR_WORKSPACE and enqueue nothing.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (other streams, other threads) race and give undefined results; calls
+ * ordered on one stream are safe.  The scratch keeps the last call's
+ * contents, and each call rewrites what it reads before reading it.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+pa_status pa_attention_varlen_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                                      const int32_t* block_tables, const pa_attn_params* p, void* stream);
+
 /* Bits of the result word written by pa_validate_metadata. */
 #define PA_BAD_CU_SEQLENS   1   /* cu[0] != 0, cu decreasing, or cu[B] != total_q */
 #define PA_BAD_LENGTHS      2   /* n_b > L_b, L_b < 0, n_b > max_query_len or L_b > max_seq_len */
@@ -284,7 +306,7 @@ const char* pa_status_string(pa_status s);
  * 204: the fast decode kernel and 8-bit pools at D = 64 and 256, the MFMA
  * prefill kernel at D = 64 and 256; 205: the fast decode kernel and 8-bit
  * pools for Hq/Hkv above 8, and above 2 at D = 256; the MFMA prefill kernel
- * for Hq/Hkv above 8). */
+ * for Hq/Hkv above 8; 206: pa_attention_varlen_noalloc). */
 int32_t pa_abi_version(void);
 
 #ifdef __cplusplus

@@ -20,6 +20,7 @@ __all__ = [
     "exported_symbols",
     "cache_write",
     "attention_varlen",
+    "attention_varlen_noalloc",
     "make_params",
     "workspace_size",
     "validate_metadata",
@@ -63,6 +64,7 @@ _SIGNATURES = {
                                           ctypes.c_float, ctypes.c_void_p]),
     "pa_attention_varlen_fp8": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_float, ctypes.c_float,
                                                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "pa_attention_varlen_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 9),
     "pa_attention_plan": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]),
     "pa_attention_run": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_void_p,
                                                               ctypes.c_size_t, ctypes.c_void_p]),
@@ -351,6 +353,39 @@ def attention_varlen(out, q, k_cache, v_cache, cu_seqlens, seq_lens, block_table
         _check(fn(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cu_seqlens.data_ptr(),
                   seq_lens.data_ptr(), block_tables.data_ptr(), ctypes.byref(p), workspace.data_ptr(), ws_bytes,
                   _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # PA_NOALLOC_SCRATCH_BYTES
+
+
+def attention_varlen_noalloc(out, q, k_cache, v_cache, cu_seqlens, seq_lens, block_tables, scale: float,
+                             max_query_len: int, max_seq_len: int, partition_size: int = 0, stream=None,
+                             sliding_window: int = 0):
+    """``attention_varlen`` through pa_attention_varlen_noalloc: no workspace, the
+    library's static per-GPU scratch instead (bf16 or fp32 pools)."""
+    torch = _torch()
+    for t, nm in ((out, "out"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (cu_seqlens, "cu_seqlens"),
+                  (seq_lens, "seq_lens"), (block_tables, "block_tables")):
+        _dev(t, nm)
+    for t, nm in ((cu_seqlens, "cu_seqlens"), (seq_lens, "seq_lens"), (block_tables, "block_tables")):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise TypeError(f"{nm} must be a contiguous int32 tensor")
+    if q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q and out must be [total_q, Hq, D]")
+    if q.stride(2) != 1 or q.stride(1) != q.shape[2] or out.stride(2) != 1 or out.stride(1) != out.shape[2]:
+        raise ValueError("q and out rows must hold contiguous [Hq, D]")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()) or k_cache.shape != v_cache.shape:
+        raise ValueError("pools must be contiguous [NB, Hkv, 16, D] tensors of one shape")
+    if len({q.dtype, out.dtype, k_cache.dtype, v_cache.dtype}) != 1:
+        raise TypeError("q, out and the pools must share one dtype")
+    if seq_lens.shape[0] != cu_seqlens.shape[0] - 1 or block_tables.shape[0] != seq_lens.shape[0]:
+        raise ValueError("cu_seqlens [B+1], seq_lens [B] and block_tables [B, W] disagree on B")
+    p = make_params(q, k_cache, cu_seqlens, block_tables, int(k_cache.shape[1]), scale, max_query_len, max_seq_len,
+                    out=out, partition_size=partition_size, sliding_window=sliding_window)
+    _check(lib().pa_attention_varlen_noalloc(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                             cu_seqlens.data_ptr(), seq_lens.data_ptr(), block_tables.data_ptr(),
+                                             ctypes.byref(p), _stream(stream)))
     return out
 
 

@@ -6,8 +6,10 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
+#include <mutex>
 
 #include "pa_internal.h"
 
@@ -189,7 +191,7 @@ pa_status check_params(const pa_attn_params* p) {
 
 extern "C" {
 
-int32_t pa_abi_version(void) { return 205; }
+int32_t pa_abi_version(void) { return 206; }
 
 const char* pa_status_string(pa_status s) {
   switch (s) {
@@ -387,7 +389,55 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
   return PA_OK;
 }
 
+// Scratch of pa_attention_varlen_noalloc: one copy per GPU, in the code
+// object's static device memory, held until the process ends.  Host code
+// never uses the array's name as an address (on the host it is a stand-in
+// for the symbol); it uses the per-device address from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kScratchDevices];
+
+// Device address of the current device's scratch, looked up once per device
+// (with that device current) and kept; nullptr if the lookup fails.
+void* scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+    g_scratch_ptr[dev].store(addr, std::memory_order_release);
+    ptr = addr;
+  }
+  return ptr;
+}
+
 }  // namespace
+
+pa_status pa_attention_varlen_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                                      const int32_t* block_tables, const pa_attn_params* p, void* stream) {
+  pa_status st = check_params(p);
+  if (st != PA_OK) return st;
+  const size_t need = pa_attention_workspace_size(p);
+  if (need > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+  if (p->num_seqs == 0 || p->total_q == 0) return PA_OK;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_of_current_device();
+    if (!ws) return PA_ERR_LAUNCH;
+  }
+  // The plan stage rewrites the work lists and re-arms their counters at the
+  // start of the scratch; the partials behind them are written before they
+  // are read, so nothing left by an earlier call needs clearing.
+  return attention_impl(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, block_tables, p, ws,
+                        ws ? size_t(PA_NOALLOC_SCRATCH_BYTES) : 0, stream, false, 1.f, 1.f, kPlanStage | kRunStage);
+}
 
 pa_status pa_attention_varlen(void* out, const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* cu_seqlens_q, const int32_t* seq_lens, const int32_t* block_tables,

@@ -58,7 +58,7 @@ def test_struct_layout_matches_c(tmp_path):
 
 
 def test_status_strings_and_version(L):
-    assert L.pa_abi_version() == 205
+    assert L.pa_abi_version() == 206
     for code in range(0, -11, -1):
         s = L.pa_status_string(code).decode()
         assert s.startswith("PA_")
@@ -182,6 +182,19 @@ def test_fp8_host_errors(L):
              1.0, 1.0, None, 0, None) == -5
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(num_q_heads=6, q_row_stride=768, o_row_stride=768)),
              1.0, 1.0, None, 0, None) == -3
+
+
+def test_noalloc_host_errors(L):
+    """The no-allocation entry point checks its arguments like pa_attention_varlen,
+    and refuses parameters whose workspace exceeds its static scratch."""
+    f = L.pa_attention_varlen_noalloc
+    assert f(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(block_size=12)), None) == -3
+    assert f(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(scale=0.0)), None) == -2
+    assert f(16, 16, 16, 16, 16, 16, 16, None, None) == -1
+    big = _params(num_seqs=60000, total_q=60000, max_seq_len=8192, max_blocks_per_seq=512, partition_size=512)
+    assert L.pa_attention_workspace_size(ctypes.byref(big)) > pa.NOALLOC_SCRATCH_BYTES
+    assert f(16, 16, 16, 16, 16, 16, 16, ctypes.byref(big), None) == -5
+    assert f(None, None, None, None, None, None, None, ctypes.byref(_params(num_seqs=0, total_q=0)), None) == 0
 
 
 def test_validate_host_errors(L):
