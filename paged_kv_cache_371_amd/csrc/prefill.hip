@@ -444,18 +444,47 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
     // staging write of a stage from the computes that read it, before and
     // after.
     __syncthreads();   // the previous item is done with both stages
-    TileRegs<D> rg;
-    uint64_t ph_next = phys_of(kt0 + 1);
-    fetch(rg, kt0, phys_of(kt0));
-    stage_write(rg, kt0, 0);
+    // Registers one or two tiles ahead.  With two register sets (where they
+    // fit without spills: D <= 128 on 16- and 32-token blocks), tile kt+2 is
+    // fetched while tile kt is computed from its stage and tile kt+1, fetched a
+    // step earlier, is written to the other stage, so each load has two tiles
+    // of compute to arrive; with one set, tile kt+1 is fetched and staged in
+    // the step of tile kt.  Each barrier separates the staging write of a
+    // stage from the computes that read it, before and after.  The loop is
+    // unrolled by the two stages (tile kt is in stage (kt - kt0) & 1), so every
+    // LDS address is a base plus an immediate offset.
+    constexpr int kAhead = (D <= 128 && BS != 8) ? 2 : 1;
+    TileRegs<D> rg0, rg1;
+    uint64_t ph_next = phys_of(kt0 + kAhead);
+    fetch(rg0, kt0, phys_of(kt0));
+    if constexpr (kAhead == 2) fetch(rg1, kt0 + 1, phys_of(kt0 + 1));
+    stage_write(rg0, kt0, 0);
     __syncthreads();
-    for (int kt = kt0; kt < kt1; ++kt) {
-      const int st = (kt - kt0) & 1;
-      fetch(rg, kt + 1, ph_next);
-      ph_next = phys_of(kt + 2);
+    auto step = [&](int kt, TileRegs<D>& free_rg, TileRegs<D>& next_rg, auto st) {
+      TileRegs<D>& fetch_rg = kAhead == 2 ? free_rg : rg0;
+      TileRegs<D>& stage_rg = kAhead == 2 ? next_rg : rg0;
+      fetch(fetch_rg, kt + kAhead, ph_next);
+      ph_next = phys_of(kt + kAhead + 1);
       compute(kt, st);
-      if (kt + 1 < kt1) stage_write(rg, kt + 1, st ^ 1);
+      if (kt + 1 < kt1) stage_write(stage_rg, kt + 1, st ^ 1);
       __syncthreads();
+    };
+    if constexpr (D == 256 && BS == 8) {
+      // not unrolled: the unrolled loop needs more registers than this shape has
+      for (int kt = kt0; kt < kt1; ++kt) {
+        const int st = (kt - kt0) & 1;
+        fetch(rg0, kt + 1, ph_next);
+        ph_next = phys_of(kt + 2);
+        compute(kt, st);
+        if (kt + 1 < kt1) stage_write(rg0, kt + 1, st ^ 1);
+        __syncthreads();
+      }
+    } else {
+      for (int kt = kt0; kt < kt1; kt += 2) {
+        step(kt, rg0, rg1, std::integral_constant<int, 0>{});
+        if (kt + 1 >= kt1) break;
+        step(kt + 1, rg1, rg0, std::integral_constant<int, 1>{});
+      }
     }
 
     if (split) {
