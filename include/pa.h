@@ -235,10 +235,11 @@ pa_status pa_cache_write_fp8(const void* k_new, const void* v_new, int64_t kv_ro
  * pa_attention_varlen_fp8 -- as pa_attention_varlen with 8-bit pools: the
  * attention runs over K = decode(k_cache) * k_scale and V = decode(v_cache) *
  * v_scale.  q and out are bf16 (p->dtype == PA_BF16); D = 64, 128 or 256 with
- * Hq/Hkv a power of two up to 64; block size 8, 16 or 32; single-row (decode)
- * requests only
- * (max_query_len <= 1), otherwise PA_ERR_UNSUPPORTED.  Scales finite and > 0.  The workspace is
- * sized by pa_attention_workspace_size(p).
+ * Hq/Hkv a power of two up to 64; block size 8, 16 or 32; other shapes return
+ * PA_ERR_UNSUPPORTED.  Requests with one row run on the split-K decode kernel,
+ * requests with more rows (chunked prefill, [Q67] §4.2) on the MFMA kernel,
+ * which widens the codes to bf16 as it stages them.  Scales finite and > 0.
+ * The workspace is sized by pa_attention_workspace_size(p).
  */
 pa_status pa_attention_varlen_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
                                   const int32_t* cu_seqlens_q, const int32_t* seq_lens,
@@ -306,7 +307,8 @@ const char* pa_status_string(pa_status s);
  * 204: the fast decode kernel and 8-bit pools at D = 64 and 256, the MFMA
  * prefill kernel at D = 64 and 256; 205: the fast decode kernel and 8-bit
  * pools for Hq/Hkv above 8, and above 2 at D = 256; the MFMA prefill kernel
- * for Hq/Hkv above 8; 206: pa_attention_varlen_noalloc). */
+ * for Hq/Hkv above 8; 206: pa_attention_varlen_noalloc; 207: multi-row
+ * requests on 8-bit pools). */
 int32_t pa_abi_version(void);
 
 #ifdef __cplusplus

@@ -191,7 +191,7 @@ pa_status check_params(const pa_attn_params* p) {
 
 extern "C" {
 
-int32_t pa_abi_version(void) { return 206; }
+int32_t pa_abi_version(void) { return 207; }
 
 const char* pa_status_string(pa_status s) {
   switch (s) {
@@ -260,8 +260,9 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
     if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !(k_scale > 0.f) || !(v_scale > 0.f))
       return PA_ERR_SHAPE;
     const int g8 = p->num_q_heads / p->num_kv_heads;
-    if (p->dtype != PA_BF16 || p->max_query_len > 1 ||
-        !pa::decode_gqa_supported(1, p->head_dim, g8, effective_partition(p), p->block_size))
+    if (p->dtype != PA_BF16 ||
+        !pa::decode_gqa_supported(1, p->head_dim, g8, effective_partition(p), p->block_size) ||
+        (p->max_query_len > 1 && !pa::prefill_supported(p->head_dim, g8, p->block_size)))
       return PA_ERR_UNSUPPORTED;
   }
   if (p->num_seqs == 0 || p->total_q == 0) return PA_OK;
@@ -378,7 +379,8 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
     f.max_parts = d.max_parts;
     f.ws_o = pl.split_rows ? region_a : nullptr;
     f.ws_ml = pl.split_rows ? region_a + int64_t(pl.rows_a) * p->num_q_heads * pl.parts * p->head_dim : nullptr;
-    e = pa::launch_prefill(p->head_dim, g, f, s);
+    f.lsum_scale = d.lsum_scale;
+    e = pa::launch_prefill(p->head_dim, g, fp8, f, s);
     if (e != hipSuccess) return PA_ERR_LAUNCH;
   }
   // partitions of single-row requests and of split short requests

@@ -81,6 +81,7 @@ struct PrefillArgs {
   int32_t sliding_window;
   int32_t block_size;   // tokens per physical block: 8, 16 or 32
   int32_t head_split_log2;   // a KV head's query heads are served by 2^this items (set by launch_prefill)
+  float lsum_scale;          // 8-bit pools: the softmax sum is multiplied by this (1 / v_scale)
 };
 
 hipError_t launch_cache_write(const void* k_new, const void* v_new, int64_t kv_row_stride_bytes, void* k_cache,
@@ -150,8 +151,9 @@ hipError_t launch_merge(int dtype, int head_dim, const DecodeArgs& a, int64_t pa
 hipError_t launch_merge_list(int head_dim, const DecodeArgs& a, hipStream_t stream);
 size_t decode_lds_bytes(int dtype, int head_dim, int group, int part_size);
 
-// MFMA kernel for multi-row requests (bf16, D = 128, G in {1, 2, 4, 8}, blocks of 8, 16 or 32 tokens).
-hipError_t launch_prefill(int head_dim, int group, const PrefillArgs& a, hipStream_t stream);
+// MFMA kernel for multi-row requests (bf16 q and out; bf16 or 8-bit pools; D = 64, 128 or 256; G a
+// power of two up to 64; blocks of 8, 16 or 32 tokens).
+hipError_t launch_prefill(int head_dim, int group, bool fp8_cache, const PrefillArgs& a, hipStream_t stream);
 bool prefill_supported(int head_dim, int group, int block_size);
 // Query heads per prefill work item: the group, at most 8 (larger groups are
 // served by several items per KV head; the work list's row tiles use this).

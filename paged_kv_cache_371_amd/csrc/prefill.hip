@@ -115,24 +115,48 @@ __device__ __forceinline__ f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, co
 //   D = 64:  the same for lanes 0..31 with d-chunk lane%8 for k
 //   D = 256: k[kk]: key 8*(lane/32) + kk, d-chunk lane%32 (kk < 8);
 //            v[4g + kk]: key 4*(lane%4) + kk, d-chunk lane/4 + 16g
-template <int D>
+//   The registers hold the cached encoding: 16 bytes (8 bf16) per chunk, or
+//   with 8-bit pools 8 bytes (8 E4M3 codes), widened to bf16 when staged.
+template <int D, bool F8>
 struct TileRegs {
   static constexpr int kN = D == 256 ? 8 : 4;
-  u32x4_t k[kN];
-  u32x4_t v[kN];
+  using Raw = typename std::conditional<F8, u32x2_t, u32x4_t>::type;
+  Raw k[kN];
+  Raw v[kN];
+  // a chunk of 8 cached elements at byte offset off of the range rsrc
+  static __device__ __forceinline__ Raw load(__amdgpu_buffer_rsrc_t rsrc, int off) {
+    if constexpr (F8)
+      return __builtin_amdgcn_raw_buffer_load_b64(rsrc, off, 0, 0);
+    else
+      return __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+  }
+  // the chunk as 8 bf16 values; E4M3 -> bf16 is exact (every E4M3 value is a
+  // bf16 value), the pool's scale is applied elsewhere
+  static __device__ __forceinline__ u32x4_t widen(const Raw& w) {
+    if constexpr (F8) {
+      auto cvt = [](uint32_t x, auto hi) {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.f, decltype(hi)::value));
+      };
+      return u32x4_t{cvt(w[0], std::false_type{}), cvt(w[0], std::true_type{}), cvt(w[1], std::false_type{}),
+                     cvt(w[1], std::true_type{})};
+    } else {
+      return w;
+    }
+  }
 };
 
 // W = 4 for chunked prefill; W = 2 for batches whose multi-row requests are
 // short (speculative-decode verification), where a 128-pair tile would be
 // mostly empty and the LDS reads per tile, not HBM, would set the pace.
-template <int G, int W, int BS, int D>
+template <int G, int W, int BS, int D, bool F8>
 __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefill_kernel(PrefillArgs a) {
   using S = Shape<W, D>;
-  constexpr int kTileBytes = kBlock * D * 2;   // one 16-key unit of one KV head, bf16
+  constexpr int kEB = F8 ? 1 : 2;                // bytes per cached element
+  constexpr int kTileBytes = kBlock * D * kEB;   // one 16-key unit of one KV head
   constexpr int kSteps = D / 32;               // 32-wide d steps of S^T = K Q^T
   constexpr int kDB = D / 16;                  // 16-row d blocks of O^T
   constexpr int kMB = D == 256 ? 1 : 2;       // 16-column MFMA blocks per wave (registers at D = 256)
-  constexpr int kNK = TileRegs<D>::kN;        // 16-byte K (and V) chunks a lane stages per unit
+  constexpr int kNK = TileRegs<D, F8>::kN;    // 8-element K (and V) chunks a lane stages per unit
   constexpr int kPairs = 16 * kMB * W;
   constexpr int kKeys = S::kKeys;
   constexpr int kCB = S::kCB;
@@ -161,7 +185,7 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
   const int kchunk = D == 256 ? lane & 31 : D == 128 ? lane & 15 : lane & 7;
   const int vkey = 4 * (lane & 3), vchunk = lane >> 2;
   const bool stager = D != 64 || lane < 32;
-  constexpr int kHeadBytes = BS * D * 2;   // one KV head's rows of a physical block
+  constexpr int kHeadBytes = BS * D * kEB;   // one KV head's rows of a physical block
   const int64_t bstride = int64_t(hkv) * kHeadBytes;
   const float scale_log2 = a.scale_log2;
   const int32_t* entries = a.plan + kPlanHeaderInts + a.pref_off_ints;
@@ -269,7 +293,8 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
         return uint64_t(first) | (uint64_t(second) << 32);
       }
     };
-    auto fetch = [&](TileRegs<D>& rg, int kt, uint64_t phys_v) {
+    using Regs = TileRegs<D, F8>;
+    auto fetch = [&](TileRegs<D, F8>& rg, int kt, uint64_t phys_v) {
       if (!stager) return;
       const int u = unit_of(kt);
       const int64_t phys = uni(int(uint32_t(phys_v)));
@@ -289,22 +314,20 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
         if (kkey < 8) {
 #pragma unroll
           for (int kk = 0; kk < kNK; ++kk)
-            rg.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, (kkey + kk) * (D * 2) + kchunk * 16, 0, 0);
+            rg.k[kk] = Regs::load(rk, (kkey + kk) * (D * kEB) + kchunk * 8 * kEB);
         } else {
 #pragma unroll
           for (int kk = 0; kk < kNK; ++kk)
-            rg.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk2, (kkey - 8 + kk) * (D * 2) + kchunk * 16, 0, 0);
+            rg.k[kk] = Regs::load(rk2, (kkey - 8 + kk) * (D * kEB) + kchunk * 8 * kEB);
         }
         if (vkey < 8) {
 #pragma unroll
           for (int x = 0; x < kNK; ++x)
-            rg.v[x] = __builtin_amdgcn_raw_buffer_load_b128(
-                rv, (vkey + (x & 3)) * (D * 2) + (vchunk + 16 * (x >> 2)) * 16, 0, 0);
+            rg.v[x] = Regs::load(rv, (vkey + (x & 3)) * (D * kEB) + (vchunk + 16 * (x >> 2)) * 8 * kEB);
         } else {
 #pragma unroll
           for (int x = 0; x < kNK; ++x)
-            rg.v[x] = __builtin_amdgcn_raw_buffer_load_b128(
-                rv2, (vkey - 8 + (x & 3)) * (D * 2) + (vchunk + 16 * (x >> 2)) * 16, 0, 0);
+            rg.v[x] = Regs::load(rv2, (vkey - 8 + (x & 3)) * (D * kEB) + (vchunk + 16 * (x >> 2)) * 8 * kEB);
         }
       } else {
         const int64_t off = BS == 32 ? phys * bstride + (u & 1) * kTileBytes : phys * bstride;
@@ -315,20 +338,19 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
             __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + off), 0, nrec, kRsrcWord3);
 #pragma unroll
         for (int kk = 0; kk < kNK; ++kk)
-          rg.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, (kkey + kk) * (D * 2) + kchunk * 16, 0, 0);
+          rg.k[kk] = Regs::load(rk, (kkey + kk) * (D * kEB) + kchunk * 8 * kEB);
 #pragma unroll
         for (int x = 0; x < kNK; ++x)
-          rg.v[x] = __builtin_amdgcn_raw_buffer_load_b128(rv, (vkey + (x & 3)) * (D * 2) + (vchunk + 16 * (x >> 2)) * 16,
-                                                          0, 0);
+          rg.v[x] = Regs::load(rv, (vkey + (x & 3)) * (D * kEB) + (vchunk + 16 * (x >> 2)) * 8 * kEB);
       }
     };
-    auto stage_write = [&](TileRegs<D>& rg, int kt, int st) {
+    auto stage_write = [&](TileRegs<D, F8>& rg, int kt, int st) {
       if (!stager) return;
       char* ks = smem + st * kStageBytes;
       char* vs = ks + kKBytes;
       const int key0 = kt * kKeys + wave * kBlock;   // first position of this wave's block
       if (kt * kKeys + kKeys > L) {   // the context ends in this tile: zero what lies past it
-        const u32x4_t z = {0u, 0u, 0u, 0u};
+        const typename Regs::Raw z = {};   // code 0 is +0 in both encodings
 #pragma unroll
         for (int kk = 0; kk < kNK; ++kk) {   // v[kk] holds key vkey + kk % 4
           if (key0 + kkey + kk >= L) rg.k[kk] = z;
@@ -337,12 +359,13 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
       }
 #pragma unroll
       for (int kk = 0; kk < kNK; ++kk)
-        *reinterpret_cast<u32x4_t*>(ks + kchunk * kKChunk + (wave * kBlock + kkey + kk) * 16) = rg.k[kk];
+        *reinterpret_cast<u32x4_t*>(ks + kchunk * kKChunk + (wave * kBlock + kkey + kk) * 16) = Regs::widen(rg.k[kk]);
       // V^T: d rows 8*(vchunk + 16g) + 2w (+1) get this thread's 4 keys (8 bytes each)
       char* vcol = vs + (wave * kBlock + vkey) * 2;
 #pragma unroll
       for (int g = 0; g < kNK / 4; ++g) {
-        const u32x4_t* vv = rg.v + 4 * g;
+        const u32x4_t vv[4] = {Regs::widen(rg.v[4 * g]), Regs::widen(rg.v[4 * g + 1]), Regs::widen(rg.v[4 * g + 2]),
+                               Regs::widen(rg.v[4 * g + 3])};
         const int dc = vchunk + 16 * g;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -454,15 +477,15 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
     // unrolled by the two stages (tile kt is in stage (kt - kt0) & 1), so every
     // LDS address is a base plus an immediate offset.
     constexpr int kAhead = (D <= 128 && BS != 8) ? 2 : 1;
-    TileRegs<D> rg0, rg1;
+    TileRegs<D, F8> rg0, rg1;
     uint64_t ph_next = phys_of(kt0 + kAhead);
     fetch(rg0, kt0, phys_of(kt0));
     if constexpr (kAhead == 2) fetch(rg1, kt0 + 1, phys_of(kt0 + 1));
     stage_write(rg0, kt0, 0);
     __syncthreads();
-    auto step = [&](int kt, TileRegs<D>& free_rg, TileRegs<D>& next_rg, auto st) {
-      TileRegs<D>& fetch_rg = kAhead == 2 ? free_rg : rg0;
-      TileRegs<D>& stage_rg = kAhead == 2 ? next_rg : rg0;
+    auto step = [&](int kt, TileRegs<D, F8>& free_rg, TileRegs<D, F8>& next_rg, auto st) {
+      TileRegs<D, F8>& fetch_rg = kAhead == 2 ? free_rg : rg0;
+      TileRegs<D, F8>& stage_rg = kAhead == 2 ? next_rg : rg0;
       fetch(fetch_rg, kt + kAhead, ph_next);
       ph_next = phys_of(kt + kAhead + 1);
       compute(kt, st);
@@ -491,7 +514,7 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
       // unnormalised partial output and (max, sum) of this partition
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb) {
-        const float lsum = rows_sum(lrun[mb]);
+        const float lsum = rows_sum(lrun[mb]) * (F8 ? PA_KARG(lsum_scale) : 1.f);
         if (mvalid[mb]) {
           const int64_t idx = (int64_t(PA_KARG(num_seqs) + q0 + jrow[mb]) * PA_KARG(num_q_heads) + hq[mb]) *
                                   PA_KARG(max_parts) +
@@ -506,7 +529,7 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
       // ---- normalise and store --------------------------------------------------
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb) {
-        const float inv = 1.f / rows_sum(lrun[mb]);
+        const float inv = 1.f / (rows_sum(lrun[mb]) * (F8 ? PA_KARG(lsum_scale) : 1.f));
         if (mvalid[mb]) {
           __bf16* orow =
               static_cast<__bf16*>(PA_KARG(out)) + int64_t(q0 + jrow[mb]) * PA_KARG(o_row_stride) + int64_t(hq[mb]) * D;
@@ -522,7 +545,7 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
   }
 }
 
-template <int G, int W, int BS, int D>
+template <int G, int W, int BS, int D, bool F8>
 int prefill_groups() {
   static std::atomic<int> cache{0};
   int v = cache.load(std::memory_order_relaxed);
@@ -530,7 +553,7 @@ int prefill_groups() {
   int dev = 0, cus = 0, occ = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, prefill_kernel<G, W, BS, D>, Shape<W, D>::kThreads,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, prefill_kernel<G, W, BS, D, F8>, Shape<W, D>::kThreads,
                                                    Shape<W, D>::kLdsBytes) != hipSuccess ||
       occ <= 0)
     occ = 1;
@@ -539,15 +562,15 @@ int prefill_groups() {
   return v;
 }
 
-template <int G, int W, int BS, int D>
+template <int G, int W, int BS, int D, bool F8>
 hipError_t launch_g(const PrefillArgs& a, hipStream_t stream) {
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<G, W, BS, D>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel<G, W, BS, D, F8>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, Shape<W, D>::kLdsBytes);
   if (attr != hipSuccess) return attr;
   using Sh = Shape<W, D>;
-  const int groups = prefill_groups<G, W, BS, D>();
-  hipLaunchKernelGGL((prefill_kernel<G, W, BS, D>), dim3(groups), dim3(Sh::kThreads), Sh::kLdsBytes, stream, a);
+  const int groups = prefill_groups<G, W, BS, D, F8>();
+  hipLaunchKernelGGL((prefill_kernel<G, W, BS, D, F8>), dim3(groups), dim3(Sh::kThreads), Sh::kLdsBytes, stream, a);
   return hipGetLastError();
 }
 
@@ -561,46 +584,51 @@ bool prefill_supported(int head_dim, int group, int block_size) {
          (block_size == 8 || block_size == 16 || block_size == 32);
 }
 
-template <int W, int BS, int D>
+template <int W, int BS, int D, bool F8>
 hipError_t launch_w(int group, const PrefillArgs& a, hipStream_t stream) {
   switch (group) {
-    case 1: return launch_g<1, W, BS, D>(a, stream);
-    case 2: return launch_g<2, W, BS, D>(a, stream);
-    case 4: return launch_g<4, W, BS, D>(a, stream);
-    case 8: return launch_g<8, W, BS, D>(a, stream);
+    case 1: return launch_g<1, W, BS, D, F8>(a, stream);
+    case 2: return launch_g<2, W, BS, D, F8>(a, stream);
+    case 4: return launch_g<4, W, BS, D, F8>(a, stream);
+    case 8: return launch_g<8, W, BS, D, F8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int W, int D>
+template <int W, int D, bool F8>
 hipError_t launch_b(int group, const PrefillArgs& a, hipStream_t stream) {
   switch (a.block_size) {
-    case 8: return launch_w<W, 8, D>(group, a, stream);
-    case 16: return launch_w<W, 16, D>(group, a, stream);
-    case 32: return launch_w<W, 32, D>(group, a, stream);
+    case 8: return launch_w<W, 8, D, F8>(group, a, stream);
+    case 16: return launch_w<W, 16, D, F8>(group, a, stream);
+    case 32: return launch_w<W, 32, D, F8>(group, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 // W waves of 16 * kMB pairs each: 128 / 64 pairs per item (32 per wave), or
 // 64 / 32 at D = 256 (16 per wave)
-template <int D>
+template <int D, bool F8>
 hipError_t launch_d(int group, const PrefillArgs& a, hipStream_t stream) {
   const int per_wave = D == 256 ? 16 : 32;
-  if (a.tile_pairs == 2 * per_wave) return launch_b<2, D>(group, a, stream);
-  if (a.tile_pairs == 4 * per_wave) return launch_b<4, D>(group, a, stream);
+  if (a.tile_pairs == 2 * per_wave) return launch_b<2, D, F8>(group, a, stream);
+  if (a.tile_pairs == 4 * per_wave) return launch_b<4, D, F8>(group, a, stream);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_prefill(int head_dim, int group, const PrefillArgs& a, hipStream_t stream) {
+hipError_t launch_prefill(int head_dim, int group, bool fp8_cache, const PrefillArgs& a, hipStream_t stream) {
   if (!prefill_supported(head_dim, group, a.block_size)) return hipErrorInvalidValue;
   const int gi = prefill_item_group(group);
   PrefillArgs b = a;
   b.head_split_log2 = 0;
   while ((gi << b.head_split_log2) < group) ++b.head_split_log2;
-  if (head_dim == 128) return launch_d<128>(gi, b, stream);
-  if (head_dim == 64) return launch_d<64>(gi, b, stream);
-  return launch_d<256>(gi, b, stream);
+  if (fp8_cache) {
+    if (head_dim == 128) return launch_d<128, true>(gi, b, stream);
+    if (head_dim == 64) return launch_d<64, true>(gi, b, stream);
+    return launch_d<256, true>(gi, b, stream);
+  }
+  if (head_dim == 128) return launch_d<128, false>(gi, b, stream);
+  if (head_dim == 64) return launch_d<64, false>(gi, b, stream);
+  return launch_d<256, false>(gi, b, stream);
 }
 
 int prefill_tile_pairs(int head_dim, bool short_rows) {

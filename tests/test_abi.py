@@ -58,7 +58,7 @@ def test_struct_layout_matches_c(tmp_path):
 
 
 def test_status_strings_and_version(L):
-    assert L.pa_abi_version() == 206
+    assert L.pa_abi_version() == 207
     for code in range(0, -11, -1):
         s = L.pa_status_string(code).decode()
         assert s.startswith("PA_")
@@ -168,7 +168,8 @@ def test_fp8_host_errors(L):
     a = L.pa_attention_varlen_fp8
     p = _params()
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(p), 1.0, -1.0, None, 0, None) == -2
-    assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(max_query_len=4)), 1.0, 1.0, None, 0, None) == -3
+    # multi-row requests run on the MFMA kernel (here the missing workspace is the error)
+    assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(max_query_len=4)), 1.0, 1.0, None, 0, None) == -5
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(dtype=pa.PA_F32)), 1.0, 1.0, None, 0, None) == -3
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(block_size=12)), 1.0, 1.0, None, 0, None) == -3
     # 8- and 32-token blocks are served (here the missing workspace is the error)

@@ -181,8 +181,54 @@ def test_gqa_config_fp8_every_row():
     assert ok, (mx, mean)
 
 
-def test_fp8_multirow_is_rejected():
-    c = build_case("mr8", 34, "bf16", 8, 2, 128, [3, 1], [20, 30])
+@pytest.mark.parametrize("D,Hq,Hkv,bs", [(128, 32, 8, 16), (128, 8, 8, 16), (128, 64, 8, 16), (64, 16, 8, 16),
+                                         (256, 16, 8, 16), (128, 32, 8, 8), (128, 32, 8, 32), (128, 128, 8, 16)])
+def test_prefill_fp8_chunks(D, Hq, Hkv, bs):
+    """Multi-row requests on 8-bit pools (the MFMA kernel widens the codes to
+    bf16 when it stages them): chunks of 2, 17, 65 and 300 rows with and without
+    a cached prefix, next to decode rows and an empty request."""
+    n = [2, 17, 1, 65, 0, 300, 1]
+    L = [2, 17 + 401, 900, 65 + 1000, 3, 300 + 77, 33]
+    c = build_case(f"pf8_{D}_{Hq}_{bs}", 60 + D + bs, "bf16", Hq, Hkv, D, n, L, block_size=bs)
+    fc = Fp8Case(c, 12, 0.5, 0.25)
+    for psize in (0, 256):
+        fc.write_and_attend(psize)
+        mx, mean, ok = fc.compare(check_pool=psize == 0)
+        say(f"fp8 prefill D={D} {Hq}/{Hkv} bs {bs} psize {psize}: max {mx:.3g} mean {mean:.3g}")
+        assert ok, (psize, mx, mean)
+
+
+@pytest.mark.parametrize("Hq,Hkv,maxn", [(64, 8, 8), (32, 8, 16)])
+def test_fp8_short_multirow_split(Hq, Hkv, maxn):
+    """Short multi-row requests on 8-bit pools whose contexts span several
+    partitions: computed per partition by the MFMA kernel and merged."""
+    n = [2, maxn, 3, 1, 5, maxn]
+    L = [2049, 5000, 513, 3000, 1030, 2048 + maxn]
+    c = build_case(f"split8_{Hq}_{maxn}", 70 + maxn, "bf16", Hq, Hkv, 128, n, L)
+    fc = Fp8Case(c, 13, 0.5, 0.25)
+    for psize in (0, 512):
+        fc.write_and_attend(psize)
+        mx, mean, ok = fc.compare(check_pool=psize == 0)
+        say(f"fp8 split {Hq}/{Hkv} psize {psize}: max {mx:.3g} mean {mean:.3g}")
+        assert ok, (psize, mx, mean)
+
+
+def test_mixed_config_fp8_every_row():
+    """The mixed chunked-prefill step (8 chunks of 512 rows with cached prefixes and
+    248 decode rows, 32/8 heads) on 8-bit pools in the launch configuration the
+    benchmark times: the whole pool bit for bit and every row against the oracle."""
+    c = make_config("mixed_prefill_bf16", 0)
+    fc = Fp8Case(c, 14, 0.5, 0.25)
+    fc.write_and_attend(0)
+    mx, mean, ok = fc.compare(sharded=True)
+    say(f"mixed fp8 every row: max {mx:.3g} mean {mean:.3g}")
+    assert ok, (mx, mean)
+
+
+def test_fp8_multirow_needs_a_built_group():
+    """Multi-row requests on 8-bit pools run on the MFMA kernel only; a group
+    size it does not build (not a power of two) is refused."""
+    c = build_case("mr8", 34, "bf16", 12, 2, 128, [3, 1], [20, 30])
     fc = Fp8Case(c, 11, 1.0, 1.0)
     with pytest.raises(pa.PAError) as e:
         fc.write_and_attend(0)
