@@ -202,6 +202,25 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+
+// S^T += K Q^T over 32 d (16 keys x 16 head columns).
+__device__ __forceinline__ f32x4_t mfma_k32(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                  0, 0, 0);
+}
+// O += P V over 16 keys (16 head rows x 16 d columns).
+__device__ __forceinline__ f32x4_t mfma_k16(const u32x2_t& a, const u32x2_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b), c,
+                                                   0, 0, 0);
+}
+// Two E4M3 codes as a bf16 pair (exact), the low (Hi = false) or high two of w.
+template <bool Hi>
+__device__ __forceinline__ uint32_t cvt8(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, Hi));
+}
+
 template <int Ctrl>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
   return uint32_t(__builtin_amdgcn_mov_dpp(int(v), Ctrl, 0xF, 0xF, true));
@@ -313,8 +332,21 @@ __device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t,
 // the last load group of an item already fetches the next item's first kRing
 // tiles and the HBM queue of the wave never drains at item boundaries.  The
 // physical block id of the slot issued next is fetched one issue ahead.
-template <int G, bool F8, int BS, int D>
+//
+// MF: the matrix-core form of the tile math (D = 128, items of 4 or 8 heads).  S^T = K Q^T runs on v_mfma_f32_16x16x32_bf16
+// with the tile's 16 keys as rows and the item's heads as columns (padded to
+// 16 with zero q), so lane l holds head l % 16's scores of keys 4(l/16) ..
+// 4(l/16)+3; those scores, exponentiated and rounded to bf16, are directly the
+// A operand of O = P V on v_mfma_f32_16x16x16_bf16, whose B operand is V in
+// its stored order: lane l loads keys 4(l/16) .. +3 at d = 8(l%16) .. +7 and
+// output column n of product j is d = 8n + j.  K is loaded with key l % 16 per
+// lane (the A-operand order), 16 bytes per load; the contraction order over d
+// is a fixed permutation shared by K and q.  The VALU work per tile drops from
+// ~G * D / 4 dot instructions per lane to the softmax and the operand
+// conversions.
+template <int G, bool F8, int BS, int D, bool MF>
 __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kernel(DecodeArgs a) {
+  static_assert(!MF || (D == 128 && (G == 4 || G == 8)), "matrix-core tiles: D = 128, items of 4 or 8 heads");
   using T = Kv<F8, D>;
   constexpr int kRing = T::kRing;
   constexpr int kTileBytes = T::kTileBytes;
@@ -502,6 +534,28 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
     return;
   }
 
+  // ---- matrix-core form: lane geometry and q operands ----------------------------
+  constexpr int kEB = F8 ? 1 : 2;                  // bytes per cached element
+  constexpr int kKLoads = F8 ? 2 : 4;              // 16-byte K loads per lane and tile
+  const int mrow = lane & 15;                      // MFMA row / column of the lane
+  const int mg = lane >> 4;                        // its group of 4 (k slots, output rows)
+  const int kmf_off = mrow * (D * kEB) + 16 * mg;  // K: key mrow, then + 64 per load
+  const int vmf_off = 4 * mg * (D * kEB) + 8 * mrow * kEB;   // V: key 4 mg, d 8 mrow; + D*kEB per key
+  // d of element 0 of the lane's K (and q) operand of 32-d step st: bf16 loads hold
+  // d 8 mg + 32 st; 8-bit loads hold 16 codes, d 16 mg + 64 (st / 2), split in halves
+  auto mf_d0 = [&](int st) { return F8 ? 16 * mg + 64 * (st >> 1) + 8 * (st & 1) : 8 * mg + 32 * st; };
+  // registers of one tile as loaded: K, V
+  using KR = typename std::conditional<MF, u32x4_t, Raw>::type;
+  using VR = typename std::conditional<MF, typename std::conditional<F8, u32x2_t, u32x4_t>::type, Raw>::type;
+  constexpr int kKR = MF ? kKLoads : 4;
+  u32x4_t qmf[4];   // B operand of step st: head mrow's q at d mf_d0(st) .. +7, zero for padding heads
+  auto q_mf_from = [&](const char* rows) {   // rows: the item's G q rows of D bf16
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      qmf[st] = mrow < G ? *reinterpret_cast<const u32x4_t*>(rows + mrow * (D * 2) + mf_d0(st) * 2)
+                         : u32x4_t{0u, 0u, 0u, 0u};
+  };
+
   auto load_q = [&](Words(&qreg)[G], const Item& it) {   // q slices, lane-relative order h(r ^ M_j)
     const char* qrow =
         static_cast<const char*>(a.q) + (int64_t(it.q0) * a.q_row_stride + int64_t(it.hg) * G * D) * 2;
@@ -513,8 +567,59 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
   };
   // Load slot i reads rows 4i .. 4i+3 of the tile.  With BS = 8 slots 0, 1
   // read the first block and slots 2, 3 the second (rows 0..7 of each).
-  auto load_tile = [&](Raw(&kb)[4], Raw(&vb)[4], const char* kbase, const char* vbase, bool live, int64_t key) {
-    if constexpr (BS == 8) {
+  auto load_tile = [&](KR(&kb)[kKR], VR(&vb)[4], const char* kbase, const char* vbase, bool live, int64_t key) {
+    if constexpr (MF && BS == 8) {
+      // Keys 0..7 of the tile are rows 0..7 of the first block, keys 8..15 of
+      // the second.  Each lane reads its rows from both blocks at row index
+      // r (first) and r ^ 8 (second): exactly one of the two lies inside its
+      // block's 8-row range, the other reads past it and returns zeros without
+      // touching memory, so the OR of the two is the lane's data.
+      const int64_t id0 = int64_t(uint32_t(uint64_t(key)));
+      const int id1 = int(uint32_t(uint64_t(key) >> 32));
+      const int nrec0 = live ? kHeadBytes : 0;
+      const int nrec1 = live && id1 >= 0 ? kHeadBytes : 0;
+      const int64_t off1 = int64_t(id1 >= 0 ? id1 : 0) * bstride;
+      const __amdgpu_buffer_rsrc_t rk0 =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + id0 * bstride), 0, nrec0, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rk1 =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + off1), 0, nrec1, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv0 =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + id0 * bstride), 0, nrec0, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv1 =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + off1), 0, nrec1, kRsrcWord3);
+      constexpr int kRow = D * kEB;
+      const int k_alt = kmf_off ^ (8 * kRow);   // key row mrow ^ 8
+#pragma unroll
+      for (int i = 0; i < kKR; ++i)
+        kb[i] = __builtin_amdgcn_raw_buffer_load_b128(rk0, kmf_off + 64 * i, 0, 0) |
+                __builtin_amdgcn_raw_buffer_load_b128(rk1, k_alt + 64 * i, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {   // key 4 mg + i: rows 0..7 of block 0 for mg < 2, else of block 1
+        const int v0 = vmf_off + i * kRow;
+        const int v1 = v0 ^ (8 * kRow);
+        if constexpr (F8)
+          vb[i] = __builtin_amdgcn_raw_buffer_load_b64(rv0, v0, 0, 0) | __builtin_amdgcn_raw_buffer_load_b64(rv1, v1, 0, 0);
+        else
+          vb[i] = __builtin_amdgcn_raw_buffer_load_b128(rv0, v0, 0, 0) |
+                  __builtin_amdgcn_raw_buffer_load_b128(rv1, v1, 0, 0);
+      }
+    } else if constexpr (MF) {
+      const int64_t off = BS == 32 ? (key >> 1) * bstride + (key & 1) * kTileBytes : key * bstride;
+      const int nrec = live ? kTileBytes : 0;
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + off), 0, nrec, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + off), 0, nrec, kRsrcWord3);
+#pragma unroll
+      for (int i = 0; i < kKR; ++i) kb[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, kmf_off + 64 * i, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (F8)
+          vb[i] = __builtin_amdgcn_raw_buffer_load_b64(rv, vmf_off + i * (D * kEB), 0, 0);
+        else
+          vb[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vmf_off + i * (D * kEB), 0, 0);
+      }
+    } else if constexpr (BS == 8) {
       const int64_t id0 = int64_t(uint32_t(uint64_t(key)));
       const int id1 = int(uint32_t(uint64_t(key) >> 32));
       const int nrec0 = live ? kHeadBytes : 0;
@@ -547,8 +652,13 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
   };
 
   Words qreg[G];
-  Raw kr[kRing][4], vr[kRing][4];   // the ring: K and V of kRing tiles, as loaded
-  load_q(qreg, cur);
+  // the ring: K and V of kRing tiles, as loaded
+  KR kr[kRing][kKR];
+  VR vr[kRing][4];
+  if constexpr (MF)
+    q_mf_from(static_cast<const char*>(a.q) + (int64_t(cur.q0) * a.q_row_stride + int64_t(cur.hg) * G * D) * 2);
+  else
+    load_q(qreg, cur);
   int64_t ph0[kRing];   // keys of the first tiles, all requested before any is used
   static_for<kRing>([&](auto S) {
     constexpr int st = decltype(S)::value;
@@ -606,13 +716,92 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
       return tile_key<BS>(tb, lb0 + max(min(jj, nbl - 1), 0), own ? cur.tok1 : nxt.tok1);
     };
     int64_t pf = slot_phys(kRing);   // tile key of the next slot to issue
-    auto issue = [&](Raw(&kb)[4], Raw(&vb)[4], int j) {
+    auto issue = [&](KR(&kb)[kKR], VR(&vb)[4], int j) {
       const int64_t phys = pf;
       pf = slot_phys(j + 1);
       const bool own = j < cur.nbr;
       const int jj = own ? j : j - cur.nbr;
       const int nbl = own ? cur.nb : nxt.nb;
       load_tile(kb, vb, own ? cur.kbase : nxt.kbase, own ? cur.vbase : nxt.vbase, jj < nbl, phys);
+    };
+
+    // matrix-core form: O accumulators (product j: rows heads 4 mg .. +3, column
+    // mrow = d 8 mrow + j) and the tile step
+    f32x4_t oacc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) oacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto process_mf = [&](auto& kraw, auto& vraw, int k) {   // generic: instantiated only where called
+      f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        u32x4_t ka;
+        if constexpr (F8) {
+          const u32x4_t& w = kraw[st >> 1];
+          ka = (st & 1) ? u32x4_t{cvt8<false>(w[2]), cvt8<true>(w[2]), cvt8<false>(w[3]), cvt8<true>(w[3])}
+                        : u32x4_t{cvt8<false>(w[0]), cvt8<true>(w[0]), cvt8<false>(w[1]), cvt8<true>(w[1])};
+        } else {
+          ka = kraw[st];
+        }
+        s4 = mfma_k32(ka, qmf[st], s4);
+      }
+      const int tb = (cur.lb0 + k) * kBlock;   // first token of the tile
+      float sc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[i] = s4[i] * scale_log2;   // key tb + 4 mg + i, head mrow
+      using VV = std::remove_cv_t<std::remove_reference_t<decltype(vraw[0])>>;   // VR (dependent)
+      VV vv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vv[i] = vraw[i];
+      if (tb + kBlock > cur.tok1 || tb < cur.lo) {   // the context ends, or the window starts, in this tile
+        const uint32_t span = uint32_t(cur.tok1 - cur.lo);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool dead = uint32_t(tb + 4 * mg + i - cur.lo) >= span;
+          sc[i] = dead ? -__builtin_inff() : sc[i];
+          vv[i] = dead ? VV{} : vv[i];   // rows past the context may hold anything
+        }
+      }
+      // every lane: the tile max of head mrow (its 4 keys, then the 4 lane groups)
+      const float bm = rows_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+      if (__builtin_amdgcn_ballot_w64(bm > m + kRescaleThreshold)) {
+        const float mn = fmaxf(m, bm);
+        const float alpha = fast_exp2(m - mn);
+        m = mn;
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {   // output row i of the lane is head 4 mg + i
+          const float ai = __shfl(alpha, 4 * mg + i);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) oacc[j][i] *= ai;
+        }
+      }
+      const u32x2_t pa = {pack_bf16x2(fast_exp2(sc[0] - m), fast_exp2(sc[1] - m)),
+                          pack_bf16x2(fast_exp2(sc[2] - m), fast_exp2(sc[3] - m))};
+      l = dot2_bf16(pa[0], kBf16OnePair, l);
+      l = dot2_bf16(pa[1], kBf16OnePair, l);
+      // B operand of product j: keys 4 mg .. +3 at d 8 mrow + j, as two bf16 pairs
+      if constexpr (F8) {
+#pragma unroll
+        for (int w = 0; w < 2; ++w)
+#pragma unroll
+          for (int b = 0; b < 4; b += 2) {
+            // codes b, b+1 of word w of keys (0, 1) and (2, 3), interleaved by key
+            const uint32_t sel = b == 0 ? 0x05010400u : 0x07030602u;
+            const uint32_t x01 = __builtin_amdgcn_perm(vv[1][w], vv[0][w], sel);
+            const uint32_t x23 = __builtin_amdgcn_perm(vv[3][w], vv[2][w], sel);
+            const int j = 4 * w + b;
+            oacc[j] = mfma_k16(pa, u32x2_t{cvt8<false>(x01), cvt8<false>(x23)}, oacc[j]);
+            oacc[j + 1] = mfma_k16(pa, u32x2_t{cvt8<true>(x01), cvt8<true>(x23)}, oacc[j + 1]);
+          }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+          const u32x2_t vb = {__builtin_amdgcn_perm(vv[1][j >> 1], vv[0][j >> 1], sel),
+                              __builtin_amdgcn_perm(vv[3][j >> 1], vv[2][j >> 1], sel)};
+          oacc[j] = mfma_k16(pa, vb, oacc[j]);
+        }
+      }
     };
 
     auto process = [&](Raw(&kraw)[4], Raw(&vraw)[4], int k) {
@@ -697,7 +886,12 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
       }
       static_for<kRing>([&](auto S) {
         constexpr int st = decltype(S)::value;
-        if (st == 0 || k + st < cur.nb) process(kr[st], vr[st], k + st);
+        if (st == 0 || k + st < cur.nb) {
+          if constexpr (MF)
+            process_mf(kr[st], vr[st], k + st);
+          else
+            process(kr[st], vr[st], k + st);
+        }
         __builtin_amdgcn_sched_barrier(0);
         issue(kr[st], vr[st], k + kRing + st);
         __builtin_amdgcn_sched_barrier(0);
@@ -707,6 +901,43 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
       // and waits for vmcnt(8*kRing), leaving the next item's first tiles in
       // flight (after the loop it could only wait for vmcnt(0) and drain them).
       if (k + kRing >= cur.nb && nxt.valid) park_q(qt);
+    }
+
+    if constexpr (MF) {
+      // ---- matrix-core form: normalise or leave partials -------------------------
+      // m is already common to the lane groups of a head; the sum is not
+      const float lw = rows_sum(l) * a.lsum_scale;   // every lane: sum of head mrow (carries 1 / v_scale)
+      if (nxt.valid) q_mf_from(reinterpret_cast<const char*>(&sq[wave][0]));   // parked in the last group
+      const bool whole = (cur.parts >> 16) == 1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {   // output row i: head 4 mg + i, d 8 mrow .. +7
+        const int head = 4 * mg + i;
+        const float Lh = __shfl(lw, head);
+        if (head < G) {
+          const int hq = cur.hg * G + head;
+          if (whole) {
+            const float inv = 1.f / Lh;
+            u32x4_t o;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) o[w] = pack_bf16x2(oacc[2 * w][i] * inv, oacc[2 * w + 1][i] * inv);
+            *reinterpret_cast<u32x4_t*>(static_cast<__bf16*>(a.out) + int64_t(cur.q0) * a.o_row_stride +
+                                        int64_t(hq) * D + 8 * mrow) = o;
+          } else {
+            const int64_t slot = (int64_t(cur.b) * a.num_q_heads + hq) * a.max_parts + (cur.parts & 0xffff);
+            float* dst = a.ws_o + slot * D + 8 * mrow;
+            *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{oacc[0][i], oacc[1][i], oacc[2][i], oacc[3][i]};
+            *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{oacc[4][i], oacc[5][i], oacc[6][i], oacc[7][i]};
+          }
+        }
+      }
+      if (!whole && mg == 0 && mrow < G) {
+        const int64_t slot = (int64_t(cur.b) * a.num_q_heads + cur.hg * G + mrow) * a.max_parts + (cur.parts & 0xffff);
+        a.ws_ml[2 * slot] = m;
+        a.ws_ml[2 * slot + 1] = lw;
+      }
+      if (!nxt.valid) break;
+      cur = nxt;
+      continue;
     }
 
     // ---- combine the 4 token rows: common max, rescale, reduce-scatter -----------
@@ -817,7 +1048,7 @@ bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size, int
 namespace {
 
 // Resident workgroups per device for kernel K: CUs x occupancy, queried once per device.
-template <int G, bool F8, int BS, int D>
+template <int G, bool F8, int BS, int D, bool MF>
 int persistent_groups() {
   static std::atomic<int> cache[kMaxDevices];
   int dev = 0;
@@ -826,7 +1057,7 @@ int persistent_groups() {
   if (v > 0) return v;
   int cus = 0, occ = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_gqa_kernel<G, F8, BS, D>, 64 * (kWavesPerGroup + 1),
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_gqa_kernel<G, F8, BS, D, MF>, 64 * (kWavesPerGroup + 1),
                                                    0) != hipSuccess ||
       occ <= 0)
     occ = 1;
@@ -835,12 +1066,24 @@ int persistent_groups() {
   return v;
 }
 
+// The matrix-core tile form serves 8-bit pools at D = 128 with items of 4 or 8
+// heads (every block size, so results stay bitwise the same across block
+// sizes): there the dot-product form is bound by the VALU issue of the code
+// conversions and v_dot2 instructions, not by HBM.  bf16 pools keep the
+// dot-product form, which streams at the HBM ceiling already (the matrix-core
+// form measured 0.8% faster on the GQA decode layer).
+template <int G, bool F8, int BS, int D>
+constexpr bool use_mfma_tiles() {
+  return F8 && D == 128 && (G == 4 || G == 8);
+}
+
 template <int G, bool F8, int BS, int D>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
+  constexpr bool MF = use_mfma_tiles<G, F8, BS, D>();
   const int64_t upper = (int64_t(a.num_seqs) * a.max_parts * a.num_kv_heads) << a.head_split_log2;
-  const int64_t grid = std::min<int64_t>(upper, persistent_groups<G, F8, BS, D>());
+  const int64_t grid = std::min<int64_t>(upper, persistent_groups<G, F8, BS, D, MF>());
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_gqa_kernel<G, F8, BS, D>), dim3(grid), dim3(64 * (kWavesPerGroup + 1)), 0, stream, a);
+  hipLaunchKernelGGL((decode_gqa_kernel<G, F8, BS, D, MF>), dim3(grid), dim3(64 * (kWavesPerGroup + 1)), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -895,10 +1138,10 @@ hipError_t launch_f(int group, int head_dim, const DecodeArgs& a, hipStream_t st
 int decode_gqa_workers(int group) {
   int g = 0;
   switch (item_group(128, group)) {
-    case 1: g = persistent_groups<1, false, 16, 128>(); break;
-    case 2: g = persistent_groups<2, false, 16, 128>(); break;
-    case 4: g = persistent_groups<4, false, 16, 128>(); break;
-    case 8: g = persistent_groups<8, false, 16, 128>(); break;
+    case 1: g = persistent_groups<1, false, 16, 128, false>(); break;
+    case 2: g = persistent_groups<2, false, 16, 128, false>(); break;
+    case 4: g = persistent_groups<4, false, 16, 128, false>(); break;
+    case 8: g = persistent_groups<8, false, 16, 128, false>(); break;
     default: g = 256;
   }
   return g * kWavesPerGroup;

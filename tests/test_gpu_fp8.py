@@ -158,6 +158,42 @@ def test_decode_fp8_head_dim_64(D, Hq, Hkv):
         assert ok, (psize, mx, mean)
 
 
+@pytest.mark.parametrize("Hq,Hkv,n,lens", [
+    (64, 8, [1] * 10, [1, 8, 9, 16, 17, 33, 100, 700, 2049, 3000]),   # items of 8 heads
+    (32, 8, [1] * 10, [1, 8, 9, 16, 17, 33, 100, 700, 2049, 3000]),   # items of 4 heads
+    (32, 8, [40, 1, 7, 1], [1000, 700, 37, 33]),                       # chunked prefill with decode rows
+])
+def test_fp8_bitwise_across_block_sizes(Hq, Hkv, n, lens):
+    """The same 8-bit K/V paged on 8-, 16- and 32-token blocks gives bitwise the
+    same outputs (16-token tiles in the same order at every block size; with 8-
+    token blocks a tile's two halves come from two blocks)."""
+    from tests.test_gpu_variants import _repage
+
+    c = build_case(f"f8xbs{Hq}", 150 + Hq, "bf16", Hq, Hkv, 128, n, lens)
+    k16, v16 = Fp8Case(c, 15, 0.5, 0.25).oracle_pools()   # the pools after this step's (quantising) cache write
+    rng = np.random.default_rng(16)
+    outs = {}
+    for bs in (16, 8, 32):
+        if bs == 16:
+            kp, vp, tables = k16, v16, c.block_tables
+        else:
+            nb = sum(-(-int(L) // bs) for L in lens) + 3
+            (kp, vp), tables = _repage((k16, v16), c.block_tables, lens, bs, nb, rng)
+        out = torch.empty_like(to_dev(c.q, "bf16"))
+        pa.attention_varlen(out, to_dev(c.q, "bf16"), to_dev_u8(kp), to_dev_u8(vp),
+                            torch.from_numpy(c.cu_seqlens).to("cuda:0"), torch.from_numpy(c.seq_lens).to("cuda:0"),
+                            torch.from_numpy(np.ascontiguousarray(tables)).to("cuda:0"), float(c.scale),
+                            c.max_query_len, c.max_seq_len, partition_size=256, k_scale=0.5, v_scale=0.25)
+        torch.cuda.synchronize()
+        outs[bs] = to_host(out, "bf16")
+    assert np.array_equal(outs[8], outs[16]) and np.array_equal(outs[32], outs[16])
+    want = oracle.oracle_attention_varlen(c.q, k16, v16, c.cu_seqlens, c.seq_lens, c.block_tables, c.scale,
+                                          c.num_kv_heads, "bf16", 16, kv_dtype="fp8", k_scale=0.5, v_scale=0.25)
+    mx, mean, ok = oracle.compare_outputs(oracle.widen(outs[16], "bf16"), want, "bf16")
+    say(f"fp8 {Hq}/{Hkv}: bitwise equal across block sizes; max {mx:.3g} mean {mean:.3g}")
+    assert ok, (mx, mean)
+
+
 def test_decode_fp8_deterministic_bitwise():
     c = build_case("det8", 33, "bf16", 64, 8, 128, [1] * 6, [3000, 17, 900, 2049, 1, 4500])
     fc = Fp8Case(c, 9, 0.5, 0.25)

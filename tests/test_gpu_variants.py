@@ -113,12 +113,14 @@ def test_fast_decode_block_size(bs, Hq, Hkv):
 
 def _repage(pool_bits, tables, lens, bs, num_blocks, rng):
     """Lay each request's contiguous rows (read from a 16-token-block pool) out
-    again on bs-token blocks in shuffled order; unused slots hold bf16 NaN."""
+    again on bs-token blocks in shuffled order; unused slots hold NaN (bf16
+    bits, or the E4M3 NaN code for 8-bit pools)."""
     Hkv, D = pool_bits[0].shape[1], pool_bits[0].shape[3]
     perm = rng.permutation(num_blocks)
     width = max(-(-int(L) // bs) for L in lens)
     new_tables = np.full((len(lens), width), num_blocks - 1, np.int32)
-    pools = [np.full((num_blocks, Hkv, bs, D), 0x7FC0, np.uint16) for _ in pool_bits]
+    fill = 0x7F if pool_bits[0].dtype == np.uint8 else 0x7FC0
+    pools = [np.full((num_blocks, Hkv, bs, D), fill, src.dtype) for src in pool_bits]
     nxt = 0
     for b, L in enumerate(lens):
         for j in range(-(-int(L) // bs)):
