@@ -24,11 +24,14 @@ the digest recorded there (null otherwise).  ``cpu_baseline`` times the fp64
 CPU oracle on a bounded sample of the same requests.
 
 ``--calibrate-copy`` runs only a 1 GiB device-to-device copy (the counters'
-calibration run).  ``--flush-cache`` reads a 1 GiB buffer before each
-timed plan and run call (a read, so no dirty lines are left to be written
-back during the call), so those times start with no part of the batch in
-the L2s or the Infinity Cache (for the shared-prefix workload, whose logical
-bytes count the shared blocks once per request).  ``--block-size 8|32`` builds the same workload on 8- or
+calibration run).  By default a 1 GiB buffer is read before each timed plan
+and run call (a read, so no dirty lines are left to be written back during
+the call), so those times, and ``roofline``, start with no part of the batch
+in the L2s or the Infinity Cache; the run stage is also timed back to back
+(``attention_run_ms_unflushed``), and ``--no-flush-cache`` drops the flushed
+timing.  For workloads with multi-row requests, ``prefill_kernel`` times the
+call over those requests alone and reports the prefill kernel's TFLOP/s
+against the bf16 matrix-core peak.  ``--block-size 8|32`` builds the same workload on 8- or
 32-token blocks.  ``--sliding-window W`` runs the workload with a sliding
 window of W tokens (KV bytes then count only the keys in some row's window).  ``--op copy_blocks`` times copy-on-write block copies
 (pa_copy_blocks) and ``--op swap_out`` / ``--op swap_in`` time swapping a
@@ -344,6 +347,59 @@ class _DeviceBatch:
                                  v_scale=V_SCALE_FP8 if self.fp8 else None, stage=stage)
 
 
+class _MultiRowBatch:
+    """The multi-row requests of a device batch as a batch of their own: their
+    query rows copied out, the same pools and block-table rows, own workspace."""
+
+    def __init__(self, dc, torch):
+        c = dc.c
+        idx = np.nonzero(c.q_lens > 1)[0]
+        rows = np.concatenate([np.arange(c.cu_seqlens[b], c.cu_seqlens[b + 1]) for b in idx]).astype(np.int64)
+        q_lens = c.q_lens[idx]
+        cu = np.zeros(len(idx) + 1, dtype=c.cu_seqlens.dtype)
+        cu[1:] = np.cumsum(q_lens)
+        self.c = _SubConfig(c, idx, q_lens, cu)
+        self.torch, self.pa, self.fp8, self.window = torch, dc.pa, dc.fp8, dc.window
+        dev = dc.q.device
+        self.q = dc.q[torch.from_numpy(rows).to(dev)].contiguous()
+        self.k_cache, self.v_cache = dc.k_cache, dc.v_cache
+        self.cu = torch.from_numpy(cu).to(dev)
+        self.seq_lens = torch.from_numpy(np.ascontiguousarray(c.seq_lens[idx])).to(dev)
+        self.tables = torch.from_numpy(np.ascontiguousarray(c.block_tables[idx])).to(dev)
+        self.out = torch.empty_like(self.q)
+        self.ws = None
+        self.partition_size = None
+
+    attention = _DeviceBatch.attention
+
+
+class _SubConfig:
+    """The fields of a workload config that the attention call and the flop count read, for a subset of its requests."""
+
+    def __init__(self, c, idx, q_lens, cu):
+        self.num_kv_heads, self.num_q_heads, self.head_dim = c.num_kv_heads, c.num_q_heads, c.head_dim
+        self.scale, self.block_size = c.scale, c.block_size
+        self.q_lens, self.seq_lens, self.cu_seqlens = q_lens, c.seq_lens[idx], cu
+        self.num_seqs, self.total_q = len(idx), int(q_lens.sum())
+        self.max_query_len, self.max_seq_len = int(q_lens.max()), int(self.seq_lens.max())
+
+
+def profiled_kernel_us(workload: str, kernel: str):
+    """Average duration of a kernel in the committed kernel-trace summary of the
+    workload, or None when there is none or the kernels changed since it was taken."""
+    import re
+
+    path = os.path.join(PROFILES, f"attention_call_{workload}_kernels.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    dig = re.search(r"^source_sha256:\s*([0-9a-f]{64})", text, re.M)
+    row = re.search(r"^\| `pa::" + kernel + r"<[^`]*>` \| \d+ \| ([0-9.]+) \|", text, re.M)
+    if not dig or not row or dig.group(1) != kernel_source_digest():
+        return None
+    return float(row.group(1))
+
+
 def _timed_loop(torch, fn, steps, warmup, stream):
     """Warm up, then time `steps` calls of fn with HIP events on `stream` and the host clock."""
     for _ in range(warmup):
@@ -540,9 +596,15 @@ def main() -> None:
                     help="W > 0: each row sees only the last W positions up to its own")
     ap.add_argument("--block-size", type=int, default=16, choices=(8, 16, 32),
                     help="tokens per physical block")
-    ap.add_argument("--flush-cache", action="store_true",
-                    help="before each timed plan/run call, read a 1 GiB buffer (outside the events) so the "
-                         "L2s and the Infinity Cache hold none of the batch")
+    ap.add_argument("--flush-cache", dest="flush_cache", action="store_true", default=True,
+                    help="(default) before each timed plan/run call, read a 1 GiB buffer (outside the events) so "
+                         "the L2s and the Infinity Cache hold none of the batch; the run stage is timed unflushed "
+                         "as well and reported beside it")
+    ap.add_argument("--no-flush-cache", dest="flush_cache", action="store_false",
+                    help="time the plan/run calls back to back only")
+    ap.add_argument("--no-prefill-alone", action="store_true",
+                    help="skip timing the call over the multi-row requests alone (profiler runs: its decode and "
+                         "merge launches have empty lists and would enter those kernels' per-dispatch figures)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this framework runs the path on one GPU; --gpus must be 1 "
@@ -614,23 +676,48 @@ def main() -> None:
     # built once per step from the request lengths and shared by every layer)
     # and one layer's attention over them (pa_attention_run), each timed with
     # HIP events on the launch stream.
-    flush = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda:0") if args.flush_cache else None
+    flush_buf = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda:0") if args.flush_cache else None
 
-    def stage_ms(stage):
+    def stage_ms(stage, flush, batch=dc):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
         torch.cuda.synchronize()
         for i, (a_, b_) in enumerate(evs):
-            if flush is not None:   # a read of 1 GiB: evicts with clean lines, leaves nothing to write back
-                flush.sum()
+            if flush:   # a read of 1 GiB: evicts with clean lines, leaves nothing to write back
+                flush_buf.sum()
             a_.record(stream)
-            dc.attention(partition_size=args.partition_size, stage=stage)
+            batch.attention(partition_size=args.partition_size, stage=stage)
             b_.record(stream)
         torch.cuda.synchronize()
         return np.array([a_.elapsed_time(b_) for a_, b_ in evs])
 
-    plan_ms = float(stage_ms("plan").mean())
-    run_all = stage_ms("run")
+    flushed = flush_buf is not None
+    plan_ms = float(stage_ms("plan", flushed).mean())
+    run_unflushed = stage_ms("run", False)
+    run_all = stage_ms("run", True) if flushed else run_unflushed
     run_ms = float(run_all.mean())
+
+    # The prefill kernel on its own: the same call over the batch's multi-row
+    # requests alone (same pools and table rows), whose run stage is the
+    # prefill kernel plus the decode and merge launches with empty lists.
+    prefill = None
+    if c.max_query_len > 1 and not args.no_prefill_alone:
+        sub = _MultiRowBatch(dc, torch)
+        sub.attention(partition_size=args.partition_size, stage="plan")
+        sub_run = stage_ms("run", flushed, batch=sub)
+        sub_ms = float(sub_run.mean())
+        sub_flops = attention_flops(sub.c, W)
+        prefill = {
+            "what": "pa_attention_run over the multi-row requests alone: prefill_kernel, plus the decode and "
+                    "merge kernels launched with empty work lists",
+            "requests": int(sub.c.num_seqs),
+            "rows": int(sub.c.total_q),
+            "run_ms": round(sub_ms, 5),
+            "flops": sub_flops,
+            "tflops": round(sub_flops / (sub_ms * 1e-3) / 1e12, 2),
+            "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
+            "mfma_frac": round(sub_flops / (sub_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "profiled_prefill_kernel_us": profiled_kernel_us(c.name, "prefill_kernel") if not fp8 and not W else None,
+        }
 
     value = ab["kv"] / (ms_per_step * 1e-3) / 1e9
     achieved = ab["attention"] / (run_ms * 1e-3) / 1e9
@@ -670,6 +757,9 @@ def main() -> None:
         "attention_ms": round(attn_ms, 5),
         "attention_run_ms": round(run_ms, 5),
         "attention_run_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(run_all, [10, 50, 90])],
+        "attention_run_ms_unflushed": round(float(run_unflushed.mean()), 5),
+        "attention_run_frac_unflushed": round(ab["attention"] / (float(run_unflushed.mean()) * 1e-3) / 1e9
+                                              / HBM_PEAK_GBS, 4),
         "attention_plan_ms": round(plan_ms, 5),
         "cache_write_ms": round(cw_ms, 5),
         "kv_bytes_per_step": ab["kv"],
@@ -689,6 +779,8 @@ def main() -> None:
             "attention_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 3),
         },
     }
+    if prefill is not None:
+        result["prefill_kernel"] = prefill
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(c, args.cpu_budget, pools8, W, pool=cpu_pool)
     if cpu_pool is not None:
