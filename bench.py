@@ -344,7 +344,8 @@ class _DeviceBatch:
                                  float(c.scale), c.max_query_len, c.max_seq_len, workspace=self.ws,
                                  partition_size=partition_size, sliding_window=self.window,
                                  k_scale=K_SCALE_FP8 if self.fp8 else None,
-                                 v_scale=V_SCALE_FP8 if self.fp8 else None, stage=stage)
+                                 v_scale=V_SCALE_FP8 if self.fp8 else None, stage=stage,
+                                 num_decode_rows=int((c.q_lens == 1).sum()))
 
 
 class _MultiRowBatch:

@@ -115,6 +115,17 @@ typedef struct {
                                   keys max(0, p - W + 1) .. p with p = L_b - n_b + j ([Q67]
                                   §10.8 lists the sliding-window mask among the kernel
                                   variants; this is its reading).  Must be >= 0. */
+  int32_t num_decode_rows;     /* host hint, >= 0: requests with exactly one query row (0 if none
+                                  or unknown).  Scheduling only -- results are the same bits
+                                  whatever it says.  When > 0 and the batch also has multi-row
+                                  requests on the MFMA prefill kernel, the run overlaps the two
+                                  kernels ([ICE]: one step packs decode and prefill rows; prefill is
+                                  compute-bound, decode bandwidth-bound): the prefill kernel runs
+                                  on a second stream of the library's (one per device, default
+                                  priority), forked from and joined back to the caller's stream,
+                                  so the call still completes in the caller's stream order.  A
+                                  call captured into a graph records the fork and join; two
+                                  captures that overlap on one device must not both use it. */
 } pa_attn_params;
 
 /*
@@ -308,7 +319,7 @@ const char* pa_status_string(pa_status s);
  * prefill kernel at D = 64 and 256; 205: the fast decode kernel and 8-bit
  * pools for Hq/Hkv above 8, and above 2 at D = 256; the MFMA prefill kernel
  * for Hq/Hkv above 8; 206: pa_attention_varlen_noalloc; 207: multi-row
- * requests on 8-bit pools). */
+ * requests on 8-bit pools; 208: pa_attn_params.num_decode_rows). */
 int32_t pa_abi_version(void);
 
 #ifdef __cplusplus

@@ -135,6 +135,7 @@ class AttnParams(ctypes.Structure):
         ("dtype", ctypes.c_int),
         ("partition_size", ctypes.c_int32),
         ("sliding_window", ctypes.c_int32),
+        ("num_decode_rows", ctypes.c_int32),
     ]
 
 
@@ -256,7 +257,8 @@ def cache_write_fp8(k_new, v_new, k_cache, v_cache, slot_mapping, k_scale: float
 
 
 def make_params(q, k_cache, cu_seqlens, block_tables, num_kv_heads: int, scale: float, max_query_len: int,
-                max_seq_len: int, out=None, partition_size: int = 0, sliding_window: int = 0) -> AttnParams:
+                max_seq_len: int, out=None, partition_size: int = 0, sliding_window: int = 0,
+                num_decode_rows: int = 0) -> AttnParams:
     total_q, Hq, D = q.shape
     p = AttnParams()
     p.num_seqs = int(cu_seqlens.shape[0]) - 1
@@ -275,6 +277,7 @@ def make_params(q, k_cache, cu_seqlens, block_tables, num_kv_heads: int, scale: 
     p.dtype = _dtype_code(q)
     p.partition_size = int(partition_size)
     p.sliding_window = int(sliding_window)
+    p.num_decode_rows = int(num_decode_rows)
     return p
 
 
@@ -289,11 +292,13 @@ def partition_size(params: AttnParams) -> int:
 
 def attention_varlen(out, q, k_cache, v_cache, cu_seqlens, seq_lens, block_tables, scale: float,
                      max_query_len: int, max_seq_len: int, workspace=None, partition_size: int = 0,
-                     stream=None, k_scale=None, v_scale=None, sliding_window: int = 0, stage: str = "all"):
+                     stream=None, k_scale=None, v_scale=None, sliding_window: int = 0, stage: str = "all",
+                     num_decode_rows: int = 0):
     """Paged causal attention of packed rows; writes ``out`` [total_q, Hq, D] and returns it.
 
     ``sliding_window`` W > 0 limits each row to the last W positions up to
-    its own.  ``stage``: "all" (pa_attention_varlen), "plan" (only the work
+    its own.  ``num_decode_rows``: the host's count of requests with one query
+    row (0: none or unknown); scheduling only (pa_attn_params.num_decode_rows).  ``stage``: "all" (pa_attention_varlen), "plan" (only the work
     lists, pa_attention_plan: once per step, into ``workspace``) or "run" (one
     layer over the lists already in ``workspace``, pa_attention_run).
 
@@ -327,7 +332,8 @@ def attention_varlen(out, q, k_cache, v_cache, cu_seqlens, seq_lens, block_table
         raise ValueError("cu_seqlens [B+1], seq_lens [B] and block_tables [B, W] disagree on B")
     num_kv_heads = int(k_cache.shape[1])
     p = make_params(q, k_cache, cu_seqlens, block_tables, num_kv_heads, scale, max_query_len, max_seq_len,
-                    out=out, partition_size=partition_size, sliding_window=sliding_window)
+                    out=out, partition_size=partition_size, sliding_window=sliding_window,
+                    num_decode_rows=num_decode_rows)
     need = workspace_size(p)
     if workspace is None:
         if stage != "all":
@@ -361,7 +367,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20   # PA_NOALLOC_SCRATCH_BYTES
 
 def attention_varlen_noalloc(out, q, k_cache, v_cache, cu_seqlens, seq_lens, block_tables, scale: float,
                              max_query_len: int, max_seq_len: int, partition_size: int = 0, stream=None,
-                             sliding_window: int = 0):
+                             sliding_window: int = 0, num_decode_rows: int = 0):
     """``attention_varlen`` through pa_attention_varlen_noalloc: no workspace, the
     library's static per-GPU scratch instead (bf16 or fp32 pools)."""
     torch = _torch()
@@ -382,7 +388,8 @@ def attention_varlen_noalloc(out, q, k_cache, v_cache, cu_seqlens, seq_lens, blo
     if seq_lens.shape[0] != cu_seqlens.shape[0] - 1 or block_tables.shape[0] != seq_lens.shape[0]:
         raise ValueError("cu_seqlens [B+1], seq_lens [B] and block_tables [B, W] disagree on B")
     p = make_params(q, k_cache, cu_seqlens, block_tables, int(k_cache.shape[1]), scale, max_query_len, max_seq_len,
-                    out=out, partition_size=partition_size, sliding_window=sliding_window)
+                    out=out, partition_size=partition_size, sliding_window=sliding_window,
+                    num_decode_rows=num_decode_rows)
     _check(lib().pa_attention_varlen_noalloc(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                              cu_seqlens.data_ptr(), seq_lens.data_ptr(), block_tables.data_ptr(),
                                              ctypes.byref(p), _stream(stream)))

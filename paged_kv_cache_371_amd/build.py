@@ -38,7 +38,8 @@ FLAGS = [
 # Per-source extras.  The decode kernel claims work with a single-lane atomic
 # whose result it reads much later; the atomic optimizer would rewrite it into
 # a wave-wide broadcast read right after the atomic, stalling on its round trip.
-# The prefill kernel's softmax maxima are taken over MFMA results: under the
+# The prefill kernel claims its next work item the same way (one lane, the
+# value read when the item ends).  Its softmax maxima are taken over MFMA results: under the
 # IEEE mode of compute kernels each fmaxf operand that may be a signalling NaN
 # is first quieted (one v_max x, x each), about 50 extra VALU instructions per
 # key tile, and on gfx950 every VALU instruction takes SIMD cycles from the
@@ -46,7 +47,7 @@ FLAGS = [
 # by position, and masked scores are -inf.
 EXTRA_FLAGS = {
     "decode_gqa.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
-    "prefill.hip": ["-fno-honor-nans"],
+    "prefill.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
 }
 
 

@@ -63,7 +63,14 @@
 namespace pa {
 namespace {
 
-constexpr int kWavesPerGroup = 4;
+// Worker waves per workgroup (each workgroup also has one scheduler wave).
+// Four by default.  Three where a prefill launch runs beside this one and no
+// KV head is split over items: a workgroup is then four waves, one per SIMD,
+// and a four-wave prefill workgroup fits on the same CU (184 + 256 of the 512
+// registers per lane of each SIMD), where five would leave one SIMD without
+// room for it.
+constexpr int kWorkersDefault = 4;
+constexpr int kWorkersBesidePrefill = 3;
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
 constexpr float kRescaleThreshold = 8.f;      // log2 units
 constexpr float kMinusBig = -1e30f;           // finite "no token yet" max
@@ -169,8 +176,6 @@ constexpr int kClaimBatch = PA_DECODE_CLAIM_BATCH; // items per claim
 #define PA_DECODE_REQUEST_TILES 6
 #endif
 constexpr int kRequestTiles = PA_DECODE_REQUEST_TILES;   // tiles before an item's end its worker asks for the next
-static_assert(kClaimBatch <= kWavesPerGroup && kWavesPerGroup <= kQueue, "one queued item per worker at most");
-static_assert(kStaticRounds * kWavesPerGroup % 4 == 0, "claims of up to 4 items start aligned");
 
 // Pairing masks of the 16-lane reduction steps and their DPP controls.
 constexpr int kStepMask[4] = {8, 7, 2, 1};
@@ -314,7 +319,7 @@ __device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t,
   return it;
 }
 
-// Persistent kernel.  Each workgroup has kWavesPerGroup worker waves, which
+// Persistent kernel.  Each workgroup has WK worker waves, which
 // never synchronise with each other, plus one scheduler wave.  The list is
 // sorted by decreasing size.  Rounds 0 .. kStaticRounds-1 are dealt
 // statically: worker w of NW takes item i*NW + w in even rounds i and
@@ -344,9 +349,14 @@ __device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t,
 // is a fixed permutation shared by K and q.  The VALU work per tile drops from
 // ~G * D / 4 dot instructions per lane to the softmax and the operand
 // conversions.
-template <int G, bool F8, int BS, int D, bool MF>
-__global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kernel(DecodeArgs a) {
+template <int G, bool F8, int BS, int D, bool MF, int WK>
+__global__ __launch_bounds__(64 * (WK + 1), 1) void decode_gqa_kernel(DecodeArgs a) {
   static_assert(!MF || (D == 128 && (G == 4 || G == 8)), "matrix-core tiles: D = 128, items of 4 or 8 heads");
+  static_assert(kClaimBatch <= WK && WK <= kQueue, "one queued item per worker at most");
+  // Claims of a KV head's head groups (up to 4 items) start aligned when the
+  // static rounds hand out a multiple of 4 items; three workers are launched
+  // only where no KV head is split over items.
+  static_assert(WK == kWorkersBesidePrefill || kStaticRounds * WK % 4 == 0, "claims of up to 4 items start aligned");
   using T = Kv<F8, D>;
   constexpr int kRing = T::kRing;
   constexpr int kTileBytes = T::kTileBytes;
@@ -365,8 +375,8 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
   const int total = load_const(a.plan, kPlanCountInt) * nh;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int NW = gridDim.x * kWavesPerGroup;
-  const int wid = int(blockIdx.x) * kWavesPerGroup + wave;
+  const int NW = gridDim.x * WK;
+  const int wid = int(blockIdx.x) * WK + wave;
   auto item_of_round = [&](int i) {   // item index of static round i, or total if none
     const int64_t base = int64_t(i) * NW;
     const int64_t t = base + ((i & 1) ? NW - 1 - wid : wid);
@@ -392,7 +402,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
   int* done_counter = a.plan + kPlanDoneInt;
   auto count_out = [&]() {
     if ((threadIdx.x & 63) == 0) {
-      const int waves = int(gridDim.x) * (kWavesPerGroup + 1);
+      const int waves = int(gridDim.x) * (WK + 1);
       if (__hip_atomic_fetch_add(done_counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == waves - 1) {
         __hip_atomic_store(claim_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(done_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -423,13 +433,13 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
   auto lds_store = [](int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP); };
   const int4* entries = reinterpret_cast<const int4*>(a.plan + kPlanHeaderInts);
 
-  if (wave == kWavesPerGroup) {   // the scheduler: one claim per batch of requests
+  if (wave == WK) {   // the scheduler: one claim per batch of requests
     if (lane == 0) {
       const int64_t ndyn = int64_t(total) - dyn0;
       // The items of one KV head's head groups are claimed together (up to
       // one per worker, aligned), so this workgroup's workers stream the same
       // tiles side by side and the repeated reads are served by L2.
-      const int unit = min(1 << a.head_split_log2, kWavesPerGroup);
+      const int unit = min(1 << a.head_split_log2, WK);
       int pushed = 0, served = 0;
       for (bool more = ndyn > 0; more;) {
         int req;
@@ -499,7 +509,7 @@ __global__ __launch_bounds__(64 * (kWavesPerGroup + 1), 1) void decode_gqa_kerne
   // never waits for them) and moved to qreg through LDS after the item.
   constexpr int kQD = G * D / 2;                    // q dwords of an item: G rows of D bf16
   constexpr int kQDw = kQD >= 64 ? kQD / 64 : 1;    // per lane (lanes >= kQD idle when kQD < 64)
-  __shared__ uint32_t sq[kWavesPerGroup][64 * kQDw];
+  __shared__ uint32_t sq[WK][64 * kQDw];
   auto fetch_q = [&](const Item& it, uint32_t(&qt)[kQDw]) {
     const uint32_t* src = reinterpret_cast<const uint32_t*>(
         static_cast<const char*>(a.q) + (int64_t(it.q0) * a.q_row_stride + int64_t(it.hg) * G * D) * 2);
@@ -1048,7 +1058,7 @@ bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size, int
 namespace {
 
 // Resident workgroups per device for kernel K: CUs x occupancy, queried once per device.
-template <int G, bool F8, int BS, int D, bool MF>
+template <int G, bool F8, int BS, int D, bool MF, int WK>
 int persistent_groups() {
   static std::atomic<int> cache[kMaxDevices];
   int dev = 0;
@@ -1057,8 +1067,8 @@ int persistent_groups() {
   if (v > 0) return v;
   int cus = 0, occ = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_gqa_kernel<G, F8, BS, D, MF>, 64 * (kWavesPerGroup + 1),
-                                                   0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_gqa_kernel<G, F8, BS, D, MF, WK>, 64 * (WK + 1), 0) !=
+          hipSuccess ||
       occ <= 0)
     occ = 1;
   v = cus * std::min(occ, 1);
@@ -1077,56 +1087,62 @@ constexpr bool use_mfma_tiles() {
   return F8 && D == 128 && (G == 4 || G == 8);
 }
 
-template <int G, bool F8, int BS, int D>
-hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
+template <int G, bool F8, int BS, int D, int WK>
+hipError_t launch_wk(const DecodeArgs& a, hipStream_t stream) {
   constexpr bool MF = use_mfma_tiles<G, F8, BS, D>();
   const int64_t upper = (int64_t(a.num_seqs) * a.max_parts * a.num_kv_heads) << a.head_split_log2;
-  const int64_t grid = std::min<int64_t>(upper, persistent_groups<G, F8, BS, D, MF>());
+  const int64_t grid = std::min<int64_t>(upper, persistent_groups<G, F8, BS, D, MF, WK>());
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_gqa_kernel<G, F8, BS, D, MF>), dim3(grid), dim3(64 * (kWavesPerGroup + 1)), 0, stream, a);
+  hipLaunchKernelGGL((decode_gqa_kernel<G, F8, BS, D, MF, WK>), dim3(grid), dim3(64 * (WK + 1)), 0, stream, a);
   return hipGetLastError();
 }
 
+template <int G, bool F8, int BS, int D>
+hipError_t launch_g(const DecodeArgs& a, hipStream_t stream, bool beside_prefill) {
+  if (beside_prefill && a.head_split_log2 == 0) return launch_wk<G, F8, BS, D, kWorkersBesidePrefill>(a, stream);
+  return launch_wk<G, F8, BS, D, kWorkersDefault>(a, stream);
+}
+
 template <bool F8, int BS, int D>
-hipError_t launch_bs(int group, const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_bs(int group, const DecodeArgs& a, hipStream_t stream, bool bp) {
   switch (group) {
-    case 1: return launch_g<1, F8, BS, D>(a, stream);
-    case 2: return launch_g<2, F8, BS, D>(a, stream);
-    case 4: return launch_g<4, F8, BS, D>(a, stream);
-    case 8: return launch_g<8, F8, BS, D>(a, stream);
+    case 1: return launch_g<1, F8, BS, D>(a, stream, bp);
+    case 2: return launch_g<2, F8, BS, D>(a, stream, bp);
+    case 4: return launch_g<4, F8, BS, D>(a, stream, bp);
+    case 8: return launch_g<8, F8, BS, D>(a, stream, bp);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <bool F8, int D>
-hipError_t launch_d(int group, const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_d(int group, const DecodeArgs& a, hipStream_t stream, bool bp) {
   switch (a.block_size) {
-    case 8: return launch_bs<F8, 8, D>(group, a, stream);
-    case 16: return launch_bs<F8, 16, D>(group, a, stream);
-    case 32: return launch_bs<F8, 32, D>(group, a, stream);
+    case 8: return launch_bs<F8, 8, D>(group, a, stream, bp);
+    case 16: return launch_bs<F8, 16, D>(group, a, stream, bp);
+    case 32: return launch_bs<F8, 32, D>(group, a, stream, bp);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <bool F8, int BS>
-hipError_t launch_bs256(int group, const DecodeArgs& a, hipStream_t stream) {   // G <= 2 at D = 256
+hipError_t launch_bs256(int group, const DecodeArgs& a, hipStream_t stream, bool bp) {   // G <= 2 at D = 256
   switch (group) {
-    case 1: return launch_g<1, F8, BS, 256>(a, stream);
-    case 2: return launch_g<2, F8, BS, 256>(a, stream);
+    case 1: return launch_g<1, F8, BS, 256>(a, stream, bp);
+    case 2: return launch_g<2, F8, BS, 256>(a, stream, bp);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <bool F8>
-hipError_t launch_f(int group, int head_dim, const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_f(int group, int head_dim, const DecodeArgs& a, hipStream_t stream, bool bp) {
   switch (head_dim) {
-    case 64: return launch_d<F8, 64>(group, a, stream);
-    case 128: return launch_d<F8, 128>(group, a, stream);
+    case 64: return launch_d<F8, 64>(group, a, stream, bp);
+    case 128: return launch_d<F8, 128>(group, a, stream, bp);
     case 256:
       switch (a.block_size) {
-        case 8: return launch_bs256<F8, 8>(group, a, stream);
-        case 16: return launch_bs256<F8, 16>(group, a, stream);
-        case 32: return launch_bs256<F8, 32>(group, a, stream);
+        case 8: return launch_bs256<F8, 8>(group, a, stream, bp);
+        case 16: return launch_bs256<F8, 16>(group, a, stream, bp);
+        case 32: return launch_bs256<F8, 32>(group, a, stream, bp);
         default: return hipErrorInvalidValue;
       }
     default: return hipErrorInvalidValue;
@@ -1138,25 +1154,27 @@ hipError_t launch_f(int group, int head_dim, const DecodeArgs& a, hipStream_t st
 int decode_gqa_workers(int group) {
   int g = 0;
   switch (item_group(128, group)) {
-    case 1: g = persistent_groups<1, false, 16, 128, false>(); break;
-    case 2: g = persistent_groups<2, false, 16, 128, false>(); break;
-    case 4: g = persistent_groups<4, false, 16, 128, false>(); break;
-    case 8: g = persistent_groups<8, false, 16, 128, false>(); break;
+    case 1: g = persistent_groups<1, false, 16, 128, false, kWorkersDefault>(); break;
+    case 2: g = persistent_groups<2, false, 16, 128, false, kWorkersDefault>(); break;
+    case 4: g = persistent_groups<4, false, 16, 128, false, kWorkersDefault>(); break;
+    case 8: g = persistent_groups<8, false, 16, 128, false, kWorkersDefault>(); break;
     default: g = 256;
   }
-  return g * kWavesPerGroup;
+  return g * kWorkersDefault;
 }
 
 // a.block_size selects the paging (8, 16 or 32 tokens per block); the kernel
 // is instantiated for the item group, and a.head_split_log2 is set here.
-hipError_t launch_decode_gqa(int group, int head_dim, bool fp8_cache, const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode_gqa(int group, int head_dim, bool fp8_cache, const DecodeArgs& a, hipStream_t stream,
+                             bool beside_prefill) {
   const int gi = item_group(head_dim, group);
   const int split = decode_gqa_head_split(head_dim, group);
   if (gi <= 0 || gi * split != group || group > kMaxGroup) return hipErrorInvalidValue;
   DecodeArgs b = a;
   b.head_split_log2 = 0;
   while ((1 << b.head_split_log2) < split) ++b.head_split_log2;
-  return fp8_cache ? launch_f<true>(gi, head_dim, b, stream) : launch_f<false>(gi, head_dim, b, stream);
+  return fp8_cache ? launch_f<true>(gi, head_dim, b, stream, beside_prefill)
+                   : launch_f<false>(gi, head_dim, b, stream, beside_prefill);
 }
 
 }  // namespace pa

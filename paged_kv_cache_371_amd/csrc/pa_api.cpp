@@ -181,7 +181,7 @@ pa_status check_params(const pa_attn_params* p) {
   if (!std::isfinite(p->scale) || !(p->scale > 0.f)) return PA_ERR_SHAPE;
   if (p->partition_size != 0 && (p->partition_size < 16 || p->partition_size > 8192 || p->partition_size % 16))
     return PA_ERR_SHAPE;
-  if (p->sliding_window < 0) return PA_ERR_SHAPE;
+  if (p->sliding_window < 0 || p->num_decode_rows < 0) return PA_ERR_SHAPE;
   const int eb = elem_bytes(p->dtype);
   if ((p->q_row_stride * eb) % 16 || (p->o_row_stride * eb) % 16) return PA_ERR_ALIGN;
   return PA_OK;
@@ -191,7 +191,7 @@ pa_status check_params(const pa_attn_params* p) {
 
 extern "C" {
 
-int32_t pa_abi_version(void) { return 207; }
+int32_t pa_abi_version(void) { return 208; }
 
 const char* pa_status_string(pa_status s) {
   switch (s) {
@@ -250,6 +250,45 @@ enum Stage : int { kPlanStage = 1, kRunStage = 2 };
 
 // Every attention entry point.  fp8: the pools hold OCP FP8 E4M3 codes with
 // per-tensor scales (decode rows only; q and out are bf16).
+// The second stream of a run whose batch has both single-row and multi-row
+// requests: the prefill kernel runs on it while the decode kernel runs on the
+// caller's stream, so the decode kernel's HBM streaming and the prefill
+// kernel's matrix-core work share the CUs ([ICE]: one forward over the packed
+// decode and prefill rows of a step; prefill is compute-bound, decode
+// bandwidth-bound).  One stream (default priority) and two events per device,
+// created on first use; the lock is held over the short enqueue-only
+// sequence, so the events' records and waits of two host threads never mix.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr;
+  hipEvent_t join = nullptr;
+  bool ready = false;
+};
+constexpr int kSideDevices = 64;
+std::mutex g_side_mu[kSideDevices];
+SideStream g_side[kSideDevices];
+
+// The current device's side stream and its lock, or nullptr if there is none
+// (the run then launches everything on the caller's stream).
+SideStream* side_of_current_device(std::mutex** mu) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kSideDevices) return nullptr;
+  *mu = &g_side_mu[dev];
+  SideStream& ss = g_side[dev];
+  std::lock_guard<std::mutex> lock(g_side_mu[dev]);
+  if (!ss.ready) {
+    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+      (void)hipStreamDestroy(ss.stream);
+      ss.stream = nullptr;
+      return nullptr;
+    }
+    ss.ready = true;
+  }
+  return &ss;
+}
+
 pa_status attention_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* cu_seqlens_q, const int32_t* seq_lens, const int32_t* block_tables,
                          const pa_attn_params* p, void* workspace, size_t workspace_bytes, void* stream, bool fp8,
@@ -339,13 +378,26 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
     if (pa::launch_plan(pa_, s) != hipSuccess) return PA_ERR_LAUNCH;
   }
   if (!(stages & kRunStage)) return PA_OK;
+  // Fork: the decode kernel goes first on the caller's stream, the prefill
+  // kernel on the side stream from the same point; the partial-output regions
+  // and output rows of the two are disjoint, and the merge waits for both.
+  std::mutex* side_mu = nullptr;
+  SideStream* side = (pl.fast && pl.prefill && pl.generic_mode < 0 && p->num_decode_rows > 0)
+                         ? side_of_current_device(&side_mu)
+                         : nullptr;
+  std::unique_lock<std::mutex> side_lock;
+  if (side) {
+    side_lock = std::unique_lock<std::mutex>(*side_mu);
+    if (hipEventRecord(side->fork, s) != hipSuccess) return PA_ERR_LAUNCH;
+  }
   if (pl.fast) {
     point_at(region_a, pl.rows_a);
     d.row_mode = pa::kSingleRowOnly;
     d.partial_by_seq = 1;
-    e = pa::launch_decode_gqa(g, p->head_dim, fp8, d, s);
+    e = pa::launch_decode_gqa(g, p->head_dim, fp8, d, s, side != nullptr);
     if (e != hipSuccess) return PA_ERR_LAUNCH;
   }
+  if (side && hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess) return PA_ERR_LAUNCH;
   if (pl.generic_mode >= 0) {
     point_at(pl.generic_by_seq ? region_a : region_b, pl.generic_by_seq ? pl.rows_a : pl.rows_b);
     d.row_mode = pl.generic_mode;
@@ -368,7 +420,7 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
     f.num_q_heads = p->num_q_heads;
     f.num_kv_heads = p->num_kv_heads;
     f.max_blocks_per_seq = p->max_blocks_per_seq;
-    f.plan = static_cast<const int32_t*>(workspace);
+    f.plan = static_cast<int32_t*>(workspace);
     f.pref_off_ints = pref_off(p, pl);
     f.scale_log2 = scale_log2;
     f.split_rows = pl.split_rows;
@@ -380,9 +432,15 @@ pa_status attention_impl(void* out, const void* q, const void* k_cache, const vo
     f.ws_o = pl.split_rows ? region_a : nullptr;
     f.ws_ml = pl.split_rows ? region_a + int64_t(pl.rows_a) * p->num_q_heads * pl.parts * p->head_dim : nullptr;
     f.lsum_scale = d.lsum_scale;
-    e = pa::launch_prefill(p->head_dim, g, fp8, f, s);
+    f.claim_items = side ? 1 : 0;
+    e = pa::launch_prefill(p->head_dim, g, fp8, f, side ? side->stream : s);
     if (e != hipSuccess) return PA_ERR_LAUNCH;
   }
+  // Join: the caller's stream waits for the prefill kernel.
+  if (side && (hipEventRecord(side->join, side->stream) != hipSuccess ||
+               hipStreamWaitEvent(s, side->join, 0) != hipSuccess))
+    return PA_ERR_LAUNCH;
+  if (side) side_lock.unlock();
   // partitions of single-row requests and of split short requests
   if (pl.fast && pl.parts > 1) {
     point_at(region_a, pl.rows_a);

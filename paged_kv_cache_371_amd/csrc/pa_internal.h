@@ -65,7 +65,8 @@ struct PrefillArgs {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t max_blocks_per_seq;
-  const int32_t* plan;    // work list (prefill entries at plan + kPlanHeaderInts + pref_off_ints)
+  int32_t* plan;          // work list (prefill entries at plan + kPlanHeaderInts + pref_off_ints; the header's
+                          // prefill claim counters are updated by the kernel)
   int64_t pref_off_ints;
   float scale_log2;
   // Context split of short requests (see PlanArgs::split_rows): a request with
@@ -82,6 +83,8 @@ struct PrefillArgs {
   int32_t block_size;   // tokens per physical block: 8, 16 or 32
   int32_t head_split_log2;   // a KV head's query heads are served by 2^this items (set by launch_prefill)
   float lsum_scale;          // 8-bit pools: the softmax sum is multiplied by this (1 / v_scale)
+  int32_t claim_items;       // 1: items after the first are claimed from the list header's counter (beside a
+                             // decode launch); 0: dealt out statically
 };
 
 hipError_t launch_cache_write(const void* k_new, const void* v_new, int64_t kv_row_stride_bytes, void* k_cache,
@@ -106,6 +109,9 @@ constexpr int kPlanMergeCountInt = 10;   // header slot: number of merge entries
 constexpr int kPlanClaimInt = 11;        // header slot: claim counter of the fast decode kernel (zeroed by the plan,
                                          // re-armed by the last wave of each decode launch)
 constexpr int kPlanDoneInt = 12;         // header slot: waves of the fast decode launch that have finished
+constexpr int kPlanPrefClaimInt = 13;    // header slot: claim counter of the prefill kernel (zeroed by the plan,
+                                         // re-armed by the last workgroup of each prefill launch)
+constexpr int kPlanPrefDoneInt = 14;     // header slot: workgroups of the prefill launch that have finished
 constexpr int kMaxPartBuckets = 512;     // partition_size / 16 of the fast kernel, at most
 constexpr int kPrefillKeys = 64;         // keys per prefill K/V tile
 
@@ -143,7 +149,11 @@ int decode_gqa_workers(int group);
 // where one item cannot hold all of a KV head's query heads.
 int decode_gqa_head_split(int head_dim, int group);
 // fp8_cache: the pools hold OCP FP8 E4M3 codes (scales folded into scale_log2 and lsum_scale).
-hipError_t launch_decode_gqa(int group, int head_dim, bool fp8_cache, const DecodeArgs& a, hipStream_t stream);
+// beside_prefill: a prefill launch runs at the same time on another stream;
+// the kernel then uses workgroups of three workers (where no KV head is split
+// over items) so a prefill workgroup fits beside each of them.
+hipError_t launch_decode_gqa(int group, int head_dim, bool fp8_cache, const DecodeArgs& a, hipStream_t stream,
+                             bool beside_prefill = false);
 // Partition merge alone (for a DecodeArgs whose partials are already written).
 hipError_t launch_merge(int dtype, int head_dim, const DecodeArgs& a, int64_t partial_rows, hipStream_t stream);
 // Merge for the fast decode kernel's partials (bf16, D = 64 or 128): only the

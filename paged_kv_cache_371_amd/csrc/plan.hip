@@ -8,6 +8,8 @@
 //   [kPlanClaimInt]      claim counter of the decode kernel's dynamic rounds, zeroed here
 //   [kPlanDoneInt]       finished waves of a decode launch, zeroed here (each launch's last wave
 //                        zeroes both again, so one list serves any number of launches)
+//   [kPlanPrefClaimInt]  claim counter of the prefill kernel, zeroed here
+//   [kPlanPrefDoneInt]   finished workgroups of a prefill launch, zeroed here (re-armed the same way)
 //   [kPlanHeaderInts ..)                   decode entries, int4 (request, partition, query row, context length)
 //   [kPlanHeaderInts + pref_off ..)        prefill entries, int4 (request, row tile | partition << 16,
 //                                          first query row, query rows)
@@ -196,7 +198,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     });
     __syncthreads();
     const int total = scan_desc(s_hist, s_tmp, kPrefBuckets, 0);
-    if (tid == 0) a.plan[kPlanPrefCountInt] = total;
+    if (tid == 0) {
+      a.plan[kPlanPrefCountInt] = total;
+      a.plan[kPlanPrefClaimInt] = 0;
+      a.plan[kPlanPrefDoneInt] = 0;
+    }
     int4* entries = reinterpret_cast<int4*>(a.plan + kPlanHeaderInts + a.pref_off_ints);
     int4* merge = reinterpret_cast<int4*>(a.plan + kPlanHeaderInts + a.merge_off_ints);
     for_each_request([&](int b, int q0, int n, int L) {

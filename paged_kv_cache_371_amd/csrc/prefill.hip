@@ -190,11 +190,24 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
   const float scale_log2 = a.scale_log2;
   const int32_t* entries = a.plan + kPlanHeaderInts + a.pref_off_ints;
 
-  // Items in list order (largest first), dealt out round-robin, every other
-  // round in reverse, so the large items spread over the workgroups.
-  for (int i = 0, base = 0; base < total; ++i, base += ngroups) {
-    const int t = base + ((i & 1) ? ngroups - 1 - wg : wg);
-    if (t >= total) continue;
+  // Items in list order (largest first); workgroup wg's first item is item
+  // wg.  Alone on the GPU, later items are dealt out round-robin, every other
+  // round in reverse, so the large items spread over the workgroups.  Beside
+  // a decode launch (claim_items), a CU holds one prefill workgroup until the
+  // decode workgroups leave, so later items are claimed from a counter in the
+  // list's header instead: the workgroups that run longer, or start later,
+  // take more of the small items at the end.  The next claim is issued when
+  // an item starts and its value read when the item ends, so the round trip
+  // overlaps the item's tiles (a claim costs about 4% of a lone prefill
+  // launch, which is why the lone one keeps the static deal).
+  const bool claim_items = PA_KARG(claim_items) != 0;
+  int* claim_counter = a.plan + kPlanPrefClaimInt;
+  int* done_counter = a.plan + kPlanPrefDoneInt;
+  __shared__ int s_next;
+  for (int t = wg, round = 0; t < total;) {
+    int claimed = 0;
+    if (claim_items && tid == 0)
+      claimed = __hip_atomic_fetch_add(claim_counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int e = t / nh;
     const int hg = t - e * nh;
     const int kvh = hg >> split_log2;
@@ -542,6 +555,23 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
         }
       }
     }
+    if (claim_items) {   // the item claimed when this one started
+      if (tid == 0) s_next = ngroups + claimed;
+      __syncthreads();
+      t = uni(s_next);
+    } else {   // the next round of the static deal; later rounds only hold larger indices
+      ++round;
+      t = round * ngroups + ((round & 1) ? ngroups - 1 - wg : wg);
+    }
+  }
+  // With claims, every workgroup counts itself out once its last claim has
+  // returned; the last one re-arms the claim counter (and this count), so the
+  // next launch on the same list starts from zero.  No claim of this launch is
+  // in flight then.
+  if (claim_items && tid == 0 &&
+      __hip_atomic_fetch_add(done_counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ngroups - 1) {
+    __hip_atomic_store(claim_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(done_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -50,12 +50,15 @@ class DeviceCase:
     def cache_write(self):
         pa.cache_write(self.k_new, self.v_new, self.k_cache, self.v_cache, self.slots)
 
-    def attention(self, partition_size=0, out=None, sliding_window=0):
+    def attention(self, partition_size=0, out=None, sliding_window=0, decode_hint=True):
+        # decode_hint: pass the count of single-row requests (a mixed batch then
+        # runs its decode and prefill kernels side by side)
         c = self.c
         out = self.out if out is None else out
         pa.attention_varlen(out, self.q, self.k_cache, self.v_cache, self.cu, self.seq_lens, self.tables,
                             float(c.scale), c.max_query_len, c.max_seq_len, partition_size=partition_size,
-                            sliding_window=sliding_window)
+                            sliding_window=sliding_window,
+                            num_decode_rows=int((c.q_lens == 1).sum()) if decode_hint else 0)
         return out
 
 

@@ -177,7 +177,11 @@ def _layers(dc, n, fp8):
 def test_plan_once_run_many_layers_bitwise(kind):
     """pa_attention_plan once, then pa_attention_run for several layers (new q
     and pools, same metadata): every layer equals pa_attention_varlen bit for
-    bit, and the decode kernel leaves its claim and exit counters re-armed."""
+    bit, and the decode kernel leaves its claim and exit counters re-armed.
+    The runs pass the count of single-row requests (mixed batches then run the
+    prefill kernel beside the decode kernel and claim its items), the
+    reference calls do not: the same bits either way, and the prefill claim
+    counters re-armed too."""
     rng = np.random.default_rng(21)
     if kind.startswith("decode"):
         B, Hq, Hkv = 300, 64, 8
@@ -208,12 +212,60 @@ def test_plan_once_run_many_layers_bitwise(kind):
         want.append(o)
     pa.attention_varlen(dc.out, dc.q, layers[0][1], layers[0][2], dc.cu, dc.seq_lens, dc.tables, float(c.scale),
                         c.max_query_len, c.max_seq_len, workspace=ws, stage="plan", **kw)
+    hint = int((n == 1).sum())
     for (q, k, v), w in zip(layers, want):
         o = torch.empty_like(q)
         pa.attention_varlen(o, q, k, v, dc.cu, dc.seq_lens, dc.tables, float(c.scale), c.max_query_len,
-                            c.max_seq_len, workspace=ws, stage="run", **kw)
+                            c.max_seq_len, workspace=ws, stage="run", num_decode_rows=hint, **kw)
         torch.cuda.synchronize()
         assert torch.equal(o.view(torch.int16), w.view(torch.int16))
     hdr = ws[:64 * 4].view(torch.int32).cpu().numpy()
-    say(f"{kind}: decode entries {hdr[8]}, prefill entries {hdr[9]}, counters {hdr[11]} {hdr[12]}")
-    assert hdr[11] == 0 and hdr[12] == 0
+    say(f"{kind}: decode entries {hdr[8]}, prefill entries {hdr[9]}, counters {hdr[11]} {hdr[12]} {hdr[13]} {hdr[14]}")
+    assert hdr[11] == 0 and hdr[12] == 0 and hdr[13] == 0 and hdr[14] == 0
+
+
+@pytest.mark.parametrize("case", ["mixed", "mixed_fp8", "mixed_d64", "mixed_d256", "mixed_bs8", "mixed_g16",
+                                  "prefill_only_wrong_hint", "short_rows"])
+def test_decode_hint_changes_no_bits(case):
+    """num_decode_rows only schedules: with it the decode and prefill kernels
+    of a mixed batch run side by side (prefill items claimed), without it one
+    after the other (prefill items dealt statically); the outputs are the same
+    bits, also when the hint is wrong (no single-row request at all)."""
+    rng = np.random.default_rng(31)
+    D, Hq, Hkv, bs, B = 128, 32, 8, 16, 96
+    if case == "mixed_d64":
+        D = 64
+    elif case == "mixed_d256":
+        D, Hq, Hkv = 256, 32, 8
+    elif case == "mixed_bs8":
+        bs = 8
+    elif case == "mixed_g16":
+        Hq, Hkv = 64, 4
+    n = np.ones(B, np.int64)
+    n[:6] = [700, 300, 129, 64, 17, 2]
+    if case == "prefill_only_wrong_hint":
+        n = rng.integers(2, 200, 24)
+        B = 24
+    elif case == "short_rows":
+        n = rng.integers(1, 9, B)
+    L = np.maximum(n, rng.integers(1, 4000, B))
+    c = build_case(f"hint_{case}", 32, "bf16", Hq, Hkv, D, n, L, poison=False, block_size=bs)
+    dc = DeviceCase(c)
+    kw = {}
+    if case == "mixed_fp8":
+        g = torch.Generator(device="cuda:0").manual_seed(3)
+        dc.k_cache = torch.randint(0, 0x77, dc.k_cache.shape, generator=g, device="cuda:0", dtype=torch.uint8)
+        dc.v_cache = torch.randint(0, 0x77, dc.v_cache.shape, generator=g, device="cuda:0", dtype=torch.uint8)
+        kw = dict(k_scale=0.5, v_scale=0.25)
+    hint = int((n == 1).sum()) if case != "prefill_only_wrong_hint" else 5
+    outs = []
+    for h in (0, hint, 0, hint):
+        o = torch.empty_like(dc.q)
+        pa.attention_varlen(o, dc.q, dc.k_cache, dc.v_cache, dc.cu, dc.seq_lens, dc.tables, float(c.scale),
+                            c.max_query_len, c.max_seq_len, num_decode_rows=h, **kw)
+        outs.append(o)
+    torch.cuda.synchronize()
+    say(f"{case}: {B} requests, {int((n == 1).sum())} single-row, hint {hint}")
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    assert bool(torch.isfinite(outs[0].float()).all())
