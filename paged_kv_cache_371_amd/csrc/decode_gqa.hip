@@ -1097,9 +1097,18 @@ hipError_t launch_wk(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Three workers also where four would not fit the registers a wave needs: the
+// matrix-core form on 8-bit pools with 8-token blocks needs more than the 256
+// a wave may take when one SIMD holds two of a workgroup's five waves.
+template <int G, bool F8, int BS, int D>
+constexpr bool three_workers_fit_better() {
+  return use_mfma_tiles<G, F8, BS, D>() && BS == 8;
+}
+
 template <int G, bool F8, int BS, int D>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream, bool beside_prefill) {
-  if (beside_prefill && a.head_split_log2 == 0) return launch_wk<G, F8, BS, D, kWorkersBesidePrefill>(a, stream);
+  if ((beside_prefill || three_workers_fit_better<G, F8, BS, D>()) && a.head_split_log2 == 0)
+    return launch_wk<G, F8, BS, D, kWorkersBesidePrefill>(a, stream);
   return launch_wk<G, F8, BS, D, kWorkersDefault>(a, stream);
 }
 

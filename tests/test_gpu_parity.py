@@ -215,6 +215,23 @@ def test_config_full_size_every_row(name):
     assert ok, (mx, mean)
 
 
+def test_config_d256_g16_sampled_rows():
+    """The GQA decode layer at head dim 256 with 128 query / 8 KV heads (8 work
+    items per KV head and partition), in the launch configuration bench.py
+    times: the whole pool bit for bit, and the rows of 48 requests (the 16
+    longest, the 16 shortest, 16 seeded others) against the oracle."""
+    c = make_config("gqa_decode_d256_g16_bf16", 0)
+    order = np.argsort(c.seq_lens, kind="stable")
+    rng = np.random.default_rng(5)
+    pick = set(order[:16].tolist()) | set(order[-16:].tolist())
+    pick |= set(rng.choice(order[16:-16], 16, replace=False).tolist())
+    rows = sorted(int(c.cu_seqlens[b]) for b in pick)
+    say("config gqa_decode_d256_g16_bf16 rows", len(rows))
+    mx, mean, ok, dc = run_and_compare(c, rows=rows, sharded=True)
+    say(f"  max {mx:.3g} mean {mean:.3g}")
+    assert ok, (mx, mean)
+
+
 # ---------------------------------------------------------------------------
 # scale extremes: many requests, one very long context
 

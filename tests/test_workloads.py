@@ -76,7 +76,8 @@ def test_shared_prefix_tables_and_negative_slots():
 
 
 @pytest.mark.parametrize("name,lo,hi,B", [("mha_decode_bf16", 128, 2048, 64), ("gqa_decode_bf16", 16, 8192, 256),
-                                          ("gqa_decode_d256_bf16", 16, 8192, 256)])
+                                          ("gqa_decode_d256_bf16", 16, 8192, 256),
+                                          ("gqa_decode_d256_g16_bf16", 16, 8192, 256)])
 def test_decode_config_lengths_and_pool(name, lo, hi, B):
     c = make_config(name, 0, poison=False)
     assert c.num_seqs == B and (c.q_lens == 1).all()

@@ -300,6 +300,15 @@ def _gqa_decode_d256_bf16(seed, **kw):
                       max_blocks_per_seq=512, **kw)
 
 
+def _gqa_decode_d256_g16_bf16(seed, **kw):
+    # the GQA decode layer's requests and lengths at head dim 256 with 128 query / 8 KV heads:
+    # 16 query heads per KV head, 8 work items per (KV head, partition)
+    g = _gen(seed, S_LENGTHS)
+    L = np.clip(np.rint(g.lognormal(math.log(1024.0), 1.0, size=256)), 16, 8192).astype(np.int64)
+    return build_case("gqa_decode_d256_g16_bf16", seed, "bf16", 128, 8, 256, np.ones(256, np.int64), L,
+                      max_blocks_per_seq=512, **kw)
+
+
 def _mixed_prefill_bf16(seed, **kw):
     g = _gen(seed, S_LENGTHS)
     prior = g.integers(0, 4096, size=8, endpoint=True)
@@ -332,6 +341,7 @@ _CONFIGS = {
     "mha_decode_bf16": _mha_decode_bf16,
     "gqa_decode_bf16": _gqa_decode_bf16,
     "gqa_decode_d256_bf16": _gqa_decode_d256_bf16,
+    "gqa_decode_d256_g16_bf16": _gqa_decode_d256_g16_bf16,
     "mixed_prefill_bf16": _mixed_prefill_bf16,
     "prefix_long_bf16": _prefix_long_bf16,
     "spec_verify_bf16": _spec_verify_bf16,
