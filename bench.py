@@ -7,7 +7,10 @@ requests, 64 query / 8 KV heads, D=128, bf16, log-normal contexts with median
 1024 clipped to [16, 8192], shuffled 16-token blocks).
 
 Prints one JSON line.  ``value`` is KV GB/s: the attention's algorithmic
-K/V bytes per step divided by the step time (inputs resident in HBM).
+K/V bytes per step divided by the step time (inputs resident in HBM), over
+the K timed steps; before the W warm-up steps the step runs untimed for 50 ms
+so the GPU's clocks settle (``settle_steps``), and the timed steps make the C
+calls through the binding's prepared calls (checks and marshalling done once).
 ``roofline`` reports one layer's attention: pa_attention_run over the
 step's work lists (the split-K decode kernel and the partition merge; the
 prefill kernel too when the batch has multi-row requests), timed with HIP
@@ -64,6 +67,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "paged_kv_cache_371_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30
+SETTLE_S = 0.05   # seconds of untimed steps before the warm-up (clock settle)
 
 
 # Sources that decide what one pa_attention_varlen call moves: its argument
@@ -324,9 +328,31 @@ class _DeviceBatch:
         self.out = torch.empty_like(self.q)
         self.ws = None
         self.partition_size = None
+        self._fast = {}
+
+    def prepare(self, partition_size):
+        """Marshal the step's C calls once (after a checked call): the timed loops
+        then make only the C calls, so the host's per-call Python work does not
+        hold the GPU back (prepare_* of the binding)."""
+        pa, c = self.pa, self.c
+        if getattr(self, "k_new", None) is None:   # a batch without new rows (the multi-row sub-batch)
+            pass
+        elif self.fp8:
+            self._fast["cw"] = pa.prepare_cache_write_fp8(self.k_new, self.v_new, self.k_cache, self.v_cache,
+                                                          self.slots, K_SCALE_FP8, V_SCALE_FP8)
+        else:
+            self._fast["cw"] = pa.prepare_cache_write(self.k_new, self.v_new, self.k_cache, self.v_cache, self.slots)
+        for stage in ("all", "plan", "run"):
+            self._fast[stage] = pa.prepare_attention_varlen(
+                self.out, self.q, self.k_cache, self.v_cache, self.cu, self.seq_lens, self.tables, float(c.scale),
+                c.max_query_len, c.max_seq_len, workspace=self.ws, partition_size=partition_size,
+                sliding_window=self.window, k_scale=K_SCALE_FP8 if self.fp8 else None,
+                v_scale=V_SCALE_FP8 if self.fp8 else None, stage=stage, num_decode_rows=int((c.q_lens == 1).sum()))
 
     def cache_write(self):
-        if self.fp8:
+        if "cw" in self._fast:
+            self._fast["cw"]()
+        elif self.fp8:
             self.pa.cache_write_fp8(self.k_new, self.v_new, self.k_cache, self.v_cache, self.slots, K_SCALE_FP8,
                                     V_SCALE_FP8)
         else:
@@ -340,6 +366,9 @@ class _DeviceBatch:
                                     sliding_window=self.window)
             self.ws = self.torch.empty(max(16, self.pa.workspace_size(p)), dtype=self.torch.uint8, device="cuda:0")
             self.partition_size = self.pa.partition_size(p)
+        if stage in self._fast:
+            self._fast[stage]()
+            return
         self.pa.attention_varlen(self.out, self.q, self.k_cache, self.v_cache, self.cu, self.seq_lens, self.tables,
                                  float(c.scale), c.max_query_len, c.max_seq_len, workspace=self.ws,
                                  partition_size=partition_size, sliding_window=self.window,
@@ -370,8 +399,10 @@ class _MultiRowBatch:
         self.out = torch.empty_like(self.q)
         self.ws = None
         self.partition_size = None
+        self._fast = {}
 
     attention = _DeviceBatch.attention
+    prepare = _DeviceBatch.prepare
 
 
 class _SubConfig:
@@ -603,6 +634,9 @@ def main() -> None:
                          "as well and reported beside it")
     ap.add_argument("--no-flush-cache", dest="flush_cache", action="store_false",
                     help="time the plan/run calls back to back only")
+    ap.add_argument("--multi-row-only", action="store_true",
+                    help="the workload's multi-row requests alone, laid out as a batch of their own (the same "
+                         "lengths, heads and block size; workload name + '_multirow')")
     ap.add_argument("--no-prefill-alone", action="store_true",
                     help="skip timing the call over the multi-row requests alone (profiler runs: its decode and "
                          "merge launches have empty lists and would enter those kernels' per-dispatch figures)")
@@ -634,6 +668,15 @@ def main() -> None:
     from workloads import make_config
 
     c = make_config(args.workload, args.seed, poison=False, block_size=args.block_size)
+    if args.multi_row_only:
+        from workloads import build_case
+
+        keep = c.q_lens > 1
+        if not keep.any():
+            raise SystemExit("the workload has no multi-row requests")
+        c = build_case(c.name + "_multirow", args.seed, c.dtype, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                       c.q_lens[keep], c.seq_lens[keep], poison=False, block_size=c.block_size,
+                       rescale_tables=c.block_size != 16)
     fp8 = args.kv_dtype == "fp8"
     if fp8 and c.dtype != "bf16":
         raise SystemExit("8-bit pools need a bf16 workload")
@@ -653,7 +696,19 @@ def main() -> None:
     torch.cuda.synchronize()
     if not bool(torch.isfinite(dc.out.float()).all()):
         raise SystemExit("non-finite attention output")
+    dc.prepare(args.partition_size)
 
+    # Clock settle: the GPU reaches its sustained clocks only after some tens of
+    # milliseconds of work (with 5 warm-up steps, ~1.5 ms, the timed steps ran
+    # 3% slower than after 50).  The step runs untimed until SETTLE_S seconds
+    # have passed, then the W warm-up steps, then the K timed ones.
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < SETTLE_S:
+        for _ in range(10):
+            step()
+        settle_steps += 10
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -704,6 +759,7 @@ def main() -> None:
     if c.max_query_len > 1 and not args.no_prefill_alone:
         sub = _MultiRowBatch(dc, torch)
         sub.attention(partition_size=args.partition_size, stage="plan")
+        sub.prepare(args.partition_size)
         sub_run = stage_ms("run", flushed, batch=sub)
         sub_ms = float(sub_run.mean())
         sub_flops = attention_flops(sub.c, W)
@@ -717,7 +773,8 @@ def main() -> None:
             "tflops": round(sub_flops / (sub_ms * 1e-3) / 1e12, 2),
             "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
             "mfma_frac": round(sub_flops / (sub_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-            "profiled_prefill_kernel_us": profiled_kernel_us(c.name, "prefill_kernel") if not fp8 and not W else None,
+            "profiled_prefill_kernel_us": (profiled_kernel_us(c.name + "_multirow", "prefill_kernel")
+                                           if not fp8 and not W else None),
         }
 
     value = ab["kv"] / (ms_per_step * 1e-3) / 1e9
@@ -730,6 +787,7 @@ def main() -> None:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -198,7 +198,18 @@ def _dev(t, name: str):
     return t
 
 
-def cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None) -> None:
+def _call(fn, args, prepare: bool, keep=()):
+    """Make the C call now, or (prepare) return a function of no arguments that
+    makes exactly this call (the same pointers and stream) each time it is called."""
+    if prepare:
+        def call(_fn=fn, _args=args, _keep=keep):
+            _check(_fn(*_args))
+        return call
+    _check(fn(*args))
+    return None
+
+
+def cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None, _prepare: bool = False):
     """Scatter new K/V rows [N, Hkv, D] into pools [NB, Hkv, 16, D] via int64 slots."""
     torch = _torch()
     for t, nm in ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache"),
@@ -220,13 +231,13 @@ def cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None) -> No
     NB, Hc, bs, Dc = k_cache.shape
     if Hc != Hkv or Dc != D:
         raise ValueError("pool heads/head_dim differ from the new rows")
-    _check(lib().pa_cache_write(k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0), k_cache.data_ptr(),
-                                v_cache.data_ptr(), slot_mapping.data_ptr(), N, Hkv, D, bs, NB,
-                                _dtype_code(k_cache), _stream(stream)))
+    return _call(lib().pa_cache_write, (k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0), k_cache.data_ptr(),
+                                        v_cache.data_ptr(), slot_mapping.data_ptr(), N, Hkv, D, bs, NB,
+                                        _dtype_code(k_cache), _stream(stream)), _prepare)
 
 
 def cache_write_fp8(k_new, v_new, k_cache, v_cache, slot_mapping, k_scale: float, v_scale: float,
-                    stream=None) -> None:
+                    stream=None, _prepare: bool = False):
     """Quantise new bf16 K/V rows [N, Hkv, D] into 8-bit (OCP E4M3) pools
     [NB, Hkv, 16, D] (uint8 tensors) with per-pool scales."""
     torch = _torch()
@@ -251,9 +262,9 @@ def cache_write_fp8(k_new, v_new, k_cache, v_cache, slot_mapping, k_scale: float
     NB, Hc, bs, Dc = k_cache.shape
     if Hc != Hkv or Dc != D:
         raise ValueError("pool heads/head_dim differ from the new rows")
-    _check(lib().pa_cache_write_fp8(k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0), k_cache.data_ptr(),
-                                    v_cache.data_ptr(), slot_mapping.data_ptr(), N, Hkv, D, bs, NB, float(k_scale),
-                                    float(v_scale), _stream(stream)))
+    return _call(lib().pa_cache_write_fp8, (k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0), k_cache.data_ptr(),
+                                            v_cache.data_ptr(), slot_mapping.data_ptr(), N, Hkv, D, bs, NB,
+                                            float(k_scale), float(v_scale), _stream(stream)), _prepare)
 
 
 def make_params(q, k_cache, cu_seqlens, block_tables, num_kv_heads: int, scale: float, max_query_len: int,
@@ -293,7 +304,7 @@ def partition_size(params: AttnParams) -> int:
 def attention_varlen(out, q, k_cache, v_cache, cu_seqlens, seq_lens, block_tables, scale: float,
                      max_query_len: int, max_seq_len: int, workspace=None, partition_size: int = 0,
                      stream=None, k_scale=None, v_scale=None, sliding_window: int = 0, stage: str = "all",
-                     num_decode_rows: int = 0):
+                     num_decode_rows: int = 0, _prepare: bool = False):
     """Paged causal attention of packed rows; writes ``out`` [total_q, Hq, D] and returns it.
 
     ``sliding_window`` W > 0 limits each row to the last W positions up to
@@ -345,21 +356,39 @@ def attention_varlen(out, q, k_cache, v_cache, cu_seqlens, seq_lens, block_table
     ws_bytes = workspace.numel() * workspace.element_size()
     if stage not in ("all", "plan", "run"):
         raise ValueError("stage must be 'all', 'plan' or 'run'")
+    keep = (p, workspace)
     if stage == "plan":
-        _check(lib().pa_attention_plan(cu_seqlens.data_ptr(), seq_lens.data_ptr(), ctypes.byref(p),
-                                       workspace.data_ptr(), ws_bytes, _stream(stream)))
-        return out
-    if fp8:
+        call = _call(lib().pa_attention_plan, (cu_seqlens.data_ptr(), seq_lens.data_ptr(), ctypes.byref(p),
+                                               workspace.data_ptr(), ws_bytes, _stream(stream)), _prepare, keep)
+    elif fp8:
         fn = lib().pa_attention_run_fp8 if stage == "run" else lib().pa_attention_varlen_fp8
-        _check(fn(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cu_seqlens.data_ptr(),
-                  seq_lens.data_ptr(), block_tables.data_ptr(), ctypes.byref(p), float(k_scale), float(v_scale),
-                  workspace.data_ptr(), ws_bytes, _stream(stream)))
+        call = _call(fn, (out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cu_seqlens.data_ptr(),
+                          seq_lens.data_ptr(), block_tables.data_ptr(), ctypes.byref(p), float(k_scale),
+                          float(v_scale), workspace.data_ptr(), ws_bytes, _stream(stream)), _prepare, keep)
     else:
         fn = lib().pa_attention_run if stage == "run" else lib().pa_attention_varlen
-        _check(fn(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cu_seqlens.data_ptr(),
-                  seq_lens.data_ptr(), block_tables.data_ptr(), ctypes.byref(p), workspace.data_ptr(), ws_bytes,
-                  _stream(stream)))
-    return out
+        call = _call(fn, (out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cu_seqlens.data_ptr(),
+                          seq_lens.data_ptr(), block_tables.data_ptr(), ctypes.byref(p), workspace.data_ptr(),
+                          ws_bytes, _stream(stream)), _prepare, keep)
+    return call if _prepare else out
+
+
+def prepare_cache_write(*args, **kwargs):
+    """``cache_write`` with its checks and argument marshalling done once: returns
+    a function of no arguments that makes only the C call (the same tensors and
+    stream) each time -- for loops that repeat one step."""
+    return cache_write(*args, _prepare=True, **kwargs)
+
+
+def prepare_cache_write_fp8(*args, **kwargs):
+    """``cache_write_fp8`` prepared the same way (see ``prepare_cache_write``)."""
+    return cache_write_fp8(*args, _prepare=True, **kwargs)
+
+
+def prepare_attention_varlen(*args, **kwargs):
+    """``attention_varlen`` prepared the same way (see ``prepare_cache_write``); a
+    workspace it allocates is kept alive by the returned function."""
+    return attention_varlen(*args, _prepare=True, **kwargs)
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20   # PA_NOALLOC_SCRATCH_BYTES
