@@ -1076,15 +1076,17 @@ int persistent_groups() {
   return v;
 }
 
-// The matrix-core tile form serves 8-bit pools at D = 128 with items of 4 or 8
-// heads (every block size, so results stay bitwise the same across block
-// sizes): there the dot-product form is bound by the VALU issue of the code
-// conversions and v_dot2 instructions, not by HBM.  bf16 pools keep the
-// dot-product form, which streams at the HBM ceiling already (the matrix-core
-// form measured 0.8% faster on the GQA decode layer).
+// The matrix-core tile form serves D = 128 with items of 4 or 8 heads, on
+// bf16 and 8-bit pools, at every block size (so results stay bitwise the same
+// across block sizes).  On 8-bit pools the dot-product form is bound by the
+// VALU issue of the code conversions and v_dot2 instructions (205 -> 153 us
+// on the GQA decode layer); on bf16 pools the kernel streams at the HBM
+// ceiling either way, and the form's lighter vector work shortens the tail
+// (273.8 -> 272.4 us) and leaves more issue slots to a prefill launch beside
+// it (mixed chunked-prefill step 507.7 -> 499 us).
 template <int G, bool F8, int BS, int D>
 constexpr bool use_mfma_tiles() {
-  return F8 && D == 128 && (G == 4 || G == 8);
+  return D == 128 && (G == 4 || G == 8);
 }
 
 template <int G, bool F8, int BS, int D, int WK>
@@ -1098,8 +1100,8 @@ hipError_t launch_wk(const DecodeArgs& a, hipStream_t stream) {
 }
 
 // Three workers also where four would not fit the registers a wave needs: the
-// matrix-core form on 8-bit pools with 8-token blocks needs more than the 256
-// a wave may take when one SIMD holds two of a workgroup's five waves.
+// matrix-core form with 8-token blocks needs more than the 256 a wave may take
+// when one SIMD holds two of a workgroup's five waves.
 template <int G, bool F8, int BS, int D>
 constexpr bool three_workers_fit_better() {
   return use_mfma_tiles<G, F8, BS, D>() && BS == 8;
