@@ -395,18 +395,22 @@ __global__ __launch_bounds__(64 * (WK + 1), 1) void decode_gqa_kernel(DecodeArgs
   };
   const int4 entry0 = static_entry(0);
   int* claim_counter = a.plan + kPlanClaimInt;
-  // Every wave counts itself out when it leaves; the last one re-arms the
-  // claim counter (and this count) for the next run on the same work list.
-  // Each scheduler's claims have returned their values before it counts out,
-  // so when the count completes no claim of this launch is still in flight.
+  // Every wave counts itself out when it leaves, in its workgroup's LDS; the
+  // workgroup's last wave counts the workgroup out on a device-scope counter,
+  // and the last workgroup re-arms the claim counter (and this count) for the
+  // next run on the same work list.  Each scheduler's claims have returned
+  // their values before it counts out, so when the count completes no claim of
+  // this launch is still in flight.  (One device-scope atomic per workgroup,
+  // not per wave: a launch whose list is empty has all its waves leave at
+  // once, and 1280 atomics on one address took about 13 us.)
   int* done_counter = a.plan + kPlanDoneInt;
+  __shared__ int s_out;   // waves of this workgroup that have left
   auto count_out = [&]() {
-    if ((threadIdx.x & 63) == 0) {
-      const int waves = int(gridDim.x) * (WK + 1);
-      if (__hip_atomic_fetch_add(done_counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == waves - 1) {
-        __hip_atomic_store(claim_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(done_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+    if ((threadIdx.x & 63) == 0 &&
+        __hip_atomic_fetch_add(&s_out, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == WK &&
+        __hip_atomic_fetch_add(done_counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == int(gridDim.x) - 1) {
+      __hip_atomic_store(claim_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(done_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
 
@@ -427,6 +431,7 @@ __global__ __launch_bounds__(64 * (WK + 1), 1) void decode_gqa_kernel(DecodeArgs
     s_qhead = 0;
     s_qtail = 0;
     s_qend = 0x7fffffff;
+    s_out = 0;
   }
   __syncthreads();
   auto lds_load = [](int* p) { return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP); };

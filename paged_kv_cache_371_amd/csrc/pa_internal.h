@@ -108,7 +108,7 @@ constexpr int kPlanPrefCountInt = 9;     // header slot: number of prefill entri
 constexpr int kPlanMergeCountInt = 10;   // header slot: number of merge entries (rows with > 1 partition)
 constexpr int kPlanClaimInt = 11;        // header slot: claim counter of the fast decode kernel (zeroed by the plan,
                                          // re-armed by the last wave of each decode launch)
-constexpr int kPlanDoneInt = 12;         // header slot: waves of the fast decode launch that have finished
+constexpr int kPlanDoneInt = 12;         // header slot: workgroups of the fast decode launch that have finished
 constexpr int kPlanPrefClaimInt = 13;    // header slot: claim counter of the prefill kernel (zeroed by the plan,
                                          // re-armed by the last workgroup of each prefill launch)
 constexpr int kPlanPrefDoneInt = 14;     // header slot: workgroups of the prefill launch that have finished

@@ -6,7 +6,7 @@
 //   [kPlanPrefCountInt]  number of prefill entries
 //   [kPlanMergeCountInt] number of merge entries
 //   [kPlanClaimInt]      claim counter of the decode kernel's dynamic rounds, zeroed here
-//   [kPlanDoneInt]       finished waves of a decode launch, zeroed here (each launch's last wave
+//   [kPlanDoneInt]       finished workgroups of a decode launch, zeroed here (each launch's last one
 //                        zeroes both again, so one list serves any number of launches)
 //   [kPlanPrefClaimInt]  claim counter of the prefill kernel, zeroed here
 //   [kPlanPrefDoneInt]   finished workgroups of a prefill launch, zeroed here (re-armed the same way)
