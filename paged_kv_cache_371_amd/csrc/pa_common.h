@@ -105,6 +105,17 @@ __device__ __forceinline__ float rows_max(float v) {
   swap16(a, b);
   return fmaxf(a, b);
 }
+// max / sum over lanes l and l^32 (the two 32-lane halves); every lane gets the result.
+__device__ __forceinline__ float halves_max(float v) {
+  float a = v, b = v;
+  swap32(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float halves_sum(float v) {
+  float a = v, b = v;
+  swap32(a, b);
+  return a + b;
+}
 __device__ __forceinline__ float rows_sum(float v) {
   float a = v, b = v;
   swap32(a, b);

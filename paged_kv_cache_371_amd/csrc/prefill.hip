@@ -6,28 +6,31 @@
 // alignment: row j of a request with n rows and context L sees keys
 // 0 .. L-n+j).  Every K/V byte serves many query rows here, so Q.K^T and P.V
 // are dense contractions and run on the matrix cores
-// (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
+// (v_mfma_f32_32x32x16_bf16, or 16x16x32 at D = 256; fp32 accumulation).
 //
 // Work item: (request, KV head, tile of 128 -- or, for batches of short
 // requests, 64 -- (query row, head) pairs), the pairs packed as m = row * G +
-// head over the G query heads of the KV head.  Four waves own 32 (16) pairs
-// each: two (one) 16-column MFMA blocks.  A short request whose context spans
+// head over the G query heads of the KV head.  Four (or two) waves own 32
+// pairs each, 16 at D = 256.  A short request whose context spans
 // several partitions is one item per partition (its key tiles only), and
 // leaves unnormalised partials and (max, sum) for the merge kernel.  Keys are
 // visited in tiles of 64 (four paged blocks; wave w fetches block w of the tile, so
 // every load has a wave-uniform base).  Tiles are fetched into registers one
 // ahead and written to one of two LDS stages: K as 16-byte d-chunks, chunk
-// major (a 16-lane MFMA read is 256 contiguous bytes), V transposed (V^T,
+// major (the MFMA reads of one chunk are contiguous), V transposed (V^T,
 // d-major, rows padded to 136 bytes) by a 4 x 8 register transpose.  Both
 // layouts make the staging writes and the MFMA operand reads bank-conflict
 // free.
 //
-// Per tile and wave: S^T = K Q^T (keys x pairs, d contracted in 4 steps of
-// 32), so a lane holds one pair's column and the online softmax over keys is
-// in-lane plus two permlane swaps.  P^T then feeds O^T = V^T P^T as the B
-// operand without moving data: inside each 32-key step the keys are taken in
-// the order the S^T accumulators hold them (lane row h owns keys 4h..4h+3 and
-// 16+4h..16+4h+3), and V^T is read from LDS in that same order.  P is rounded
+// Per tile and wave: S^T = K Q^T (keys x pairs), so a lane holds scores of
+// one pair and the online softmax over keys is in-lane plus one permlane swap
+// between the wave's two 32-lane halves (two swaps over the four 16-lane rows
+// at D = 256).  32 x 32 x 16 MFMAs take half the instructions of 16 x 16 x 32
+// ones for the same products, and leave the vector ALUs more issue cycles for
+// the softmax beside them.  P^T then feeds O^T = V^T P^T as the B operand
+// without moving data: inside each MFMA step of P.V the keys are taken in the
+// order the S^T accumulators hold them (two runs of 4 keys per lane), and V^T
+// is read from LDS in that same order.  P is rounded
 // to bf16 for the MFMA, and the softmax sum uses the rounded values.  The
 // running max is raised only when a tile's max exceeds it by more than 8
 // (log2 units), so most tiles neither rescale the accumulators nor spend a
@@ -79,6 +82,7 @@ struct Shape {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
@@ -106,6 +110,12 @@ static_assert(std::is_standard_layout<PrefillArgs>::value, "offsetof on the argu
 
 __device__ __forceinline__ f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
+                                                  0);
+}
+// 32 x 32 x 16: lane l holds row (A) / column (B) l % 32 with k = 8 (l / 32) .. +7;
+// element r of the result is row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
+__device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
                                                   0);
 }
 
@@ -166,6 +176,14 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
   constexpr int kKBytes = S::kKBytes;
   constexpr int kStageBytes = S::kStageBytes;
   constexpr int kRows = kPairs / G;   // query rows per work item
+  // With 32 pairs per wave the products are 32 x 32 x 16 MFMAs (half the
+  // instructions of 16 x 16 x 32 for the same work, which leaves more issue
+  // cycles to the softmax); D = 256 keeps 16 pairs per wave on 16 x 16 x 32.
+  constexpr bool kM32 = kMB == 2;
+  constexpr int kNP = kM32 ? 1 : kMB;            // pairs per lane
+  constexpr int kQSteps = kM32 ? D / 16 : kSteps;   // d steps of S^T
+  constexpr int kAB = kM32 ? D / 32 : kDB;          // d blocks of O^T
+  using Acc = typename std::conditional<kM32, f32x16_t, f32x4_t>::type;
   extern __shared__ __align__(16) char smem[];
 
   const int hkv = a.num_kv_heads;
@@ -178,7 +196,8 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
   const int lane = tid & 63;
   const int wave = uni(tid >> 6);
   const int h = lane >> 4;    // 16-lane row of the wave
-  const int lc = lane & 15;   // MFMA column of the lane
+  const int lc = lane & 15;   // 16 x 16 MFMA column of the lane
+  const int hf = lane >> 5;   // 32-lane half of the wave
   // staging coordinates (see TileRegs): at D = 64 the unit's 8 d-chunks per key
   // are staged by lanes 0..31 and lanes 32..63 stage nothing
   const int kkey = D == 256 ? 8 * (lane >> 5) : D == 128 ? 4 * (lane >> 4) : 4 * ((lane >> 3) & 3);
@@ -206,6 +225,17 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
   // priority over it (measured on the mixed chunked-prefill step: 580 -> 510
   // us; raising the decode waves' priority instead changed nothing).
   if (claim_items) __builtin_amdgcn_s_setprio(2);
+  // There, a wave takes one level more while it issues its matrix-core
+  // products (mixed chunked-prefill step: 490.5 -> 473.5 us).  Alone on the
+  // GPU the same raise made the prefill kernel 4% slower, so it is not done.
+  auto matrix_phase = [&](bool on) {
+    if (claim_items) {
+      if (on)
+        __builtin_amdgcn_s_setprio(3);
+      else
+        __builtin_amdgcn_s_setprio(2);
+    }
+  };
   int* claim_counter = a.plan + kPlanPrefClaimInt;
   int* done_counter = a.plan + kPlanPrefDoneInt;
   __shared__ int s_next;
@@ -250,14 +280,17 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
     const char* kbase = static_cast<const char*>(PA_KARG(k_cache)) + int64_t(kvh) * kHeadBytes;
     const char* vbase = static_cast<const char*>(PA_KARG(v_cache)) + int64_t(kvh) * kHeadBytes;
 
-    // ---- this lane's two pairs: m = wave*32 + mb*16 + lc ----------------------
-    // visible keys of a pair: lolim .. lolim + span (one unsigned compare per score)
-    int jrow[kMB], hq[kMB], lolim[kMB], span[kMB];
-    bool mvalid[kMB];
-    u32x4_t qb[kMB][kSteps];   // B operand Q^T: pair lc, d = 32s + 8h .. +7
+    // ---- this lane's pairs -----------------------------------------------------
+    // 32 pairs per wave (D <= 128): one pair per lane, m = wave*32 + lane % 32;
+    // lanes l and l + 32 hold the same pair (each half of every 32-key block).
+    // 16 pairs per wave (D = 256): m = wave*16 + lc, one per 16-lane row.
+    // Visible keys of a pair: lolim .. lolim + span (one unsigned compare per score).
+    int jrow[kNP], hq[kNP], lolim[kNP], span[kNP];
+    bool mvalid[kNP];
+    u32x4_t qb[kNP][kQSteps];   // B operand Q^T: pair m, d = 16s + 8hf .. +7 (32-pair) or 32s + 8h .. +7
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
-      const int m = wave * (16 * kMB) + mb * 16 + lc;
+    for (int mb = 0; mb < kNP; ++mb) {
+      const int m = kM32 ? wave * 32 + (lane & 31) : wave * (16 * kMB) + mb * 16 + lc;
       jrow[mb] = j0 + m / G;
       hq[mb] = hg * G + m % G;
       mvalid[mb] = jrow[mb] < j1;
@@ -266,20 +299,22 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
       const char* qrow = static_cast<const char*>(PA_KARG(q)) +
                          (int64_t(q0 + (mvalid[mb] ? jrow[mb] : 0)) * PA_KARG(q_row_stride) + int64_t(hq[mb]) * D) * 2;
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qrow + (32 * s + 8 * h) * 2);
+      for (int s = 0; s < kQSteps; ++s) {
+        const int d0 = kM32 ? 16 * s + 8 * hf : 32 * s + 8 * h;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qrow + d0 * 2);
         qb[mb][s] = mvalid[mb] ? v : u32x4_t{0u, 0u, 0u, 0u};
       }
     }
 
-    f32x4_t acc[kMB][kDB];   // O^T blocks: d = 16*db + 4h + r, pair lc
+    // O^T blocks: d = 32*db + 8*(r/4) + 4*hf + r%4 (32-pair), or 16*db + 4h + r; pair m
+    Acc acc[kNP][kAB];
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
+    for (int mb = 0; mb < kNP; ++mb)
 #pragma unroll
-      for (int db = 0; db < kDB; ++db) acc[mb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float mrun[kMB], lrun[kMB];
+      for (int db = 0; db < kAB; ++db) acc[mb][db] = Acc{};
+    float mrun[kNP], lrun[kNP];
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
+    for (int mb = 0; mb < kNP; ++mb) {
       mrun[mb] = kMinusBig;
       lrun[mb] = 0.f;
     }
@@ -398,85 +433,178 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
     };
 
     // ---- one tile from LDS stage st -----------------------------------------------
+    // The lazy rescale of one pair's state, given the tile's max in log2 units
+    // (the same value in every lane that holds the pair).  The reference max is
+    // raised only when the tile's max exceeds it by more than kRescaleThreshold
+    // (log2 units); otherwise p <= 2^8 is used as is.  Exact: the normalisation
+    // uses the same reference.
+    auto rescale = [&](int mb, float tmax) {
+      if (__builtin_amdgcn_ballot_w64(tmax > mrun[mb] + kRescaleThreshold)) {
+        const float mnew = fmaxf(mrun[mb], tmax);
+        const float alpha = fast_exp2(mrun[mb] - mnew);
+        mrun[mb] = mnew;
+        lrun[mb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < kAB; ++db) acc[mb][db] *= alpha;
+      }
+    };
+    // p = 2^(s * scale_log2 - m) of 8 scores, packed as bf16 pairs; the sum of the
+    // rounded values goes into lsum
+    auto softmax8 = [&](float s0, float s1, float s2, float s3, float s4, float s5, float s6, float s7, float nm,
+                        float& lsum) {
+      uint32_t w[4];
+      w[0] = pack_bf16x2(fast_exp2(fmaf(s0, scale_log2, nm)), fast_exp2(fmaf(s1, scale_log2, nm)));
+      w[1] = pack_bf16x2(fast_exp2(fmaf(s2, scale_log2, nm)), fast_exp2(fmaf(s3, scale_log2, nm)));
+      w[2] = pack_bf16x2(fast_exp2(fmaf(s4, scale_log2, nm)), fast_exp2(fmaf(s5, scale_log2, nm)));
+      w[3] = pack_bf16x2(fast_exp2(fmaf(s6, scale_log2, nm)), fast_exp2(fmaf(s7, scale_log2, nm)));
+#pragma unroll
+      for (int x = 0; x < 4; ++x) lsum = dot2_bf16(w[x], kBf16OnePair, lsum);
+      return u32x4_t{w[0], w[1], w[2], w[3]};
+    };
+    // Keys past a row's limit, or before its window, get a score of -inf (raw
+    // scores: the scale is positive, so the order and the masking survive
+    // scaling).  Only tiles that reach past the first row's limit or before
+    // the last row's window start need it.
+    auto needs_mask = [&](int kt) { return kt * kKeys + kKeys - 1 > P + j0 || kt * kKeys < lo_last; };
+    // ---- 32 pairs per wave: the pieces of a tile ------------------------------------
+    // S^T block c of a tile: keys 32c + 8(r/4) + 4hf + r%4 (element r), pair lane % 32.
+    constexpr int kKB = kKeys / 32;
+    using STile = f32x16_t[kKB];
+    // S^T of the tile whose K is in stage kst
+    auto qk32 = [&](STile& sacc, int kst) {
+      const char* ks = smem + kst * kStageBytes;
+#pragma unroll
+      for (int c = 0; c < kKB; ++c) sacc[c] = f32x16_t{};
+#pragma unroll
+      for (int s = 0; s < kQSteps; ++s)
+#pragma unroll
+        for (int c = 0; c < kKB; ++c) {
+          const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(ks + (2 * s + hf) * kKChunk + (32 * c + (lane & 31)) * 16);
+          sacc[c] = mfma32(ka, qb[0][s], sacc[c]);
+        }
+    };
+    auto mask32 = [&](STile& sacc, int kt) {
+#pragma unroll
+      for (int c = 0; c < kKB; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt * kKeys + 32 * c + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (uint32_t(key - lolim[0]) > uint32_t(span[0])) sacc[c][r] = -__builtin_inff();
+        }
+    };
+    // the tile's max over the pair's keys, in log2 units
+    auto max32 = [&](const STile& sacc) {
+      float tmax = -__builtin_inff();
+#pragma unroll
+      for (int c = 0; c < kKB; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4)
+          tmax = fmaxf(fmaxf(tmax, fmaxf(sacc[c][r], sacc[c][r + 1])), fmaxf(sacc[c][r + 2], sacc[c][r + 3]));
+      return halves_max(tmax) * scale_log2;
+    };
+    // B operands P^T of the tile's 16-key steps 2c + u: keys 32c + 16u + 8(t/4) +
+    // 4hf + t%4 for the lane's slots t = 0..7, i.e. elements 8u .. 8u+7 of block c
+    auto probs32 = [&](const STile& sacc, u32x4_t* pb) {
+      const float nm = -mrun[0];
+      float lsum = lrun[0];
+#pragma unroll
+      for (int c = 0; c < kKB; ++c)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const f32x16_t& sv = sacc[c];
+          pb[2 * c + u] = softmax8(sv[8 * u], sv[8 * u + 1], sv[8 * u + 2], sv[8 * u + 3], sv[8 * u + 4], sv[8 * u + 5],
+                                   sv[8 * u + 6], sv[8 * u + 7], nm, lsum);
+        }
+      lrun[0] = lsum;
+    };
+    // O^T += V^T P^T with V from stage vst.  A operand of step k, d block db: row
+    // 32db + lane % 32 and the same keys as P^T's slots, two runs of 4 keys.
+    auto pv32 = [&](const u32x4_t* pb, int vst) {
+      if constexpr (kM32) {
+        const char* vs = smem + vst * kStageBytes + kKBytes;
+#pragma unroll
+        for (int k = 0; k < 2 * kKB; ++k)
+#pragma unroll
+          for (int db = 0; db < kAB; ++db) {
+            const char* vrow = vs + (32 * db + (lane & 31)) * kVRow;
+            const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow + (16 * k + 4 * hf) * 2);
+            const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + (16 * k + 8 + 4 * hf) * 2);
+            acc[0][db] = mfma32(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pb[k], acc[0][db]);
+          }
+      }
+    };
+
+    // ---- one tile from LDS stage st -------------------------------------------------
     auto compute = [&](int kt, int st) {
       const char* ks = smem + st * kStageBytes;
       const char* vs = ks + kKBytes;
-      f32x4_t sacc[kCB][kMB];
-#pragma unroll
-      for (int c = 0; c < kCB; ++c)
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) sacc[c][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < kSteps; ++s)
-#pragma unroll
-        for (int c = 0; c < kCB; ++c) {
-          const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(ks + (4 * s + h) * kKChunk + (16 * c + lc) * 16);
-#pragma unroll
-          for (int mb = 0; mb < kMB; ++mb) sacc[c][mb] = mfma16(ka, qb[mb][s], sacc[c][mb]);
-        }
-      // Keys past a row's limit, or before its window, get a score of -inf
-      // (raw scores: the scale is positive, so the order and the masking
-      // survive scaling).  Only tiles that reach past the first row's limit or
-      // before the last row's window start need it.
-      if (kt * kKeys + kKeys - 1 > P + j0 || kt * kKeys < lo_last) {
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-          for (int c = 0; c < kCB; ++c)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int key = kt * kKeys + 16 * c + 4 * h + r;
-              if (uint32_t(key - lolim[mb]) > uint32_t(span[mb])) sacc[c][mb][r] = -__builtin_inff();
-            }
-      }
-      u32x4_t pb[kMB][kU];   // B operand P^T per (pair block, 32-key step)
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) {
-        float tmax = -__builtin_inff();
+      if constexpr (kM32) {
+        f32x16_t sacc[kKB];
+        matrix_phase(true);
+        qk32(sacc, st);
+        matrix_phase(false);
+        if (needs_mask(kt)) mask32(sacc, kt);
+        rescale(0, max32(sacc));
+        u32x4_t pb[2 * kKB];
+        probs32(sacc, pb);
+        matrix_phase(true);
+        pv32(pb, st);
+        matrix_phase(false);
+      } else {   // 16 pairs per wave (D = 256)
+        f32x4_t sacc[kCB][kMB];
 #pragma unroll
         for (int c = 0; c < kCB; ++c)
-          tmax = fmaxf(fmaxf(tmax, fmaxf(sacc[c][mb][0], sacc[c][mb][1])), fmaxf(sacc[c][mb][2], sacc[c][mb][3]));
-        tmax = rows_max(tmax) * scale_log2;
-        // The reference max is raised only when the tile's max exceeds it by
-        // more than kRescaleThreshold (log2 units); otherwise p <= 2^8 is used
-        // as is.  Exact: the normalisation uses the same reference.
-        if (__builtin_amdgcn_ballot_w64(tmax > mrun[mb] + kRescaleThreshold)) {
-          const float mnew = fmaxf(mrun[mb], tmax);
-          const float alpha = fast_exp2(mrun[mb] - mnew);
-          mrun[mb] = mnew;
-          lrun[mb] *= alpha;
 #pragma unroll
-          for (int db = 0; db < kDB; ++db) acc[mb][db] *= alpha;
-        }
-        const float nm = -mrun[mb];
-        float lsum = lrun[mb];
+          for (int mb = 0; mb < kMB; ++mb) sacc[c][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          uint32_t w[4];
+        for (int s = 0; s < kSteps; ++s)
 #pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const f32x4_t& sv = sacc[2 * u + half][mb];
-            w[2 * half] = pack_bf16x2(fast_exp2(fmaf(sv[0], scale_log2, nm)), fast_exp2(fmaf(sv[1], scale_log2, nm)));
-            w[2 * half + 1] =
-                pack_bf16x2(fast_exp2(fmaf(sv[2], scale_log2, nm)), fast_exp2(fmaf(sv[3], scale_log2, nm)));
+          for (int c = 0; c < kCB; ++c) {
+            const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(ks + (4 * s + h) * kKChunk + (16 * c + lc) * 16);
+#pragma unroll
+            for (int mb = 0; mb < kMB; ++mb) sacc[c][mb] = mfma16(ka, qb[mb][s], sacc[c][mb]);
           }
+        if (needs_mask(kt)) {
 #pragma unroll
-          for (int x = 0; x < 4; ++x) lsum = dot2_bf16(w[x], kBf16OnePair, lsum);
-          pb[mb][u] = u32x4_t{w[0], w[1], w[2], w[3]};
+          for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+            for (int c = 0; c < kCB; ++c)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int key = kt * kKeys + 16 * c + 4 * h + r;
+                if (uint32_t(key - lolim[mb]) > uint32_t(span[mb])) sacc[c][mb][r] = -__builtin_inff();
+              }
         }
-        lrun[mb] = lsum;
+        u32x4_t pb[kMB][kU];   // B operand P^T per (pair block, 32-key step)
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb) {
+          float tmax = -__builtin_inff();
+#pragma unroll
+          for (int c = 0; c < kCB; ++c)
+            tmax = fmaxf(fmaxf(tmax, fmaxf(sacc[c][mb][0], sacc[c][mb][1])), fmaxf(sacc[c][mb][2], sacc[c][mb][3]));
+          rescale(mb, rows_max(tmax) * scale_log2);
+          const float nm = -mrun[mb];
+          float lsum = lrun[mb];
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            const f32x4_t& a0 = sacc[2 * u][mb];
+            const f32x4_t& a1 = sacc[2 * u + 1][mb];
+            pb[mb][u] = softmax8(a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3], nm, lsum);
+          }
+          lrun[mb] = lsum;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+#pragma unroll
+          for (int db = 0; db < kDB; ++db) {
+            const char* vrow = vs + (16 * db + lc) * kVRow;
+            const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow + (32 * u + 4 * h) * 2);
+            const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + (32 * u + 16 + 4 * h) * 2);
+            const u32x4_t va = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+            for (int mb = 0; mb < kMB; ++mb) acc[mb][db] = mfma16(va, pb[mb][u], acc[mb][db]);
+          }
       }
-#pragma unroll
-      for (int u = 0; u < kU; ++u)
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-          const char* vrow = vs + (16 * db + lc) * kVRow;
-          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow + (32 * u + 4 * h) * 2);
-          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + (32 * u + 16 + 4 * h) * 2);
-          const u32x4_t va = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-          for (int mb = 0; mb < kMB; ++mb) acc[mb][db] = mfma16(va, pb[mb][u], acc[mb][db]);
-        }
     };
 
     // ---- tile pipeline: registers one tile ahead, two LDS stages -------------------
@@ -528,34 +656,49 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
       }
     }
 
+    // A lane's output values come in runs of 4 consecutive d: run x of pair mb
+    // starts at d = run_d(x) and holds run_v(mb, x).
+    constexpr int kRuns = kM32 ? 4 * kAB : kAB;
+    auto run_d = [&](int x) { return kM32 ? 32 * (x >> 2) + 8 * (x & 3) + 4 * hf : 16 * x + 4 * h; };
+    auto run_v = [&](int mb, int x) -> f32x4_t {
+      if constexpr (kM32) {
+        const f32x16_t& v = acc[mb][x >> 2];
+        const int r = 4 * (x & 3);
+        return f32x4_t{v[r], v[r + 1], v[r + 2], v[r + 3]};
+      } else {
+        return acc[mb][x];
+      }
+    };
+    // the pair's sum over every key: lanes l, l^32 (32-pair) or the four rows
+    auto pair_sum = [&](float v) { return kM32 ? halves_sum(v) : rows_sum(v); };
     if (split) {
       // unnormalised partial output and (max, sum) of this partition
 #pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) {
-        const float lsum = rows_sum(lrun[mb]) * (F8 ? PA_KARG(lsum_scale) : 1.f);
+      for (int mb = 0; mb < kNP; ++mb) {
+        const float lsum = pair_sum(lrun[mb]) * (F8 ? PA_KARG(lsum_scale) : 1.f);
         if (mvalid[mb]) {
           const int64_t idx = (int64_t(PA_KARG(num_seqs) + q0 + jrow[mb]) * PA_KARG(num_q_heads) + hq[mb]) *
                                   PA_KARG(max_parts) +
                               (part - p_lo);
           float* po = PA_KARG(ws_o) + idx * D;
 #pragma unroll
-          for (int db = 0; db < kDB; ++db) *reinterpret_cast<f32x4_t*>(po + 16 * db + 4 * h) = acc[mb][db];
-          if (h == 0) *reinterpret_cast<float2*>(PA_KARG(ws_ml) + 2 * idx) = make_float2(mrun[mb], lsum);
+          for (int x = 0; x < kRuns; ++x) *reinterpret_cast<f32x4_t*>(po + run_d(x)) = run_v(mb, x);
+          if ((kM32 ? hf : h) == 0) *reinterpret_cast<float2*>(PA_KARG(ws_ml) + 2 * idx) = make_float2(mrun[mb], lsum);
         }
       }
     } else {
       // ---- normalise and store --------------------------------------------------
 #pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) {
-        const float inv = 1.f / (rows_sum(lrun[mb]) * (F8 ? PA_KARG(lsum_scale) : 1.f));
+      for (int mb = 0; mb < kNP; ++mb) {
+        const float inv = 1.f / (pair_sum(lrun[mb]) * (F8 ? PA_KARG(lsum_scale) : 1.f));
         if (mvalid[mb]) {
           __bf16* orow =
               static_cast<__bf16*>(PA_KARG(out)) + int64_t(q0 + jrow[mb]) * PA_KARG(o_row_stride) + int64_t(hq[mb]) * D;
 #pragma unroll
-          for (int db = 0; db < kDB; ++db) {
-            const u32x2_t o = {pack_bf16x2(acc[mb][db][0] * inv, acc[mb][db][1] * inv),
-                               pack_bf16x2(acc[mb][db][2] * inv, acc[mb][db][3] * inv)};
-            *reinterpret_cast<u32x2_t*>(orow + 16 * db + 4 * h) = o;
+          for (int x = 0; x < kRuns; ++x) {
+            const f32x4_t v = run_v(mb, x);
+            const u32x2_t o = {pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv)};
+            *reinterpret_cast<u32x2_t*>(orow + run_d(x)) = o;
           }
         }
       }
