@@ -93,11 +93,18 @@ inline Plan make_plan(const pa_attn_params* p) {
   // 32 / G at D = 256) use half-size prefill tiles; such short requests (one
   // row tile) are split over context partitions when the partition is a
   // whole number of prefill key tiles.
+  // Full tiles at D <= 128 hold 256 pairs: alone on the GPU an 8-wave
+  // workgroup serves one; beside the decode kernel (a mixed step with the
+  // num_decode_rows hint) a 4-wave workgroup serves each half.  Each wave
+  // computes the same pairs the same way in both, and the split rule counts
+  // 128-pair tiles either way, so the hint changes neither the lists nor a bit.
   const int gp = pa::prefill_item_group(g);   // query heads per prefill work item
-  pl.tile_pairs = pa::prefill_tile_pairs(p->head_dim, p->max_query_len <= pa::prefill_tile_pairs(p->head_dim, true) / gp);
+  const bool short_rows = p->max_query_len <= pa::prefill_tile_pairs(p->head_dim, true) / gp;
+  const int split_pairs = short_rows ? pa::prefill_tile_pairs(p->head_dim, true) : (p->head_dim == 256 ? 64 : 128);
+  pl.tile_pairs = pa::prefill_tile_pairs(p->head_dim, short_rows);
   pl.split_rows = (pl.fast && pl.prefill && pl.parts > 1 && ps % pa::kPrefillKeys == 0 &&
-                   p->max_query_len <= pl.tile_pairs / gp)
-                      ? pl.tile_pairs / gp
+                   p->max_query_len <= split_pairs / gp)
+                      ? split_pairs / gp
                       : 0;
   if (pl.fast) {
     pl.generic_mode = (multi && !pl.prefill) ? pa::kMultiRowOnly : -1;

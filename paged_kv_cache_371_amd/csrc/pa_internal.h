@@ -78,7 +78,7 @@ struct PrefillArgs {
   int32_t max_parts;
   float* ws_o;
   float* ws_ml;
-  int32_t tile_pairs;   // (query row, head) pairs per work item: 128, or 64 for short requests
+  int32_t tile_pairs;   // (query row, head) pairs per list entry: 256 (64 at D = 256), or 64 (32) for short requests
   int32_t sliding_window;
   int32_t block_size;   // tokens per physical block: 8, 16 or 32
   int32_t head_split_log2;   // a KV head's query heads are served by 2^this items (set by launch_prefill)
@@ -132,7 +132,7 @@ struct PlanArgs {
   // tile) get one prefill entry per context partition of part_size tokens when
   // they span more than one, and one merge entry per row.
   int32_t split_rows;
-  int32_t tile_pairs;      // (query row, head) pairs per prefill work item (64 or 128)
+  int32_t tile_pairs;      // (query row, head) pairs per prefill list entry (32, 64 or 256)
   int32_t sliding_window;  // partitions wholly before a request's window get no entries
 };
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
@@ -168,8 +168,11 @@ bool prefill_supported(int head_dim, int group, int block_size);
 // Query heads per prefill work item: the group, at most 8 (larger groups are
 // served by several items per KV head; the work list's row tiles use this).
 int prefill_item_group(int group);
-// (query row, head) pairs per prefill work item: 128 (64 at D = 256), or half
-// that when every multi-row request is short.
+// (query row, head) pairs per prefill list entry (row tile): 256 at D <= 128
+// (64 at D = 256), or 64 (32) when every multi-row request is short.  A 256-pair
+// entry is one item of an 8-wave workgroup when the prefill kernel runs alone,
+// two items of a 4-wave workgroup beside the decode kernel (8-wave workgroups
+// do not fit on a CU beside a decode workgroup).
 int prefill_tile_pairs(int head_dim, bool short_rows);
 
 hipError_t launch_validate(const int32_t* cu, const int32_t* seq_lens, const int32_t* bt, const int64_t* slots,

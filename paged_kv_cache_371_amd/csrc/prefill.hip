@@ -57,22 +57,30 @@ constexpr float kRescaleThreshold = 8.f;      // log2 units
 constexpr uint32_t kBf16OnePair = 0x3F803F80u;
 constexpr int kWavesPerSimd = 2;              // register budget: 256 per lane
 
-// Workgroup shape: W waves, each fetching one paged block of every key tile
-// (so a tile holds 16 W keys) and owning 32 (row, head) pairs.  W = 4: 128
-// pairs, 64-key tiles, two workgroups per CU (the LDS holds two).  W = 2: 64
-// pairs, 32-key tiles, four workgroups per CU -- the same waves per SIMD,
-// half the LDS reads per pair (each wave reads the whole staged tile).
+// Workgroup shape: W waves, each owning 32 (row, head) pairs (16 at D = 256).
+// W = 4: 128 pairs, 64-key tiles, each wave fetching one 16-key unit of every
+// tile, two workgroups per CU (the LDS holds two).  W = 2: 64 pairs, 32-key
+// tiles, four workgroups per CU -- the same waves per SIMD, half the LDS reads
+// per pair (each wave reads the whole staged tile).  W = 8: 256 pairs and
+// 64-key tiles, one workgroup per CU, the waves in two groups of four that
+// share every staged tile and take turns on the matrix cores (wave w fetches
+// the K of unit w, wave w + 4 its V).
 template <int W, int D>
 struct Shape {
   static constexpr int kWaves = W;
   static constexpr int kThreads = 64 * W;
-  static constexpr int kKeys = kBlock * W;           // keys per tile
+  static constexpr int kUnits = W == 8 ? 4 : W;      // 16-key units per tile
+  static constexpr int kKeys = kBlock * kUnits;      // keys per tile
   static constexpr int kCB = kKeys / 16;             // 16-key column blocks of S^T
   static constexpr int kU = kKeys / 32;              // 32-key MFMA steps of O^T
   static constexpr int kKChunk = kKeys * 16 + 16;    // LDS bytes per 8-wide d-chunk of K (+ pad)
-  // LDS bytes per d row of V^T: keys + pad chosen so that the 16 rows x 4 row
-  // groups of a 32-lane 8-byte read land on distinct banks
-  static constexpr int kVRow = W == 4 ? kKeys * 2 + 8 : kKeys * 2 + 16;
+  // LDS bytes per d row of V^T.  At D <= 128 (32 x 32 x 16 products) a lane
+  // reads 8 keys of a row as one 16-byte load: rows are 16-byte aligned and
+  // padded by 16 bytes, so the 8 rows of an 8-lane read phase land on distinct
+  // banks.  At D = 256 (16 x 16 x 32) a lane reads two 8-byte runs: keys + pad
+  // chosen so that the 16 rows x 4 row groups of a 32-lane 8-byte read land on
+  // distinct banks.
+  static constexpr int kVRow = D != 256 || kKeys != 64 ? kKeys * 2 + 16 : kKeys * 2 + 8;
   static constexpr int kKBytes = (D / 8) * kKChunk;
   static constexpr int kVBytes = D * kVRow;
   static constexpr int kStageBytes = kKBytes + kVBytes;
@@ -189,7 +197,11 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
   const int hkv = a.num_kv_heads;
   const int split_log2 = PA_KARG(head_split_log2);
   const int nh = hkv << split_log2;   // head groups of G query heads; group hg reads KV head hg >> split_log2
-  const int total = load_const(a.plan, kPlanPrefCountInt) * nh;
+  // A list entry holds tile_pairs pairs: one item, or (256-pair entries on
+  // 4-wave workgroups) two items, its first and second half of rows.
+  const int subs = PA_KARG(tile_pairs) > kPairs ? 2 : 1;
+  const int nhs = nh * subs;   // items per list entry
+  const int total = load_const(a.plan, kPlanPrefCountInt) * nhs;
   const int ngroups = gridDim.x;
   const int wg = blockIdx.x;
   const int tid = threadIdx.x;
@@ -243,8 +255,9 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
     int claimed = 0;
     if (claim_items && tid == 0)
       claimed = __hip_atomic_fetch_add(claim_counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int e = t / nh;
-    const int hg = t - e * nh;
+    const int e = t / nhs;
+    const int sub = t - e * nhs >= nh ? 1 : 0;
+    const int hg = t - e * nhs - sub * nh;
     const int kvh = hg >> split_log2;
     const int b = load_const(entries, 4 * int64_t(e));
     const int tile_part = load_const(entries, 4 * int64_t(e) + 1);
@@ -254,7 +267,8 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
     const int part = tile_part >> 16;
     const int L = load_const(PA_KARG(seq_lens), b);
     const int P = L - n;                  // cached tokens before this request's rows
-    const int j0 = mt * kRows;            // rows [j0, j1) of the request
+    const int j0 = (mt * subs + sub) * kRows;   // rows [j0, j1) of the request
+    const bool empty = j0 >= n;   // the second half of a short entry: no rows, no tiles
     const int j1 = min(n, j0 + kRows);
     const int kmax = P + j1;              // keys visible to the last row
     const int KT = (kmax + kKeys - 1) / kKeys;
@@ -271,7 +285,7 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
     const int part_tiles = part_size / kKeys;
     const int kt_lo = lo_first / kKeys;
     const int kt0 = split ? max(part * part_tiles, kt_lo) : kt_lo;
-    const int kt1 = split ? min(KT, (part + 1) * part_tiles) : KT;
+    const int kt1 = empty ? kt0 : split ? min(KT, (part + 1) * part_tiles) : KT;
     const int mbps = PA_KARG(max_blocks_per_seq);
     // the request's table entries, and its 16-key units (a wave's share of a key tile)
     const int nblk = max(1, min((L + BS - 1) / BS, mbps));
@@ -332,7 +346,9 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
     // not be the request's).  The ids travel packed in one 64-bit value.
     const __amdgpu_buffer_rsrc_t rtab =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(table), 0, nblk * 4, kRsrcWord3);
-    auto unit_of = [&](int kt) { return min(kt * W + wave, nunits - 1); };
+    constexpr int kUnits = S::kUnits;
+    const int wunit = wave % kUnits;   // the 16-key unit of every tile this wave fetches
+    auto unit_of = [&](int kt) { return min(kt * kUnits + wunit, nunits - 1); };
     auto phys_of = [&](int kt) -> uint64_t {
       const int u = unit_of(kt);
       if constexpr (BS == 16) {
@@ -347,78 +363,84 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
       }
     };
     using Regs = TileRegs<D, F8>;
-    auto fetch = [&](TileRegs<D, F8>& rg, int kt, uint64_t phys_v) {
+    using Raw = typename Regs::Raw;
+    // The lane's chunks of this wave's unit of tile kt from the K pool (base
+    // kbase) or the V pool, in the K mapping (key kkey + i, d-chunk kchunk) or
+    // the V mapping (key vkey + i % 4, d-chunk vchunk + 16 (i / 4)).
+    auto load_part = [&](Raw* r, int kt, uint64_t phys_v, const char* base, bool kmap) {
       if (!stager) return;
       const int u = unit_of(kt);
       const int64_t phys = uni(int(uint32_t(phys_v)));
+      auto off_of = [&](int i, int key_base) {
+        return kmap ? (key_base + i) * (D * kEB) + kchunk * 8 * kEB
+                    : (key_base + (i & 3)) * (D * kEB) + (vchunk + 16 * (i >> 2)) * 8 * kEB;
+      };
+      const int key = kmap ? kkey : vkey;
       if constexpr (BS == 8) {
         // keys 0..7 of the unit from the first block, 8..15 from the second
         const int64_t phys2 = uni(int(uint32_t(phys_v >> 32)));
         const int nrec = kt < kt1 ? kHeadBytes : 0;
         const int nrec2 = kt < kt1 && u * kBlock + 8 < L ? kHeadBytes : 0;
-        const __amdgpu_buffer_rsrc_t rk =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + phys * bstride), 0, nrec, kRsrcWord3);
-        const __amdgpu_buffer_rsrc_t rv =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + phys * bstride), 0, nrec, kRsrcWord3);
-        const __amdgpu_buffer_rsrc_t rk2 =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + phys2 * bstride), 0, nrec2, kRsrcWord3);
-        const __amdgpu_buffer_rsrc_t rv2 =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + phys2 * bstride), 0, nrec2, kRsrcWord3);
-        if (kkey < 8) {
+        const __amdgpu_buffer_rsrc_t r1 =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + phys * bstride), 0, nrec, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t r2 =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + phys2 * bstride), 0, nrec2, kRsrcWord3);
+        if (key < 8) {
 #pragma unroll
-          for (int kk = 0; kk < kNK; ++kk)
-            rg.k[kk] = Regs::load(rk, (kkey + kk) * (D * kEB) + kchunk * 8 * kEB);
+          for (int i = 0; i < kNK; ++i) r[i] = Regs::load(r1, off_of(i, key));
         } else {
 #pragma unroll
-          for (int kk = 0; kk < kNK; ++kk)
-            rg.k[kk] = Regs::load(rk2, (kkey - 8 + kk) * (D * kEB) + kchunk * 8 * kEB);
-        }
-        if (vkey < 8) {
-#pragma unroll
-          for (int x = 0; x < kNK; ++x)
-            rg.v[x] = Regs::load(rv, (vkey + (x & 3)) * (D * kEB) + (vchunk + 16 * (x >> 2)) * 8 * kEB);
-        } else {
-#pragma unroll
-          for (int x = 0; x < kNK; ++x)
-            rg.v[x] = Regs::load(rv2, (vkey - 8 + (x & 3)) * (D * kEB) + (vchunk + 16 * (x >> 2)) * 8 * kEB);
+          for (int i = 0; i < kNK; ++i) r[i] = Regs::load(r2, off_of(i, key - 8));
         }
       } else {
         const int64_t off = BS == 32 ? phys * bstride + (u & 1) * kTileBytes : phys * bstride;
         const int nrec = kt < kt1 ? kTileBytes : 0;
-        const __amdgpu_buffer_rsrc_t rk =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + off), 0, nrec, kRsrcWord3);
-        const __amdgpu_buffer_rsrc_t rv =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + off), 0, nrec, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t r1 =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + off), 0, nrec, kRsrcWord3);
 #pragma unroll
-        for (int kk = 0; kk < kNK; ++kk)
-          rg.k[kk] = Regs::load(rk, (kkey + kk) * (D * kEB) + kchunk * 8 * kEB);
-#pragma unroll
-        for (int x = 0; x < kNK; ++x)
-          rg.v[x] = Regs::load(rv, (vkey + (x & 3)) * (D * kEB) + (vchunk + 16 * (x >> 2)) * 8 * kEB);
+        for (int i = 0; i < kNK; ++i) r[i] = Regs::load(r1, off_of(i, key));
       }
     };
-    auto stage_write = [&](TileRegs<D, F8>& rg, int kt, int st) {
-      if (!stager) return;
-      char* ks = smem + st * kStageBytes;
-      char* vs = ks + kKBytes;
-      const int key0 = kt * kKeys + wave * kBlock;   // first position of this wave's block
-      if (kt * kKeys + kKeys > L) {   // the context ends in this tile: zero what lies past it
-        const typename Regs::Raw z = {};   // code 0 is +0 in both encodings
+    // Positions past the context in the lane's chunks (K or V mapping) become
+    // zeros: code 0 is +0 in both encodings.
+    auto zero_past = [&](Raw* r, int kt, bool kmap) {
+      if (kt * kKeys + kKeys > L) {   // the context ends in this tile
+        const int key0 = kt * kKeys + wunit * kBlock + (kmap ? kkey : vkey);
 #pragma unroll
-        for (int kk = 0; kk < kNK; ++kk) {   // v[kk] holds key vkey + kk % 4
-          if (key0 + kkey + kk >= L) rg.k[kk] = z;
-          if (key0 + vkey + (kk & 3) >= L) rg.v[kk] = z;
-        }
+        for (int i = 0; i < kNK; ++i)
+          if (key0 + (kmap ? i : (i & 3)) >= L) r[i] = Raw{};
       }
+    };
+    // K chunks of tile kt to the K half of stage st
+    auto write_k = [&](Raw* r, int kt, int st) {
+      if (!stager) return;
+      zero_past(r, kt, true);
+      char* ks = smem + st * kStageBytes;
 #pragma unroll
-      for (int kk = 0; kk < kNK; ++kk)
-        *reinterpret_cast<u32x4_t*>(ks + kchunk * kKChunk + (wave * kBlock + kkey + kk) * 16) = Regs::widen(rg.k[kk]);
-      // V^T: d rows 8*(vchunk + 16g) + 2w (+1) get this thread's 4 keys (8 bytes each)
-      char* vcol = vs + (wave * kBlock + vkey) * 2;
+      for (int i = 0; i < kNK; ++i)
+        *reinterpret_cast<u32x4_t*>(ks + kchunk * kKChunk + (wunit * kBlock + kkey + i) * 16) = Regs::widen(r[i]);
+    };
+    // V chunks of tile kt to the V half of stage st, transposed: d rows
+    // 8*(vchunk + 16g) + 2w (+1) get this lane's 4 keys (8 bytes each).  At D <=
+    // 128 the 16-key group of unit u sits at group slot u ^ ((d / 16) % units)
+    // of row d, and inside a group the keys come as 0-3, 8-11, 4-7, 12-15 (a
+    // lane of the wave's first half takes keys 0-3 and 8-11 for a 32 x 32 x 16
+    // step, of the second half 4-7 and 12-15).  With 64 LDS banks and 144-byte
+    // rows, the 16 rows of a 16-lane read phase then share one slot and fall on
+    // distinct banks, and so do the 8 chunks x 4 lanes of a 32-lane write phase
+    // (rows 8 apart: the slot separates the pairs of chunks that the row
+    // stride alone would put on one bank).
+    auto write_v = [&](Raw* r, int kt, int st) {
+      if (!stager) return;
+      zero_past(r, kt, false);
+      const int vslot = kM32 ? 16 * (wunit ^ ((vchunk >> 1) & (kUnits - 1))) + 8 * ((vkey >> 2) & 1) +
+                                   4 * ((vkey >> 3) & 1)
+                             : wunit * kBlock + vkey;
+      char* vcol = smem + st * kStageBytes + kKBytes + vslot * 2;
 #pragma unroll
       for (int g = 0; g < kNK / 4; ++g) {
-        const u32x4_t vv[4] = {Regs::widen(rg.v[4 * g]), Regs::widen(rg.v[4 * g + 1]), Regs::widen(rg.v[4 * g + 2]),
-                               Regs::widen(rg.v[4 * g + 3])};
+        const u32x4_t vv[4] = {Regs::widen(r[4 * g]), Regs::widen(r[4 * g + 1]), Regs::widen(r[4 * g + 2]),
+                               Regs::widen(r[4 * g + 3])};
         const int dc = vchunk + 16 * g;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -430,6 +452,14 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
           *reinterpret_cast<u32x2_t*>(vcol + (8 * dc + 2 * w + 1) * kVRow) = u32x2_t{hi01, hi23};
         }
       }
+    };
+    auto fetch = [&](TileRegs<D, F8>& rg, int kt, uint64_t phys_v) {
+      load_part(rg.k, kt, phys_v, kbase, true);
+      load_part(rg.v, kt, phys_v, vbase, false);
+    };
+    auto stage_write = [&](TileRegs<D, F8>& rg, int kt, int st) {
+      write_k(rg.k, kt, st);
+      write_v(rg.v, kt, st);
     };
 
     // ---- one tile from LDS stage st -----------------------------------------------
@@ -471,17 +501,49 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
     constexpr int kKB = kKeys / 32;
     using STile = f32x16_t[kKB];
     // S^T of the tile whose K is in stage kst
+    // Operand reads run kReadAhead MFMAs ahead of their products in the 8-wave
+    // loop, where one wave per SIMD issues the products of a phase with no
+    // other wave's products to hide its LDS round trips: the reads of the next
+    // group of operands are issued, then the products of the current group,
+    // and scheduling barriers keep the compiler from sinking the reads back
+    // next to their use.  The 4-wave loops leave the schedule to the compiler.
+    constexpr int kReadAhead = W == 8 ? 4 : 0;
+    auto pipelined = [&](auto nops, auto read, auto product) {
+      constexpr int N = decltype(nops)::value;
+      if constexpr (kReadAhead == 0) {
+#pragma unroll
+        for (int q = 0; q < N; ++q) product(q, read(q));
+      } else {
+        constexpr int B = kReadAhead;
+        static_assert(N % B == 0, "whole groups of operands");
+        u32x4_t buf[2][B];
+#pragma unroll
+        for (int x = 0; x < B; ++x) buf[0][x] = read(x);
+#pragma unroll
+        for (int g = 0; g < N / B; ++g) {
+          if (g + 1 < N / B) {
+#pragma unroll
+            for (int x = 0; x < B; ++x) buf[(g + 1) & 1][x] = read((g + 1) * B + x);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int x = 0; x < B; ++x) product(g * B + x, buf[g & 1][x]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    // S^T of the tile whose K is in stage kst; operand q: d step q / kKB, block q % kKB
     auto qk32 = [&](STile& sacc, int kst) {
       const char* ks = smem + kst * kStageBytes;
 #pragma unroll
       for (int c = 0; c < kKB; ++c) sacc[c] = f32x16_t{};
-#pragma unroll
-      for (int s = 0; s < kQSteps; ++s)
-#pragma unroll
-        for (int c = 0; c < kKB; ++c) {
-          const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(ks + (2 * s + hf) * kKChunk + (32 * c + (lane & 31)) * 16);
-          sacc[c] = mfma32(ka, qb[0][s], sacc[c]);
-        }
+      pipelined(
+          std::integral_constant<int, kQSteps * kKB>{},
+          [&](int q) {
+            return *reinterpret_cast<const u32x4_t*>(ks + (2 * (q / kKB) + hf) * kKChunk +
+                                                     (32 * (q % kKB) + (lane & 31)) * 16);
+          },
+          [&](int q, const u32x4_t& ka) { sacc[q % kKB] = mfma32(ka, qb[0][q / kKB], sacc[q % kKB]); });
     };
     auto mask32 = [&](STile& sacc, int kt) {
 #pragma unroll
@@ -519,18 +581,27 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
     };
     // O^T += V^T P^T with V from stage vst.  A operand of step k, d block db: row
     // 32db + lane % 32 and the same keys as P^T's slots, two runs of 4 keys.
+    // operand q: 16-key step k = q / kAB, d block db = q % kAB, row 32 db + lane
+    // % 32.  The lane's 8 keys are the 16 bytes at 32 * slot + 16 hf of the row,
+    // slot = k ^ ((row / 16) % units) = k2 ^ hl with k2 = k ^ (2 (db & 1)) (4
+    // units) or k (2 units) and hl = (lane / 16) % 2.  32 (k2 ^ hl) is 32 k2 +
+    // 32 hl for even k2 and 32 k2 - 32 hl for odd k2, so each read is one of two
+    // per-lane bases plus an immediate offset.
+    const int vrow_lane = (lane & 31) * kVRow + 16 * hf;
+    const int vbase_even = vrow_lane + 32 * ((lane >> 4) & 1);
+    const int vbase_odd = vrow_lane - 32 * ((lane >> 4) & 1);
     auto pv32 = [&](const u32x4_t* pb, int vst) {
       if constexpr (kM32) {
         const char* vs = smem + vst * kStageBytes + kKBytes;
-#pragma unroll
-        for (int k = 0; k < 2 * kKB; ++k)
-#pragma unroll
-          for (int db = 0; db < kAB; ++db) {
-            const char* vrow = vs + (32 * db + (lane & 31)) * kVRow;
-            const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow + (16 * k + 4 * hf) * 2);
-            const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + (16 * k + 8 + 4 * hf) * 2);
-            acc[0][db] = mfma32(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pb[k], acc[0][db]);
-          }
+        pipelined(
+            std::integral_constant<int, 2 * kKB * kAB>{},
+            [&](int q) {
+              const int db = q % kAB;
+              const int k2 = (q / kAB) ^ (kUnits == 4 ? 2 * (db & 1) : 0);
+              return *reinterpret_cast<const u32x4_t*>(vs + 32 * db * kVRow + 32 * k2 +
+                                                       ((k2 & 1) ? vbase_odd : vbase_even));
+            },
+            [&](int q, const u32x4_t& va) { acc[0][q % kAB] = mfma32(va, pb[q / kAB], acc[0][q % kAB]); });
       }
     };
 
@@ -607,52 +678,116 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
       }
     };
 
-    // ---- tile pipeline: registers one tile ahead, two LDS stages -------------------
-    // Tile kt+1 is fetched into registers while tile kt is computed from its
-    // stage, then written to the other stage.  Each barrier separates the
-    // staging write of a stage from the computes that read it, before and
-    // after.
     __syncthreads();   // the previous item is done with both stages
-    // Registers one or two tiles ahead.  With two register sets (where they
-    // fit without spills: D <= 128 on 16- and 32-token blocks), tile kt+2 is
-    // fetched while tile kt is computed from its stage and tile kt+1, fetched a
-    // step earlier, is written to the other stage, so each load has two tiles
-    // of compute to arrive; with one set, tile kt+1 is fetched and staged in
-    // the step of tile kt.  Each barrier separates the staging write of a
-    // stage from the computes that read it, before and after.  The loop is
-    // unrolled by the two stages (tile kt is in stage (kt - kt0) & 1), so every
-    // LDS address is a base plus an immediate offset.
-    constexpr int kAhead = (D <= 128 && BS != 8) ? 2 : 1;
-    TileRegs<D, F8> rg0, rg1;
-    uint64_t ph_next = phys_of(kt0 + kAhead);
-    fetch(rg0, kt0, phys_of(kt0));
-    if constexpr (kAhead == 2) fetch(rg1, kt0 + 1, phys_of(kt0 + 1));
-    stage_write(rg0, kt0, 0);
-    __syncthreads();
-    auto step = [&](int kt, TileRegs<D, F8>& free_rg, TileRegs<D, F8>& next_rg, auto st) {
-      TileRegs<D, F8>& fetch_rg = kAhead == 2 ? free_rg : rg0;
-      TileRegs<D, F8>& stage_rg = kAhead == 2 ? next_rg : rg0;
-      fetch(fetch_rg, kt + kAhead, ph_next);
-      ph_next = phys_of(kt + kAhead + 1);
-      compute(kt, st);
-      if (kt + 1 < kt1) stage_write(stage_rg, kt + 1, st ^ 1);
+    if constexpr (W == 8) {
+      // ---- two groups of four waves taking turns on the matrix cores -----------------
+      // Group g (waves 4g .. 4g+3) runs phase t - g in tick t: phase 2i is the
+      // products of tile i (P.V of tile i-1, then Q.K^T of tile i) and phase
+      // 2i+1 its softmax (mask, max, rescale, P), so in every tick one wave per
+      // SIMD feeds the matrix cores while the other does its vector work.  Every
+      // tick ends at a barrier, and every wave runs the same 2T + 2 ticks.  The
+      // two groups share the staged tiles: at the end of tick 2j group 0 writes
+      // K of tile j+1 (wave w: unit w) and group 1 V of tile j (wave 4+w: unit
+      // w), tile i in stage i & 1.  Phase 2i reads K of tile i and V of tile
+      // i-1, in ticks 2i and 2i+1, and nothing writes those stage halves then.
+      // A wave issues the loads of its next share right after writing one, two
+      // ticks before they are written.  Each wave computes the same pairs with
+      // the same arithmetic as a wave of the one-tile-at-a-time loop below.
+      static_assert(W != 8 || kM32, "8-wave items need 32 pairs per wave");
+      const int grp = wave >> 2;
+      const int T = kt1 - kt0;
+      Raw r[kNK];
+      f32x16_t sacc[kKB];
+      u32x4_t pb[2 * kKB];
+      // phase 2i: the products of tile i (i = 0 .. T)
+      auto gemm = [&](int i) {
+        if (i >= 1) pv32(pb, (i - 1) & 1);
+        if (i < T) qk32(sacc, i & 1);
+      };
+      // phase 2i+1: the softmax of tile i
+      auto valu = [&](int i) {
+        if (needs_mask(kt0 + i)) mask32(sacc, kt0 + i);
+        rescale(0, max32(sacc));
+        probs32(sacc, pb);
+      };
+      // Both groups run one loop body; group 1 enters it one tick late (its
+      // idle first tick writes V of tile 0) and skips the loop's last barrier,
+      // so every wave passes the same 2T + 3 barriers.
+      const bool kpart = grp == 0;
+      const char* pbase = kpart ? kbase : vbase;
+      load_part(r, kt0, phys_of(kt0), pbase, kpart);
+      if (kpart) {
+        write_k(r, kt0, 0);
+        load_part(r, kt0 + 1, phys_of(kt0 + 1), kbase, true);
+      }
+      uint64_t ph_next = phys_of(kt0 + (kpart ? 2 : 1));
       __syncthreads();
-    };
-    if constexpr (D == 256 && BS == 8) {
-      // not unrolled: the unrolled loop needs more registers than this shape has
-      for (int kt = kt0; kt < kt1; ++kt) {
-        const int st = (kt - kt0) & 1;
-        fetch(rg0, kt + 1, ph_next);
-        ph_next = phys_of(kt + 2);
-        compute(kt, st);
-        if (kt + 1 < kt1) stage_write(rg0, kt + 1, st ^ 1);
+      if (!kpart) {   // tick 0 of group 1
+        write_v(r, kt0, 0);
+        load_part(r, kt0 + 1, ph_next, vbase, false);
+        ph_next = phys_of(kt0 + 2);
         __syncthreads();
       }
+      for (int j = 0; j <= T; ++j) {
+        gemm(j);   // tick 2j (group 0), 2j + 1 (group 1)
+        if (kpart) {
+          write_k(r, kt0 + j + 1, (j + 1) & 1);
+          load_part(r, kt0 + j + 2, ph_next, kbase, true);
+          ph_next = phys_of(kt0 + j + 3);
+        }
+        __syncthreads();
+        if (j < T) {
+          valu(j);   // tick 2j + 1 (group 0), 2j + 2 (group 1)
+          if (!kpart) {
+            write_v(r, kt0 + j + 1, (j + 1) & 1);
+            load_part(r, kt0 + j + 2, ph_next, vbase, false);
+            ph_next = phys_of(kt0 + j + 3);
+          }
+        }
+        if (kpart || j < T) __syncthreads();
+      }
     } else {
-      for (int kt = kt0; kt < kt1; kt += 2) {
-        step(kt, rg0, rg1, std::integral_constant<int, 0>{});
-        if (kt + 1 >= kt1) break;
-        step(kt + 1, rg1, rg0, std::integral_constant<int, 1>{});
+      // Registers one or two tiles ahead.  With two register sets (where they
+      // fit without spills: D <= 128 on 16- and 32-token blocks), tile kt+2 is
+      // fetched while tile kt is computed from its stage and tile kt+1, fetched a
+      // step earlier, is written to the other stage, so each load has two tiles
+      // of compute to arrive; with one set, tile kt+1 is fetched and staged in
+      // the step of tile kt.  Each barrier separates the staging write of a
+      // stage from the computes that read it, before and after.  The loop is
+      // unrolled by the two stages (tile kt is in stage (kt - kt0) & 1), so every
+      // LDS address is a base plus an immediate offset.
+      constexpr int kAhead = (D <= 128 && BS != 8) ? 2 : 1;
+      TileRegs<D, F8> rg0, rg1;
+      uint64_t ph_next = phys_of(kt0 + kAhead);
+      fetch(rg0, kt0, phys_of(kt0));
+      if constexpr (kAhead == 2) fetch(rg1, kt0 + 1, phys_of(kt0 + 1));
+      stage_write(rg0, kt0, 0);
+      __syncthreads();
+      auto step = [&](int kt, TileRegs<D, F8>& free_rg, TileRegs<D, F8>& next_rg, auto st) {
+        TileRegs<D, F8>& fetch_rg = kAhead == 2 ? free_rg : rg0;
+        TileRegs<D, F8>& stage_rg = kAhead == 2 ? next_rg : rg0;
+        fetch(fetch_rg, kt + kAhead, ph_next);
+        ph_next = phys_of(kt + kAhead + 1);
+        compute(kt, st);
+        if (kt + 1 < kt1) stage_write(stage_rg, kt + 1, st ^ 1);
+        __syncthreads();
+      };
+      if constexpr (D == 256 && BS == 8) {
+        // not unrolled: the unrolled loop needs more registers than this shape has
+        for (int kt = kt0; kt < kt1; ++kt) {
+          const int st = (kt - kt0) & 1;
+          fetch(rg0, kt + 1, ph_next);
+          ph_next = phys_of(kt + 2);
+          compute(kt, st);
+          if (kt + 1 < kt1) stage_write(rg0, kt + 1, st ^ 1);
+          __syncthreads();
+        }
+      } else {
+        for (int kt = kt0; kt < kt1; kt += 2) {
+          step(kt, rg0, rg1, std::integral_constant<int, 0>{});
+          if (kt + 1 >= kt1) break;
+          step(kt + 1, rg1, rg0, std::integral_constant<int, 1>{});
+        }
       }
     }
 
@@ -783,13 +918,18 @@ hipError_t launch_b(int group, const PrefillArgs& a, hipStream_t stream) {
   }
 }
 
-// W waves of 16 * kMB pairs each: 128 / 64 pairs per item (32 per wave), or
-// 64 / 32 at D = 256 (16 per wave)
+// W waves of 16 * kMB pairs each: 256 / 64 pairs per entry (32 per wave), or
+// 64 / 32 at D = 256 (16 per wave).  A 256-pair entry is one 8-wave item, or
+// beside the decode kernel two 4-wave items.
 template <int D, bool F8>
 hipError_t launch_d(int group, const PrefillArgs& a, hipStream_t stream) {
   const int per_wave = D == 256 ? 16 : 32;
   if (a.tile_pairs == 2 * per_wave) return launch_b<2, D, F8>(group, a, stream);
   if (a.tile_pairs == 4 * per_wave) return launch_b<4, D, F8>(group, a, stream);
+  if constexpr (D != 256) {
+    if (a.tile_pairs == 8 * per_wave)
+      return a.claim_items ? launch_b<4, D, F8>(group, a, stream) : launch_b<8, D, F8>(group, a, stream);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -810,8 +950,8 @@ hipError_t launch_prefill(int head_dim, int group, bool fp8_cache, const Prefill
 }
 
 int prefill_tile_pairs(int head_dim, bool short_rows) {
-  const int full = head_dim == 256 ? 64 : 128;
-  return short_rows ? full / 2 : full;
+  if (head_dim == 256) return short_rows ? 32 : 64;
+  return short_rows ? 64 : 256;
 }
 
 }  // namespace pa

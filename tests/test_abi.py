@@ -95,8 +95,8 @@ def _params(**over):
     (dict(sliding_window=-1), -2),
     # 32768 partitions: the kernels pack a request's partition count as count << 16 in an int
     (dict(partition_size=16, max_seq_len=32768 * 16, max_blocks_per_seq=32768), -2),
-    # 65536 prefill row tiles of one request (16 rows per tile at G = 4... 8): the tile index takes 16 bits
-    (dict(max_query_len=65536 * 32, max_seq_len=65536 * 32, max_blocks_per_seq=65536 * 2), -2),
+    # 65536 prefill row tiles of one request (64 rows per 256-pair tile at G = 4): the tile index takes 16 bits
+    (dict(max_query_len=65536 * 64, max_seq_len=65536 * 64, max_blocks_per_seq=65536 * 4), -2),
 ])
 def test_host_rejects_bad_params_before_any_launch(L, over, code):
     p = _params(**over)

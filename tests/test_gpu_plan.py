@@ -36,22 +36,24 @@ def _gpu():
     yield
 
 
-def _run_and_read(c, partition_size):
+def _run_and_read(c, partition_size, num_decode_rows=0):
     dc = DeviceCase(c)
     dc.cache_write()
     p = pa.make_params(dc.q, dc.k_cache, dc.cu, dc.tables, c.num_kv_heads, float(c.scale), c.max_query_len,
-                       c.max_seq_len, out=dc.out, partition_size=partition_size)
+                       c.max_seq_len, out=dc.out, partition_size=partition_size, num_decode_rows=num_decode_rows)
     need = pa.workspace_size(p)
     ps = pa.partition_size(p)
     ws = torch.full((need // 4,), -7, dtype=torch.int32, device="cuda:0")
     pa.attention_varlen(dc.out, dc.q, dc.k_cache, dc.v_cache, dc.cu, dc.seq_lens, dc.tables, float(c.scale),
-                        c.max_query_len, c.max_seq_len, workspace=ws, partition_size=partition_size)
+                        c.max_query_len, c.max_seq_len, workspace=ws, partition_size=partition_size,
+                        num_decode_rows=num_decode_rows)
     torch.cuda.synchronize()
     return ws.cpu().numpy(), ps
 
 
+@pytest.mark.parametrize("hint", [0, 1])
 @pytest.mark.parametrize("partition_size", [0, 256])
-def test_work_lists(partition_size):
+def test_work_lists(partition_size, hint):
     rng = np.random.default_rng(11)
     B = 300
     n = np.ones(B, np.int64)
@@ -59,12 +61,14 @@ def test_work_lists(partition_size):
     L = np.maximum(n, rng.integers(1, 3000, B))
     Hq, Hkv = 16, 4
     c = build_case("plan", 3, "bf16", Hq, Hkv, 128, n, L, poison=False)
-    w, P = _run_and_read(c, partition_size)
+    w, P = _run_and_read(c, partition_size, int((n == 1).sum()) if hint else 0)
     say("partition", P)
     G = Hq // Hkv
     parts_max = -(-c.max_seq_len // P)
     dec_cap = B * parts_max
-    rows = 128 // G
+    # prefill row tiles of 256 (row, head) pairs at D = 128, with or without
+    # the decode-row hint (beside the decode kernel each is two items)
+    rows = 256 // G
     pref_cap = B * -(-c.max_query_len // rows)
     pref_off = HEADER + 4 * dec_cap
     merge_off = pref_off + 4 * pref_cap
