@@ -507,7 +507,7 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
     // group of operands are issued, then the products of the current group,
     // and scheduling barriers keep the compiler from sinking the reads back
     // next to their use.  The 4-wave loops leave the schedule to the compiler.
-    constexpr int kReadAhead = W == 8 ? 4 : 0;
+    constexpr int kReadAhead = W == 8 ? 2 : 0;   // 2: 202.7 us alone on the mixed step's chunks, 1: 206.4, 4: 209.6
     auto pipelined = [&](auto nops, auto read, auto product) {
       constexpr int N = decltype(nops)::value;
       if constexpr (kReadAhead == 0) {
