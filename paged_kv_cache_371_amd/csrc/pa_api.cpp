@@ -31,12 +31,15 @@ inline bool block_size_ok(int32_t bs) { return bs == 8 || bs == 16 || bs == 32; 
 // then a request's result depends only on the request itself (bitwise the
 // same in any batch).  The default (0) picks, for the fast decode kernel, the
 // largest of 2048 / 1024 / 512 tokens that still gives every wave of the
-// persistent grid about 2 work items by the host's upper bound
+// persistent grid 4 work items by the host's upper bound
 // B * Hkv * S * ceil(max_seq_len / P) (S: work items per KV head, 1 unless a
 // KV head has more query heads than one item holds): long partitions cost less per token (one
-// merge per partition), but too few of them leave waves idle.  (With 8 items
-// a wave the MHA decode layer took 512-token partitions: 203.2 us against
-// 196.5 with 2048; the mixed chunked-prefill step 495.6 against 493.6.)
+// merge per partition), but too few of them leave waves idle.  The bound
+// counts every request at the longest length, so it overstates the items of
+// batches with short requests.  Measured on one MI355X: the MHA decode layer
+// (contexts 128..2048) takes 1024 with 4 items a wave, 191.7 us against 199.7
+// with 2048 (2 a wave) and 203.2 with 512 (8 a wave); the GQA decode layer,
+// the mixed chunked-prefill step and the other workloads keep 2048.
 inline int effective_partition(const pa_attn_params* p) {
   if (p->partition_size > 0) return p->partition_size;
   const int g = p->num_kv_heads > 0 ? p->num_q_heads / p->num_kv_heads : 0;
@@ -47,7 +50,7 @@ inline int effective_partition(const pa_attn_params* p) {
   // kernel, whose per-workgroup scores of one partition must fit its LDS.
   const bool generic_rows =
       p->max_query_len > 1 && !(dt == 1 && pa::prefill_supported(p->head_dim, g, p->block_size));
-  const int64_t want = int64_t(2) * pa::decode_gqa_workers(g);
+  const int64_t want = int64_t(4) * pa::decode_gqa_workers(g);
   for (int ps : {2048, 1024}) {
     const int64_t items = int64_t(p->num_seqs) * p->num_kv_heads * pa::decode_gqa_head_split(p->head_dim, g) *
                           ((int64_t(p->max_seq_len) + ps - 1) / ps);
