@@ -8,19 +8,22 @@
 // are dense contractions and run on the matrix cores
 // (v_mfma_f32_32x32x16_bf16, or 16x16x32 at D = 256; fp32 accumulation).
 //
-// Work item: (request, KV head, tile of 128 -- or, for batches of short
-// requests, 64 -- (query row, head) pairs), the pairs packed as m = row * G +
-// head over the G query heads of the KV head.  Four (or two) waves own 32
-// pairs each, 16 at D = 256.  A short request whose context spans
-// several partitions is one item per partition (its key tiles only), and
-// leaves unnormalised partials and (max, sum) for the merge kernel.  Keys are
-// visited in tiles of 64 (four paged blocks; wave w fetches block w of the tile, so
-// every load has a wave-uniform base).  Tiles are fetched into registers one
-// ahead and written to one of two LDS stages: K as 16-byte d-chunks, chunk
-// major (the MFMA reads of one chunk are contiguous), V transposed (V^T,
-// d-major, rows padded to 136 bytes) by a 4 x 8 register transpose.  Both
-// layouts make the staging writes and the MFMA operand reads bank-conflict
-// free.
+// Work list entry: (request, KV head, tile of 256 -- or, for batches of short
+// requests, 64 -- (query row, head) pairs; 64 and 32 at D = 256), the pairs
+// packed as m = row * G + head over the G query heads of the KV head.  Every
+// wave owns 32 pairs (16 at D = 256).  Alone on the GPU an 8-wave workgroup
+// serves a 256-pair entry, its two groups of four waves taking turns on the
+// matrix cores; beside the decode kernel two 4-wave items serve it (an 8-wave
+// workgroup does not fit on a CU beside a decode workgroup).  A short request
+// whose context spans several partitions is one entry per partition (its key
+// tiles only), and leaves unnormalised partials and (max, sum) for the merge
+// kernel.  Keys are visited in tiles of 64 (four 16-key units of paged
+// blocks; every load of a wave has a wave-uniform base), staged through two
+// LDS stages: K as 16-byte d-chunks, chunk major (the MFMA reads of one chunk
+// are contiguous), V transposed (V^T, d-major) by a 4 x 8 register transpose,
+// in a row layout that lets one 16-byte read feed a 32 x 32 x 16 operand.
+// The layouts keep the staging writes and the MFMA operand reads free of bank
+// conflicts.
 //
 // Per tile and wave: S^T = K Q^T (keys x pairs), so a lane holds scores of
 // one pair and the online softmax over keys is in-lane plus one permlane swap
@@ -163,9 +166,10 @@ struct TileRegs {
   }
 };
 
-// W = 4 for chunked prefill; W = 2 for batches whose multi-row requests are
-// short (speculative-decode verification), where a 128-pair tile would be
-// mostly empty and the LDS reads per tile, not HBM, would set the pace.
+// W = 8 for chunked prefill alone on the GPU, W = 4 beside the decode kernel
+// (and at D = 256); W = 2 for batches whose multi-row requests are short
+// (speculative-decode verification), where a larger tile would be mostly
+// empty and the LDS reads per tile, not HBM, would set the pace.
 template <int G, int W, int BS, int D, bool F8>
 __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefill_kernel(PrefillArgs a) {
   using S = Shape<W, D>;
