@@ -221,7 +221,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     });
   }
   __syncthreads();
-  if (tid == 0) a.plan[kPlanMergeCountInt] = s_merge;
+  if (tid == 0) {
+    a.plan[kPlanMergeCountInt] = s_merge;
+    // a list this call does not build is empty, with its counters at rest
+    if (!a.decode) {
+      a.plan[kPlanCountInt] = 0;
+      a.plan[kPlanClaimInt] = 0;
+      a.plan[kPlanDoneInt] = 0;
+    }
+    if (!a.prefill) {
+      a.plan[kPlanPrefCountInt] = 0;
+      a.plan[kPlanPrefClaimInt] = 0;
+      a.plan[kPlanPrefDoneInt] = 0;
+    }
+  }
 }
 
 }  // namespace
