@@ -34,7 +34,9 @@ in the L2s or the Infinity Cache; the run stage is also timed back to back
 (``attention_run_ms_unflushed``), and ``--no-flush-cache`` drops the flushed
 timing.  For workloads with multi-row requests, ``prefill_kernel`` times the
 call over those requests alone and reports the prefill kernel's TFLOP/s
-against the bf16 matrix-core peak.  ``--block-size 8|32`` builds the same workload on 8- or
+against the bf16 matrix-core peak, and ``roofline.combined`` sets the run
+stage against the step's HBM time and matrix-core time at peak: the larger of
+the two (perfect overlap) and their sum (none).  ``--block-size 8|32`` builds the same workload on 8- or
 32-token blocks.  ``--sliding-window W`` runs the workload with a sliding
 window of W tokens (KV bytes then count only the keys in some row's window).  ``--op copy_blocks`` times copy-on-write block copies
 (pa_copy_blocks) and ``--op swap_out`` / ``--op swap_in`` time swapping a
@@ -838,6 +840,20 @@ def main() -> None:
             "attention_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 3),
         },
     }
+    if c.max_query_len > 1:
+        # A step with multi-row requests against its two bounds: the larger of
+        # its HBM time and its matrix-core time (both overlapped perfectly), and
+        # their sum (nothing overlapped).
+        bytes_ms = ab["attention"] / (HBM_PEAK_GBS * 1e9) * 1e3
+        flops_ms = flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) * 1e3
+        result["roofline"]["combined"] = {
+            "hbm_ms": round(bytes_ms, 5),
+            "mfma_ms": round(flops_ms, 5),
+            "max_bound_ms": round(max(bytes_ms, flops_ms), 5),
+            "frac_of_max_bound": round(max(bytes_ms, flops_ms) / run_ms, 4),
+            "sum_bound_ms": round(bytes_ms + flops_ms, 5),
+            "frac_of_sum_bound": round((bytes_ms + flops_ms) / run_ms, 4),
+        }
     if prefill is not None:
         result["prefill_kernel"] = prefill
     if not args.no_cpu_baseline:
