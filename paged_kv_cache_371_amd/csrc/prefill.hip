@@ -471,9 +471,12 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
     // (the same value in every lane that holds the pair).  The reference max is
     // raised only when the tile's max exceeds it by more than kRescaleThreshold
     // (log2 units); otherwise p <= 2^8 is used as is.  Exact: the normalisation
-    // uses the same reference.
+    // uses the same reference.  The wave rescales when any of its valid pairs
+    // asks; pairs past the item's last row (zero queries, written nowhere) take
+    // no part, so a pair's bits depend only on the valid pairs beside it and not
+    // on how far the item's tile range reaches below the window of its rows.
     auto rescale = [&](int mb, float tmax) {
-      if (__builtin_amdgcn_ballot_w64(tmax > mrun[mb] + kRescaleThreshold)) {
+      if (__builtin_amdgcn_ballot_w64(mvalid[mb] && tmax > mrun[mb] + kRescaleThreshold)) {
         const float mnew = fmaxf(mrun[mb], tmax);
         const float alpha = fast_exp2(mrun[mb] - mnew);
         mrun[mb] = mnew;

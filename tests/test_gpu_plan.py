@@ -229,14 +229,38 @@ def test_plan_once_run_many_layers_bitwise(kind):
 
 
 @pytest.mark.parametrize("case", ["mixed", "mixed_fp8", "mixed_d64", "mixed_d256", "mixed_bs8", "mixed_g16",
-                                  "prefill_only_wrong_hint", "short_rows"])
+                                  "prefill_only_wrong_hint", "short_rows", "window_ragged_tile"])
 def test_decode_hint_changes_no_bits(case):
     """num_decode_rows only schedules: with it the decode and prefill kernels
     of a mixed batch run side by side (prefill items claimed), without it one
     after the other (prefill items dealt statically); the outputs are the same
-    bits, also when the hint is wrong (no single-row request at all)."""
+    bits, also when the hint is wrong (no single-row request at all).
+
+    window_ragged_tile: a sliding window with requests whose last row tile is
+    partly empty (101 and 89 rows at 4 heads per KV head); the 8-wave item and
+    the two 4-wave halves of it start at different tiles below the window, and
+    the empty pairs must not move the rescale of the valid ones."""
     rng = np.random.default_rng(31)
     D, Hq, Hkv, bs, B = 128, 32, 8, 16, 96
+    kw = {}
+    if case == "window_ragged_tile":
+        n = np.array([89, 1, 1, 1, 1, 1, 1, 144, 101, 1, 230, 1], np.int64)
+        L = np.array([2840, 658, 1, 1754, 1420, 2445, 1, 576, 1236, 3000, 900, 77], np.int64)
+        c = build_case("hint_window", 33, "bf16", 4, 1, 128, n, L, poison=False, block_size=8)
+        dc = DeviceCase(c)
+        outs = []
+        for h in (0, int((n == 1).sum()), 0):
+            o = torch.empty_like(dc.q)
+            pa.attention_varlen(o, dc.q, dc.k_cache, dc.v_cache, dc.cu, dc.seq_lens, dc.tables, float(c.scale),
+                                c.max_query_len, c.max_seq_len, partition_size=96, sliding_window=132,
+                                num_decode_rows=h)
+            outs.append(o)
+        torch.cuda.synchronize()
+        say(f"{case}: rows {n.tolist()}, window 132, partition 96")
+        for o in outs[1:]:
+            assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+        assert bool(torch.isfinite(outs[0].float()).all())
+        return
     if case == "mixed_d64":
         D = 64
     elif case == "mixed_d256":
@@ -255,7 +279,6 @@ def test_decode_hint_changes_no_bits(case):
     L = np.maximum(n, rng.integers(1, 4000, B))
     c = build_case(f"hint_{case}", 32, "bf16", Hq, Hkv, D, n, L, poison=False, block_size=bs)
     dc = DeviceCase(c)
-    kw = {}
     if case == "mixed_fp8":
         g = torch.Generator(device="cuda:0").manual_seed(3)
         dc.k_cache = torch.randint(0, 0x77, dc.k_cache.shape, generator=g, device="cuda:0", dtype=torch.uint8)
