@@ -73,11 +73,30 @@ def test_random_shape_large_groups(seed):
     _check(seed, _draw(seed, large_groups=True))
 
 
+@pytest.mark.parametrize("seed", range(1000, 1200))
+def test_random_shape_sweep(seed):
+    """A wider sweep of the same draw: every fourth case with large groups, and
+    in every third no single-row request at all, so the MFMA prefill kernel
+    runs alone (its 8-wave workgroups) and not beside the decode kernel."""
+    s = _draw(seed, large_groups=(seed % 4 == 3))
+    if seed % 3 == 0:
+        s["n"] = np.maximum(s["n"], 2)
+        s["L"] = np.maximum(s["L"], s["n"])
+    _check(seed, s)
+
+
 def _check(seed, s):
     c = build_case(f"rand{seed}", 300 + seed, s["dtype"], s["G"] * s["Hkv"], s["Hkv"], s["D"], s["n"], s["L"],
                    block_size=s["bs"])
     say(f"seed {seed}: {s['dtype']} D={s['D']} G={s['G']} Hkv={s['Hkv']} bs={s['bs']} B={len(s['n'])} "
         f"max n={int(s['n'].max())} max L={int(s['L'].max())} window={s['window']} psize={s['psize']}")
-    mx, mean, ok, _ = run_and_compare(c, partition_size=s["psize"], sliding_window=s["window"])
+    mx, mean, ok, dc = run_and_compare(c, partition_size=s["psize"], sliding_window=s["window"])
     say(f"  max {mx:.3g} mean {mean:.3g}")
     assert ok, (mx, mean)
+    # The count of single-row requests only schedules the kernels: without it
+    # the result is the same bits.
+    hinted = dc.out.clone()
+    dc.attention(s["psize"], sliding_window=s["window"], decode_hint=False)
+    torch.cuda.synchronize()
+    bits = torch.int16 if c.dtype == "bf16" else torch.int32
+    assert torch.equal(hinted.view(bits), dc.out.view(bits)), "the decode-row count changed bits"
