@@ -269,3 +269,44 @@ def test_fp8_multirow_needs_a_built_group():
     with pytest.raises(pa.PAError) as e:
         fc.write_and_attend(0)
     assert e.value.status == -3
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_random_shape_fp8(seed):
+    """The random-shape draw of the bf16 sweep (head dims, groups, block sizes,
+    decode, chunked and short multi-row requests, windows, explicit partitions)
+    on 8-bit pools at three scale pairs: the cache write bit for bit, the
+    attention against the oracle, and the same bits without the count of
+    single-row requests."""
+    from tests.test_gpu_random_shapes import _draw
+
+    s = _draw(seed, large_groups=(seed % 4 == 3))
+    if seed % 3 == 0:
+        s["n"] = np.maximum(s["n"], 2)
+        s["L"] = np.maximum(s["L"], s["n"])
+    c = build_case(f"f8rand{seed}", 500 + seed, "bf16", s["G"] * s["Hkv"], s["Hkv"], s["D"], s["n"], s["L"],
+                   block_size=s["bs"])
+    ks, vs = [(0.5, 0.25), (0.25, 0.125), (0.03, 0.07)][seed % 3]
+    say(f"fp8 seed {seed}: D={s['D']} G={s['G']} Hkv={s['Hkv']} bs={s['bs']} B={len(s['n'])} "
+        f"max n={int(s['n'].max())} window={s['window']} psize={s['psize']} scales {ks} {vs}")
+    fc = Fp8Case(c, 700 + seed, ks, vs)
+    pa.cache_write_fp8(fc.k_new, fc.v_new, fc.k_cache, fc.v_cache, fc.slots, ks, vs)
+    outs = []
+    for hint in (int((c.q_lens == 1).sum()), 0):
+        o = torch.empty_like(fc.q)
+        pa.attention_varlen(o, fc.q, fc.k_cache, fc.v_cache, fc.cu, fc.seq_lens, fc.tables, float(c.scale),
+                            c.max_query_len, c.max_seq_len, partition_size=s["psize"], sliding_window=s["window"],
+                            k_scale=ks, v_scale=vs, num_decode_rows=hint)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), "the decode-row count changed bits"
+    kp, vp = fc.oracle_pools()
+    assert np.array_equal(fc.k_cache.cpu().numpy(), kp), "K pool differs"
+    assert np.array_equal(fc.v_cache.cpu().numpy(), vp), "V pool differs"
+    want = oracle.oracle_attention_varlen(c.q, kp, vp, c.cu_seqlens, c.seq_lens, c.block_tables, c.scale,
+                                          c.num_kv_heads, "bf16", c.block_size, kv_dtype="fp8", k_scale=ks,
+                                          v_scale=vs, sliding_window=s["window"])
+    got = oracle.widen(to_host(outs[0], "bf16"), "bf16")
+    mx, mean, ok = oracle.compare_outputs(got, want, "bf16")
+    say(f"  max {mx:.3g} mean {mean:.3g}")
+    assert ok, (mx, mean)
