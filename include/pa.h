@@ -92,10 +92,12 @@ typedef struct {
   int32_t block_size;          /* tokens per physical block: 16 (the pages' default), 8 or 32.
                                   The fast single-row decode kernel (bf16 or 8-bit pools)
                                   takes D = 64, 128 and 256 with Hq/Hkv a power of two up
-                                  to 64, at all three block sizes; the
-                                  MFMA prefill kernel takes D = 64, 128 and 256 with
-                                  Hq/Hkv a power of two up to 64 at all three; every
-                                  other shape runs on the generic split-K kernel. */
+                                  to 64, and at D = 128 also Hq/Hkv = 3, 5 to 7 and 9 to
+                                  15, at all three block sizes; the MFMA prefill kernel
+                                  takes the same shapes; every other shape runs on the
+                                  generic split-K kernel (fp32, or bf16 with Hq/Hkv a
+                                  power of two up to 16), and the rest return
+                                  PA_ERR_UNSUPPORTED. */
   int64_t num_blocks;          /* physical blocks in each pool */
   int32_t max_blocks_per_seq;  /* row length of block_tables */
   int32_t max_query_len;       /* host bound: >= every n_b */
@@ -246,8 +248,8 @@ pa_status pa_cache_write_fp8(const void* k_new, const void* v_new, int64_t kv_ro
  * pa_attention_varlen_fp8 -- as pa_attention_varlen with 8-bit pools: the
  * attention runs over K = decode(k_cache) * k_scale and V = decode(v_cache) *
  * v_scale.  q and out are bf16 (p->dtype == PA_BF16); D = 64, 128 or 256 with
- * Hq/Hkv a power of two up to 64; block size 8, 16 or 32; other shapes return
- * PA_ERR_UNSUPPORTED.  Requests with one row run on the split-K decode kernel,
+ * Hq/Hkv a power of two up to 64, or at D = 128 also 3, 5 to 7 or 9 to 15;
+ * block size 8, 16 or 32; other shapes return PA_ERR_UNSUPPORTED.  Requests with one row run on the split-K decode kernel,
  * requests with more rows (chunked prefill, [Q67] §4.2) on the MFMA kernel,
  * which widens the codes to bf16 as it stages them.  Scales finite and > 0.
  * The workspace is sized by pa_attention_workspace_size(p).

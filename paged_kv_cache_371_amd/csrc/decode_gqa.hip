@@ -262,7 +262,8 @@ __device__ __forceinline__ float dot_bf16(const V& q, const V& k) {
 // single-row request, served by one wave.  All fields are wave-uniform.
 struct Item {
   int valid;
-  int b, hg, q0;   // hg: head group (query heads hg*G .. hg*G+G-1)
+  int b, hg, q0;   // hg: head group, the item's index among its request's items of one partition
+  int h0, gv;      // the item's query heads: h0 .. h0 + gv - 1 (gv < G: the rest are padding)
   int parts;     // partition index among the request's visible partitions (the partial
                  // slot) | their count << 16
   int lo;        // first visible key (sliding window), 0 without one
@@ -277,12 +278,15 @@ struct Item {
 
 
 // Item t of the list plan_kernel built: entry t / H, head group t % H of the
-// H = Hkv * 2^head_split_log2 groups of G query heads; the group's KV head is
-// its index >> head_split_log2.  An index past the list gives a placeholder with in-range
-// addresses and no tiles.  Every field goes through readfirstlane, so the descriptors and
-// table loads built from it stay scalar.
+// H = Hkv * 2^head_split_log2 groups of up to G query heads; the group's KV head is
+// its index >> head_split_log2.  A KV head's Hq / Hkv query heads are cut into
+// groups of G in order; where Hq / Hkv is not a multiple of G (a group that is
+// not a power of two) the last group of a KV head has fewer, and its other
+// head slots are padding (zero q, nothing written).  An index past the list
+// gives a placeholder with in-range addresses and no tiles.  Every field goes
+// through readfirstlane, so the descriptors and table loads built from it stay scalar.
 template <bool F8, int BS, int D>
-__device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t, int4 ent) {
+__device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t, int4 ent, int G) {
   constexpr int kRing = Kv<F8, D>::kRing;
   constexpr int kHeadBytes = BS * D * (F8 ? 1 : 2);   // one KV head's rows of a block
   Item it;
@@ -303,8 +307,12 @@ __device__ __forceinline__ Item make_item(const DecodeArgs& a, int total, int t,
   const int tok1 = min(part * P + P, L);
   const int lb0 = tok0 / kBlock;
   const int nb = it.valid ? (tok1 + kBlock - 1) / kBlock - lb0 : 0;
+  const int group = a.num_q_heads / a.num_kv_heads;   // query heads per KV head
+  const int hsub = hg & ((1 << a.head_split_log2) - 1);
   it.b = uni(b);
   it.hg = uni(hg);
+  it.h0 = uni((hg >> a.head_split_log2) * group + hsub * G);
+  it.gv = uni(min(G, group - hsub * G));
   it.parts = uni((part - p_lo) | (((L + P - 1) / P - p_lo) << 16));
   it.q0 = uni(q0);
   it.lo = uni(lo);
@@ -515,19 +523,25 @@ __global__ __launch_bounds__(64 * (WK + 1), 1) void decode_gqa_kernel(DecodeArgs
   constexpr int kQD = G * D / 2;                    // q dwords of an item: G rows of D bf16
   constexpr int kQDw = kQD >= 64 ? kQD / 64 : 1;    // per lane (lanes >= kQD idle when kQD < 64)
   __shared__ uint32_t sq[WK][64 * kQDw];
+  // (padding heads of the item read nothing and park zeros)
   auto fetch_q = [&](const Item& it, uint32_t(&qt)[kQDw]) {
     const uint32_t* src = reinterpret_cast<const uint32_t*>(
-        static_cast<const char*>(a.q) + (int64_t(it.q0) * a.q_row_stride + int64_t(it.hg) * G * D) * 2);
+        static_cast<const char*>(a.q) + (int64_t(it.q0) * a.q_row_stride + int64_t(it.h0) * D) * 2);
     if constexpr (kQDw >= 4) {
+      // a lane's dwords lie in one head's row (kQDw divides D / 2)
+      const bool live = lane * kQDw / (D / 2) < it.gv;
 #pragma unroll
       for (int c = 0; c < kQDw / 4; ++c) {
-        const u32x4_t v = reinterpret_cast<const u32x4_t*>(src)[lane * (kQDw / 4) + c];
+        const u32x4_t v = live ? reinterpret_cast<const u32x4_t*>(src)[lane * (kQDw / 4) + c] : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int w = 0; w < 4; ++w) qt[4 * c + w] = v[w];
       }
     } else {
 #pragma unroll
-      for (int c = 0; c < kQDw; ++c) qt[c] = lane * kQDw + c < kQD ? src[lane * kQDw + c] : 0u;
+      for (int c = 0; c < kQDw; ++c) {
+        const int i = lane * kQDw + c;
+        qt[c] = i < kQD && i / (D / 2) < it.gv ? src[i] : 0u;
+      }
     }
   };
   auto park_q = [&](const uint32_t(&qt)[kQDw]) {
@@ -543,7 +557,7 @@ __global__ __launch_bounds__(64 * (WK + 1), 1) void decode_gqa_kernel(DecodeArgs
     });
   };
 
-  Item cur = make_item<F8, BS, D>(a, total, item_of_round(0), entry0);
+  Item cur = make_item<F8, BS, D>(a, total, item_of_round(0), entry0, G);
   if (!cur.valid) {
     count_out();
     return;
@@ -564,11 +578,11 @@ __global__ __launch_bounds__(64 * (WK + 1), 1) void decode_gqa_kernel(DecodeArgs
   using VR = typename std::conditional<MF, typename std::conditional<F8, u32x2_t, u32x4_t>::type, Raw>::type;
   constexpr int kKR = MF ? kKLoads : 4;
   u32x4_t qmf[4];   // B operand of step st: head mrow's q at d mf_d0(st) .. +7, zero for padding heads
-  auto q_mf_from = [&](const char* rows) {   // rows: the item's G q rows of D bf16
+  auto q_mf_from = [&](const char* rows, int gv) {   // rows: the item's gv q rows of D bf16
 #pragma unroll
     for (int st = 0; st < 4; ++st)
-      qmf[st] = mrow < G ? *reinterpret_cast<const u32x4_t*>(rows + mrow * (D * 2) + mf_d0(st) * 2)
-                         : u32x4_t{0u, 0u, 0u, 0u};
+      qmf[st] = mrow < gv ? *reinterpret_cast<const u32x4_t*>(rows + mrow * (D * 2) + mf_d0(st) * 2)
+                          : u32x4_t{0u, 0u, 0u, 0u};
   };
 
   auto load_q = [&](Words(&qreg)[G], const Item& it) {   // q slices, lane-relative order h(r ^ M_j)
@@ -671,7 +685,7 @@ __global__ __launch_bounds__(64 * (WK + 1), 1) void decode_gqa_kernel(DecodeArgs
   KR kr[kRing][kKR];
   VR vr[kRing][4];
   if constexpr (MF)
-    q_mf_from(static_cast<const char*>(a.q) + (int64_t(cur.q0) * a.q_row_stride + int64_t(cur.hg) * G * D) * 2);
+    q_mf_from(static_cast<const char*>(a.q) + (int64_t(cur.q0) * a.q_row_stride + int64_t(cur.h0) * D) * 2, cur.gv);
   else
     load_q(qreg, cur);
   int64_t ph0[kRing];   // keys of the first tiles, all requested before any is used
@@ -692,7 +706,7 @@ __global__ __launch_bounds__(64 * (WK + 1), 1) void decode_gqa_kernel(DecodeArgs
     // second-to-last load group, just before its first block ids are needed,
     // so it is handed out as late as the tile stream allows.
     const bool dyn = i + 1 >= kStaticRounds;
-    Item nxt = make_item<F8, BS, D>(a, total, total, make_int4(0, 0, 0, 1));
+    Item nxt = make_item<F8, BS, D>(a, total, total, make_int4(0, 0, 0, 1), G);
     uint32_t qt[kQDw];
     bool requested = false;
     auto get_next = [&]() {
@@ -701,11 +715,11 @@ __global__ __launch_bounds__(64 * (WK + 1), 1) void decode_gqa_kernel(DecodeArgs
       int t;
       int4 e;
       take(t, e);
-      nxt = make_item<F8, BS, D>(a, total, t, e);
+      nxt = make_item<F8, BS, D>(a, total, t, e, G);
       if (nxt.valid) fetch_q(nxt, qt);
     };
     if (!dyn) {
-      nxt = make_item<F8, BS, D>(a, total, item_of_round(i + 1), static_entry(i + 1));
+      nxt = make_item<F8, BS, D>(a, total, item_of_round(i + 1), static_entry(i + 1), G);
       if (nxt.valid) fetch_q(nxt, qt);
     } else if (cur.nb <= 2 * kRing) {
       get_next();
@@ -922,14 +936,14 @@ __global__ __launch_bounds__(64 * (WK + 1), 1) void decode_gqa_kernel(DecodeArgs
       // ---- matrix-core form: normalise or leave partials -------------------------
       // m is already common to the lane groups of a head; the sum is not
       const float lw = rows_sum(l) * a.lsum_scale;   // every lane: sum of head mrow (carries 1 / v_scale)
-      if (nxt.valid) q_mf_from(reinterpret_cast<const char*>(&sq[wave][0]));   // parked in the last group
+      if (nxt.valid) q_mf_from(reinterpret_cast<const char*>(&sq[wave][0]), nxt.gv);   // parked in the last group
       const bool whole = (cur.parts >> 16) == 1;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {   // output row i: head 4 mg + i, d 8 mrow .. +7
         const int head = 4 * mg + i;
         const float Lh = __shfl(lw, head);
-        if (head < G) {
-          const int hq = cur.hg * G + head;
+        if (head < cur.gv) {
+          const int hq = cur.h0 + head;
           if (whole) {
             const float inv = 1.f / Lh;
             u32x4_t o;
@@ -945,8 +959,8 @@ __global__ __launch_bounds__(64 * (WK + 1), 1) void decode_gqa_kernel(DecodeArgs
           }
         }
       }
-      if (!whole && mg == 0 && mrow < G) {
-        const int64_t slot = (int64_t(cur.b) * a.num_q_heads + cur.hg * G + mrow) * a.max_parts + (cur.parts & 0xffff);
+      if (!whole && mg == 0 && mrow < cur.gv) {
+        const int64_t slot = (int64_t(cur.b) * a.num_q_heads + cur.h0 + mrow) * a.max_parts + (cur.parts & 0xffff);
         a.ws_ml[2 * slot] = m;
         a.ws_ml[2 * slot + 1] = lw;
       }
@@ -1041,21 +1055,29 @@ __global__ __launch_bounds__(64 * (WK + 1), 1) void decode_gqa_kernel(DecodeArgs
 // one KV head are adjacent in the list, so they are dealt to waves of one
 // workgroup and stream the same tiles at about the same time: the second
 // read of a tile is mostly served by L2.
+// A group that is not a power of two (D = 128 only) is served by items of the
+// next power of two, 8 at most, whose extra head slots are padding: 3 heads as
+// an item of 4, 5 to 7 as one of 8, 9 to 15 as two of 8.  The matrix-core tile
+// form pads its products to 16 heads anyway, so the padding costs no extra work.
 static int item_group(int head_dim, int group) {
   const int cap = head_dim == 256 ? 2 : 8;
-  return group < cap ? group : cap;
+  if (group >= cap) return cap;
+  int gi = 1;
+  while (gi < group) gi <<= 1;
+  return gi;
 }
 
 constexpr int kMaxGroup = 64;   // query heads per KV head served by this kernel, at most
 
 int decode_gqa_head_split(int head_dim, int group) {
   const int gi = item_group(head_dim, group);
-  return gi > 0 ? group / gi : 1;
+  return gi > 0 ? (group + gi - 1) / gi : 1;
 }
 
 bool decode_gqa_supported(int dtype, int head_dim, int group, int part_size, int block_size) {
   const bool pow2 = group >= 1 && group <= kMaxGroup && (group & (group - 1)) == 0;
-  return dtype == 1 && (head_dim == 64 || head_dim == 128 || head_dim == 256) && pow2 &&
+  const bool padded = head_dim == 128 && group >= 3 && group < 16;   // items with padding heads
+  return dtype == 1 && (head_dim == 64 || head_dim == 128 || head_dim == 256) && (pow2 || padded) &&
          (block_size == 8 || block_size == 16 || block_size == 32) && part_size % kBlock == 0 &&
          part_size / kBlock <= kMaxPartBuckets;
 }
@@ -1185,7 +1207,11 @@ hipError_t launch_decode_gqa(int group, int head_dim, bool fp8_cache, const Deco
                              bool beside_prefill) {
   const int gi = item_group(head_dim, group);
   const int split = decode_gqa_head_split(head_dim, group);
-  if (gi <= 0 || gi * split != group || group > kMaxGroup) return hipErrorInvalidValue;
+  // every item holds at least one head, and a KV head's items number a power of two
+  if (gi <= 0 || gi * split < group || gi * (split - 1) >= group || (split & (split - 1)) != 0 ||
+      group > kMaxGroup)
+    return hipErrorInvalidValue;
+  if (gi * split != group && !(head_dim == 128 && (gi == 4 || gi == 8))) return hipErrorInvalidValue;
   DecodeArgs b = a;
   b.head_split_log2 = 0;
   while ((1 << b.head_split_log2) < split) ++b.head_split_log2;

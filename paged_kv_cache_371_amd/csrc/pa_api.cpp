@@ -171,7 +171,8 @@ inline bool plan_fits(const pa_attn_params* p, const Plan& pl) {
     const int gp = pa::prefill_item_group(g);
     const int64_t rows = pl.tile_pairs / gp;
     if ((int64_t(p->max_query_len) + rows - 1) / rows > 65535) return false;
-    if (prefill_capacity(p, pl) * p->num_kv_heads * (g / gp) > INT32_MAX) return false;
+    // items: entries x KV heads x head groups, x 2 where 4-wave workgroups serve halves of entries
+    if (prefill_capacity(p, pl) * p->num_kv_heads * ((g + gp - 1) / gp) * 2 > INT32_MAX) return false;
   }
   return true;
 }

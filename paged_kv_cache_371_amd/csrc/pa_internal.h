@@ -162,7 +162,8 @@ hipError_t launch_merge_list(int head_dim, const DecodeArgs& a, hipStream_t stre
 size_t decode_lds_bytes(int dtype, int head_dim, int group, int part_size);
 
 // MFMA kernel for multi-row requests (bf16 q and out; bf16 or 8-bit pools; D = 64, 128 or 256; G a
-// power of two up to 64; blocks of 8, 16 or 32 tokens).
+// power of two up to 64, or at D = 128 also 3, 5 to 7 and 9 to 15 with padding head slots; blocks of
+// 8, 16 or 32 tokens).
 hipError_t launch_prefill(int head_dim, int group, bool fp8_cache, const PrefillArgs& a, hipStream_t stream);
 bool prefill_supported(int head_dim, int group, int block_size);
 // Query heads per prefill work item: the group, at most 8 (larger groups are

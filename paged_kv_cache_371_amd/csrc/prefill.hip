@@ -201,6 +201,7 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
   const int hkv = a.num_kv_heads;
   const int split_log2 = PA_KARG(head_split_log2);
   const int nh = hkv << split_log2;   // head groups of G query heads; group hg reads KV head hg >> split_log2
+  const int group = a.num_q_heads / hkv;   // query heads per KV head
   // A list entry holds tile_pairs pairs: one item, or (256-pair entries on
   // 4-wave workgroups) two items, its first and second half of rows.
   const int subs = PA_KARG(tile_pairs) > kPairs ? 2 : 1;
@@ -263,6 +264,12 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
     const int sub = t - e * nhs >= nh ? 1 : 0;
     const int hg = t - e * nhs - sub * nh;
     const int kvh = hg >> split_log2;
+    // The item's query heads h0 .. h0 + gv - 1: a KV head's heads cut into
+    // groups of G in order; where the group is not a power of two the last
+    // item of a KV head has fewer, and its other head slots are padding.
+    const int hsub = hg & ((1 << split_log2) - 1);
+    const int h0 = kvh * group + hsub * G;
+    const int gv = min(G, group - hsub * G);
     const int b = load_const(entries, 4 * int64_t(e));
     const int tile_part = load_const(entries, 4 * int64_t(e) + 1);
     const int q0 = load_const(entries, 4 * int64_t(e) + 2);
@@ -310,12 +317,13 @@ __global__ __launch_bounds__((Shape<W, D>::kThreads), kWavesPerSimd) void prefil
     for (int mb = 0; mb < kNP; ++mb) {
       const int m = kM32 ? wave * 32 + (lane & 31) : wave * (16 * kMB) + mb * 16 + lc;
       jrow[mb] = j0 + m / G;
-      hq[mb] = hg * G + m % G;
-      mvalid[mb] = jrow[mb] < j1;
+      hq[mb] = h0 + m % G;
+      mvalid[mb] = jrow[mb] < j1 && m % G < gv;   // a padding head slot is never valid
       lolim[mb] = mvalid[mb] ? window_start(P + jrow[mb], window) : 0;
       span[mb] = mvalid[mb] ? P + jrow[mb] - lolim[mb] : 0;
       const char* qrow = static_cast<const char*>(PA_KARG(q)) +
-                         (int64_t(q0 + (mvalid[mb] ? jrow[mb] : 0)) * PA_KARG(q_row_stride) + int64_t(hq[mb]) * D) * 2;
+                         (int64_t(q0 + (mvalid[mb] ? jrow[mb] : 0)) * PA_KARG(q_row_stride) +
+                          int64_t(mvalid[mb] ? hq[mb] : h0) * D) * 2;
 #pragma unroll
       for (int s = 0; s < kQSteps; ++s) {
         const int d0 = kM32 ? 16 * s + 8 * hf : 32 * s + 8 * h;
@@ -896,11 +904,20 @@ hipError_t launch_g(const PrefillArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-int prefill_item_group(int group) { return group < 8 ? group : 8; }
+// A group that is not a power of two (D = 128 only) takes items of the next
+// power of two, 8 at most, with padding head slots: 3 heads in items of 4, 5 to
+// 7 in items of 8, 9 to 15 in two items of 8.
+int prefill_item_group(int group) {
+  if (group >= 8) return 8;
+  int gi = 1;
+  while (gi < group) gi <<= 1;
+  return gi;
+}
 
 bool prefill_supported(int head_dim, int group, int block_size) {
   const bool pow2 = group >= 1 && group <= 64 && (group & (group - 1)) == 0;
-  return (head_dim == 64 || head_dim == 128 || head_dim == 256) && pow2 &&
+  const bool padded = head_dim == 128 && group >= 3 && group < 16;
+  return (head_dim == 64 || head_dim == 128 || head_dim == 256) && (pow2 || padded) &&
          (block_size == 8 || block_size == 16 || block_size == 32);
 }
 

@@ -176,13 +176,22 @@ def test_fp8_host_errors(L):
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(block_size=32)), 1.0, 1.0, None, 0, None) == -5
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(block_size=8, max_blocks_per_seq=8)), 1.0, 1.0, None, 0, None) == -5
     # D = 64 and 256 are served (the missing workspace is the error), D = 256 with G = 4 as two
-    # items of two heads per KV head; a group that is not a power of two is not
+    # items of two heads per KV head; a group that is not a power of two is served at D = 128
+    # (items with padding heads) and not at D = 64 or 256
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(head_dim=64, q_row_stride=512, o_row_stride=512)),
              1.0, 1.0, None, 0, None) == -5
     assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(head_dim=256, q_row_stride=2048, o_row_stride=2048)),
              1.0, 1.0, None, 0, None) == -5
-    assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(num_q_heads=6, q_row_stride=768, o_row_stride=768)),
-             1.0, 1.0, None, 0, None) == -3
+    for hq in (6, 10, 12, 14, 22, 30):   # G = 3, 5, 6, 7, 11, 15 over 2 KV heads
+        assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(num_q_heads=hq, q_row_stride=128 * hq,
+                                                                   o_row_stride=128 * hq)),
+                 1.0, 1.0, None, 0, None) == -5, hq
+        mr = _params(num_q_heads=hq, q_row_stride=128 * hq, o_row_stride=128 * hq, max_query_len=4)
+        assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(mr), 1.0, 1.0, None, 0, None) == -5, hq
+    for hq, d in ((34, 128), (6, 64), (10, 256)):   # G = 17 at D = 128; G = 3 at D = 64; G = 5 at D = 256
+        assert a(16, 16, 16, 16, 16, 16, 16, ctypes.byref(_params(num_q_heads=hq, head_dim=d, q_row_stride=d * hq,
+                                                                   o_row_stride=d * hq)),
+                 1.0, 1.0, None, 0, None) == -3, (hq, d)
 
 
 def test_noalloc_host_errors(L):

@@ -263,8 +263,8 @@ def test_mixed_config_fp8_every_row():
 
 def test_fp8_multirow_needs_a_built_group():
     """Multi-row requests on 8-bit pools run on the MFMA kernel only; a group
-    size it does not build (not a power of two) is refused."""
-    c = build_case("mr8", 34, "bf16", 12, 2, 128, [3, 1], [20, 30])
+    size it does not build (not a power of two, at D = 64) is refused."""
+    c = build_case("mr8", 34, "bf16", 6, 2, 64, [3, 1], [20, 30])
     fc = Fp8Case(c, 11, 1.0, 1.0)
     with pytest.raises(pa.PAError) as e:
         fc.write_and_attend(0)

@@ -299,9 +299,10 @@ def test_chunk_row_equals_decode_row():
         assert np.array_equal(one[0], out_chunk[j])
 
 
-def test_gqa_equals_mha_with_repeated_heads():
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (15, 3), (12, 2)])   # G = 4, 5 and 6
+def test_gqa_equals_mha_with_repeated_heads(Hq, Hkv):
     rng = np.random.default_rng(14)
-    Hq, Hkv, D = 8, 2, 8
+    D = 8
     seqs = [(1, 30), (4, 18)]
     K, V, Q = _tiny(rng, seqs, Hq, Hkv, D)
     out_gqa, _ = _run_oracle(K, V, Q, seqs, Hkv, np.float32(0.3), np.random.default_rng(1))
