@@ -585,6 +585,8 @@ __global__ __launch_bounds__(64 * (WK + 1), 1) void decode_gqa_kernel(DecodeArgs
                           : u32x4_t{0u, 0u, 0u, 0u};
   };
 
+  // The dot-product form serves groups that are powers of two only (padding
+  // head slots exist only in the matrix-core form), so there h0 = hg * G and gv = G.
   auto load_q = [&](Words(&qreg)[G], const Item& it) {   // q slices, lane-relative order h(r ^ M_j)
     const char* qrow =
         static_cast<const char*>(a.q) + (int64_t(it.q0) * a.q_row_stride + int64_t(it.hg) * G * D) * 2;
