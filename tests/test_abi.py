@@ -83,6 +83,8 @@ def _params(**over):
     (dict(dtype=7), -3),
     (dict(num_q_heads=6, num_kv_heads=4), -2),
     (dict(num_q_heads=48, num_kv_heads=2, q_row_stride=6144, o_row_stride=6144), -3),  # G=24 not built
+    (dict(num_q_heads=10, num_kv_heads=2, head_dim=64, q_row_stride=640, o_row_stride=640), -3),  # G=5 at D=64
+    (dict(num_q_heads=10, num_kv_heads=2, head_dim=128, dtype=pa.PA_F32, q_row_stride=1280, o_row_stride=1280), -3),  # fp32
     (dict(max_blocks_per_seq=3), -2),               # 3 * 16 < max_seq_len
     (dict(q_row_stride=100), -2),
     (dict(q_row_stride=1028), -4),                  # 2056 bytes: not 16-byte aligned
