@@ -95,8 +95,8 @@ typedef struct {
                                   to 64, and at D = 128 also Hq/Hkv = 3, 5 to 7 and 9 to
                                   15, at all three block sizes; the MFMA prefill kernel
                                   takes the same shapes; every other shape runs on the
-                                  generic split-K kernel (fp32, or bf16 with Hq/Hkv a
-                                  power of two up to 16), and the rest return
+                                  generic split-K kernel (fp32, or bf16 at D = 64 and
+                                  256, with Hq/Hkv up to 8 or 16), and the rest return
                                   PA_ERR_UNSUPPORTED. */
   int64_t num_blocks;          /* physical blocks in each pool */
   int32_t max_blocks_per_seq;  /* row length of block_tables */

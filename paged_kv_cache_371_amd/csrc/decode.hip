@@ -512,7 +512,11 @@ static hipError_t dispatch_group(int group, const DecodeArgs& a, int64_t partial
   switch (group) {
     case 1: return launch_one<E, D, 1>(a, partial_rows, stream);
     case 2: return launch_one<E, D, 2>(a, partial_rows, stream);
+    case 3: return launch_one<E, D, 3>(a, partial_rows, stream);
     case 4: return launch_one<E, D, 4>(a, partial_rows, stream);
+    case 5: return launch_one<E, D, 5>(a, partial_rows, stream);
+    case 6: return launch_one<E, D, 6>(a, partial_rows, stream);
+    case 7: return launch_one<E, D, 7>(a, partial_rows, stream);
     case 8: return launch_one<E, D, 8>(a, partial_rows, stream);
     case 16: return launch_one<E, D, 16>(a, partial_rows, stream);
     default: return hipErrorInvalidValue;
@@ -522,7 +526,9 @@ static hipError_t dispatch_group(int group, const DecodeArgs& a, int64_t partial
 bool decode_supported(int dtype, int head_dim, int group, int part_size) {
   if (dtype != 0 && dtype != 1) return false;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return false;
-  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16) return false;
+  // every group of up to 8 query heads per KV head (the kernel uses G only as a
+  // count: one workgroup serves all G heads of a KV head), and 16
+  if (!((group >= 1 && group <= 8) || group == 16)) return false;
   if (part_size < 16 || part_size > 8192 || part_size % 16) return false;
   return decode_lds_bytes(dtype, head_dim, group, part_size) <= kGenericLdsMax;
 }

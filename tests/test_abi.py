@@ -83,8 +83,8 @@ def _params(**over):
     (dict(dtype=7), -3),
     (dict(num_q_heads=6, num_kv_heads=4), -2),
     (dict(num_q_heads=48, num_kv_heads=2, q_row_stride=6144, o_row_stride=6144), -3),  # G=24 not built
-    (dict(num_q_heads=10, num_kv_heads=2, head_dim=64, q_row_stride=640, o_row_stride=640), -3),  # G=5 at D=64
-    (dict(num_q_heads=10, num_kv_heads=2, head_dim=128, dtype=pa.PA_F32, q_row_stride=1280, o_row_stride=1280), -3),  # fp32
+    (dict(num_q_heads=18, num_kv_heads=2, head_dim=64, q_row_stride=1152, o_row_stride=1152), -3),  # G=9 at D=64
+    (dict(num_q_heads=24, num_kv_heads=2, head_dim=128, dtype=pa.PA_F32, q_row_stride=3072, o_row_stride=3072), -3),  # fp32, G=12
     (dict(max_blocks_per_seq=3), -2),               # 3 * 16 < max_seq_len
     (dict(q_row_stride=100), -2),
     (dict(q_row_stride=1028), -4),                  # 2056 bytes: not 16-byte aligned
@@ -213,3 +213,21 @@ def test_validate_host_errors(L):
     p = _params()
     assert L.pa_validate_metadata(16, 16, 16, None, 0, ctypes.byref(p), None, None) == -1
     assert L.pa_validate_metadata(None, 16, 16, None, 0, ctypes.byref(p), 16, None) == -1
+
+
+def test_every_group_up_to_8_is_served(L):
+    """Every group of up to 8 query heads per KV head is served at every head dim
+    and dtype (the sizing query returns a workspace), the fast kernels' padded
+    groups at D = 128 up to 15; larger groups that are not a power of two are not."""
+    bf16, f32 = pa.PA_BF16, pa.PA_F32
+    for hq, d, dt, mq in ((10, 64, bf16, 1), (14, 256, bf16, 4), (10, 128, f32, 4), (6, 128, bf16, 4),
+                          (30, 128, bf16, 4), (12, 64, f32, 1)):
+        # contexts up to 4096 tokens: several partitions, so even the generic kernel needs a workspace
+        p = _params(num_q_heads=hq, head_dim=d, dtype=dt, q_row_stride=d * hq, o_row_stride=d * hq, max_query_len=mq,
+                    max_seq_len=4096, max_blocks_per_seq=256, partition_size=512)
+        assert L.pa_attention_workspace_size(ctypes.byref(p)) > 0, (hq, d, dt)
+        assert L.pa_attention_varlen(16, 16, 16, 16, 16, 16, 16, ctypes.byref(p), None, 0, None) == -5, (hq, d, dt)
+    p = _params(num_q_heads=22, head_dim=64, q_row_stride=64 * 22, o_row_stride=64 * 22, max_seq_len=4096,
+                max_blocks_per_seq=256, partition_size=512)   # G = 11 at D = 64
+    assert L.pa_attention_workspace_size(ctypes.byref(p)) == 0
+    assert L.pa_attention_varlen(16, 16, 16, 16, 16, 16, 16, ctypes.byref(p), None, 0, None) == -3

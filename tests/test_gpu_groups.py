@@ -105,3 +105,20 @@ def test_padded_group_last_head_of_last_row():
     torch.cuda.synchronize()
     assert torch.equal(view.view(torch.int16), dc.out.view(torch.int16))
     assert bool((out[-1] == 0x7FC0).all()), "a row past the batch was written"
+
+
+@pytest.mark.parametrize("dtype,D,G", [("f32", 128, 5), ("f32", 64, 3), ("bf16", 64, 6), ("bf16", 256, 7),
+                                       ("f32", 256, 5)])
+def test_generic_kernel_groups(dtype, D, G):
+    """Shapes the fast kernels do not build (fp32; bf16 at D = 64 and 256 with a
+    group that is not a power of two) run on the generic split-K kernel, which
+    takes every group of up to 8 heads: decode rows and chunked prefill rows,
+    default and explicit partitions."""
+    Hkv = 2
+    n, L = _mixed(G, Hkv, 150 + G + D)
+    n, L = n[:10], L[:10]
+    c = build_case(f"grpgen_{dtype}{D}_{G}", 160 + G, dtype, G * Hkv, Hkv, D, n, L)
+    for psize in (0, 128):
+        mx, mean, ok, dc = run_and_compare(c, partition_size=psize, check_pool=psize == 0)
+        say(f"generic {dtype} D={D} G={G} psize {psize}: max {mx:.3g} mean {mean:.3g}")
+        assert ok, (psize, mx, mean)
