@@ -122,3 +122,31 @@ def test_generic_kernel_groups(dtype, D, G):
         mx, mean, ok, dc = run_and_compare(c, partition_size=psize, check_pool=psize == 0)
         say(f"generic {dtype} D={D} G={G} psize {psize}: max {mx:.3g} mean {mean:.3g}")
         assert ok, (psize, mx, mean)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_shape_padded_groups(seed):
+    """The random-shape draw (request mixes, windows, partitions, block sizes) with
+    a group of 3, 5, 6, 7, 10, 12 or 15 heads at D = 128, bf16 pools: against the
+    oracle, the pools bit-exact, and the same bits without the decode-row hint."""
+    from tests.test_gpu_random_shapes import _draw
+
+    s = _draw(seed)
+    rng = np.random.default_rng(50000 + seed)
+    G = int(rng.choice([3, 5, 6, 7, 10, 12, 15]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    n, L = s["n"], s["L"]
+    if seed % 3 == 0:   # no single-row request: the prefill kernel runs alone
+        n = np.maximum(n, 2)
+        L = np.maximum(L, n)
+    while int((n * L).sum()) * G * Hkv * 128 > 3e8:   # the oracle's work, about a second
+        big = int(np.argmax(n * L))
+        if n[big] > 2:
+            n[big] = max(2, n[big] // 2)
+        L[big] = max(int(n[big]), int(L[big]) // 2)
+    c = build_case(f"grprand{seed}", 900 + seed, "bf16", G * Hkv, Hkv, 128, n, L, block_size=s["bs"])
+    say(f"seed {seed}: G={G} Hkv={Hkv} bs={s['bs']} B={len(n)} max n={int(n.max())} window={s['window']} "
+        f"psize={s['psize']}")
+    mx, mean, ok, dc = run_and_compare(c, partition_size=s["psize"], sliding_window=s["window"])
+    assert ok, (mx, mean)
+    _no_hint_same(c, dc, s["psize"], s["window"])
