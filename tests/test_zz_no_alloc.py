@@ -64,6 +64,14 @@ def test_noalloc_fp32_generic_path():
     _check(c)
 
 
+def test_noalloc_padded_group():
+    """A group of 5 query heads per KV head (items with padding head slots):
+    decode rows and a prefill chunk, default and 256-token partitions."""
+    c = build_case("noalloc_g5", 9, "bf16", 40, 8, 128, [1, 90, 1, 1], [2600, 700, 33, 1900])
+    _check(c)
+    _check(c, 256)
+
+
 def test_noalloc_rejects_beyond_scratch():
     """A batch whose workspace exceeds the scratch is refused before any launch."""
     c = build_case("noalloc_tiny", 8, "bf16", 64, 8, 128, [1], [64])
